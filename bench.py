@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the host-built slot
+mapping is already resident (fixed device buffer), the scatter writes the
+step's new K/V through it, and paged decode attention reads every sequence's
+context through its block table.  Inputs are seeded synthetic data resident
+in HBM before timing starts.
+
+Default workload: Llama-3-8B-shaped decode layer (64 sequences, 32 query /
+8 KV heads, head_dim 128, block 16, context lengths U[512, 4096], block tables
+from a shuffled free list over a pool of 1.25x the blocks needed, bf16).
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention achieved HBM GB/s (% of peak) + decode tokens/sec/layer"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+KERNEL_SOURCES = ["paged_kv_cache_num_amd/csrc/decode.hip", "paged_kv_cache_num_amd/csrc/device_common.hpp"]
+
+WORKLOADS = {
+    "C1": "tiny fp32 paged decode: 4 sequences, lengths {17,33,100,200}, 8 query / 2 KV heads, head_dim 64, block 16, 64-block pool",
+    "C2": "Llama-3-8B-shaped decode layer: 64 sequences, 32 query / 8 KV heads, head_dim 128, block 16, lengths U[512,4096], shuffled free-list tables, pool 1.25x, bf16",
+    "C3": "70B-class GQA decode layer: 256 sequences, 64 query / 8 KV heads, head_dim 128, block 16, lognormal lengths (median 1024, sigma 1, clip [16,8192]), permuted blocks, plus a 2048-token prefill-chunk scatter, bf16",
+    "C4": "prefix-sharing decode: 128 sequences sharing 128 blocks (2048-token prefix) plus private suffixes U[64,512], 32 query / 8 KV heads, head_dim 128, bf16",
+    "C5": "long-context split decode: 8 sequences, lengths U[32768,131072], 32 query / 8 KV heads, head_dim 128, partitions of 512 tokens, fragmented pool, bf16",
+}
+DEFAULT_PARTITION = {"C1": 0, "C2": 512, "C3": 512, "C4": 512, "C5": 512}
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def algorithmic_bytes(wl):
+    """Bytes the step must move at minimum.
+
+    attention: every distinct (physical block, token) K and V row once, plus q
+    in and the output out, plus the table entries and lengths read;
+    scatter: new K/V rows read and written, plus the slot mapping.
+    Split-partition partial states are not counted.
+    """
+    import numpy as np
+    B, Hkv, D, e = wl.block_size, wl.num_kv_heads, wl.head_dim, wl.elem_bytes
+    row = 2 * Hkv * D * e                      # K and V of one token, all KV heads
+    used = {}
+    for i, L in enumerate(wl.context_lens):
+        L = int(L)
+        nb = -(-L // B)
+        for b in range(nb):
+            phys = int(wl.block_tables[i, b])
+            tokens = min(B, L - b * B)
+            used[phys] = max(used.get(phys, 0), tokens)
+    kv_unique = sum(used.values()) * row
+    kv_logical = int(np.sum(wl.context_lens)) * row
+    nblk = int(sum(-(-int(L) // B) for L in wl.context_lens))
+    qo = 2 * wl.num_seqs * wl.num_q_heads * D * e
+    attn = kv_unique + qo + 4 * nblk + 4 * wl.num_seqs
+    T = wl.num_write_tokens
+    scatter = 2 * T * row + 8 * T
+    return dict(attn=attn, attn_logical=kv_logical + qo + 4 * nblk + 4 * wl.num_seqs, scatter=scatter,
+                kv_unique=kv_unique, kv_logical=kv_logical, blocks=nblk)
+
+
+def traffic_for(config: str, partition: int):
+    """HBM bytes per decode launch from committed counter runs, or None if stale/absent."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(f"{config}/p{partition}")
+    if not entry or entry.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return entry.get("traffic_bytes_per_launch")
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return float("nan")
+    k = (len(xs) - 1) * q
+    lo, hi = int(math.floor(k)), int(math.ceil(k))
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def cpu_baseline(wl, bytes_total):
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.run_step(wl, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(bytes_total / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"the whole {wl.name} step (all {wl.num_seqs} sequences): slot mapping, scatter and fp64 attention",
+            "tokens_per_s_per_layer": round(wl.num_seqs / dt, 3)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="C2", choices=sorted(WORKLOADS))
+    ap.add_argument("--partition", type=int, default=None, help="tokens per partition (0 = single pass)")
+    ap.add_argument("--variant", default="spec")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing pass")
+    ap.add_argument("--probe-copy-mib", type=int, default=0,
+                    help="also run the copy probe once on buffers of this size (counter calibration)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the hot path on one GPU only; --gpus must be 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import kvgen
+    from paged_kv_cache_num_amd import DecodeStep, probe_copy
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    part = DEFAULT_PARTITION[args.config] if args.partition is None else args.partition
+
+    print(f"bench: generating {args.config} ({args.variant})", file=sys.stderr, flush=True)
+    wl = kvgen.make_workload(args.config, variant=args.variant)
+    nbytes = algorithmic_bytes(wl)
+    step = DecodeStep.from_workload(wl, partition_size=part)
+    torch.cuda.synchronize()
+
+    if args.probe_copy_mib:
+        n = args.probe_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        probe_copy(dst, src)      # first touch
+        e0.record()
+        probe_copy(dst, src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_us = e0.elapsed_time(e1) * 1e3
+        print(f"bench: copy probe {args.probe_copy_mib} MiB: {copy_us:.1f} us, "
+              f"{2 * n / copy_us / 1e3:.1f} GB/s (read+write)", file=sys.stderr, flush=True)
+        del src, dst
+
+    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, events on the stream the kernels run on
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        a, b, c = ev[i]
+        a.record()
+        step.scatter()
+        b.record()
+        step.attend()
+        c.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    scatter_us = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(K)]
+    attn_us = [ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(K)]
+    print(f"bench: timed {K} steps, {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    attn_mean = sum(attn_us) / K
+    achieved = nbytes["attn"] / (attn_mean * 1e-6) / 1e9
+    step_bytes = nbytes["attn"] + nbytes["scatter"]
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    cold = None
+    if not args.no_cold:
+        # evict L2 and the 256 MB MALL before every attention call (outside its events)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold_us = []
+        for _ in range(min(K, 30)):
+            flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step.attend()
+            b.record()
+            b.synchronize()
+            cold_us.append(a.elapsed_time(b) * 1e3)
+        del flush
+        cm = sum(cold_us) / len(cold_us)
+        cold = {"attn_us_mean": round(cm, 2), "attn_us_p50": round(percentile(cold_us, 0.5), 2),
+                "achieved_gbps": round(nbytes["attn"] / (cm * 1e-6) / 1e9, 1),
+                "frac": round(nbytes["attn"] / (cm * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    traffic = traffic_for(args.config, part)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config, "variant": args.variant,
+                   "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "block_size": wl.block_size, "partition_size": part,
+                   "context_tokens": int(np.sum(wl.context_lens)), "scatter_tokens": wl.num_write_tokens,
+                   "seed": wl.info.get("seed")},
+        "tokens_per_s_per_layer": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes["attn"],
+                     "launch_us_mean": round(attn_mean, 2), "launch_us_p10": round(percentile(attn_us, 0.1), 2),
+                     "launch_us_p50": round(percentile(attn_us, 0.5), 2),
+                     "launch_us_p90": round(percentile(attn_us, 0.9), 2)},
+        "scatter_us_mean": round(sum(scatter_us) / K, 2),
+        "step_bytes": step_bytes,
+        "cold": cold,
+        "pool_utilization": round(float(wl.info.get("utilization") or 0.0), 4),
+        "blocks_per_seq_mean": round(nbytes["blocks"] / max(1, wl.num_seqs), 2),
+        "internal_waste_tokens": int(nbytes["blocks"] * wl.block_size - int(np.sum(wl.context_lens))),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, step_bytes)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

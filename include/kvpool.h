@@ -1,0 +1,201 @@
+/*
+ * kvpool.h - C ABI of the MI355X (gfx950) paged KV-cache hot path.
+ *
+ * Two device steps and the host step that feeds them:
+ *   - kv_build_slot_mapping   (host)  turns each sequence's block table and the
+ *                                     positions written this step into one
+ *                                     linear slot per token;
+ *   - reshape_and_cache       (GPU)   scatters the new tokens' K and V into the
+ *                                     block pool through that slot mapping;
+ *   - paged_attention_decode  (GPU)   one query token per sequence attends over
+ *                                     its whole context, reading K and V through
+ *                                     the sequence's block table (grouped-query
+ *                                     attention, online softmax, optional split
+ *                                     of the context into partitions merged by
+ *                                     a second kernel).
+ *
+ * Sources (page title, section):
+ *   [KVC] aicassindra.com "GPU paged KV cache":
+ *         "Fixed-size blocks and the block-table indirection" (blocks of B
+ *         tokens, table entry i names the physical block of tokens
+ *         [i*B, (i+1)*B), one 32-bit index per block);
+ *         "Sizing the pool" (pool preallocated once, one K and one V tensor per
+ *         layer; per-token cost 2 * kv_heads * head_dim * bytes per layer);
+ *         "The write path: slot mapping and scatter" (one integer per token,
+ *         block_index * B + offset, built on the host each step; tables at a
+ *         fixed address, updated in place, for graph replay; head_dim
+ *         innermost and contiguous);
+ *         "Inside the paged attention kernel" (per (sequence, KV head) walk of
+ *         logical blocks through the table, online softmax, split of long
+ *         contexts over several workgroups merged by a cheap reduction).
+ *   [PIF] "PagedAttention, Internals First", "02 Block tables" (token t in
+ *         logical block t / B at offset t % B; each KV head serves its group of
+ *         query heads).
+ *   [TMP] aicassindra.com transformer-math "paged attention", "End-to-end
+ *         flow" (the step attends over the full history including the token
+ *         written this step).
+ *
+ * Conventions for every call:
+ *   - Device pointers are borrowed: the caller allocates them and keeps them
+ *     alive until the work queued on `stream` has finished.  The library never
+ *     allocates device memory and never synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is queued and the call returns; results are ordered by the stream.
+ *   - Host-checkable argument errors return a negative kv_status before any
+ *     launch; kv_last_error_message() then holds a readable detail (per thread).
+ *   - Device-side data (slot mappings, tables, lengths) is trusted but bounded:
+ *     kernels never read or write outside the pool, the tables or the outputs
+ *     whatever those values are; values that break the preconditions give an
+ *     unspecified result for the tokens or sequences concerned.
+ *
+ * Pool layout, per layer, for both the K and the V tensor:
+ *     [num_blocks][num_kv_heads][block_size][head_dim]      (head_dim innermost)
+ * and layers follow each other: layer l starts at base + l * (bytes of one layer).
+ * One (block, KV head) tile is block_size * head_dim contiguous elements.
+ */
+#ifndef KVPOOL_H
+#define KVPOOL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kv_status {
+    KV_OK = 0,
+    KV_ERR_INVALID_ARGUMENT = -1,   /* null or misaligned pointer, bad size, bad index */
+    KV_ERR_UNSUPPORTED = -2,        /* valid but not built: dtype, head_dim, block size, group size */
+    KV_ERR_WORKSPACE_TOO_SMALL = -3,
+    KV_ERR_HIP = -4,                /* the HIP runtime reported an error at launch */
+    KV_ERR_OUT_OF_RANGE = -5        /* host-side table entry or position outside the pool or the table */
+} kv_status;
+
+typedef enum kv_dtype {
+    KV_F32 = 0,    /* IEEE binary32 */
+    KV_BF16 = 1    /* bfloat16 (upper half of binary32); fp32 accumulation, round-to-nearest-even stores */
+} kv_dtype;
+
+typedef struct kv_pool_desc {
+    int32_t num_layers;     /* >= 1 */
+    int32_t num_blocks;     /* physical blocks per layer, >= 1 */
+    int32_t block_size;     /* tokens per block (B); the kernels are built for 16 */
+    int32_t num_kv_heads;   /* KV heads per layer */
+    int32_t head_dim;       /* elements per head row; the kernels are built for 64 and 128 */
+    int32_t dtype;          /* kv_dtype of the pool, of q, of k_new/v_new and of the output */
+} kv_pool_desc;
+
+/* Opaque host-side handle: the descriptor and the two base pointers.  Immutable
+ * after creation, so one handle may be used from several threads at once. */
+typedef struct kv_pool* kv_pool_t;
+
+/*
+ * Bytes of ONE of the two pool tensors (K or V), all layers:
+ *     num_layers * num_blocks * block_size * num_kv_heads * head_dim * elem_bytes
+ * [KVC "Sizing the pool"].  Pure arithmetic: accepts any positive sizes, also
+ * ones the kernels are not built for.  Errors: KV_ERR_INVALID_ARGUMENT for a
+ * null pointer, a non-positive size, an unknown dtype or a 64-bit overflow.
+ */
+kv_status kv_pool_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tensor);
+
+/*
+ * Wrap two caller-allocated device buffers of kv_pool_bytes() bytes each as a
+ * pool.  No device memory is allocated or touched.  k_base and v_base must be
+ * 16-byte aligned.  Errors: KV_ERR_INVALID_ARGUMENT (null, misaligned, bad
+ * descriptor), KV_ERR_UNSUPPORTED (block_size != 16, head_dim not 64 or 128).
+ */
+kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, kv_pool_t* out);
+
+/* Free the handle (not the buffers).  NULL is accepted. */
+kv_status kv_pool_destroy(kv_pool_t pool);
+
+/*
+ * Host step [KVC "The write path"; PIF "02 Block tables"]: for each request r
+ * and each logical position p in [write_start[r], write_start[r] + write_count[r]),
+ * in request order, emit
+ *     slot = block_tables[write_seq[r]][p / B] * B + p % B.
+ * All pointers are HOST pointers.  block_tables is int32 [num_rows][max_blocks_per_seq],
+ * row-major.  On success *num_tokens holds the number of slots written to
+ * slot_mapping (capacity entries available).  Errors: KV_ERR_INVALID_ARGUMENT
+ * (null pointer, negative count or start, row outside [0, num_rows), capacity
+ * too small), KV_ERR_OUT_OF_RANGE (p / B >= max_blocks_per_seq, or a table
+ * entry outside [0, num_blocks)).  Nothing is written past the first error.
+ */
+kv_status kv_build_slot_mapping(const int32_t* block_tables, int32_t num_rows,
+                                int32_t max_blocks_per_seq, int32_t block_size, int32_t num_blocks,
+                                const int32_t* write_seq, const int32_t* write_start,
+                                const int32_t* write_count, int32_t num_requests,
+                                int64_t* slot_mapping, int64_t capacity, int64_t* num_tokens);
+
+/*
+ * GPU step [KVC "The write path: slot mapping and scatter"]: for every token t
+ * with 0 <= slot_mapping[t] < num_blocks * B, copy the bits of k_new[t][h][:]
+ * and v_new[t][h][:] to row (slot / B, h, slot % B) of layer `layer` of the K
+ * and V pools, for every KV head h.  Tokens with a negative slot (padding) or a
+ * slot past the pool are skipped.  A bit-exact copy.
+ *   k_new, v_new:   device, [num_tokens][num_kv_heads][head_dim], pool dtype, 16-byte aligned
+ *   slot_mapping:   device, int64 [num_tokens]
+ * Precondition: non-negative slots are unique (two tokens for one slot race).
+ * num_tokens == 0 queues nothing.  Errors: KV_ERR_INVALID_ARGUMENT (null
+ * handle or pointer, misalignment, layer out of range, num_tokens < 0),
+ * KV_ERR_HIP.
+ */
+kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_tokens, void* stream);
+
+/*
+ * Workspace needed by paged_attention_decode for this shape: 0 when
+ * partition_size is 0 (single pass) or when one partition covers
+ * max_context_len; otherwise
+ *     num_seqs * num_q_heads * ceil(max_context_len / partition_size) * (head_dim + 2) * 4
+ * bytes (fp32 running max, sum and unnormalised output per partition).
+ * Errors: KV_ERR_INVALID_ARGUMENT (null, negative sizes, partition_size not a
+ * multiple of the block size).
+ */
+kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t max_context_len, int32_t partition_size,
+                                          uint64_t* bytes);
+
+/*
+ * GPU step [KVC "Inside the paged attention kernel"; PIF "02 Block tables";
+ * TMP "End-to-end flow"]: for every sequence i and query head h, with
+ * g = num_q_heads / num_kv_heads and kv = h / g,
+ *     out[i][h][:] = sum_j softmax_j(scale * q[i][h] . K_i[j]) V_i[j],
+ * j over the first L_i = context_lens[i] logical tokens of sequence i, where
+ * K_i[j] / V_i[j] are row (block_tables[i][j / B], kv, j % B) of layer `layer`.
+ * L_i counts the token written this step.  L_i == 0 gives a zero output.
+ *   out, q:        device, [num_seqs][num_q_heads][head_dim], pool dtype, 16-byte aligned
+ *   block_tables:  device, int32 [num_seqs][max_blocks_per_seq]; entries at
+ *                  b >= ceil(L_i / B) are never read
+ *   context_lens:  device, int32 [num_seqs], each in [0, max_context_len]
+ *   max_context_len: host bound on every L_i (sizes the grid); <= max_blocks_per_seq * B
+ *   partition_size: 0 = one workgroup per (sequence, KV head) walks the whole
+ *                  context; otherwise a multiple of B: the context is cut into
+ *                  partitions of that many tokens, each handled by its own
+ *                  workgroup, and a second kernel merges them (log-sum-exp).
+ *   workspace:     device, >= paged_attention_workspace_bytes(...) bytes, 16-byte
+ *                  aligned; may be NULL when that size is 0.  Its contents on
+ *                  entry do not matter.
+ * Results do not depend on where blocks live: two tables naming different
+ * physical blocks with the same contents give bitwise equal outputs.
+ * Errors: KV_ERR_INVALID_ARGUMENT, KV_ERR_UNSUPPORTED (group size not in
+ * {1, 2, 4, 8}), KV_ERR_WORKSPACE_TOO_SMALL, KV_ERR_HIP.
+ */
+kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const void* q,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 float scale, int32_t max_context_len, int32_t partition_size,
+                                 void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Static name of a status code ("KV_OK", ...); never NULL. */
+const char* kv_status_string(kv_status status);
+
+/* Detail of the last failed call on this thread ("" if none); valid until the
+ * next call on this thread. */
+const char* kv_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPOOL_H */

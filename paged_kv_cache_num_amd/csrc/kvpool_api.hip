@@ -1,0 +1,292 @@
+// C ABI of the paged KV-cache hot path: argument checks, launch set-up, errors.
+// The operations themselves are described in include/kvpool.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "kvpool.h"
+#include "launch.hpp"
+
+struct kv_pool {
+    kv_pool_desc desc;
+    char* k_base;
+    char* v_base;
+    uint64_t layer_bytes;   // bytes of one layer of one tensor
+    int32_t elem_bytes;
+};
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kv_status fail(kv_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+kv_status ok() {
+    g_last_error[0] = '\0';
+    return KV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes_of(int32_t dtype) { return dtype == KV_F32 ? 4 : (dtype == KV_BF16 ? 2 : 0); }
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
+    if (a != 0 && b > UINT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+kv_status check_desc(const kv_pool_desc* d) {
+    if (!d) return fail(KV_ERR_INVALID_ARGUMENT, "descriptor is NULL");
+    if (d->num_layers <= 0 || d->num_blocks <= 0 || d->block_size <= 0 || d->num_kv_heads <= 0 ||
+        d->head_dim <= 0)
+        return fail(KV_ERR_INVALID_ARGUMENT,
+                    "descriptor sizes must be positive (layers %d, blocks %d, block_size %d, kv_heads %d, head_dim %d)",
+                    d->num_layers, d->num_blocks, d->block_size, d->num_kv_heads, d->head_dim);
+    if (elem_bytes_of(d->dtype) == 0) return fail(KV_ERR_INVALID_ARGUMENT, "unknown dtype %d", d->dtype);
+    return KV_OK;
+}
+
+kv_status hip_fail(hipError_t e, const char* what) {
+    return fail(KV_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// Partition geometry shared by the workspace query and the launch.
+struct PartGeo {
+    int32_t part_tokens;
+    int32_t max_parts;
+};
+
+PartGeo part_geo(int32_t max_context_len, int32_t partition_size, int32_t block_size) {
+    PartGeo g;
+    if (partition_size == 0 || partition_size >= max_context_len) {
+        int32_t whole = (int32_t)round_up((uint64_t)(max_context_len > 0 ? max_context_len : 1), (uint64_t)block_size);
+        g.part_tokens = partition_size > whole ? partition_size : whole;
+        g.max_parts = 1;
+    } else {
+        g.part_tokens = partition_size;
+        g.max_parts = (max_context_len + partition_size - 1) / partition_size;
+    }
+    return g;
+}
+
+// Workspace split: (m, l) pairs first, then the fp32 partial outputs at a 256-byte boundary.
+void workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_parts, int32_t head_dim,
+                      uint64_t* ml_bytes, uint64_t* total) {
+    const uint64_t entries = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)max_parts;
+    *ml_bytes = round_up(entries * 8u, 256u);
+    *total = *ml_bytes + entries * (uint64_t)head_dim * 4u;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv_status_string(kv_status status) {
+    switch (status) {
+        case KV_OK: return "KV_OK";
+        case KV_ERR_INVALID_ARGUMENT: return "KV_ERR_INVALID_ARGUMENT";
+        case KV_ERR_UNSUPPORTED: return "KV_ERR_UNSUPPORTED";
+        case KV_ERR_WORKSPACE_TOO_SMALL: return "KV_ERR_WORKSPACE_TOO_SMALL";
+        case KV_ERR_HIP: return "KV_ERR_HIP";
+        case KV_ERR_OUT_OF_RANGE: return "KV_ERR_OUT_OF_RANGE";
+    }
+    return "KV_ERR_UNKNOWN";
+}
+
+const char* kv_last_error_message(void) { return g_last_error; }
+
+kv_status kv_pool_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tensor) {
+    if (!bytes_per_tensor) return fail(KV_ERR_INVALID_ARGUMENT, "bytes_per_tensor is NULL");
+    kv_status s = check_desc(desc);
+    if (s != KV_OK) return s;
+    uint64_t v = (uint64_t)elem_bytes_of(desc->dtype);
+    if (!mul_ok(v, (uint64_t)desc->head_dim, &v) || !mul_ok(v, (uint64_t)desc->num_kv_heads, &v) ||
+        !mul_ok(v, (uint64_t)desc->block_size, &v) || !mul_ok(v, (uint64_t)desc->num_blocks, &v) ||
+        !mul_ok(v, (uint64_t)desc->num_layers, &v))
+        return fail(KV_ERR_INVALID_ARGUMENT, "pool size overflows 64 bits");
+    *bytes_per_tensor = v;
+    return ok();
+}
+
+kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, kv_pool_t* out) {
+    if (!out) return fail(KV_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    uint64_t total = 0;
+    kv_status s = kv_pool_bytes(desc, &total);
+    if (s != KV_OK) return s;
+    if (!k_base || !v_base) return fail(KV_ERR_INVALID_ARGUMENT, "pool base pointer is NULL");
+    if (!aligned16(k_base) || !aligned16(v_base)) return fail(KV_ERR_INVALID_ARGUMENT, "pool base pointers must be 16-byte aligned");
+    if (desc->block_size != kvp::kBlockTokens)
+        return fail(KV_ERR_UNSUPPORTED, "block_size %d: kernels are built for %d", desc->block_size, kvp::kBlockTokens);
+    if (desc->head_dim != 64 && desc->head_dim != 128)
+        return fail(KV_ERR_UNSUPPORTED, "head_dim %d: kernels are built for 64 and 128", desc->head_dim);
+    kv_pool* p = new (std::nothrow) kv_pool;
+    if (!p) return fail(KV_ERR_INVALID_ARGUMENT, "out of host memory");
+    p->desc = *desc;
+    p->k_base = static_cast<char*>(k_base);
+    p->v_base = static_cast<char*>(v_base);
+    p->layer_bytes = total / (uint64_t)desc->num_layers;
+    p->elem_bytes = elem_bytes_of(desc->dtype);
+    *out = p;
+    return ok();
+}
+
+kv_status kv_pool_destroy(kv_pool_t pool) {
+    delete pool;
+    return ok();
+}
+
+kv_status kv_build_slot_mapping(const int32_t* block_tables, int32_t num_rows, int32_t max_blocks_per_seq,
+                                int32_t block_size, int32_t num_blocks, const int32_t* write_seq,
+                                const int32_t* write_start, const int32_t* write_count, int32_t num_requests,
+                                int64_t* slot_mapping, int64_t capacity, int64_t* num_tokens) {
+    if (!num_tokens) return fail(KV_ERR_INVALID_ARGUMENT, "num_tokens is NULL");
+    *num_tokens = 0;
+    if (num_requests < 0 || num_rows < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0 || capacity < 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "negative or zero size argument");
+    if (num_requests > 0 && (!block_tables || !write_seq || !write_start || !write_count || (!slot_mapping && capacity > 0)))
+        return fail(KV_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    int64_t n = 0;
+    for (int32_t r = 0; r < num_requests; ++r) {
+        const int32_t row = write_seq[r];
+        if (row < 0 || row >= num_rows) return fail(KV_ERR_INVALID_ARGUMENT, "request %d names row %d of %d", r, row, num_rows);
+        if (write_start[r] < 0 || write_count[r] < 0)
+            return fail(KV_ERR_INVALID_ARGUMENT, "request %d has negative start or count", r);
+        const int32_t* trow = block_tables + (int64_t)row * max_blocks_per_seq;
+        for (int64_t p = write_start[r], e = (int64_t)write_start[r] + write_count[r]; p < e; ++p) {
+            const int64_t lb = p / block_size;
+            if (lb >= max_blocks_per_seq)
+                return fail(KV_ERR_OUT_OF_RANGE, "request %d position %lld is past its %d-entry table row", r,
+                            (long long)p, max_blocks_per_seq);
+            const int32_t phys = trow[lb];
+            if (phys < 0 || phys >= num_blocks)
+                return fail(KV_ERR_OUT_OF_RANGE, "row %d entry %lld = %d is outside the %d-block pool", row,
+                            (long long)lb, phys, num_blocks);
+            if (n >= capacity) return fail(KV_ERR_INVALID_ARGUMENT, "slot_mapping capacity %lld too small", (long long)capacity);
+            slot_mapping[n++] = (int64_t)phys * block_size + (p - lb * block_size);
+        }
+    }
+    *num_tokens = n;
+    return ok();
+}
+
+kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, const void* v_new,
+                            const int64_t* slot_mapping, int64_t num_tokens, void* stream) {
+    if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "pool is NULL");
+    if (layer < 0 || layer >= pool->desc.num_layers)
+        return fail(KV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, pool->desc.num_layers);
+    if (num_tokens < 0) return fail(KV_ERR_INVALID_ARGUMENT, "num_tokens %lld < 0", (long long)num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!k_new || !v_new || !slot_mapping) return fail(KV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) return fail(KV_ERR_INVALID_ARGUMENT, "slot_mapping must be 8-byte aligned");
+    kvp::ScatterArgs a;
+    a.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
+    a.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_slots = (int64_t)pool->desc.num_blocks * pool->desc.block_size;
+    a.num_kv_heads = pool->desc.num_kv_heads;
+    a.row_chunks = pool->desc.head_dim * pool->elem_bytes / 16;
+    hipError_t e = kvp::launch_scatter(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "scatter launch");
+    return ok();
+}
+
+kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t max_context_len, int32_t partition_size, uint64_t* bytes) {
+    if (!pool || !bytes) return fail(KV_ERR_INVALID_ARGUMENT, "NULL argument");
+    *bytes = 0;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_size < 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "negative size argument");
+    if (partition_size % pool->desc.block_size != 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "partition_size %d is not a multiple of the block size %d", partition_size,
+                    pool->desc.block_size);
+    PartGeo g = part_geo(max_context_len, partition_size, pool->desc.block_size);
+    if (g.max_parts > 1) {
+        uint64_t ml = 0;
+        workspace_layout(num_seqs, num_q_heads, g.max_parts, pool->desc.head_dim, &ml, bytes);
+    }
+    return ok();
+}
+
+kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const void* q,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                                 int32_t max_context_len, int32_t partition_size, void* workspace,
+                                 uint64_t workspace_bytes, void* stream) {
+    if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "pool is NULL");
+    const kv_pool_desc& d = pool->desc;
+    if (layer < 0 || layer >= d.num_layers) return fail(KV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, d.num_layers);
+    if (num_seqs < 0 || max_context_len < 0 || partition_size < 0 || max_blocks_per_seq <= 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "negative size argument");
+    if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads != 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                    d.num_kv_heads);
+    const int group = num_q_heads / d.num_kv_heads;
+    if (!kvp::decode_shape_supported(d.dtype, d.head_dim, group))
+        return fail(KV_ERR_UNSUPPORTED, "query group size %d: kernels are built for 1, 2, 4 and 8", group);
+    if (partition_size % d.block_size != 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "partition_size %d is not a multiple of the block size %d", partition_size,
+                    d.block_size);
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * d.block_size)
+        return fail(KV_ERR_INVALID_ARGUMENT, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
+                    max_context_len, (long long)max_blocks_per_seq * d.block_size);
+    if (!std::isfinite(scale)) return fail(KV_ERR_INVALID_ARGUMENT, "scale is not finite");
+    if (num_seqs > 65535 || num_q_heads > 65535)
+        return fail(KV_ERR_UNSUPPORTED, "num_seqs %d / num_q_heads %d above the 65535 grid limit", num_seqs, num_q_heads);
+    if (num_seqs == 0) return ok();
+    if (!out || !q || !block_tables || !context_lens) return fail(KV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+    if (!aligned16(out) || !aligned16(q)) return fail(KV_ERR_INVALID_ARGUMENT, "q/out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(context_lens)) & 3u)
+        return fail(KV_ERR_INVALID_ARGUMENT, "block_tables/context_lens must be 4-byte aligned");
+
+    PartGeo g = part_geo(max_context_len, partition_size, d.block_size);
+    kvp::DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    if (g.max_parts > 1) {
+        uint64_t ml = 0, need = 0;
+        workspace_layout(num_seqs, num_q_heads, g.max_parts, d.head_dim, &ml, &need);
+        if (!workspace || workspace_bytes < need)
+            return fail(KV_ERR_WORKSPACE_TOO_SMALL, "workspace of %llu bytes given, %llu needed",
+                        (unsigned long long)workspace_bytes, (unsigned long long)need);
+        if (!aligned16(workspace)) return fail(KV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+        a.ws_ml = static_cast<float*>(workspace);
+        a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+    }
+    a.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
+    a.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
+    a.q = q;
+    a.out = out;
+    a.tables = block_tables;
+    a.lens = context_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = d.num_kv_heads;
+    a.num_blocks = d.num_blocks;
+    a.max_context = max_context_len;
+    a.part_tokens = g.part_tokens;
+    a.max_parts = g.max_parts;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // exp(x) = 2^(x log2 e)
+    hipError_t e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+}
+
+}  // extern "C"

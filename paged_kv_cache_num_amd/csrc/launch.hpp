@@ -1,0 +1,49 @@
+// Launchers shared between the C-ABI layer (kvpool_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvp {
+
+constexpr int kBlockTokens = 16;   // tokens per KV block the kernels are built for
+
+struct ScatterArgs {
+    void* k_layer;               // layer base of the K pool
+    void* v_layer;               // layer base of the V pool
+    const void* k_new;           // [T][Hkv][D]
+    const void* v_new;
+    const int64_t* slot_mapping; // [T]
+    int64_t num_tokens;
+    int64_t num_slots;           // num_blocks * block_size
+    int32_t num_kv_heads;
+    int32_t row_chunks;          // 16-byte chunks per (token, head) row = D * elem / 16
+};
+
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void* k_layer;
+    const void* v_layer;
+    const void* q;               // [S][Hq][D]
+    void* out;                   // [S][Hq][D]
+    const int32_t* tables;       // [S][max_blocks]
+    const int32_t* lens;         // [S]
+    float* ws_ml;                // [S][Hq][max_parts] x (m, l), or null
+    float* ws_acc;               // [S][Hq][max_parts][D], or null
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_blocks;
+    int32_t max_context;         // clamp for lens[i]
+    int32_t part_tokens;         // tokens per partition (multiple of 16)
+    int32_t max_parts;           // ceil(max_context / part_tokens), >= 1
+    float scale_log2;            // softmax scale * log2(e)
+};
+
+// dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for a shape without a kernel.
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+bool decode_shape_supported(int dtype, int head_dim, int group);
+
+}  // namespace kvp

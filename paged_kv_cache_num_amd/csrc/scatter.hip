@@ -1,0 +1,60 @@
+// Slot-mapping scatter ("reshape_and_cache").
+//
+// aicassindra.com "GPU paged KV cache", "The write path: slot mapping and
+// scatter": after the K/V projection, every new token's K and V rows are copied
+// into the pool at the linear slot block_index * B + offset that the host
+// computed for it; head_dim is innermost, so each row is a contiguous,
+// vectorisable store even though the destinations are scattered.
+//
+// One thread moves one 16-byte chunk.  Work items are numbered
+//     ((token * 2 + {K,V}) * num_kv_heads + head) * row_chunks + chunk
+// so neighbouring lanes read neighbouring bytes of k_new / v_new and write
+// neighbouring bytes of one destination row (a 128-512 byte run).  The copy is
+// bit-exact: data moves as 32-bit words and is never converted.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace kvp {
+
+namespace {
+
+constexpr int kScatterThreads = 256;
+
+__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a) {
+    const int64_t chunks_per_token = 2LL * a.num_kv_heads * a.row_chunks;
+    const int64_t total = a.num_tokens * chunks_per_token;
+    const int64_t stride = (int64_t)gridDim.x * kScatterThreads;
+    for (int64_t item = (int64_t)blockIdx.x * kScatterThreads + threadIdx.x; item < total; item += stride) {
+        const int64_t t = item / chunks_per_token;
+        const int64_t rem = item - t * chunks_per_token;
+        const int which = (int)(rem / ((int64_t)a.num_kv_heads * a.row_chunks));   // 0: K, 1: V
+        const int64_t rem2 = rem - (int64_t)which * a.num_kv_heads * a.row_chunks;
+        const int h = (int)(rem2 / a.row_chunks);
+        const int c = (int)(rem2 - (int64_t)h * a.row_chunks);
+
+        const int64_t slot = a.slot_mapping[t];
+        if (slot < 0 || slot >= a.num_slots) continue;   // padding token, or outside the pool
+        const int64_t block = slot / kBlockTokens;
+        const int64_t offset = slot - block * kBlockTokens;
+
+        // destination row (block, head, offset) in 16-byte chunks
+        const int64_t dst_chunk = ((block * a.num_kv_heads + h) * kBlockTokens + offset) * a.row_chunks + c;
+        const int64_t src_chunk = (t * a.num_kv_heads + h) * a.row_chunks + c;
+        const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new);
+        uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);
+        dst[dst_chunk] = src[src_chunk];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream) {
+    if (a.num_tokens <= 0) return hipSuccess;
+    const int64_t total = a.num_tokens * 2LL * a.num_kv_heads * a.row_chunks;
+    int64_t blocks = (total + kScatterThreads - 1) / kScatterThreads;
+    if (blocks > 65536) blocks = 65536;   // grid-stride loop covers the rest
+    scatter_kernel<<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace kvp

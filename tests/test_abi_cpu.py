@@ -1,0 +1,228 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the header
+declares, and its host-side logic (pool arithmetic, slot mapping, argument
+checks) behaves as documented.  No kernel is launched here: every call below
+either is host-only or returns an error before any HIP call.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kvgen
+import oracle
+import paged_kv_cache_num_amd as kvp
+from paged_kv_cache_num_amd import kvpool as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_numbers.json")))
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?([a-z_][a-z0-9_]*)\s*\(",
+                            text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert set(_declared_functions()) == set(K.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _desc(**kw):
+    base = dict(num_layers=1, num_blocks=64, block_size=16, num_kv_heads=2, head_dim=64, dtype="f32")
+    base.update(kw)
+    return kvp.make_desc(**base)
+
+
+# ---------------------------------------------------------- pool arithmetic --
+
+def test_pool_bytes_reproduces_the_pages_per_token_figures():
+    g = GOLDEN["kv_bytes_per_token_70b"]
+    one_token = _desc(num_layers=g["layers"], num_blocks=1, block_size=1, num_kv_heads=g["kv_heads"],
+                      head_dim=g["head_dim"], dtype="bf16")
+    assert 2 * kvp.kv_pool_bytes(one_token) == g["expected_bytes"]
+    r = GOLDEN["reserve_4k_70b"]
+    seq = _desc(num_layers=80, num_blocks=1, block_size=r["tokens"], num_kv_heads=8, head_dim=128, dtype="bf16")
+    assert 2 * kvp.kv_pool_bytes(seq) == r["expected_gib"] * 2**30
+    g = GOLDEN["kv_bytes_per_token_8b"]
+    tok = _desc(num_layers=g["layers"], num_blocks=1, block_size=1, num_kv_heads=g["kv_heads"],
+                head_dim=g["head_dim"], dtype="bf16")
+    assert 2 * kvp.kv_pool_bytes(tok) == g["expected_bytes"]
+    blk = _desc(num_layers=g["layers"], num_blocks=1, block_size=g["block_size"], num_kv_heads=g["kv_heads"],
+                head_dim=g["head_dim"], dtype="bf16")
+    assert 2 * kvp.kv_pool_bytes(blk) == g["expected_block_bytes"]
+    pool = _desc(num_layers=g["layers"], num_blocks=g["kv_budget_blocks"], block_size=16,
+                 num_kv_heads=8, head_dim=128, dtype="bf16")
+    assert 2 * kvp.kv_pool_bytes(pool) // g["expected_block_bytes"] * 16 == g["expected_tokens"]
+
+
+def test_pool_bytes_reproduces_the_70b_capacity_printout():
+    c = GOLDEN["llama70b_capacity"]
+    one = _desc(num_layers=c["layers"], num_blocks=1, block_size=c["context"], num_kv_heads=c["kv_heads"],
+                head_dim=c["head_dim"], dtype="bf16")
+    assert 2 * kvp.kv_pool_bytes(one) / 2**30 == c["expected_gib_one_seq"]
+    users = _desc(num_layers=c["layers"], num_blocks=c["users"], block_size=c["context"],
+                  num_kv_heads=c["kv_heads"], head_dim=c["head_dim"], dtype="bf16")
+    assert 2 * kvp.kv_pool_bytes(users) / 2**30 == c["expected_gib_users"]
+    mha = _desc(num_layers=c["layers"], num_blocks=1, block_size=c["context"], num_kv_heads=c["kv_heads_mha"],
+                head_dim=c["head_dim"], dtype="bf16")
+    assert 2 * kvp.kv_pool_bytes(mha) / 2**30 == c["expected_gib_mha"]
+
+
+def test_table_entry_counts():
+    for c in GOLDEN["table_entries"]:
+        # slots for the last token of the context go through entry ceil(n/B) - 1: the row must have that many
+        n, B = c["tokens"], c["block_size"]
+        need = c["expected_entries"]
+        table = np.arange(need, dtype=np.int32)[None, :]
+        s = kvp.kv_build_slot_mapping(table, B, need, [0], [n - 1], [1])
+        assert s[0] == n - 1
+        with pytest.raises(kvp.KVError):
+            kvp.kv_build_slot_mapping(table[:, :need - 1], B, need, [0], [n - 1], [1])
+        assert need * 4 == c["expected_bytes"]
+
+
+def test_pool_bytes_errors():
+    with pytest.raises(kvp.KVError) as e:
+        kvp.kv_pool_bytes(_desc(num_blocks=0))
+    assert e.value.status == K.KV_ERR_INVALID_ARGUMENT
+    bad = _desc()
+    bad.dtype = 7
+    with pytest.raises(kvp.KVError):
+        kvp.kv_pool_bytes(bad)
+    with pytest.raises(kvp.KVError):
+        kvp.kv_pool_bytes(_desc(num_layers=2**30, num_blocks=2**30, head_dim=2**20))
+
+
+# ------------------------------------------------------------ slot mapping --
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+def test_host_slot_mapping_matches_the_oracle_bit_exactly(name):
+    wl = kvgen.make_workload(name, num_seqs=None if name in ("C1", "C5") else 24)
+    tables = wl.all_tables()
+    got = kvp.kv_build_slot_mapping(tables, wl.block_size, wl.num_blocks, wl.write_seq,
+                                    wl.write_start, wl.write_count)
+    ref = oracle.slot_mapping(tables, wl.block_size, wl.num_blocks, wl.write_seq,
+                              wl.write_start, wl.write_count)
+    assert got.dtype == np.int64 and np.array_equal(got, ref)
+
+
+def test_host_slot_mapping_errors():
+    t = np.array([[3, 1]], dtype=np.int32)
+    with pytest.raises(kvp.KVError) as e:
+        kvp.kv_build_slot_mapping(t, 16, 4, [0], [32], [1])
+    assert e.value.status == K.KV_ERR_OUT_OF_RANGE
+    with pytest.raises(kvp.KVError) as e:
+        kvp.kv_build_slot_mapping(np.array([[9]], dtype=np.int32), 16, 4, [0], [0], [1])
+    assert e.value.status == K.KV_ERR_OUT_OF_RANGE
+    with pytest.raises(kvp.KVError) as e:
+        kvp.kv_build_slot_mapping(t, 16, 4, [1], [0], [1])
+    assert e.value.status == K.KV_ERR_INVALID_ARGUMENT
+    with pytest.raises(kvp.KVError):
+        kvp.kv_build_slot_mapping(t, 16, 4, [0], [-1], [1])
+    assert kvp.kv_build_slot_mapping(t, 16, 4, [0], [5], [0]).size == 0
+
+
+# ------------------------------------------------------- argument checks --
+
+FAKE_K = 0x10000000   # never dereferenced: every call below fails its host checks first
+FAKE_V = 0x20000000
+
+
+def _pool(**kw):
+    d = _desc(**kw)
+    h = ctypes.c_void_p(0)
+    st = K.lib.kv_pool_create(ctypes.byref(d), FAKE_K, FAKE_V, ctypes.byref(h))
+    return st, h
+
+
+def test_pool_create_checks():
+    st, h = _pool()
+    assert st == K.KV_OK and h.value
+    K.lib.kv_pool_destroy(h)
+    assert _pool(block_size=32)[0] == K.KV_ERR_UNSUPPORTED
+    assert _pool(head_dim=96)[0] == K.KV_ERR_UNSUPPORTED
+    d = _desc()
+    h = ctypes.c_void_p(0)
+    assert K.lib.kv_pool_create(ctypes.byref(d), FAKE_K + 8, FAKE_V, ctypes.byref(h)) == K.KV_ERR_INVALID_ARGUMENT
+    assert K.lib.kv_pool_create(ctypes.byref(d), None, FAKE_V, ctypes.byref(h)) == K.KV_ERR_INVALID_ARGUMENT
+    assert b"NULL" in K.lib.kv_last_error_message()
+    assert K.lib.kv_pool_destroy(None) == K.KV_OK
+
+
+def _decode(h, **kw):
+    a = dict(layer=0, out=0x30000000, q=0x40000000, tables=0x50000000, mb=16, lens=0x60000000, S=4, Hq=8,
+             scale=0.125, max_ctx=200, part=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return K.lib.paged_attention_decode(h, a["layer"], a["out"], a["q"], a["tables"], a["mb"], a["lens"], a["S"],
+                                        a["Hq"], a["scale"], a["max_ctx"], a["part"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_argument_checks_return_before_any_launch():
+    st, h = _pool()
+    assert st == K.KV_OK
+    E = K
+    assert _decode(None) == E.KV_ERR_INVALID_ARGUMENT
+    assert _decode(h, layer=1) == E.KV_ERR_INVALID_ARGUMENT
+    assert _decode(h, Hq=7) == E.KV_ERR_INVALID_ARGUMENT          # not a multiple of 2 KV heads
+    assert _decode(h, Hq=6) == E.KV_ERR_UNSUPPORTED               # group of 3
+    assert _decode(h, Hq=32) == E.KV_ERR_UNSUPPORTED              # group of 16
+    assert _decode(h, part=40) == E.KV_ERR_INVALID_ARGUMENT       # not a multiple of B
+    assert _decode(h, max_ctx=16 * 16 + 1) == E.KV_ERR_INVALID_ARGUMENT
+    assert _decode(h, scale=float("nan")) == E.KV_ERR_INVALID_ARGUMENT
+    assert _decode(h, out=0x30000008) == E.KV_ERR_INVALID_ARGUMENT
+    assert _decode(h, q=None) == E.KV_ERR_INVALID_ARGUMENT
+    assert _decode(h, part=64) == E.KV_ERR_WORKSPACE_TOO_SMALL
+    need = ctypes.c_uint64(0)
+    assert K.lib.paged_attention_workspace_bytes(h, 4, 8, 200, 64, ctypes.byref(need)) == E.KV_OK
+    assert _decode(h, part=64, ws=0x70000000, ws_bytes=need.value - 1) == E.KV_ERR_WORKSPACE_TOO_SMALL
+    assert _decode(h, S=0) == E.KV_OK                              # nothing to do, nothing launched
+    K.lib.kv_pool_destroy(h)
+
+
+def test_workspace_size_formula():
+    st, h = _pool(head_dim=128, num_kv_heads=8, dtype="bf16")
+    out = ctypes.c_uint64(0)
+    assert K.lib.paged_attention_workspace_bytes(h, 8, 32, 131072, 512, ctypes.byref(out)) == K.KV_OK
+    parts = 131072 // 512
+    entries = 8 * 32 * parts
+    assert out.value == -(-entries * 8 // 256) * 256 + entries * 128 * 4
+    assert K.lib.paged_attention_workspace_bytes(h, 8, 32, 4096, 0, ctypes.byref(out)) == K.KV_OK
+    assert out.value == 0
+    assert K.lib.paged_attention_workspace_bytes(h, 8, 32, 4096, 4096, ctypes.byref(out)) == K.KV_OK
+    assert out.value == 0
+    K.lib.kv_pool_destroy(h)
+
+
+def test_scatter_argument_checks():
+    st, h = _pool()
+    L = K.lib
+    assert L.reshape_and_cache(None, 0, 0x1000, 0x2000, 0x3000, 4, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.reshape_and_cache(h, 3, 0x1000, 0x2000, 0x3000, 4, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.reshape_and_cache(h, 0, 0x1008, 0x2000, 0x3000, 4, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.reshape_and_cache(h, 0, 0x1000, 0x2000, 0x3004, 4, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.reshape_and_cache(h, 0, 0x1000, 0x2000, None, 4, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.reshape_and_cache(h, 0, 0x1000, 0x2000, 0x3000, -1, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.reshape_and_cache(h, 0, 0x1000, 0x2000, 0x3000, 0, None) == K.KV_OK
+    K.lib.kv_pool_destroy(h)
+
+
+def test_status_strings():
+    for code, name in [(0, "KV_OK"), (-1, "KV_ERR_INVALID_ARGUMENT"), (-2, "KV_ERR_UNSUPPORTED"),
+                       (-3, "KV_ERR_WORKSPACE_TOO_SMALL"), (-4, "KV_ERR_HIP"), (-5, "KV_ERR_OUT_OF_RANGE")]:
+        assert K.lib.kv_status_string(code).decode() == name
+    assert K.lib.kv_status_string(42).decode() == "KV_ERR_UNKNOWN"

@@ -1,0 +1,174 @@
+"""HIP path vs the CPU oracle on the GPU: scatter bit-exact, attention within
+1e-4 (fp32) / 2e-2 (bf16), at the full configuration sizes and on edge cases.
+
+Every case prints its name, seed and shape before it touches the GPU.
+"""
+import numpy as np
+import pytest
+
+import kvgen
+import oracle
+from parity_util import TOL, check_step, max_err, reference, run_gpu, say, to_f64, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(gpu_available):
+    yield
+
+
+# --------------------------------------------------------- full configs --
+
+C1_CASES = [(v, p) for v in ("spec", "sharp", "hot", "needle") for p in (0, 32, 64)]
+
+
+@pytest.mark.parametrize("variant,partition", C1_CASES)
+def test_c1_tiny_fp32(variant, partition):
+    say(f"C1 variant={variant} partition={partition}")
+    wl = workload("C1", variant)
+    ref = reference("C1", variant)
+    step = run_gpu(wl, partition_size=partition)
+    check_step(step, wl, ref, label=f"C1/{variant}/p{partition}")
+
+
+@pytest.mark.parametrize("variant", ["spec", "sharp", "hot", "needle"])
+@pytest.mark.parametrize("partition", [0, 512])
+def test_c2_llama8b_decode(variant, partition):
+    say(f"C2 variant={variant} partition={partition} S=64 Hq=32 Hkv=8 D=128 bf16")
+    wl = workload("C2", variant)
+    ref = reference("C2", variant)
+    step = run_gpu(wl, partition_size=partition)
+    check_step(step, wl, ref, label=f"C2/{variant}/p{partition}")
+
+
+@pytest.mark.parametrize("variant", ["spec", "sharp", "needle"])
+def test_c3_70b_gqa8_with_prefill_scatter(variant):
+    say(f"C3 variant={variant} S=256 Hq=64 Hkv=8 D=128 bf16, 2048-token prefill chunk")
+    wl = workload("C3", variant)
+    ref = reference("C3", variant)
+    step = run_gpu(wl, partition_size=512)
+    check_step(step, wl, ref, label=f"C3/{variant}")
+
+
+def test_c4_prefix_sharing_equals_private_copies():
+    say("C4 sharp S=128 shared 2048-token prefix")
+    wl = workload("C4", "sharp")
+    ref = reference("C4", "sharp")
+    shared = run_gpu(wl, partition_size=512)
+    check_step(shared, wl, ref, label="C4/shared")
+    priv = kvgen.privatize_blocks(wl)
+    say("C4 private copies")
+    private = run_gpu(priv, partition_size=512)
+    assert np.array_equal(shared.out_host(), private.out_host()), "shared and private copies differ"
+
+
+@pytest.mark.parametrize("variant", ["sharp", "needle"])
+def test_c5_long_context_split(variant):
+    say(f"C5 variant={variant} S=8 L in [32768,131072] partition=512")
+    wl = workload("C5", variant)
+    ref = reference("C5", variant)
+    step = run_gpu(wl, partition_size=512)
+    check_step(step, wl, ref, label=f"C5/{variant}")
+
+
+# ------------------------------------------------------------ invariances --
+
+def test_bitwise_invariance_to_block_placement():
+    say("C2 sharp: permuted and contiguous placements")
+    wl = workload("C2", "sharp")
+    base = run_gpu(wl, partition_size=512).out_host()
+    for seed in (1, 2):
+        perm = run_gpu(kvgen.permute_blocks(wl, seed), partition_size=512).out_host()
+        assert np.array_equal(base, perm), f"permutation {seed} changed the output bits"
+    dense = run_gpu(kvgen.privatize_blocks(wl, contiguous=True), partition_size=512).out_host()
+    assert np.array_equal(base, dense), "identity (contiguous) tables changed the output bits"
+
+
+def test_repeated_runs_are_bitwise_identical():
+    import torch
+    say("C2 sharp: repeated runs")
+    wl = workload("C2", "sharp")
+    step = run_gpu(wl, partition_size=512)
+    first = step.out_host()
+    for _ in range(3):
+        step.attend()
+        torch.cuda.synchronize()
+        assert np.array_equal(first, step.out_host())
+
+
+@pytest.mark.parametrize("partition", [16, 48, 128, 1024, 4096])
+def test_partition_sizes_agree_with_the_oracle(partition):
+    say(f"C2 sharp partition={partition}")
+    wl = workload("C2", "sharp")
+    ref = reference("C2", "sharp")
+    step = run_gpu(wl, partition_size=partition)
+    check_step(step, wl, ref, check_pool=False, label=f"C2/p{partition}")
+
+
+# ------------------------------------------------------------- edge cases --
+
+EDGE = [
+    # (dtype, Hq, Hkv, D, lengths, partition)
+    ("bf16", 8, 8, 128, [1, 2, 15, 16, 17], 0),         # g = 1
+    ("bf16", 16, 8, 128, [33, 64, 65, 1000], 64),       # g = 2
+    ("bf16", 64, 8, 64, [300, 5, 129], 0),              # g = 8, D = 64
+    ("bf16", 32, 8, 64, [511, 512, 513, 2048], 512),    # partition edges, D = 64
+    ("f32", 8, 2, 128, [17, 1, 250, 3000], 256),        # fp32, D = 128
+    ("f32", 16, 2, 64, [4096, 31], 0),                  # fp32, g = 8
+    ("bf16", 32, 8, 128, [0, 7, 0, 40], 0),             # empty sequences
+    ("bf16", 32, 8, 128, [0, 7, 0, 1600], 512),         # empty sequences, split
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,lengths,partition", EDGE)
+def test_edge_shapes(dtype, hq, hkv, d, lengths, partition):
+    say(f"edge dtype={dtype} Hq={hq} Hkv={hkv} D={d} lengths={lengths} partition={partition}")
+    for variant in ("sharp", "hot"):
+        wl = kvgen.custom_workload(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                   dtype=dtype, seed=21, variant=variant, poison=True, table_pad=3)
+        ref = oracle.run_step(wl)
+        step = run_gpu(wl, partition_size=partition)
+        check_step(step, wl, ref, label=f"edge/{variant}")
+        for i, L in enumerate(lengths):
+            if L == 0:
+                assert not to_f64(step.out_host()[i], dtype).any(), "zero-length sequence must give zeros"
+
+
+def test_single_token_output_is_its_value_bit_exact():
+    say("single-token contexts: out == v_new bits")
+    for dtype in ("bf16", "f32"):
+        wl = kvgen.custom_workload(lengths=[1, 1, 1, 1], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                   dtype=dtype, seed=4, variant="hot", poison=True)
+        step = run_gpu(wl)
+        out = step.out_host()
+        for i in range(4):
+            for h in range(8):
+                assert out[i, h].tobytes() == wl.v_new[i, h // 4].tobytes()
+
+
+def test_other_layer_of_a_multi_layer_pool():
+    import torch
+    say("3-layer pool, layer 1")
+    wl = kvgen.custom_workload(lengths=[100, 37, 260], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                               dtype="bf16", seed=8, variant="sharp", poison=True)
+    ref = oracle.run_step(wl)
+    step = run_gpu(wl, num_layers=3, layer=1, partition_size=64)
+    check_step(step, wl, ref, label="layer 1 of 3")
+    k0, _ = step.pool_host(layer=0)
+    k2, _ = step.pool_host(layer=2)
+    assert k0.tobytes() == wl.k_pool.tobytes() and k2.tobytes() == wl.k_pool.tobytes(), \
+        "scatter wrote outside its layer"
+
+
+def test_padding_tokens_with_negative_slots_are_skipped():
+    import torch
+    say("scatter with padding slots")
+    wl = workload("C1", "sharp")
+    step = run_gpu(wl)
+    kp0, vp0 = step.pool_host()
+    pad = torch.full((4,), -1, dtype=torch.int64, device="cuda")
+    step.pool.reshape_and_cache(0, step.k_new, step.v_new, pad)
+    torch.cuda.synchronize()
+    kp1, vp1 = step.pool_host()
+    assert kp0.tobytes() == kp1.tobytes() and vp0.tobytes() == vp1.tobytes()
