@@ -50,6 +50,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m paged_kv_cache_num_amd.build` "
                           "(the HIP library is required; there is no CPU fallback)")
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Loading torch first makes this library bind to that one copy; loading it
+    # first would put two HIP runtimes in the process, and the second one to
+    # initialise sees no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, u64, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p
     P = ctypes.POINTER
