@@ -30,7 +30,8 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention achieved HBM GB/s (% of peak) + decode tokens/sec/layer"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNEL_SOURCES = ["paged_kv_cache_num_amd/csrc/decode.hip", "paged_kv_cache_num_amd/csrc/device_common.hpp"]
+KERNEL_SOURCES = ["paged_kv_cache_num_amd/csrc/decode.hip", "paged_kv_cache_num_amd/csrc/decode_mfma.hip",
+                  "paged_kv_cache_num_amd/csrc/device_common.hpp"]
 
 WORKLOADS = {
     "C1": "tiny fp32 paged decode: 4 sequences, lengths {17,33,100,200}, 8 query / 2 KV heads, head_dim 64, block 16, 64-block pool",
@@ -39,7 +40,8 @@ WORKLOADS = {
     "C4": "prefix-sharing decode: 128 sequences sharing 128 blocks (2048-token prefix) plus private suffixes U[64,512], 32 query / 8 KV heads, head_dim 128, bf16",
     "C5": "long-context split decode: 8 sequences, lengths U[32768,131072], 32 query / 8 KV heads, head_dim 128, partitions of 512 tokens, fragmented pool, bf16",
 }
-DEFAULT_PARTITION = {"C1": 0, "C2": 512, "C3": 512, "C4": 512, "C5": 512}
+# 0 = balanced split across the GPU; C5 names 512-token partitions explicitly
+DEFAULT_PARTITION = {"C1": 0, "C2": 0, "C3": 0, "C4": 0, "C5": 512}
 
 
 def kernel_sha() -> str:
@@ -137,7 +139,7 @@ def main(argv=None):
     import torch
 
     import kvgen
-    from paged_kv_cache_num_amd import DecodeStep, probe_copy
+    from paged_kv_cache_num_amd import DecodeStep, probe_copy, probe_read
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -150,6 +152,21 @@ def main(argv=None):
     nbytes = algorithmic_bytes(wl)
     step = DecodeStep.from_workload(wl, partition_size=part)
     torch.cuda.synchronize()
+
+    # achievable HBM read rate on this machine: a plain 16-byte-load read of 2 GiB (larger than the caches)
+    big = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    sink = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    read_us = []
+    for _ in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        probe_read(big, sink)
+        e1.record()
+        e1.synchronize()
+        read_us.append(e0.elapsed_time(e1) * 1e3)
+    read_gbps = big.numel() / (min(read_us[1:]) * 1e-6) / 1e9
+    print(f"bench: read probe 2 GiB: {read_gbps:.0f} GB/s", file=sys.stderr, flush=True)
 
     if args.probe_copy_mib:
         n = args.probe_copy_mib << 20
@@ -200,22 +217,22 @@ def main(argv=None):
 
     cold = None
     if not args.no_cold:
-        # evict L2 and the 256 MB MALL before every attention call (outside its events)
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # evict L2 and the 256 MB MALL before every attention call by reading 2 GiB (outside its
+        # events); a read leaves no dirty lines whose write-back would be charged to the kernel
         cold_us = []
         for _ in range(min(K, 30)):
-            flush.zero_()
+            probe_read(big, sink)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             step.attend()
             b.record()
             b.synchronize()
             cold_us.append(a.elapsed_time(b) * 1e3)
-        del flush
         cm = sum(cold_us) / len(cold_us)
         cold = {"attn_us_mean": round(cm, 2), "attn_us_p50": round(percentile(cold_us, 0.5), 2),
                 "achieved_gbps": round(nbytes["attn"] / (cm * 1e-6) / 1e9, 1),
                 "frac": round(nbytes["attn"] / (cm * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del big
 
     traffic = traffic_for(args.config, part)
     result = {
@@ -245,6 +262,8 @@ def main(argv=None):
                      "launch_us_p50": round(percentile(attn_us, 0.5), 2),
                      "launch_us_p90": round(percentile(attn_us, 0.9), 2)},
         "scatter_us_mean": round(sum(scatter_us) / K, 2),
+        "read_probe_gbps": round(read_gbps, 1),
+        "frac_of_read_probe": round(achieved / read_gbps, 4),
         "step_bytes": step_bytes,
         "cold": cold,
         "pool_utilization": round(float(wl.info.get("utilization") or 0.0), 4),

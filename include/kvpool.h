@@ -144,13 +144,15 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
                             const int64_t* slot_mapping, int64_t num_tokens, void* stream);
 
 /*
- * Workspace needed by paged_attention_decode for this shape: 0 when
- * partition_size is 0 (single pass) or when one partition covers
- * max_context_len; otherwise
- *     num_seqs * num_q_heads * ceil(max_context_len / partition_size) * (head_dim + 2) * 4
- * bytes (fp32 running max, sum and unnormalised output per partition).
+ * Workspace needed by paged_attention_decode for this shape and mode (see
+ * partition_size below).  Zero when no workspace is used.  With partitions it
+ * holds one fp32 running max, sum and unnormalised output per (sequence,
+ * query head, partition); in the balanced mode, the tiles before each
+ * sequence (int64, num_seqs + 1) and at most two fp32 partial states per
+ * worker.  The balanced-mode size depends on the current device's compute
+ * unit count: query it on the device that will run the call.
  * Errors: KV_ERR_INVALID_ARGUMENT (null, negative sizes, partition_size not a
- * multiple of the block size).
+ * multiple of the block size, num_q_heads not a multiple of num_kv_heads).
  */
 kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int32_t num_q_heads,
                                           int32_t max_context_len, int32_t partition_size,
@@ -169,10 +171,17 @@ kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int3
  *                  b >= ceil(L_i / B) are never read
  *   context_lens:  device, int32 [num_seqs], each in [0, max_context_len]
  *   max_context_len: host bound on every L_i (sizes the grid); <= max_blocks_per_seq * B
- *   partition_size: 0 = one workgroup per (sequence, KV head) walks the whole
- *                  context; otherwise a multiple of B: the context is cut into
- *                  partitions of that many tokens, each handled by its own
- *                  workgroup, and a second kernel merges them (log-sum-exp).
+ *   partition_size: 0 = the library balances the work itself.  For bf16 pools
+ *                  with head_dim 128 and at most 1024 sequences, the
+ *                  (sequence, KV head, block) tiles of the whole batch are cut
+ *                  into equal contiguous slices, one per resident wave, and
+ *                  a second kernel merges the (sequence, KV head) pairs that
+ *                  straddle slices; other shapes walk each context in one
+ *                  workgroup per (sequence, KV head).
+ *                  > 0: a multiple of B; each context is cut into partitions
+ *                  of that many tokens, each handled by its own workgroup,
+ *                  and a second kernel merges them (log-sum-exp rescale).
+ *   scale:         softmax scale, finite and > 0
  *   workspace:     device, >= paged_attention_workspace_bytes(...) bytes, 16-byte
  *                  aligned; may be NULL when that size is 0.  Its contents on
  *                  entry do not matter.

@@ -28,6 +28,17 @@ extern "C" {
  */
 kv_status kv_probe_copy(void* dst, const void* src, uint64_t bytes, void* stream);
 
+/*
+ * Read `bytes` bytes of device buffer `src` with 16-byte vector loads and fold
+ * them into one 32-bit word per workgroup, written to device buffer `sink`
+ * (at least 65536 bytes, 4-byte aligned).  Reads exactly `bytes`; writes at
+ * most 64 KiB.  It measures the achievable HBM read rate, and reading a
+ * buffer larger than the caches evicts them without leaving dirty lines.
+ * src 16-byte aligned, bytes a multiple of 16.  Errors: KV_ERR_INVALID_ARGUMENT,
+ * KV_ERR_HIP.
+ */
+kv_status kv_probe_read(const void* src, uint64_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

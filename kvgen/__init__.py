@@ -162,7 +162,7 @@ class BlockAllocator:
         return len(self.free)
 
     def utilization(self) -> float:
-        return 1.0 - len(self.free) / self.num_blocks
+        return 1.0 - len(self.free) / self.num_blocks if self.num_blocks else 0.0
 
 
 # ----------------------------------------------------------------------------
@@ -363,7 +363,7 @@ def make_workload(name: str, seed: Optional[int] = None, variant: str = "spec", 
     else:
         prefill = 2048 if (name == "C3" and cfg is not None) else 0
         need = int(nblk.sum())
-        N = num_blocks or int(math.ceil(1.25 * need)) + prefill // B
+        N = num_blocks or max(1, int(math.ceil(1.25 * need))) + prefill // B
         alloc = BlockAllocator(N, rng_tab.permutation(N))
         for i in range(S):
             tables_rows.append([alloc.alloc() for _ in range(int(nblk[i]))])

@@ -290,14 +290,20 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(DecodeArgs a) {
     }
 }
 
+template <int DT, int D>
+hipError_t launch_reduce(const DecodeArgs& a, hipStream_t stream) {
+    if (a.max_parts <= 1) return hipSuccess;
+    reduce_kernel<DT, D><<<dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(kWave), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 template <int DT, int D, int G>
 hipError_t launch_tpl(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     decode_kernel<DT, D, G><<<grid, dim3(kDecodeWaves * kWave), 0, stream>>>(a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.max_parts <= 1) return e;
-    reduce_kernel<DT, D><<<dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(kWave), 0, stream>>>(a);
-    return hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_reduce<DT, D>(a, stream);
 }
 
 template <int DT, int D>
@@ -322,9 +328,12 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream
     if (a.num_seqs <= 0) return hipSuccess;
     const int group = a.num_q_heads / a.num_kv_heads;
     if (!decode_shape_supported(dtype, head_dim, group)) return hipErrorInvalidValue;
-    if (dtype == 1) {
-        return head_dim == 128 ? launch_group<1, 128>(a, group, stream) : launch_group<1, 64>(a, group, stream);
+    if (dtype == 1 && head_dim == 128) {
+        hipError_t e = launch_decode_bf16_mfma(a, group, stream);
+        if (e != hipSuccess) return e;
+        return launch_reduce<1, 128>(a, stream);
     }
+    if (dtype == 1) return launch_group<1, 64>(a, group, stream);
     return head_dim == 128 ? launch_group<0, 128>(a, group, stream) : launch_group<0, 64>(a, group, stream);
 }
 

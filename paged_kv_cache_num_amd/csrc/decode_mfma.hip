@@ -1,0 +1,682 @@
+// Paged decode attention for bf16 pools with head_dim 128: q.k on the matrix
+// cores, online softmax and the value pass on the vector ALUs.
+//
+// What is computed is the same as decode.hip (aicassindra.com "GPU paged KV
+// cache", "Inside the paged attention kernel"; "PagedAttention, Internals
+// First", "02 Block tables"); this file only changes how a gfx950 compute unit
+// spends its cycles on it:
+//
+//   * Scores.  For one (block, KV head) tile the scores of all query heads of
+//     the group are S = K Q^T, a 16 x 128 by 128 x G product.  It runs as four
+//     v_mfma_f32_16x16x32_bf16: the K tile is the A operand, read straight
+//     from HBM (lane l holds token l%16 and eight consecutive dims), the
+//     group's queries are the B operand (columns G..15 are zero).  The result
+//     leaves lane (r, n) = (l/16, l%16) holding the scores of tokens 4r..4r+3
+//     for query head n.
+//   * Softmax.  Lane (r, n) keeps the running max and sum of head n over the
+//     token positions 4r..4r+3 of every block it walks, so the loop needs no
+//     cross-lane reduction.  The max is only moved when a block's scores
+//     exceed it by more than 2^kLazy (then the sum and the outputs are
+//     rescaled); otherwise exponentials use the old max, which changes no
+//     result beyond rounding because output = sum(p v) / sum(p) for any
+//     common reference.
+//   * Values.  Lane (r, c) reads the 16-byte chunk c (dims 8c..8c+7) of tokens
+//     4r..4r+3 of the V tile and accumulates p * v for every head of the
+//     group; p comes from lane (r, h) of the same 16-lane row through a DPP
+//     row broadcast.
+//   * Memory.  Each wave walks every 4th block of its partition.  The
+//     partition's block-table entries are fetched with one vector load per 64
+//     blocks and read out with readlane; the K and V tiles of the next block
+//     are in flight while the current one is computed.
+//   * The walk order and all reductions depend only on logical positions, so
+//     the output is bitwise independent of where the blocks live.
+#include <math.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace kvp {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kD = 128;            // head_dim this kernel is built for
+constexpr int kRC = kD / 8;        // 16-byte chunks per token row (16)
+constexpr int kKK = kD / 32;       // MFMA steps over head_dim (4)
+constexpr float kLazy = 8.0f;      // log2 headroom before the running max is moved
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+template <int CTRL>
+__device__ __forceinline__ float bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// lane h of every 16-lane row, to all lanes of that row
+template <int H>
+__device__ __forceinline__ float row_bcast(float x) {
+    return bcast<0x150 + H>(x);
+}
+
+__device__ __forceinline__ float safe_ref(float m) { return m == -INFINITY ? 0.0f : m; }
+
+struct Tile {
+    uint4 k[kKK];   // K: token n, dims 32*kk + 8*r .. +8
+    uint4 v[4];     // V: token 4*r + i, chunk c
+};
+
+// Running state of one wave.  The reference max m is the same in all four
+// rows (blocks are folded in whole), l is this row's share of the softmax
+// sum, and o holds the MFMA accumulators of P V: o[e][j] is the output of
+// query head 4r + j, dim 8n + e.
+struct State {
+    float m, l;            // lane (r, n): head n
+    f32x4_t o[8];
+};
+
+__device__ __forceinline__ void load_tile(Tile& t, const uint4* __restrict__ kt, const uint4* __restrict__ vt,
+                                          int k_off, int v_off) {
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) t.k[kk] = kt[k_off + kk * 4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.v[i] = vt[v_off + i * kRC];
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    bf16x2_t p = {(__bf16)lo, (__bf16)hi};   // round to nearest even
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ s16x4_t as_operand(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(s16x4_t, make_uint2(a, b));
+}
+
+// One block: scores on MFMA, lazy online softmax with one reference max per
+// head, P V on MFMA.
+//
+// P V is a 16-head x 16-token by 16-token x 128-dim product run as eight
+// v_mfma_f32_16x16x16_bf16, one per e = 0..7, whose output column n stands
+// for dim 8n + e.  The A operand (P) is already where the score MFMA left it:
+// lane (r, n) holds head n, tokens 4r..4r+3.  The B operand of step e is
+// dim 8n + e of tokens 4r..4r+3, which lane (r, n) also already holds in its
+// four V loads; it is only repacked.  P is split into a bfloat16 high part
+// and a bfloat16 remainder so the product keeps about 16 bits of P.
+template <int G>
+__device__ __forceinline__ void process(State& st, const Tile& t, const bf16x8_t (&qb)[kKK], int tok0, int L,
+                                        int r, int n, float sl2) {
+    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[kk]), qb[kk], s, 0, 0, 0);
+
+    uint4 v[4] = {t.v[0], t.v[1], t.v[2], t.v[3]};
+    if (tok0 + kBlockTokens > L) {   // last, partially filled block (wave-uniform branch)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (tok0 + 4 * r + i >= L) {
+                s[i] = -INFINITY;
+                v[i] = make_uint4(0u, 0u, 0u, 0u);   // stale slots may hold NaN; P is 0 there
+            }
+        }
+    }
+
+    // block max of head n over all 16 tokens (rows hold 4 tokens each)
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * sl2;
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const bool need = (n < G) && (mx > st.m + kLazy);
+    if (__builtin_amdgcn_ballot_w64(need)) {   // rare after the first block
+        const float m_new = need ? mx : st.m;
+        const float corr = need ? fast_exp2(st.m - m_new) : 1.0f;   // 0 when nothing was seen yet
+        st.l *= corr;
+        st.m = m_new;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float cj = __shfl(corr, 4 * r + j, kWave);   // head 4r + j (rows agree)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.o[e][j] *= cj;
+        }
+    }
+    const float neg_ref = -safe_ref(st.m);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = n < G ? fast_exp2(fmaf(s[i], sl2, neg_ref)) : 0.0f;
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+
+    const uint32_t h01 = bf16_pair(p[0], p[1]);
+    const uint32_t h23 = bf16_pair(p[2], p[3]);
+    const uint32_t l01 = bf16_pair(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+    const uint32_t l23 = bf16_pair(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    const s16x4_t p_hi = as_operand(h01, h23);
+    const s16x4_t p_lo = as_operand(l01, l23);
+
+    const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+    const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+    const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+    const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // dim 8n + 2w (low halves) and 8n + 2w + 1 (high halves) of tokens 4r..4r+3
+        const s16x4_t b_even = as_operand((w0[w] & 0xFFFFu) | (w1[w] << 16), (w2[w] & 0xFFFFu) | (w3[w] << 16));
+        const s16x4_t b_odd = as_operand((w0[w] >> 16) | (w1[w] & 0xFFFF0000u), (w2[w] >> 16) | (w3[w] & 0xFFFF0000u));
+        st.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, b_even, st.o[2 * w], 0, 0, 0);
+        st.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, b_even, st.o[2 * w], 0, 0, 0);
+        st.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, b_odd, st.o[2 * w + 1], 0, 0, 0);
+        st.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, b_odd, st.o[2 * w + 1], 0, 0, 0);
+    }
+}
+
+// End of a walk: lane (r, n) gets the whole softmax sum of head n.
+__device__ __forceinline__ float total_l(const State& st) {
+    float l = st.l + __shfl_xor(st.l, 16, kWave);
+    return l + __shfl_xor(l, 32, kWave);
+}
+
+// Everything one wave needs to walk blocks of one (sequence, KV head).
+struct WalkCtx {
+    const uint4* kpool;
+    const uint4* vpool;
+    size_t head_off;       // kv * tile chunks
+    size_t block_stride;   // num_kv_heads * tile chunks
+    uint32_t num_blocks;
+    int k_off, v_off;      // this lane's 16-byte chunk in a K / V tile
+    int lane, r, n;
+    float sl2;
+};
+
+__device__ __forceinline__ WalkCtx make_ctx(const DecodeArgs& a, int kv) {
+    WalkCtx c;
+    c.lane = threadIdx.x & (kWave - 1);
+    c.r = c.lane >> 4;
+    c.n = c.lane & 15;
+    c.kpool = reinterpret_cast<const uint4*>(a.k_layer);
+    c.vpool = reinterpret_cast<const uint4*>(a.v_layer);
+    c.head_off = (size_t)kv * (kBlockTokens * kRC);
+    c.block_stride = (size_t)a.num_kv_heads * (kBlockTokens * kRC);
+    c.num_blocks = (uint32_t)a.num_blocks;
+    c.k_off = c.n * kRC + c.r;          // K: token n, chunk 4*kk + r
+    c.v_off = (4 * c.r) * kRC + c.n;    // V: token 4r + i, chunk n
+    c.sl2 = a.scale_log2;
+    return c;
+}
+
+// B operand: the group's query heads as columns, zero beyond G.
+template <int G>
+__device__ __forceinline__ void load_q(bf16x8_t (&qb)[kKK], const DecodeArgs& a, int seq, int kv, const WalkCtx& c) {
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.q) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * kRC;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (c.n < G) x = qrow[c.n * kRC + kk * 4 + c.r];
+        qb[kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+}
+
+__device__ __forceinline__ void init_state(State& st) {
+    st.m = -INFINITY;
+    st.l = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// Walk nk blocks of one (sequence, KV head): logical blocks b0 + stride*k,
+// k = 0..nk-1, whose table entries start at trow (= row + b0).
+//
+// Table entries come 64 at a time from one vector load.  Within such a chunk
+// the K/V tiles of block k+1 are in flight while block k is computed.  Every
+// tile load is issued unconditionally (past the end of the chunk the last
+// tile is fetched again, an L2 hit) so the hardware's in-order load counter
+// lets each block wait for its own tile only.
+template <int G>
+__device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* trow, int stride,
+                                     int nk, int b0, int L, const WalkCtx& c) {
+    auto tile_ptrs = [&](int tv, int k, const uint4*& kt, const uint4*& vt) {
+        uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(tv, k);
+        phys = phys < c.num_blocks ? phys : c.num_blocks - 1;   // stay inside the pool whatever the table says
+        const size_t base = (size_t)phys * c.block_stride + c.head_off;
+        kt = c.kpool + base;
+        vt = c.vpool + base;
+    };
+    for (int k0 = 0; k0 < nk; k0 += 64) {
+        const int nc = min(64, nk - k0);
+        const int tv = c.lane < nc ? trow[(size_t)(k0 + c.lane) * stride] : 0;
+        Tile ta, tb;
+        const uint4 *kt, *vt;
+        tile_ptrs(tv, 0, kt, vt);
+        load_tile(ta, kt, vt, c.k_off, c.v_off);
+        for (int k = 0; k < nc; k += 2) {
+            tile_ptrs(tv, min(k + 1, nc - 1), kt, vt);
+            load_tile(tb, kt, vt, c.k_off, c.v_off);
+            __builtin_amdgcn_sched_barrier(0);   // issue the next tile before computing this one
+            process<G>(st, ta, qb, (b0 + (k0 + k) * stride) * kBlockTokens, L, c.r, c.n, c.sl2);
+            tile_ptrs(tv, min(k + 2, nc - 1), kt, vt);
+            load_tile(ta, kt, vt, c.k_off, c.v_off);
+            __builtin_amdgcn_sched_barrier(0);
+            if (k + 1 < nc) process<G>(st, tb, qb, (b0 + (k0 + k + 1) * stride) * kBlockTokens, L, c.r, c.n, c.sl2);
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(DecodeArgs a) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int part = blockIdx.x;
+    const int kv = blockIdx.y;
+    const int seq = blockIdx.z;
+
+    int L = a.lens[seq];
+    L = L < 0 ? 0 : (L > a.max_context ? a.max_context : L);
+    L = __builtin_amdgcn_readfirstlane(L);
+    const int nparts = L == 0 ? 1 : (L + a.part_tokens - 1) / a.part_tokens;
+    if (part >= nparts) return;
+    const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
+    const int bpp = a.part_tokens / kBlockTokens;
+    const int b_begin = part * bpp;
+    const int b_end = min(nblk, b_begin + bpp);
+
+    const WalkCtx c = make_ctx(a, kv);
+    const int r = c.r, n = c.n;
+    bf16x8_t qb[kKK];
+    load_q<G>(qb, a, seq, kv, c);
+    State st;
+    init_state(st);
+
+    const int first = b_begin + wave;
+    const int nk = first < b_end ? (b_end - first + kWaves - 1) / kWaves : 0;
+    walk<G>(st, qb, a.tables + (size_t)seq * a.max_blocks + first, kWaves, nk, first, L, c);
+    const float l_tot = total_l(st);
+
+    // waves of the workgroup merge through LDS
+    __shared__ float sm_m[kWaves][G];
+    __shared__ float sm_l[kWaves][G];
+    __shared__ float sm_acc[kWaves][G][kD];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int h = 4 * r + j;
+        if (h < G) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm_acc[wave][h][n * 8 + e] = st.o[e][j];
+        }
+    }
+    if (r == 0 && n < G) {
+        sm_m[wave][n] = st.m;
+        sm_l[wave][n] = l_tot;
+    }
+    __syncthreads();
+
+    const int hq0 = kv * G;
+    for (int it = threadIdx.x; it < G * (kD / 2); it += kWaves * kWave) {
+        const int h = it / (kD / 2);
+        const int d = (it - h * (kD / 2)) * 2;
+        float M = sm_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+        const float Ms = safe_ref(M);
+        float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = fast_exp2(sm_m[w][h] - Ms);
+            den = fmaf(sm_l[w][h], f, den);
+            n0 = fmaf(sm_acc[w][h][d], f, n0);
+            n1 = fmaf(sm_acc[w][h][d + 1], f, n1);
+        }
+        const size_t row = (size_t)seq * a.num_q_heads + hq0 + h;
+        if (nparts == 1) {
+            const float o0 = den > 0.0f ? n0 / den : 0.0f;
+            const float o1 = den > 0.0f ? n1 / den : 0.0f;
+            reinterpret_cast<uint32_t*>(a.out)[(row * kD + d) / 2] = pack_bf16x2(o0, o1);
+        } else {
+            const size_t slot = row * a.max_parts + part;
+            reinterpret_cast<float2*>(a.ws_acc)[(slot * kD + d) / 2] = make_float2(n0, n1);
+            if (d == 0) reinterpret_cast<float2*>(a.ws_ml)[slot] = make_float2(M, den);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split ("stream-K"): the tiles of all (sequence, KV head) pairs are
+// numbered t = 0..T-1 in (sequence, KV head, block) order and worker w (one
+// wave) takes the contiguous slice [w*T/W, (w+1)*T/W).  Every worker moves
+// the same number of bytes, so none waits for a long sequence at the end.
+// A (sequence, KV head) whose tiles all fall in one slice is written straight
+// to the output; one split over several slices leaves one fp32 partial state
+// per slice (at most two per worker: its first and its last piece) that the
+// fix-up kernel merges.
+// ---------------------------------------------------------------------------
+
+constexpr int kScanChunks = kStreamKMaxSeqs / kWave;   // sequences scanned 64 at a time
+
+__device__ __forceinline__ int clamp_len(int L, int max_context) {
+    return L < 0 ? 0 : (L > max_context ? max_context : L);
+}
+
+// Partial state of one (sequence, KV head) piece: the unnormalised output of
+// each head, then m and l of each head, padded so every record starts on a
+// 16-byte boundary.
+template <int G>
+__host__ __device__ constexpr int record_floats() {
+    return G * kD + ((2 * G + 3) / 4) * 4;
+}
+
+template <int G>
+__device__ __forceinline__ float* record_ptr(const DecodeArgs& a, int64_t slot) {
+    return a.ws_acc + slot * (int64_t)record_floats<G>();
+}
+
+__device__ __forceinline__ int64_t slice_start(int64_t w, int64_t T, int64_t W) { return w * T / W; }
+
+template <int G>
+__global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x;
+    const int64_t W = gridDim.x;
+    const int64_t w = blockIdx.x;
+    const int S = a.num_seqs;
+    const int Hkv = a.num_kv_heads;
+
+    // tiles per sequence and their exclusive prefix sums, 64 sequences per step
+    int ntile[kScanChunks];
+    int64_t carry = 0;
+    int64_t excl[kScanChunks];
+#pragma unroll
+    for (int ch = 0; ch < kScanChunks; ++ch) {
+        const int i = ch * kWave + lane;
+        int L = i < S ? clamp_len(a.lens[i], a.max_context) : 0;
+        ntile[ch] = Hkv * ((L + kBlockTokens - 1) / kBlockTokens);
+        int incl = ntile[ch];
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int y = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += y;
+        }
+        excl[ch] = carry + incl - ntile[ch];
+        if (w == 0 && i < S) a.ws_prefix[i] = excl[ch];
+        carry += __shfl(incl, kWave - 1, kWave);
+        if ((ch + 1) * kWave >= S) break;
+    }
+    const int64_t T = carry;
+    if (w == 0 && lane == 0) a.ws_prefix[S] = T;
+    int64_t t = slice_start(w, T, W);
+    const int64_t t_end = slice_start(w + 1, T, W);
+    if (t >= t_end) return;
+
+    // the sequence holding tile t: the lane whose [excl, excl + ntile) contains it
+    int seq = 0;
+    int64_t seq_first = 0;
+#pragma unroll
+    for (int ch = 0; ch < kScanChunks; ++ch) {
+        if (ch * kWave >= S) break;
+        const bool hit = ntile[ch] > 0 && excl[ch] <= t && t < excl[ch] + ntile[ch];
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
+        if (bal) {
+            const int j = __builtin_ctzll(bal);
+            seq = ch * kWave + j;
+            seq_first = __shfl(excl[ch], j, kWave);
+            break;
+        }
+    }
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    int L = __builtin_amdgcn_readfirstlane(clamp_len(a.lens[seq], a.max_context));
+    int nblk = (L + kBlockTokens - 1) / kBlockTokens;
+    int64_t off = t - seq_first;
+    int kv = (int)(off / nblk);
+    int b = (int)(off - (int64_t)kv * nblk);
+
+    bool first_piece = true;
+    while (t < t_end && seq < S) {
+        const int n_here = (int)min((int64_t)(nblk - b), t_end - t);
+        const bool whole = (b == 0) && (n_here == nblk);
+
+        const WalkCtx c = make_ctx(a, kv);
+        bf16x8_t qb[kKK];
+        load_q<G>(qb, a, seq, kv, c);
+        State st;
+        init_state(st);
+        walk<G>(st, qb, a.tables + (size_t)seq * a.max_blocks + b, 1, n_here, b, L, c);
+        const float l_tot = total_l(st);
+
+        if (whole) {
+            uint4* orow = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * kRC;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * c.r + j;
+                const float lh = __shfl(l_tot, h & 15, kWave);
+                if (h < G) {
+                    const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+                    uint4 o;
+                    o.x = pack_bf16x2(st.o[0][j] * inv, st.o[1][j] * inv);
+                    o.y = pack_bf16x2(st.o[2][j] * inv, st.o[3][j] * inv);
+                    o.z = pack_bf16x2(st.o[4][j] * inv, st.o[5][j] * inv);
+                    o.w = pack_bf16x2(st.o[6][j] * inv, st.o[7][j] * inv);
+                    orow[h * kRC + c.n] = o;
+                }
+            }
+        } else {
+            float* rec = record_ptr<G>(a, 2 * w + (first_piece ? 0 : 1));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * c.r + j;
+                if (h < G) {
+                    float4* dst = reinterpret_cast<float4*>(rec + h * kD + c.n * 8);
+                    dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
+                    dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
+                }
+            }
+            if (c.r == 0 && c.n < G) {
+                rec[G * kD + 2 * c.n] = st.m;
+                rec[G * kD + 2 * c.n + 1] = l_tot;
+            }
+        }
+
+        // next piece
+        t += n_here;
+        first_piece = false;
+        b += n_here;
+        if (b == nblk) {
+            b = 0;
+            if (++kv == Hkv) {
+                kv = 0;
+                do {
+                    ++seq;
+                    L = (seq < S) ? __builtin_amdgcn_readfirstlane(clamp_len(a.lens[seq], a.max_context)) : 0;
+                    nblk = (L + kBlockTokens - 1) / kBlockTokens;
+                } while (nblk == 0 && seq < S && t < t_end);
+            }
+        }
+    }
+}
+
+// Worker whose slice holds tile t (0 <= t < T): the largest w with
+// floor(w T / W) <= t, i.e. w T <= (t + 1) W - 1.
+__device__ __forceinline__ int64_t worker_of(int64_t t, int64_t T, int64_t W) {
+    const int64_t w = ((t + 1) * W - 1) / T;
+    return w < W - 1 ? w : W - 1;
+}
+
+// Fix-up for one (sequence, KV head): zeros for an empty sequence; nothing if
+// one slice held it whole; otherwise the log-sum-exp merge of the partial
+// states its slices left.  With fewer tiles than workers some slices are
+// empty; they left nothing and are skipped.
+//
+// One wave: lanes first read the (m, l) pairs of up to 64 records at once and
+// reduce them across the wave; then each lane sums two dims of every head
+// over the records, several records' loads in flight at a time.
+template <int G>
+__global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int num_workers) {
+    const int kv = blockIdx.x;
+    const int seq = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int L = clamp_len(a.lens[seq], a.max_context);
+    uint32_t* out = reinterpret_cast<uint32_t*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * (kD / 2);
+    if (L == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) out[h * (kD / 2) + lane] = 0u;
+        return;
+    }
+    const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
+    const int64_t T = a.ws_prefix[a.num_seqs];
+    const int64_t W = num_workers;
+    const int64_t s0 = a.ws_prefix[seq] + (int64_t)kv * nblk;
+    const int64_t w0 = worker_of(s0, T, W);
+    const int64_t w1 = worker_of(s0 + nblk - 1, T, W);
+    if (w0 == w1) return;   // written by its worker
+    const int nrec = (int)(w1 - w0 + 1);
+
+    // record slot of worker w0 + j, or -1 for an empty slice
+    auto slot_of = [&](int j) -> int64_t {
+        const int64_t w = w0 + j;
+        const int64_t st = slice_start(w, T, W);
+        if (slice_start(w + 1, T, W) <= st) return -1;
+        return (w == w0 && st < s0) ? 2 * w + 1 : 2 * w;
+    };
+
+    // pass 1: the largest m of every head over all records
+    float M[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) M[h] = -INFINITY;
+    for (int j0 = 0; j0 < nrec; j0 += kWave) {
+        const int j = j0 + lane;
+        const int64_t slot = j < nrec ? slot_of(j) : -1;
+        if (slot >= 0) {
+            const float* ml = record_ptr<G>(a, slot) + G * kD;
+#pragma unroll
+            for (int h = 0; h < G; ++h) M[h] = fmaxf(M[h], ml[2 * h]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M[h] = fmaxf(M[h], __shfl_xor(M[h], off, kWave));
+
+    // pass 2: weights, denominators and the weighted outputs
+    float den[G], n0[G], n1[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) den[h] = n0[h] = n1[h] = 0.0f;
+    const int d = lane * 2;
+    for (int j0 = 0; j0 < nrec; j0 += kWave) {
+        const int j = j0 + lane;
+        const int64_t slot = j < nrec ? slot_of(j) : -1;
+        float f[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) f[h] = 0.0f;
+        if (slot >= 0) {
+            const float* ml = record_ptr<G>(a, slot) + G * kD;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                f[h] = fast_exp2(ml[2 * h] - safe_ref(M[h]));
+                den[h] = fmaf(ml[2 * h + 1], f[h], den[h]);
+            }
+        }
+        const int cnt = min(kWave, nrec - j0);
+        constexpr int kU = 4;   // records whose loads are in flight together
+        for (int jj = 0; jj < cnt; jj += kU) {
+            float2 x[kU][G];
+            float fj[kU][G];
+            bool live[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int src = min(jj + u, cnt - 1);
+                const int64_t sl = __shfl(slot, src, kWave);
+                live[u] = (jj + u < cnt) && sl >= 0;
+                const float* rec = record_ptr<G>(a, sl >= 0 ? sl : 0);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    fj[u][h] = __shfl(f[h], src, kWave);
+                    x[u][h] = live[u] ? *reinterpret_cast<const float2*>(rec + h * kD + d) : make_float2(0.0f, 0.0f);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (!live[u]) continue;
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    n0[h] = fmaf(x[u][h].x, fj[u][h], n0[h]);
+                    n1[h] = fmaf(x[u][h].y, fj[u][h], n1[h]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) den[h] += __shfl_xor(den[h], off, kWave);
+        const float inv = den[h] > 0.0f ? 1.0f / den[h] : 0.0f;
+        out[h * (kD / 2) + lane] = pack_bf16x2(n0[h] * inv, n1[h] * inv);
+    }
+}
+
+template <int G>
+const void* streamk_kernel_ptr() {
+    return reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G>);
+}
+
+}  // namespace
+
+int streamk_workers(int group) {
+    // one resident wave per worker: compute units x single-wave workgroups that fit on one
+    constexpr int kMaxDev = 16;
+    static int cached[kMaxDev][9] = {};
+    if (group < 1 || group > 8) return 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+        (void)hipGetLastError();
+        return kStreamKDefaultWorkers;
+    }
+    if (cached[dev][group]) return cached[dev][group];
+    int cus = 0, per_cu = 0;
+    const void* fn = nullptr;
+    switch (group) {
+        case 1: fn = streamk_kernel_ptr<1>(); break;
+        case 2: fn = streamk_kernel_ptr<2>(); break;
+        case 4: fn = streamk_kernel_ptr<4>(); break;
+        case 8: fn = streamk_kernel_ptr<8>(); break;
+        default: return 0;
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kWave, 0) != hipSuccess || cus <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();
+        return kStreamKDefaultWorkers;
+    }
+    cached[dev][group] = cus * per_cu;
+    return cached[dev][group];
+}
+
+hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+    dim3 grid((unsigned)workers);
+    dim3 fix((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+    switch (group) {
+        case 1: decode_bf16_streamk_kernel<1><<<grid, kWave, 0, stream>>>(a); break;
+        case 2: decode_bf16_streamk_kernel<2><<<grid, kWave, 0, stream>>>(a); break;
+        case 4: decode_bf16_streamk_kernel<4><<<grid, kWave, 0, stream>>>(a); break;
+        case 8: decode_bf16_streamk_kernel<8><<<grid, kWave, 0, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (group) {
+        case 1: streamk_fixup_kernel<1><<<fix, kWave, 0, stream>>>(a, workers); break;
+        case 2: streamk_fixup_kernel<2><<<fix, kWave, 0, stream>>>(a, workers); break;
+        case 4: streamk_fixup_kernel<4><<<fix, kWave, 0, stream>>>(a, workers); break;
+        case 8: streamk_fixup_kernel<8><<<fix, kWave, 0, stream>>>(a, workers); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
+    dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
+    dim3 block(kWaves * kWave);
+    switch (group) {
+        case 1: decode_bf16_mfma_kernel<1><<<grid, block, 0, stream>>>(a); break;
+        case 2: decode_bf16_mfma_kernel<2><<<grid, block, 0, stream>>>(a); break;
+        case 4: decode_bf16_mfma_kernel<4><<<grid, block, 0, stream>>>(a); break;
+        case 8: decode_bf16_mfma_kernel<8><<<grid, block, 0, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvp

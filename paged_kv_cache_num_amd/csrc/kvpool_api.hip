@@ -63,31 +63,49 @@ kv_status hip_fail(hipError_t e, const char* what) {
 
 uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
-// Partition geometry shared by the workspace query and the launch.
-struct PartGeo {
-    int32_t part_tokens;
+// How one decode call is laid out; shared by the workspace query and the launch.
+enum class Mode { kSingle, kPartitions, kBalanced };
+
+struct Plan {
+    Mode mode;
+    int32_t part_tokens;   // tokens per partition (kSingle: covers max_context_len)
     int32_t max_parts;
+    int32_t workers;       // kBalanced only
+    uint64_t ws_first;     // bytes of the first workspace region (ml pairs, or tile prefix sums)
+    uint64_t ws_total;
 };
 
-PartGeo part_geo(int32_t max_context_len, int32_t partition_size, int32_t block_size) {
-    PartGeo g;
-    if (partition_size == 0 || partition_size >= max_context_len) {
-        int32_t whole = (int32_t)round_up((uint64_t)(max_context_len > 0 ? max_context_len : 1), (uint64_t)block_size);
-        g.part_tokens = partition_size > whole ? partition_size : whole;
-        g.max_parts = 1;
-    } else {
-        g.part_tokens = partition_size;
-        g.max_parts = (max_context_len + partition_size - 1) / partition_size;
+Plan plan_decode(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                 int32_t partition_size) {
+    Plan p;
+    memset(&p, 0, sizeof p);
+    const int group = num_q_heads / d.num_kv_heads;
+    if (partition_size == 0 && d.dtype == KV_BF16 && d.head_dim == 128 && num_seqs <= kvp::kStreamKMaxSeqs) {
+        p.mode = Mode::kBalanced;
+        p.workers = kvp::streamk_workers(group);
+        p.part_tokens = 0;
+        p.max_parts = 1;
+        p.ws_first = round_up((uint64_t)(num_seqs + 1) * 8u, 256u);
+        // two partial records per worker: group x head_dim outputs, then (m, l) per head padded to 16 bytes
+        const uint64_t rec_floats = (uint64_t)group * (uint64_t)d.head_dim + (uint64_t)((2 * group + 3) / 4) * 4u;
+        p.ws_total = p.ws_first + 2ull * (uint64_t)p.workers * rec_floats * 4u;
+        return p;
     }
-    return g;
-}
-
-// Workspace split: (m, l) pairs first, then the fp32 partial outputs at a 256-byte boundary.
-void workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t max_parts, int32_t head_dim,
-                      uint64_t* ml_bytes, uint64_t* total) {
-    const uint64_t entries = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)max_parts;
-    *ml_bytes = round_up(entries * 8u, 256u);
-    *total = *ml_bytes + entries * (uint64_t)head_dim * 4u;
+    if (partition_size == 0 || partition_size >= max_context_len) {
+        int32_t whole = (int32_t)round_up((uint64_t)(max_context_len > 0 ? max_context_len : 1), (uint64_t)d.block_size);
+        p.mode = Mode::kSingle;
+        p.part_tokens = partition_size > whole ? partition_size : whole;
+        p.max_parts = 1;
+        return p;
+    }
+    p.mode = Mode::kPartitions;
+    p.part_tokens = partition_size;
+    p.max_parts = (max_context_len + partition_size - 1) / partition_size;
+    // (m, l) pairs first, then the fp32 partial outputs at a 256-byte boundary
+    const uint64_t entries = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)p.max_parts;
+    p.ws_first = round_up(entries * 8u, 256u);
+    p.ws_total = p.ws_first + entries * (uint64_t)d.head_dim * 4u;
+    return p;
 }
 
 }  // namespace
@@ -217,11 +235,10 @@ kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int3
     if (partition_size % pool->desc.block_size != 0)
         return fail(KV_ERR_INVALID_ARGUMENT, "partition_size %d is not a multiple of the block size %d", partition_size,
                     pool->desc.block_size);
-    PartGeo g = part_geo(max_context_len, partition_size, pool->desc.block_size);
-    if (g.max_parts > 1) {
-        uint64_t ml = 0;
-        workspace_layout(num_seqs, num_q_heads, g.max_parts, pool->desc.head_dim, &ml, bytes);
-    }
+    if (num_q_heads % pool->desc.num_kv_heads != 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                    pool->desc.num_kv_heads);
+    *bytes = plan_decode(pool->desc, num_seqs, num_q_heads, max_context_len, partition_size).ws_total;
     return ok();
 }
 
@@ -247,7 +264,7 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * d.block_size)
         return fail(KV_ERR_INVALID_ARGUMENT, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
                     max_context_len, (long long)max_blocks_per_seq * d.block_size);
-    if (!std::isfinite(scale)) return fail(KV_ERR_INVALID_ARGUMENT, "scale is not finite");
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(KV_ERR_INVALID_ARGUMENT, "scale must be finite and positive");
     if (num_seqs > 65535 || num_q_heads > 65535)
         return fail(KV_ERR_UNSUPPORTED, "num_seqs %d / num_q_heads %d above the 65535 grid limit", num_seqs, num_q_heads);
     if (num_seqs == 0) return ok();
@@ -256,18 +273,21 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
     if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(context_lens)) & 3u)
         return fail(KV_ERR_INVALID_ARGUMENT, "block_tables/context_lens must be 4-byte aligned");
 
-    PartGeo g = part_geo(max_context_len, partition_size, d.block_size);
+    const Plan plan = plan_decode(d, num_seqs, num_q_heads, max_context_len, partition_size);
     kvp::DecodeArgs a;
     memset(&a, 0, sizeof a);
-    if (g.max_parts > 1) {
-        uint64_t ml = 0, need = 0;
-        workspace_layout(num_seqs, num_q_heads, g.max_parts, d.head_dim, &ml, &need);
-        if (!workspace || workspace_bytes < need)
+    if (plan.ws_total > 0) {
+        if (!workspace || workspace_bytes < plan.ws_total)
             return fail(KV_ERR_WORKSPACE_TOO_SMALL, "workspace of %llu bytes given, %llu needed",
-                        (unsigned long long)workspace_bytes, (unsigned long long)need);
+                        (unsigned long long)workspace_bytes, (unsigned long long)plan.ws_total);
         if (!aligned16(workspace)) return fail(KV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-        a.ws_ml = static_cast<float*>(workspace);
-        a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+        char* ws = static_cast<char*>(workspace);
+        if (plan.mode == Mode::kBalanced) {
+            a.ws_prefix = reinterpret_cast<int64_t*>(ws);
+        } else {
+            a.ws_ml = reinterpret_cast<float*>(ws);
+        }
+        a.ws_acc = reinterpret_cast<float*>(ws + plan.ws_first);
     }
     a.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
     a.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
@@ -281,10 +301,15 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
     a.num_kv_heads = d.num_kv_heads;
     a.num_blocks = d.num_blocks;
     a.max_context = max_context_len;
-    a.part_tokens = g.part_tokens;
-    a.max_parts = g.max_parts;
+    a.part_tokens = plan.part_tokens;
+    a.max_parts = plan.max_parts;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // exp(x) = 2^(x log2 e)
-    hipError_t e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (plan.mode == Mode::kBalanced) {
+        e = kvp::launch_decode_bf16_streamk(a, num_q_heads / d.num_kv_heads, plan.workers, static_cast<hipStream_t>(stream));
+    } else {
+        e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
+    }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
 }

@@ -7,6 +7,8 @@
 namespace kvp {
 
 constexpr int kBlockTokens = 16;   // tokens per KV block the kernels are built for
+constexpr int kStreamKMaxSeqs = 1024;        // batch size up to which the balanced split is used
+constexpr int kStreamKDefaultWorkers = 2048; // worker count when no device can be queried
 
 struct ScatterArgs {
     void* k_layer;               // layer base of the K pool
@@ -29,8 +31,9 @@ struct DecodeArgs {
     void* out;                   // [S][Hq][D]
     const int32_t* tables;       // [S][max_blocks]
     const int32_t* lens;         // [S]
-    float* ws_ml;                // [S][Hq][max_parts] x (m, l), or null
-    float* ws_acc;               // [S][Hq][max_parts][D], or null
+    float* ws_ml;                // partitions: [S][Hq][max_parts] x (m, l), or null
+    float* ws_acc;               // partitions: [S][Hq][max_parts][D]; balanced split: partial records
+    int64_t* ws_prefix;          // balanced split: tiles before each sequence, [S + 1]
     int32_t max_blocks;
     int32_t num_seqs;
     int32_t num_q_heads;
@@ -45,5 +48,15 @@ struct DecodeArgs {
 // dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for a shape without a kernel.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 bool decode_shape_supported(int dtype, int head_dim, int group);
+
+// bf16 pools with head_dim 128: scores on the matrix cores (decode_mfma.hip).
+// Launches the decode kernel only; the caller launches the partition merge.
+hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t stream);
+
+// bf16 / head_dim 128, balanced split over `workers` single-wave workers plus
+// the fix-up of split (sequence, KV head) pairs; no partition merge needed.
+hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
+// Worker count for the balanced split on the current device (resident waves).
+int streamk_workers(int group);
 
 }  // namespace kvp

@@ -30,7 +30,7 @@ KV_BF16 = 1
 EXPORTED = (
     "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
-    "kv_status_string", "kv_last_error_message", "kv_probe_copy",
+    "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read",
 )
 
 
@@ -78,6 +78,8 @@ def _load():
     lib.paged_attention_decode.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32, vp, u64, vp]
     lib.kv_probe_copy.restype = ctypes.c_int
     lib.kv_probe_copy.argtypes = [vp, vp, u64, vp]
+    lib.kv_probe_read.restype = ctypes.c_int
+    lib.kv_probe_read.argtypes = [vp, u64, vp, vp]
     return lib
 
 
@@ -251,3 +253,11 @@ def probe_copy(dst, src, stream=None) -> None:
         raise ValueError("copy probe needs equal sizes")
     _check(lib.kv_probe_copy(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), nbytes, _stream_handle(stream)),
            "kv_probe_copy")
+
+
+def probe_read(src, sink, stream=None) -> None:
+    """Measurement probe: read all of src (16-byte loads); sink takes >= 64 KiB of words."""
+    if sink.numel() * sink.element_size() < 65536:
+        raise ValueError("sink must hold at least 64 KiB")
+    _check(lib.kv_probe_read(_dev_ptr(src, "src"), src.numel() * src.element_size(), _dev_ptr(sink, "sink"),
+                             _stream_handle(stream)), "kv_probe_read")

@@ -184,6 +184,8 @@ def test_decode_argument_checks_return_before_any_launch():
     assert _decode(h, part=40) == E.KV_ERR_INVALID_ARGUMENT       # not a multiple of B
     assert _decode(h, max_ctx=16 * 16 + 1) == E.KV_ERR_INVALID_ARGUMENT
     assert _decode(h, scale=float("nan")) == E.KV_ERR_INVALID_ARGUMENT
+    assert _decode(h, scale=0.0) == E.KV_ERR_INVALID_ARGUMENT
+    assert _decode(h, scale=-0.5) == E.KV_ERR_INVALID_ARGUMENT
     assert _decode(h, out=0x30000008) == E.KV_ERR_INVALID_ARGUMENT
     assert _decode(h, q=None) == E.KV_ERR_INVALID_ARGUMENT
     assert _decode(h, part=64) == E.KV_ERR_WORKSPACE_TOO_SMALL
@@ -197,13 +199,23 @@ def test_decode_argument_checks_return_before_any_launch():
 def test_workspace_size_formula():
     st, h = _pool(head_dim=128, num_kv_heads=8, dtype="bf16")
     out = ctypes.c_uint64(0)
+    # partitions: (m, l) pairs padded to 256 bytes, then D fp32 per (seq, head, partition)
     assert K.lib.paged_attention_workspace_bytes(h, 8, 32, 131072, 512, ctypes.byref(out)) == K.KV_OK
     parts = 131072 // 512
     entries = 8 * 32 * parts
     assert out.value == -(-entries * 8 // 256) * 256 + entries * 128 * 4
-    assert K.lib.paged_attention_workspace_bytes(h, 8, 32, 4096, 0, ctypes.byref(out)) == K.KV_OK
-    assert out.value == 0
+    # one partition covering the longest context: no workspace
     assert K.lib.paged_attention_workspace_bytes(h, 8, 32, 4096, 4096, ctypes.byref(out)) == K.KV_OK
+    assert out.value == 0
+    # balanced split: tile prefix sums, then two partial states (4 heads x 128 fp32 + 8 fp32) per worker
+    assert K.lib.paged_attention_workspace_bytes(h, 64, 32, 4096, 0, ctypes.byref(out)) == K.KV_OK
+    prefix = -(-(64 + 1) * 8 // 256) * 256
+    workers, rem = divmod(out.value - prefix, 2 * (4 * 128 + 8) * 4)
+    assert rem == 0 and workers >= 1
+    K.lib.kv_pool_destroy(h)
+    # fp32 pools walk each context in one workgroup: no workspace
+    st, h = _pool(head_dim=64, num_kv_heads=2, dtype="f32")
+    assert K.lib.paged_attention_workspace_bytes(h, 4, 8, 200, 0, ctypes.byref(out)) == K.KV_OK
     assert out.value == 0
     K.lib.kv_pool_destroy(h)
 

@@ -43,45 +43,49 @@ def test_c2_llama8b_decode(variant, partition):
 
 
 @pytest.mark.parametrize("variant", ["spec", "sharp", "needle"])
-def test_c3_70b_gqa8_with_prefill_scatter(variant):
-    say(f"C3 variant={variant} S=256 Hq=64 Hkv=8 D=128 bf16, 2048-token prefill chunk")
+@pytest.mark.parametrize("partition", [0, 512])
+def test_c3_70b_gqa8_with_prefill_scatter(variant, partition):
+    say(f"C3 variant={variant} partition={partition} S=256 Hq=64 Hkv=8 D=128 bf16, 2048-token prefill chunk")
     wl = workload("C3", variant)
     ref = reference("C3", variant)
-    step = run_gpu(wl, partition_size=512)
-    check_step(step, wl, ref, label=f"C3/{variant}")
+    step = run_gpu(wl, partition_size=partition)
+    check_step(step, wl, ref, label=f"C3/{variant}/p{partition}")
 
 
-def test_c4_prefix_sharing_equals_private_copies():
-    say("C4 sharp S=128 shared 2048-token prefix")
+@pytest.mark.parametrize("partition", [0, 512])
+def test_c4_prefix_sharing_equals_private_copies(partition):
+    say(f"C4 sharp S=128 shared 2048-token prefix, partition={partition}")
     wl = workload("C4", "sharp")
     ref = reference("C4", "sharp")
-    shared = run_gpu(wl, partition_size=512)
-    check_step(shared, wl, ref, label="C4/shared")
+    shared = run_gpu(wl, partition_size=partition)
+    check_step(shared, wl, ref, label=f"C4/shared/p{partition}")
     priv = kvgen.privatize_blocks(wl)
     say("C4 private copies")
-    private = run_gpu(priv, partition_size=512)
+    private = run_gpu(priv, partition_size=partition)
     assert np.array_equal(shared.out_host(), private.out_host()), "shared and private copies differ"
 
 
 @pytest.mark.parametrize("variant", ["sharp", "needle"])
-def test_c5_long_context_split(variant):
-    say(f"C5 variant={variant} S=8 L in [32768,131072] partition=512")
+@pytest.mark.parametrize("partition", [512, 0])
+def test_c5_long_context_split(variant, partition):
+    say(f"C5 variant={variant} S=8 L in [32768,131072] partition={partition}")
     wl = workload("C5", variant)
     ref = reference("C5", variant)
-    step = run_gpu(wl, partition_size=512)
-    check_step(step, wl, ref, label=f"C5/{variant}")
+    step = run_gpu(wl, partition_size=partition)
+    check_step(step, wl, ref, label=f"C5/{variant}/p{partition}")
 
 
 # ------------------------------------------------------------ invariances --
 
-def test_bitwise_invariance_to_block_placement():
-    say("C2 sharp: permuted and contiguous placements")
+@pytest.mark.parametrize("partition", [0, 512])
+def test_bitwise_invariance_to_block_placement(partition):
+    say(f"C2 sharp: permuted and contiguous placements, partition={partition}")
     wl = workload("C2", "sharp")
-    base = run_gpu(wl, partition_size=512).out_host()
+    base = run_gpu(wl, partition_size=partition).out_host()
     for seed in (1, 2):
-        perm = run_gpu(kvgen.permute_blocks(wl, seed), partition_size=512).out_host()
+        perm = run_gpu(kvgen.permute_blocks(wl, seed), partition_size=partition).out_host()
         assert np.array_equal(base, perm), f"permutation {seed} changed the output bits"
-    dense = run_gpu(kvgen.privatize_blocks(wl, contiguous=True), partition_size=512).out_host()
+    dense = run_gpu(kvgen.privatize_blocks(wl, contiguous=True), partition_size=partition).out_host()
     assert np.array_equal(base, dense), "identity (contiguous) tables changed the output bits"
 
 
@@ -118,6 +122,12 @@ EDGE = [
     ("f32", 16, 2, 64, [4096, 31], 0),                  # fp32, g = 8
     ("bf16", 32, 8, 128, [0, 7, 0, 40], 0),             # empty sequences
     ("bf16", 32, 8, 128, [0, 7, 0, 1600], 512),         # empty sequences, split
+    ("bf16", 64, 8, 128, [0, 0, 0], 0),                 # nothing to attend to at all
+    ("bf16", 8, 8, 128, [1], 0),                        # fewer tiles than workers
+    ("bf16", 16, 8, 128, [3000, 1, 0, 17, 4096, 33], 0),  # ragged, balanced split, g = 2
+    ("bf16", 64, 8, 128, [5000, 20, 700], 0),           # g = 8, balanced split
+    ("bf16", 16, 8, 128, [1, 2, 15, 16, 17], 0),        # fewer tiles than workers, split pairs (g = 2)
+    ("bf16", 8, 8, 128, [40, 300], 0),                  # fewer tiles than workers, split pairs (g = 1)
 ]
 
 
