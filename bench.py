@@ -95,6 +95,63 @@ def traffic_for(config: str, partition: int):
     return entry.get("traffic_bytes_per_launch")
 
 
+ATTN_KERNEL_MARKERS = ("decode_bf16_streamk_kernel", "streamk_fixup_kernel", "decode_bf16_mfma_kernel",
+                       "decode_kernel", "reduce_kernel")
+
+
+def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, config: str, partition: int,
+                   command: str) -> dict:
+    """HBM bytes per attention call from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE).
+
+    Each counter is scaled by what it reads for the copy probe of copy_mib MiB
+    (known to read and write exactly that many bytes), then the kernels of one
+    attention call (decode + merge) are summed, averaged over dispatches.
+    """
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        out = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return out
+
+    known = float(copy_mib << 20)
+    res = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        k = per_kernel(path, counter)
+        copy = [v for name, vs in k.items() if "copy_kernel" in name for v in vs]
+        if not copy:
+            raise SystemExit(f"no copy-probe dispatch in {path}")
+        factor = known / (statistics.median(copy) * 1024.0)
+        attn = {name: statistics.mean(vs) for name, vs in k.items()
+                if any(m in name for m in ATTN_KERNEL_MARKERS)}
+        res[counter] = {"factor": round(factor, 4),
+                        "kib_per_dispatch": {n.replace("(anonymous namespace)::", "").split("(")[0][-60:]: round(v, 1)
+                                             for n, v in attn.items()},
+                        "bytes_per_call": sum(attn.values()) * 1024.0 * factor}
+    entry = {"traffic_bytes_per_launch": round(res["FETCH_SIZE"]["bytes_per_call"] + res["WRITE_SIZE"]["bytes_per_call"]),
+             "fetch_bytes_per_launch": round(res["FETCH_SIZE"]["bytes_per_call"]),
+             "write_bytes_per_launch": round(res["WRITE_SIZE"]["bytes_per_call"]),
+             "fetch_factor": res["FETCH_SIZE"]["factor"], "write_factor": res["WRITE_SIZE"]["factor"],
+             "fetch_kib_per_dispatch": res["FETCH_SIZE"]["kib_per_dispatch"],
+             "write_kib_per_dispatch": res["WRITE_SIZE"]["kib_per_dispatch"],
+             "kernel_source_sha256": kernel_sha(), "command": command}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[f"{config}/p{partition}"] = entry
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    return entry
+
+
 def percentile(xs, q):
     xs = sorted(xs)
     if not xs:
@@ -128,7 +185,18 @@ def main(argv=None):
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing pass")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="also run the copy probe once on buffers of this size (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run made with "
+                         "--probe-copy-mib into the traffic record used by the roofline line, and exit")
+    ap.add_argument("--record-command", default="", help="command line stored with --record-traffic")
     args = ap.parse_args(argv)
+
+    if args.record_traffic:
+        part = DEFAULT_PARTITION[args.config] if args.partition is None else args.partition
+        entry = record_traffic(args.record_traffic[0], args.record_traffic[1], args.probe_copy_mib or 1024,
+                               args.config, part, args.record_command)
+        print(json.dumps(entry))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

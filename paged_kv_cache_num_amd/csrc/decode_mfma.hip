@@ -61,6 +61,16 @@ __device__ __forceinline__ float row_bcast(float x) {
 
 __device__ __forceinline__ float safe_ref(float m) { return m == -INFINITY ? 0.0f : m; }
 
+// Value of lane `src` (wave-uniform) in every lane, without going through LDS.
+__device__ __forceinline__ float readlane_f(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+}
+__device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), src);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 struct Tile {
     uint4 k[kKK];   // K: token n, dims 32*kk + 8*r .. +8
     uint4 v[4];     // V: token 4*r + i, chunk c
@@ -124,12 +134,15 @@ __device__ __forceinline__ void process(State& st, const Tile& t, const bf16x8_t
         }
     }
 
-    // block max of head n over all 16 tokens (rows hold 4 tokens each)
+    // This row's max of head n.  The reference m is shared by the four rows
+    // (their P meet in one MFMA), so it only moves, to the block max over all
+    // rows, when some row would exceed it by more than 2^kLazy.
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * sl2;
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const bool need = (n < G) && (mx > st.m + kLazy);
-    if (__builtin_amdgcn_ballot_w64(need)) {   // rare after the first block
+    const bool row_need = (n < G) && (mx > st.m + kLazy);
+    if (__builtin_amdgcn_ballot_w64(row_need)) {   // rare after the first block
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const bool need = (n < G) && (mx > st.m + kLazy);
         const float m_new = need ? mx : st.m;
         const float corr = need ? fast_exp2(st.m - m_new) : 1.0f;   // 0 when nothing was seen yet
         st.l *= corr;
@@ -348,8 +361,6 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
 // fix-up kernel merges.
 // ---------------------------------------------------------------------------
 
-constexpr int kScanChunks = kStreamKMaxSeqs / kWave;   // sequences scanned 64 at a time
-
 __device__ __forceinline__ int clamp_len(int L, int max_context) {
     return L < 0 ? 0 : (L > max_context ? max_context : L);
 }
@@ -377,27 +388,31 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     const int S = a.num_seqs;
     const int Hkv = a.num_kv_heads;
 
-    // tiles per sequence and their exclusive prefix sums, 64 sequences per step
-    int ntile[kScanChunks];
-    int64_t carry = 0;
-    int64_t excl[kScanChunks];
-#pragma unroll
-    for (int ch = 0; ch < kScanChunks; ++ch) {
+    // tiles per sequence: one pass for the total (worker 0 also records the
+    // exclusive prefix sums for the fix-up), a second to find the sequence
+    // holding this worker's first tile; 64 sequences per step.
+    auto chunk_scan = [&](int ch, int& nt, int64_t& excl_lane, int64_t carry) -> int64_t {
         const int i = ch * kWave + lane;
-        int L = i < S ? clamp_len(a.lens[i], a.max_context) : 0;
-        ntile[ch] = Hkv * ((L + kBlockTokens - 1) / kBlockTokens);
-        int incl = ntile[ch];
+        const int Li = i < S ? clamp_len(a.lens[i], a.max_context) : 0;
+        nt = Hkv * ((Li + kBlockTokens - 1) / kBlockTokens);
+        int incl = nt;
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
             const int y = __shfl_up(incl, off, kWave);
             if (lane >= off) incl += y;
         }
-        excl[ch] = carry + incl - ntile[ch];
-        if (w == 0 && i < S) a.ws_prefix[i] = excl[ch];
-        carry += __shfl(incl, kWave - 1, kWave);
-        if ((ch + 1) * kWave >= S) break;
+        excl_lane = carry + incl - nt;
+        return carry + __shfl(incl, kWave - 1, kWave);
+    };
+    const int nchunks = (S + kWave - 1) / kWave;
+    int64_t T = 0;
+    for (int ch = 0; ch < nchunks; ++ch) {
+        int nt;
+        int64_t ex;
+        const int64_t next = chunk_scan(ch, nt, ex, T);
+        if (w == 0 && ch * kWave + lane < S) a.ws_prefix[ch * kWave + lane] = ex;
+        T = next;
     }
-    const int64_t T = carry;
     if (w == 0 && lane == 0) a.ws_prefix[S] = T;
     int64_t t = slice_start(w, T, W);
     const int64_t t_end = slice_start(w + 1, T, W);
@@ -406,16 +421,21 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     // the sequence holding tile t: the lane whose [excl, excl + ntile) contains it
     int seq = 0;
     int64_t seq_first = 0;
-#pragma unroll
-    for (int ch = 0; ch < kScanChunks; ++ch) {
-        if (ch * kWave >= S) break;
-        const bool hit = ntile[ch] > 0 && excl[ch] <= t && t < excl[ch] + ntile[ch];
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
-        if (bal) {
-            const int j = __builtin_ctzll(bal);
-            seq = ch * kWave + j;
-            seq_first = __shfl(excl[ch], j, kWave);
-            break;
+    {
+        int64_t carry = 0;
+        for (int ch = 0; ch < nchunks; ++ch) {
+            int nt;
+            int64_t ex;
+            const int64_t next = chunk_scan(ch, nt, ex, carry);
+            const bool hit = nt > 0 && ex <= t && t < ex + nt;
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
+            if (bal) {
+                const int j = __builtin_ctzll(bal);
+                seq = ch * kWave + j;
+                seq_first = __shfl(ex, j, kWave);
+                break;
+            }
+            carry = next;
         }
     }
     seq = __builtin_amdgcn_readfirstlane(seq);
@@ -533,76 +553,73 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
         return (w == w0 && st < s0) ? 2 * w + 1 : 2 * w;
     };
 
-    // pass 1: the largest m of every head over all records
-    float M[G];
+    // Records are taken 64 at a time: lane j holds the (m, l) pairs of record
+    // j0 + j; all lanes read two dims of each record's outputs, kU records'
+    // loads in flight together and issued before the (m, l) reduction.
+    constexpr int kU = 8;
+    float M[G], den[G], n0[G], n1[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) M[h] = -INFINITY;
-    for (int j0 = 0; j0 < nrec; j0 += kWave) {
-        const int j = j0 + lane;
-        const int64_t slot = j < nrec ? slot_of(j) : -1;
-        if (slot >= 0) {
-            const float* ml = record_ptr<G>(a, slot) + G * kD;
-#pragma unroll
-            for (int h = 0; h < G; ++h) M[h] = fmaxf(M[h], ml[2 * h]);
-        }
+    for (int h = 0; h < G; ++h) {
+        M[h] = -INFINITY;
+        den[h] = n0[h] = n1[h] = 0.0f;
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) M[h] = fmaxf(M[h], __shfl_xor(M[h], off, kWave));
-
-    // pass 2: weights, denominators and the weighted outputs
-    float den[G], n0[G], n1[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) den[h] = n0[h] = n1[h] = 0.0f;
     const int d = lane * 2;
     for (int j0 = 0; j0 < nrec; j0 += kWave) {
-        const int j = j0 + lane;
-        const int64_t slot = j < nrec ? slot_of(j) : -1;
-        float f[G];
+        const int cnt = min(kWave, nrec - j0);
+        const int64_t slot = lane < cnt ? slot_of(j0 + lane) : -1;
+        float m_j[G], l_j[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) f[h] = 0.0f;
+        for (int h = 0; h < G; ++h) {
+            m_j[h] = -INFINITY;
+            l_j[h] = 0.0f;
+        }
         if (slot >= 0) {
             const float* ml = record_ptr<G>(a, slot) + G * kD;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                f[h] = fast_exp2(ml[2 * h] - safe_ref(M[h]));
-                den[h] = fmaf(ml[2 * h + 1], f[h], den[h]);
+                m_j[h] = ml[2 * h];
+                l_j[h] = ml[2 * h + 1];
             }
         }
-        const int cnt = min(kWave, nrec - j0);
-        constexpr int kU = 4;   // records whose loads are in flight together
         for (int jj = 0; jj < cnt; jj += kU) {
             float2 x[kU][G];
-            float fj[kU][G];
             bool live[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                const int src = min(jj + u, cnt - 1);
-                const int64_t sl = __shfl(slot, src, kWave);
+                const int64_t sl = readlane64(slot, min(jj + u, cnt - 1));
                 live[u] = (jj + u < cnt) && sl >= 0;
-                const float* rec = record_ptr<G>(a, sl >= 0 ? sl : 0);
+                const float* rec = record_ptr<G>(a, live[u] ? sl : 0);
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    fj[u][h] = __shfl(f[h], src, kWave);
+                for (int h = 0; h < G; ++h)
                     x[u][h] = live[u] ? *reinterpret_cast<const float2*>(rec + h * kD + d) : make_float2(0.0f, 0.0f);
-                }
             }
+            // running reference: rescale what was summed so far when the max moves
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                if (!live[u]) continue;
+            for (int h = 0; h < G; ++h) {
+                float mb = -INFINITY;
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    n0[h] = fmaf(x[u][h].x, fj[u][h], n0[h]);
-                    n1[h] = fmaf(x[u][h].y, fj[u][h], n1[h]);
+                for (int u = 0; u < kU; ++u) mb = fmaxf(mb, readlane_f(m_j[h], min(jj + u, cnt - 1)));
+                const float m_new = fmaxf(M[h], mb);
+                const float corr = fast_exp2(M[h] - safe_ref(m_new));
+                n0[h] *= corr;
+                n1[h] *= corr;
+                den[h] *= corr;
+                M[h] = m_new;
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const int src = min(jj + u, cnt - 1);
+                    const float mj = readlane_f(m_j[h], src);
+                    const float lj = readlane_f(l_j[h], src);
+                    const float f = live[u] ? fast_exp2(mj - safe_ref(M[h])) : 0.0f;
+                    den[h] = fmaf(lj, f, den[h]);
+                    n0[h] = fmaf(x[u][h].x, f, n0[h]);
+                    n1[h] = fmaf(x[u][h].y, f, n1[h]);
                 }
             }
         }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) den[h] += __shfl_xor(den[h], off, kWave);
         const float inv = den[h] > 0.0f ? 1.0f / den[h] : 0.0f;
         out[h * (kD / 2) + lane] = pack_bf16x2(n0[h] * inv, n1[h] * inv);
     }
