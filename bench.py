@@ -11,6 +11,11 @@ Default workload: Llama-3-8B-shaped decode layer (64 sequences, 32 query /
 8 KV heads, head_dim 128, block 16, context lengths U[512, 4096], block tables
 from a shuffled free list over a pool of 1.25x the blocks needed, bf16).
 
+The K timed steps are replays of one captured HIP graph holding the step's
+launches (how a serving loop submits its decode step); ``--eager`` times
+eager launches instead.  The attention call's own duration, from events
+around each of K eager calls, gives the roofline figure.
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
 """
 from __future__ import annotations
@@ -183,6 +188,8 @@ def main(argv=None):
     ap.add_argument("--variant", default="spec")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing pass")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step from eager launches only (default: replays of a captured HIP graph)")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="also run the copy probe once on buffers of this size (counter calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -281,6 +288,23 @@ def main(argv=None):
     attn_mean = sum(attn_us) / K
     achieved = nbytes["attn"] / (attn_mean * 1e-6) / 1e9
     step_bytes = nbytes["attn"] + nbytes["scatter"]
+    eager_ms_per_step = ms_per_step
+
+    # the same K steps replayed from one captured HIP graph (how a serving loop
+    # submits its decode step): no launch gaps between the step's kernels
+    launch = "eager"
+    if not args.eager:
+        graph = step.capture()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / K
+        launch = "hip_graph"
+        print(f"bench: timed {K} graph replays, {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     cold = None
@@ -311,6 +335,8 @@ def main(argv=None):
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "launch": launch,
+        "eager_ms_per_step": round(eager_ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -44,6 +44,7 @@ constexpr int kD = 128;            // head_dim this kernel is built for
 constexpr int kRC = kD / 8;        // 16-byte chunks per token row (16)
 constexpr int kKK = kD / 32;       // MFMA steps over head_dim (4)
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max is moved
+constexpr int kStreamDepth = 2;    // tiles in registers per balanced-mode wave
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -85,15 +86,15 @@ struct State {
     f32x4_t o[8];
 };
 
-__device__ __forceinline__ void load_tile(Tile& t, const uint4* __restrict__ kt, const uint4* __restrict__ vt,
-                                          int k_off, int v_off) {
+__device__ __forceinline__ void load_k(Tile& t, const uint4* __restrict__ kt, int k_off) {
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) t.k[kk] = kt[k_off + kk * 4];
+}
+__device__ __forceinline__ void load_v(Tile& t, const uint4* __restrict__ vt, int v_off) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) t.v[i] = vt[v_off + i * kRC];
 }
 
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
@@ -101,35 +102,65 @@ __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
-__device__ __forceinline__ s16x4_t as_operand(uint32_t a, uint32_t b) {
-    return __builtin_bit_cast(s16x4_t, make_uint2(a, b));
+__device__ __forceinline__ bf16x8_t as_operand(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return __builtin_bit_cast(bf16x8_t, make_uint4(a, b, c, d));
 }
 
 // One block: scores on MFMA, lazy online softmax with one reference max per
-// head, P V on MFMA.
+// head, P V on MFMA.  The tile's registers are refilled with the next tile as
+// soon as they are consumed: after_k() is called once the K half has been
+// read, after_v() once the V half has.
 //
-// P V is a 16-head x 16-token by 16-token x 128-dim product run as eight
-// v_mfma_f32_16x16x16_bf16, one per e = 0..7, whose output column n stands
-// for dim 8n + e.  The A operand (P) is already where the score MFMA left it:
-// lane (r, n) holds head n, tokens 4r..4r+3.  The B operand of step e is
-// dim 8n + e of tokens 4r..4r+3, which lane (r, n) also already holds in its
-// four V loads; it is only repacked.  P is split into a bfloat16 high part
-// and a bfloat16 remainder so the product keeps about 16 bits of P.
-template <int G>
-__device__ __forceinline__ void process(State& st, const Tile& t, const bf16x8_t (&qb)[kKK], int tok0, int L,
-                                        int r, int n, float sl2) {
+// P V is a 16-head x 16-token by 16-token x 128-dim product, split as P =
+// P_hi + P_lo (a bfloat16 high part and the bfloat16 of the remainder, so the
+// product keeps about 16 bits of P).  It runs as eight
+// v_mfma_f32_16x16x32_bf16, one per e = 0..7, whose output column n stands
+// for dim 8n + e.  The sum over the 32 positions of the contraction only has
+// to pair the same token in A and B, so lane (r, n) puts P_hi and P_lo of
+// head n, tokens 4r..4r+3 (already where the score MFMA left them) in its
+// eight A positions and dim 8n + e of the same four tokens, twice, in its
+// eight B positions; that value is already in the lane's own V loads and is
+// only repacked.
+template <int G, class AfterK, class AfterV>
+__device__ __forceinline__ void process(State& st, Tile& t, const bf16x8_t (&qb)[kKK], int tok0, int L,
+                                        int r, int n, float sl2, AfterK after_k, AfterV after_v) {
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk)
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[kk]), qb[kk], s, 0, 0, 0);
+    // The refills reuse the tile's registers.  An empty asm statement that
+    // consumes the results and clobbers memory keeps the reads before it and
+    // the refill loads after it.
+    asm volatile("" : "+v"(s) : : "memory");
+    after_k();
 
-    uint4 v[4] = {t.v[0], t.v[1], t.v[2], t.v[3]};
+    // dim 8n + 2w (low halves) and 8n + 2w + 1 (high halves) of tokens 4r..4r+3
+    uint32_t ev[4][2], od[4][2];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = (&t.v[0].x)[w], x1 = (&t.v[1].x)[w], x2 = (&t.v[2].x)[w], x3 = (&t.v[3].x)[w];
+        ev[w][0] = (x0 & 0xFFFFu) | (x1 << 16);
+        ev[w][1] = (x2 & 0xFFFFu) | (x3 << 16);
+        od[w][0] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+        od[w][1] = (x2 >> 16) | (x3 & 0xFFFF0000u);
+    }
+    asm volatile("" : "+v"(ev[0][0]), "+v"(ev[0][1]), "+v"(ev[1][0]), "+v"(ev[1][1]), "+v"(ev[2][0]), "+v"(ev[2][1]),
+                 "+v"(ev[3][0]), "+v"(ev[3][1]), "+v"(od[0][0]), "+v"(od[0][1]), "+v"(od[1][0]), "+v"(od[1][1]),
+                 "+v"(od[2][0]), "+v"(od[2][1]), "+v"(od[3][0]), "+v"(od[3][1]) : : "memory");
+    after_v();
+
     if (tok0 + kBlockTokens > L) {   // last, partially filled block (wave-uniform branch)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (tok0 + 4 * r + i >= L) {
                 s[i] = -INFINITY;
-                v[i] = make_uint4(0u, 0u, 0u, 0u);   // stale slots may hold NaN; P is 0 there
+                // stale slots may hold NaN; P is 0 there
+                const uint32_t keep = (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    ev[w][i >> 1] &= keep;
+                    od[w][i >> 1] &= keep;
+                }
             }
         }
     }
@@ -164,22 +195,13 @@ __device__ __forceinline__ void process(State& st, const Tile& t, const bf16x8_t
     const uint32_t h23 = bf16_pair(p[2], p[3]);
     const uint32_t l01 = bf16_pair(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
     const uint32_t l23 = bf16_pair(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
-    const s16x4_t p_hi = as_operand(h01, h23);
-    const s16x4_t p_lo = as_operand(l01, l23);
-
-    const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-    const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-    const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-    const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+    const bf16x8_t pa = as_operand(h01, h23, l01, l23);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        // dim 8n + 2w (low halves) and 8n + 2w + 1 (high halves) of tokens 4r..4r+3
-        const s16x4_t b_even = as_operand((w0[w] & 0xFFFFu) | (w1[w] << 16), (w2[w] & 0xFFFFu) | (w3[w] << 16));
-        const s16x4_t b_odd = as_operand((w0[w] >> 16) | (w1[w] & 0xFFFF0000u), (w2[w] >> 16) | (w3[w] & 0xFFFF0000u));
-        st.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, b_even, st.o[2 * w], 0, 0, 0);
-        st.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, b_even, st.o[2 * w], 0, 0, 0);
-        st.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, b_odd, st.o[2 * w + 1], 0, 0, 0);
-        st.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, b_odd, st.o[2 * w + 1], 0, 0, 0);
+        st.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pa, as_operand(ev[w][0], ev[w][1], ev[w][0], ev[w][1]), st.o[2 * w], 0, 0, 0);
+        st.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pa, as_operand(od[w][0], od[w][1], od[w][0], od[w][1]), st.o[2 * w + 1], 0, 0, 0);
     }
 }
 
@@ -240,11 +262,13 @@ __device__ __forceinline__ void init_state(State& st) {
 // k = 0..nk-1, whose table entries start at trow (= row + b0).
 //
 // Table entries come 64 at a time from one vector load.  Within such a chunk
-// the K/V tiles of block k+1 are in flight while block k is computed.  Every
-// tile load is issued unconditionally (past the end of the chunk the last
-// tile is fetched again, an L2 hit) so the hardware's in-order load counter
-// lets each block wait for its own tile only.
-template <int G>
+// D tiles are held in registers: while block k is computed, blocks k+1 ..
+// k+D-1 are in flight, and block k's registers are refilled with block k+D
+// as soon as each half has been read.  Every tile load is issued
+// unconditionally (past the end of the chunk the last tile is fetched again,
+// an L2 hit) and in the order the tiles are consumed, so the hardware's
+// in-order load counter lets each block wait for its own tile only.
+template <int G, int D>
 __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* trow, int stride,
                                      int nk, int b0, int L, const WalkCtx& c) {
     auto tile_ptrs = [&](int tv, int k, const uint4*& kt, const uint4*& vt) {
@@ -257,19 +281,29 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
     for (int k0 = 0; k0 < nk; k0 += 64) {
         const int nc = min(64, nk - k0);
         const int tv = c.lane < nc ? trow[(size_t)(k0 + c.lane) * stride] : 0;
-        Tile ta, tb;
+        Tile tt[D];
         const uint4 *kt, *vt;
-        tile_ptrs(tv, 0, kt, vt);
-        load_tile(ta, kt, vt, c.k_off, c.v_off);
-        for (int k = 0; k < nc; k += 2) {
-            tile_ptrs(tv, min(k + 1, nc - 1), kt, vt);
-            load_tile(tb, kt, vt, c.k_off, c.v_off);
-            __builtin_amdgcn_sched_barrier(0);   // issue the next tile before computing this one
-            process<G>(st, ta, qb, (b0 + (k0 + k) * stride) * kBlockTokens, L, c.r, c.n, c.sl2);
-            tile_ptrs(tv, min(k + 2, nc - 1), kt, vt);
-            load_tile(ta, kt, vt, c.k_off, c.v_off);
-            __builtin_amdgcn_sched_barrier(0);
-            if (k + 1 < nc) process<G>(st, tb, qb, (b0 + (k0 + k + 1) * stride) * kBlockTokens, L, c.r, c.n, c.sl2);
+#pragma unroll
+        for (int s = 0; s < D; ++s) {
+            tile_ptrs(tv, min(s, nc - 1), kt, vt);
+            load_k(tt[s], kt, c.k_off);
+            asm volatile("" : : : "memory");
+            load_v(tt[s], vt, c.v_off);
+            asm volatile("" : : : "memory");
+        }
+        for (int k = 0; k < nc; k += D) {
+#pragma unroll
+            for (int s = 0; s < D; ++s) {
+                // tt[s] holds block k + s; it is refilled with block k + s + D.
+                // Past the end a block is a repeat, given a first token of L
+                // so that every position is masked and it adds exact zeros;
+                // running it anyway keeps the loads of every path equal.
+                tile_ptrs(tv, min(k + s + D, nc - 1), kt, vt);
+                __builtin_amdgcn_sched_barrier(0);
+                const int tok = k + s < nc ? (b0 + (k0 + k + s) * stride) * kBlockTokens : L;
+                process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2,
+                           [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off); });
+            }
         }
     }
 }
@@ -300,7 +334,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
 
     const int first = b_begin + wave;
     const int nk = first < b_end ? (b_end - first + kWaves - 1) / kWaves : 0;
-    walk<G>(st, qb, a.tables + (size_t)seq * a.max_blocks + first, kWaves, nk, first, L, c);
+    walk<G, 2>(st, qb, a.tables + (size_t)seq * a.max_blocks + first, kWaves, nk, first, L, c);
     const float l_tot = total_l(st);
 
     // waves of the workgroup merge through LDS
@@ -388,30 +422,34 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     const int S = a.num_seqs;
     const int Hkv = a.num_kv_heads;
 
-    // tiles per sequence: one pass for the total (worker 0 also records the
-    // exclusive prefix sums for the fix-up), a second to find the sequence
-    // holding this worker's first tile; 64 sequences per step.
-    auto chunk_scan = [&](int ch, int& nt, int64_t& excl_lane, int64_t carry) -> int64_t {
-        const int i = ch * kWave + lane;
-        const int Li = i < S ? clamp_len(a.lens[i], a.max_context) : 0;
-        nt = Hkv * ((Li + kBlockTokens - 1) / kBlockTokens);
-        int incl = nt;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int y = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += y;
-        }
-        excl_lane = carry + incl - nt;
-        return carry + __shfl(incl, kWave - 1, kWave);
-    };
+    // Tiles per sequence and their exclusive prefix sums, 64 sequences per
+    // chunk: every lane loads the lengths of all chunks at once (one memory
+    // round trip), then the chunks are scanned in registers.  Worker 0 also
+    // records the prefix sums for the fix-up.
+    constexpr int kMaxChunks = kStreamKMaxSeqs / kWave;
     const int nchunks = (S + kWave - 1) / kWave;
+    int len_c[kMaxChunks];
+#pragma unroll
+    for (int ch = 0; ch < kMaxChunks; ++ch) {
+        const int i = ch * kWave + lane;
+        len_c[ch] = (ch < nchunks && i < S) ? clamp_len(a.lens[i], a.max_context) : 0;
+    }
+    int64_t ex_c[kMaxChunks];
     int64_t T = 0;
-    for (int ch = 0; ch < nchunks; ++ch) {
-        int nt;
-        int64_t ex;
-        const int64_t next = chunk_scan(ch, nt, ex, T);
-        if (w == 0 && ch * kWave + lane < S) a.ws_prefix[ch * kWave + lane] = ex;
-        T = next;
+#pragma unroll
+    for (int ch = 0; ch < kMaxChunks; ++ch) {
+        if (ch < nchunks) {
+            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kBlockTokens - 1) / kBlockTokens);
+            int64_t incl = nt;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int64_t y = __shfl_up(incl, off, kWave);
+                if (lane >= off) incl += y;
+            }
+            ex_c[ch] = T + incl - nt;
+            if (w == 0 && ch * kWave + lane < S) a.ws_prefix[ch * kWave + lane] = ex_c[ch];
+            T += __shfl(incl, kWave - 1, kWave);
+        }
     }
     if (w == 0 && lane == 0) a.ws_prefix[S] = T;
     int64_t t = slice_start(w, T, W);
@@ -419,27 +457,23 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     if (t >= t_end) return;
 
     // the sequence holding tile t: the lane whose [excl, excl + ntile) contains it
-    int seq = 0;
+    int seq = S, L = 0;
     int64_t seq_first = 0;
-    {
-        int64_t carry = 0;
-        for (int ch = 0; ch < nchunks; ++ch) {
-            int nt;
-            int64_t ex;
-            const int64_t next = chunk_scan(ch, nt, ex, carry);
-            const bool hit = nt > 0 && ex <= t && t < ex + nt;
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
+#pragma unroll
+    for (int ch = 0; ch < kMaxChunks; ++ch) {
+        if (ch < nchunks && seq == S) {
+            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kBlockTokens - 1) / kBlockTokens);
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(nt > 0 && ex_c[ch] <= t && t < ex_c[ch] + nt);
             if (bal) {
                 const int j = __builtin_ctzll(bal);
                 seq = ch * kWave + j;
-                seq_first = __shfl(ex, j, kWave);
-                break;
+                seq_first = readlane64(ex_c[ch], j);
+                L = __builtin_amdgcn_readlane(len_c[ch], j);
             }
-            carry = next;
         }
     }
     seq = __builtin_amdgcn_readfirstlane(seq);
-    int L = __builtin_amdgcn_readfirstlane(clamp_len(a.lens[seq], a.max_context));
+    L = __builtin_amdgcn_readfirstlane(L);
     int nblk = (L + kBlockTokens - 1) / kBlockTokens;
     int64_t off = t - seq_first;
     int kv = (int)(off / nblk);
@@ -455,7 +489,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         load_q<G>(qb, a, seq, kv, c);
         State st;
         init_state(st);
-        walk<G>(st, qb, a.tables + (size_t)seq * a.max_blocks + b, 1, n_here, b, L, c);
+        walk<G, kStreamDepth>(st, qb, a.tables + (size_t)seq * a.max_blocks + b, 1, n_here, b, L, c);
         const float l_tot = total_l(st);
 
         if (whole) {
@@ -633,8 +667,14 @@ const void* streamk_kernel_ptr() {
 }  // namespace
 
 int streamk_workers(int group) {
-    // one resident wave per worker: compute units x single-wave workgroups that fit on one
+    // One worker wave per SIMD (four per compute unit).  With two resident
+    // waves per SIMD the older one wins the SIMD's issue arbitration: equal
+    // slices then finish about 1.5x apart, and the second half of the kernel
+    // runs with one wave per SIMD anyway.  One wave per SIMD keeps all
+    // workers at the same pace (timed per worker with the chip's realtime
+    // counter) and is 4 % faster end to end on the 8B and 70B shapes.
     constexpr int kMaxDev = 16;
+    constexpr int kWavesPerCU = 4;
     static int cached[kMaxDev][9] = {};
     if (group < 1 || group > 8) return 0;
     int dev = 0;
@@ -657,7 +697,7 @@ int streamk_workers(int group) {
         (void)hipGetLastError();
         return kStreamKDefaultWorkers;
     }
-    cached[dev][group] = cus * per_cu;
+    cached[dev][group] = cus * min(per_cu, kWavesPerCU);
     return cached[dev][group];
 }
 

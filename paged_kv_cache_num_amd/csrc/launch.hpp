@@ -8,7 +8,7 @@ namespace kvp {
 
 constexpr int kBlockTokens = 16;   // tokens per KV block the kernels are built for
 constexpr int kStreamKMaxSeqs = 1024;        // batch size up to which the balanced split is used
-constexpr int kStreamKDefaultWorkers = 2048; // worker count when no device can be queried
+constexpr int kStreamKDefaultWorkers = 1024; // worker count when no device can be queried
 
 struct ScatterArgs {
     void* k_layer;               // layer base of the K pool

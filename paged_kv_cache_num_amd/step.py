@@ -97,6 +97,26 @@ class DecodeStep:
         self.scatter(stream)
         self.attend(stream)
 
+    def capture(self):
+        """Capture one step (scatter, then attention) in a HIP graph.
+
+        Every launch of the step reads and writes buffers at fixed addresses
+        and allocates nothing, so the step can be captured once and replayed;
+        ``graph.replay()`` then runs the whole step with one submission.  The
+        step is run once on a side stream first, so that first-call set-up in
+        the library (its per-device worker count) happens outside the capture.
+        """
+        import torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run()
+        return graph
+
     def out_host(self) -> np.ndarray:
         return to_host(self.out, self.dtype)
 

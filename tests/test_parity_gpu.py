@@ -101,6 +101,26 @@ def test_repeated_runs_are_bitwise_identical():
         assert np.array_equal(first, step.out_host())
 
 
+@pytest.mark.parametrize("name,partition", [("C2", 0), ("C2", 512), ("C3", 0), ("C1", 32)])
+def test_graph_replays_match_eager_calls(name, partition):
+    """A captured step gives the eager step's bits on every replay, with eager
+    work (a fill of the output, a reduction) between the replays."""
+    import torch
+    say(f"{name} sharp: HIP graph capture of the step, partition={partition}")
+    wl = workload(name, "sharp")
+    step = run_gpu(wl, partition_size=partition)
+    eager = step.out_host()
+    graph = step.capture()
+    for i in range(4):
+        step.out.fill_(0)
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        del junk
+        assert np.array_equal(step.out_host(), eager), f"replay {i} differs from the eager call"
+
+
 @pytest.mark.parametrize("partition", [16, 48, 128, 1024, 4096])
 def test_partition_sizes_agree_with_the_oracle(partition):
     say(f"C2 sharp partition={partition}")
@@ -182,3 +202,26 @@ def test_padding_tokens_with_negative_slots_are_skipped():
     torch.cuda.synchronize()
     kp1, vp1 = step.pool_host()
     assert kp0.tobytes() == kp1.tobytes() and vp0.tobytes() == vp1.tobytes()
+
+
+@pytest.mark.parametrize("name,variant,num_seqs", [("C2", "sharp", None), ("C3", "needle", 96), ("C5", "sharp", None)])
+def test_balanced_merge_reads_fresh_partial_states(name, variant, num_seqs):
+    """Split (sequence, KV head) pairs are merged from this call's partial states.
+
+    Between calls every workspace byte is overwritten with NaN patterns by a
+    separate kernel; each later call must still match the oracle.
+    """
+    import torch
+    say(f"{name} {variant} balanced split, workspace poisoned between calls")
+    wl = kvgen.make_workload(name, variant=variant, poison=True, num_seqs=num_seqs)
+    ref = oracle.run_step(wl)
+    step = run_gpu(wl, partition_size=0)
+    check_step(step, wl, ref, check_pool=False, label=f"{name}/first call")
+    for _ in range(2):
+        step.workspace.fill_(0xFF)
+        step.out.fill_(0)
+        step.attend()
+        torch.cuda.synchronize()
+        err = max_err(step.out_host(), ref["out"], wl.dtype)
+        say(f"  after poisoning: max err {err:.3e}")
+        assert err <= TOL[wl.dtype]
