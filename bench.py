@@ -36,7 +36,7 @@ METRIC = "paged decode attention achieved HBM GB/s (% of peak) + decode tokens/s
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_num_amd/csrc/decode.hip", "paged_kv_cache_num_amd/csrc/decode_mfma.hip",
-                  "paged_kv_cache_num_amd/csrc/device_common.hpp"]
+                  "paged_kv_cache_num_amd/csrc/device_common.hpp", "paged_kv_cache_num_amd/csrc/split.hpp"]
 
 WORKLOADS = {
     "C1": "tiny fp32 paged decode: 4 sequences, lengths {17,33,100,200}, 8 query / 2 KV heads, head_dim 64, block 16, 64-block pool",
@@ -188,6 +188,10 @@ def main(argv=None):
     ap.add_argument("--variant", default="spec")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing pass")
+    ap.add_argument("--no-identity", action="store_true",
+                    help="skip timing the same batch with contiguous (identity-like) block tables")
+    ap.add_argument("--table-walk-probe", type=int, default=0, metavar="N",
+                    help="also run the table-walk probe N times in each workgroup ordering (for counter runs)")
     ap.add_argument("--eager", action="store_true",
                     help="time the step from eager launches only (default: replays of a captured HIP graph)")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
@@ -326,6 +330,55 @@ def main(argv=None):
                 "frac": round(nbytes["attn"] / (cm * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     del big
 
+    # The same batch with every sequence's blocks laid out back to back
+    # (identity-like tables, the dense layout of a contiguous cache): the
+    # ratio is what the indirection costs.
+    identity = None
+    if not args.no_identity:
+        dense = DecodeStep.from_workload(kvgen.privatize_blocks(wl, contiguous=True), partition_size=part)
+        for _ in range(args.warmup):
+            dense.attend()
+        torch.cuda.synchronize()
+        dense_us = []
+        for _ in range(K):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dense.attend()
+            b.record()
+            b.synchronize()
+            dense_us.append(a.elapsed_time(b) * 1e3)
+        # the paged calls timed the same way (one call per synchronisation)
+        paged_us = []
+        for _ in range(K):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step.attend()
+            b.record()
+            b.synchronize()
+            paged_us.append(a.elapsed_time(b) * 1e3)
+        dp, dd = percentile(paged_us, 0.5), percentile(dense_us, 0.5)
+        identity = {"paged_attn_us_p50": round(dp, 2), "identity_attn_us_p50": round(dd, 2),
+                    "paged_over_identity": round(dp / dd, 4)}
+        del dense
+        torch.cuda.synchronize()
+
+    table_walk = None
+    if args.table_walk_probe:
+        from paged_kv_cache_num_amd import probe_table_walk
+        tsink = torch.empty(1 << 14, dtype=torch.uint8, device="cuda")
+        table_walk = {}
+        for grouped in (False, True):
+            us = []
+            for _ in range(args.table_walk_probe):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                probe_table_walk(step.block_tables, step.context_lens, wl.num_kv_heads, step.max_context_len,
+                                 tsink, xcd_grouped=grouped)
+                b.record()
+                b.synchronize()
+                us.append(a.elapsed_time(b) * 1e3)
+            table_walk["xcd_grouped_us_p50" if grouped else "default_us_p50"] = round(percentile(us, 0.5), 2)
+
     traffic = traffic_for(args.config, part)
     result = {
         "metric": METRIC,
@@ -363,6 +416,8 @@ def main(argv=None):
         "pool_utilization": round(float(wl.info.get("utilization") or 0.0), 4),
         "blocks_per_seq_mean": round(nbytes["blocks"] / max(1, wl.num_seqs), 2),
         "internal_waste_tokens": int(nbytes["blocks"] * wl.block_size - int(np.sum(wl.context_lens))),
+        "identity_tables": identity,
+        "table_walk_probe": table_walk,
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)

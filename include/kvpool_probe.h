@@ -39,6 +39,22 @@ kv_status kv_probe_copy(void* dst, const void* src, uint64_t bytes, void* stream
  */
 kv_status kv_probe_read(const void* src, uint64_t bytes, void* sink, void* stream);
 
+/*
+ * Block-table walk of the balanced decode split (paged_attention_decode with
+ * partition_size 0) without the K/V stream: the same workers and slices, the
+ * same table-entry loads, no tile loads.  Its L2 hit rate under a counter
+ * profiler is the hit rate of the decode's table reads.  xcd_grouped != 0
+ * runs slice s on XCD s / (W / 8) instead of XCD s % 8, so the KV heads of a
+ * sequence share one XCD.  Arguments as for paged_attention_decode; sink is a
+ * device buffer of at least 4 bytes per worker (4096 covers 1024 workers),
+ * one folded word per worker is written there.  Errors:
+ * KV_ERR_INVALID_ARGUMENT, KV_ERR_HIP.
+ */
+kv_status kv_probe_table_walk(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                              int32_t max_context_len, int32_t xcd_grouped, void* sink, uint64_t sink_bytes,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

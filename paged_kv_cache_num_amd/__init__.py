@@ -10,7 +10,7 @@ that first use raises ImportError (there is no CPU fallback).  Importing the
 import importlib
 
 _FROM_KVPOOL = ("KV_BF16", "KV_F32", "KVError", "KVPool", "kv_build_slot_mapping", "kv_pool_bytes",
-                "make_desc", "lib", "LIB_PATH", "EXPORTED", "probe_copy", "probe_read")
+                "make_desc", "lib", "LIB_PATH", "EXPORTED", "probe_copy", "probe_read", "probe_table_walk")
 
 __all__ = list(_FROM_KVPOOL) + ["DecodeStep"]
 

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include "kvpool_probe.h"
+#include "launch.hpp"
+#include "split.hpp"
 
 namespace {
 
@@ -36,7 +38,98 @@ __global__ __launch_bounds__(kCopyThreads) void read_kernel(const uint4* __restr
     }
 }
 
+// Table walk of the balanced decode split without the K/V stream: every worker
+// scans the lengths, takes the same slice as the decode kernel and reads its
+// block-table entries the same way (one vector load per 64 entries of a
+// (sequence, KV head) piece).  Grouped: slice s runs on XCD s / (W / 8), so
+// the KV heads of a sequence, which are neighbours in the tile list, share
+// one XCD's L2 instead of being spread over all eight.
+template <bool kGrouped>
+__global__ __launch_bounds__(64) void table_walk_kernel(const int32_t* __restrict__ tables, int32_t max_blocks,
+                                                        const int32_t* __restrict__ lens, int32_t S, int32_t Hkv,
+                                                        int32_t max_context, uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x;
+    const int64_t W = gridDim.x;
+    const int64_t w = blockIdx.x;
+    const int64_t s = kGrouped ? (w % 8) * (W / 8) + w / 8 : w;
+    auto clamp = [&](int L) { return L < 0 ? 0 : (L > max_context ? max_context : L); };
+    auto tiles = [&](int i) -> int64_t {
+        return i < S ? (int64_t)Hkv * ((clamp(lens[i]) + kvp::kBlockTokens - 1) / kvp::kBlockTokens) : 0;
+    };
+    int64_t T = 0;
+    for (int b = 0; b < S; b += 64) {
+        int64_t x = tiles(b + lane);
+        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+        T += x;
+    }
+    int64_t t = kvp::slice_start(s, T, W);
+    const int64_t t_end = kvp::slice_start(s + 1, T, W);
+    uint32_t acc = 0;
+    // the sequence holding tile t, 64 sequences per step
+    int seq = S;
+    int64_t first = 0;   // first tile of sequence seq
+    int64_t carry = 0;
+    for (int b = 0; b < S && seq == S && t < t_end; b += 64) {
+        const int64_t nt = tiles(b + lane);
+        int64_t incl = nt;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        const int64_t ex = carry + incl - nt;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(nt > 0 && ex <= t && t < ex + nt);
+        if (bal) {
+            const int j = __builtin_ctzll(bal);
+            seq = b + j;
+            first = __shfl(ex, j, 64);
+        }
+        carry += __shfl(incl, 63, 64);
+    }
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    for (; seq < S && t < t_end; ++seq) {
+        const int L = __builtin_amdgcn_readfirstlane(clamp(lens[seq]));
+        const int nblk = (L + kvp::kBlockTokens - 1) / kvp::kBlockTokens;
+        const int64_t seg_end = first + (int64_t)Hkv * nblk;
+        while (t < t_end && t < seg_end) {
+            const int64_t off = t - first;
+            const int kv = (int)(off / nblk);
+            const int b = (int)(off - (int64_t)kv * nblk);
+            const int n = (int)min((int64_t)(nblk - b), t_end - t);
+            const int32_t* trow = tables + (size_t)seq * max_blocks + b;
+            for (int k0 = 0; k0 < n; k0 += 64)
+                if (k0 + lane < n) acc ^= (uint32_t)trow[k0 + lane] + (uint32_t)kv;
+            t += n;
+        }
+        first = seg_end;
+    }
+    for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+    if (lane == 0) sink[w] = acc;
+}
+
 }  // namespace
+
+extern "C" kv_status kv_probe_table_walk(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                         int32_t max_context_len, int32_t xcd_grouped, void* sink,
+                                         uint64_t sink_bytes, void* stream) {
+    if (!block_tables || !context_lens || !sink || num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+        max_blocks_per_seq <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvp::kBlockTokens ||
+        (reinterpret_cast<uintptr_t>(sink) & 3u))
+        return KV_ERR_INVALID_ARGUMENT;
+    const int workers = kvp::streamk_workers(4);
+    if (workers <= 0 || workers % 8 != 0 || sink_bytes < (uint64_t)workers * 4u) return KV_ERR_INVALID_ARGUMENT;
+    if (num_seqs == 0) return KV_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (xcd_grouped)
+        table_walk_kernel<true><<<dim3((unsigned)workers), dim3(64), 0, st>>>(
+            block_tables, max_blocks_per_seq, context_lens, num_seqs, num_kv_heads, max_context_len,
+            static_cast<uint32_t*>(sink));
+    else
+        table_walk_kernel<false><<<dim3((unsigned)workers), dim3(64), 0, st>>>(
+            block_tables, max_blocks_per_seq, context_lens, num_seqs, num_kv_heads, max_context_len,
+            static_cast<uint32_t*>(sink));
+    return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
 
 extern "C" kv_status kv_probe_read(const void* src, uint64_t bytes, void* sink, void* stream) {
     if (!src || !sink || (bytes & 15u) || (reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u))

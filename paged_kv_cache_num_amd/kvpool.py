@@ -30,7 +30,7 @@ KV_BF16 = 1
 EXPORTED = (
     "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
-    "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read",
+    "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read", "kv_probe_table_walk",
 )
 
 
@@ -80,6 +80,8 @@ def _load():
     lib.kv_probe_copy.argtypes = [vp, vp, u64, vp]
     lib.kv_probe_read.restype = ctypes.c_int
     lib.kv_probe_read.argtypes = [vp, u64, vp, vp]
+    lib.kv_probe_table_walk.restype = ctypes.c_int
+    lib.kv_probe_table_walk.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, u64, vp]
     return lib
 
 
@@ -261,3 +263,16 @@ def probe_read(src, sink, stream=None) -> None:
         raise ValueError("sink must hold at least 64 KiB")
     _check(lib.kv_probe_read(_dev_ptr(src, "src"), src.numel() * src.element_size(), _dev_ptr(sink, "sink"),
                              _stream_handle(stream)), "kv_probe_read")
+
+
+def probe_table_walk(block_tables, context_lens, num_kv_heads: int, max_context_len: int, sink, *,
+                     xcd_grouped: bool = False, stream=None) -> None:
+    """Measurement probe: the balanced decode's block-table walk without the K/V loads."""
+    import torch
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or block_tables.dim() != 2:
+        raise TypeError("block_tables [S][MB] and context_lens [S] must be int32 device tensors")
+    _check(lib.kv_probe_table_walk(_dev_ptr(block_tables, "block_tables"), block_tables.shape[1],
+                                   _dev_ptr(context_lens, "context_lens"), block_tables.shape[0],
+                                   int(num_kv_heads), int(max_context_len), 1 if xcd_grouped else 0,
+                                   _dev_ptr(sink, "sink"), sink.numel() * sink.element_size(),
+                                   _stream_handle(stream)), "kv_probe_table_walk")

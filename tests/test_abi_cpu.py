@@ -220,6 +220,18 @@ def test_workspace_size_formula():
     K.lib.kv_pool_destroy(h)
 
 
+def test_table_walk_probe_argument_checks():
+    L = K.lib
+    # null pointers, bad sizes and a context longer than the table rows fail before any launch
+    assert L.kv_probe_table_walk(None, 4, 0x1000, 2, 8, 64, 0, 0x2000, 4096, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_table_walk(0x1000, 4, None, 2, 8, 64, 0, 0x2000, 4096, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_table_walk(0x1000, 4, 0x1000, 2, 8, 64, 0, None, 4096, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_table_walk(0x1000, 4, 0x1000, -1, 8, 64, 0, 0x2000, 4096, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_table_walk(0x1000, 4, 0x1000, 2, 0, 64, 0, 0x2000, 4096, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_table_walk(0x1000, 4, 0x1000, 2, 8, 65, 0, 0x2000, 4096, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_table_walk(0x1000, 4, 0x1000, 2, 8, 64, 0, 0x2002, 4096, None) == K.KV_ERR_INVALID_ARGUMENT
+
+
 def test_scatter_argument_checks():
     st, h = _pool()
     L = K.lib
