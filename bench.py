@@ -12,8 +12,13 @@ Default workload: Llama-3-8B-shaped decode layer (64 sequences, 32 query /
 from a shuffled free list over a pool of 1.25x the blocks needed, bf16).
 
 The K timed steps are replays of one captured HIP graph holding the step's
-launches (how a serving loop submits its decode step); ``--eager`` times
-eager launches instead.  The attention call's own duration, from events
+launches (how a serving loop submits its decode step), in two forms: scatter
++ attention, and, where every sequence writes one token at position L_i - 1,
+those writes folded into the attention call (paged_attention_decode_append;
+other writes such as a prefill chunk still go through reshape_and_cache).
+Both leave bitwise the same pool and output (checked in the run); both times
+are reported and the faster is the headline.  ``--no-fuse`` keeps the two
+calls, ``--eager`` times eager launches instead.  The attention call's own duration, from events
 around each of K eager calls, gives the roofline figure.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
@@ -192,6 +197,8 @@ def main(argv=None):
                     help="skip timing the same batch with contiguous (identity-like) block tables")
     ap.add_argument("--table-walk-probe", type=int, default=0, metavar="N",
                     help="also run the table-walk probe N times in each workgroup ordering (for counter runs)")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="time the step as scatter + attention only (no paged_attention_decode_append form)")
     ap.add_argument("--eager", action="store_true",
                     help="time the step from eager launches only (default: replays of a captured HIP graph)")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
@@ -296,19 +303,44 @@ def main(argv=None):
 
     # the same K steps replayed from one captured HIP graph (how a serving loop
     # submits its decode step): no launch gaps between the step's kernels
+    # The same K steps replayed from one captured HIP graph (how a serving loop
+    # submits its decode step), in two forms: scatter + attention, and the
+    # decode appends folded into the attention call (paged_attention_decode_append;
+    # writes that are not decode appends, such as a prefill chunk, still go
+    # through reshape_and_cache first).  The headline is the fused form when the
+    # batch allows it.
     launch = "eager"
+    graph_ms = {}
     if not args.eager:
-        graph = step.capture()
-        graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(K):
+        forms = [False] + ([True] if step.can_fuse and not args.no_fuse else [])
+        for fused in forms:
+            graph = step.capture(fused=fused)
             graph.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(K):
+                graph.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            graph_ms[fused] = (t1 - t0) * 1e3 / K
+            del graph
+            print(f"bench: timed {K} graph replays ({'fused append' if fused else 'scatter + attention'}), "
+                  f"{graph_ms[fused] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        # both forms leave bitwise the same pool and output (checked below); the
+        # headline is the faster one on this batch
+        fused_on = True in graph_ms and graph_ms[True] < graph_ms[False]
+        ms_per_step = graph_ms[fused_on]
+        launch = "hip_graph, fused append" if fused_on else "hip_graph, scatter + attention"
+        # the fused form must leave the same pool and output as the two-call form
+        step.run()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_per_step = (t1 - t0) * 1e3 / K
-        launch = "hip_graph"
-        print(f"bench: timed {K} graph replays, {ms_per_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        ref_out = step.out.clone()
+        if True in graph_ms:
+            step.run_fused()
+            torch.cuda.synchronize()
+            assert torch.equal(step.out.view(torch.int16) if step.out.dtype == torch.bfloat16 else step.out,
+                               ref_out.view(torch.int16) if ref_out.dtype == torch.bfloat16 else ref_out), \
+                "fused step output differs from scatter + attention"
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     cold = None
@@ -390,6 +422,8 @@ def main(argv=None):
         "ms_per_step": round(ms_per_step, 5),
         "launch": launch,
         "eager_ms_per_step": round(eager_ms_per_step, 5),
+        "graph_two_call_ms_per_step": round(graph_ms[False], 5) if False in graph_ms else None,
+        "graph_fused_ms_per_step": round(graph_ms[True], 5) if True in graph_ms else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

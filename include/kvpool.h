@@ -196,6 +196,30 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
                                  float scale, int32_t max_context_len, int32_t partition_size,
                                  void* workspace, uint64_t workspace_bytes, void* stream);
 
+/*
+ * GPU step: the decode append and the attention of one step in one call.  The
+ * result, pool included, is bitwise that of reshape_and_cache of sequence i's
+ * new row to position L_i - 1 (slot table[i][(L_i - 1) / B] * B + (L_i - 1) % B,
+ * [KVC] "The write path: slot mapping and scatter") for every i with L_i > 0,
+ * followed by paged_attention_decode with the same arguments.
+ *   k_new, v_new: device, [num_seqs][H_kv][D] in the pool dtype, 16-byte aligned:
+ *                 the K/V row of the token each sequence writes this step
+ *                 (rows of sequences with L_i = 0 are not read).
+ *   Every other argument, and every error, as for paged_attention_decode.
+ * Precondition: the block holding position L_i - 1 of sequence i is named by no
+ * other sequence of the call (the block being appended to is private, as after
+ * copy-on-write).  In the balanced mode the wave that reads that block writes
+ * the row into the pool and uses it directly (one kernel, no separate scatter);
+ * other modes run a small scatter kernel first.  A block index outside the pool
+ * is skipped, as by reshape_and_cache.
+ */
+kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out, const void* q,
+                                        const void* k_new, const void* v_new, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, float scale, int32_t max_context_len,
+                                        int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+                                        void* stream);
+
 /* Static name of a status code ("KV_OK", ...); never NULL. */
 const char* kv_status_string(kv_status status);
 

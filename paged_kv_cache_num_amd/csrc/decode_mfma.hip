@@ -259,6 +259,33 @@ __device__ __forceinline__ void init_state(State& st) {
     for (int e = 0; e < 8; ++e) st.o[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// Decode append inside the walk: the block holding position L - 1 (the token
+// written this step) takes row j = (L - 1) % B from the new K/V row instead of
+// the pool.  The row is stored into the pool by separate waves of the same
+// launch (append_scatter_waves): stores share the in-order memory counter with
+// loads, so a store from this wave would make its next waits cover it too.
+// Whatever this wave reads for row j is replaced, so it does not matter
+// whether it sees the old or the new row.
+struct AppendRow {
+    bool active;
+    int tok0;             // first token of the block holding position L - 1
+    int j;                // (L - 1) % B
+    const uint4* krow;    // the new K row (16 chunks)
+    const uint4* vrow;
+};
+
+// Lane (r, n) holds K token n, chunks 4kk + r, and V tokens 4r + i, chunk n.
+__device__ __forceinline__ void append_into(Tile& t, const AppendRow& app, const uint4 (&nk)[kKK], uint4 nv,
+                                            const WalkCtx& c) {
+    if (c.n == app.j) {
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) t.k[kk] = nk[kk];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * c.r + i == app.j) t.v[i] = nv;
+}
+
 // Walk nk blocks of one (sequence, KV head): logical blocks b0 + stride*k,
 // k = 0..nk-1, whose table entries start at trow (= row + b0).
 //
@@ -271,7 +298,7 @@ __device__ __forceinline__ void init_state(State& st) {
 // in-order load counter lets each block wait for its own tile only.
 template <int G, int D>
 __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* trow, int stride,
-                                     int nk, int b0, int L, const WalkCtx& c) {
+                                     int nk, int b0, int L, const WalkCtx& c, const AppendRow& app) {
     auto tile_ptrs = [&](int tv, int k, const uint4*& kt, const uint4*& vt) {
         uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(tv, k);
         phys = phys < c.num_blocks ? phys : c.num_blocks - 1;   // stay inside the pool whatever the table says
@@ -279,6 +306,7 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
         kt = c.kpool + base;
         vt = c.vpool + base;
     };
+    uint4 new_k[kKK], new_v;   // the appended row, loaded once the last chunk's first tiles are in flight
     for (int k0 = 0; k0 < nk; k0 += 64) {
         const int nc = min(64, nk - k0);
         const int tv = c.lane < nc ? trow[(size_t)(k0 + c.lane) * stride] : 0;
@@ -292,6 +320,11 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
             load_v(tt[s], vt, c.v_off);
             asm volatile("" : : : "memory");
         }
+        if (app.active && k0 + 64 >= nk) {
+#pragma unroll
+            for (int kk = 0; kk < kKK; ++kk) new_k[kk] = app.krow[4 * kk + c.r];
+            new_v = app.vrow[c.n];
+        }
         for (int k = 0; k < nc; k += D) {
 #pragma unroll
             for (int s = 0; s < D; ++s) {
@@ -302,6 +335,12 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
                 tile_ptrs(tv, min(k + s + D, nc - 1), kt, vt);
                 __builtin_amdgcn_sched_barrier(0);
                 const int tok = k + s < nc ? (b0 + (k0 + k + s) * stride) * kBlockTokens : L;
+                // wave-uniform: the block holding the new token; a table entry outside
+                // the pool gets no write (as the scatter skips such a slot)
+                if (app.active && tok == app.tok0 &&
+                    (uint32_t)__builtin_amdgcn_readlane(tv, k + s) < c.num_blocks) {
+                    append_into(tt[s], app, new_k, new_v, c);
+                }
                 process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2,
                            [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off); });
             }
@@ -335,7 +374,10 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
 
     const int first = b_begin + wave;
     const int nk = first < b_end ? (b_end - first + kWaves - 1) / kWaves : 0;
-    walk<G, 2>(st, qb, a.tables + (size_t)seq * a.max_blocks + first, kWaves, nk, first, L, c);
+    AppendRow none;
+    none.active = false;
+    none.krow = none.vrow = nullptr;
+    walk<G, 2>(st, qb, a.tables + (size_t)seq * a.max_blocks + first, kWaves, nk, first, L, c, none);
     const float l_tot = total_l(st);
 
     // waves of the workgroup merge through LDS
@@ -413,11 +455,43 @@ __device__ __forceinline__ float* record_ptr(const DecodeArgs& a, int64_t slot) 
     return a.ws_acc + slot * (int64_t)record_floats<G>();
 }
 
+// Decode append, the pool side: workgroups past the workers copy each
+// sequence's new K/V row to position L - 1 of its table (the slot of "The
+// write path", computed here from the table and the length).  A block index
+// outside the pool is skipped, as by the scatter.  Items are numbered
+// ((seq * 2 + {K,V}) * Hkv + head) * kRC + chunk, one 16-byte chunk each.
+__device__ __forceinline__ void append_scatter_waves(const DecodeArgs& a, int64_t x, int64_t nx) {
+    const int64_t per_seq = 2LL * a.num_kv_heads * kRC;
+    const int64_t items = (int64_t)a.num_seqs * per_seq;
+    for (int64_t item = x * kWave + threadIdx.x; item < items; item += nx * kWave) {
+        const int64_t i = item / per_seq;
+        const int64_t rem = item - i * per_seq;
+        const int which = (int)(rem / ((int64_t)a.num_kv_heads * kRC));
+        const int64_t rem2 = rem - (int64_t)which * a.num_kv_heads * kRC;
+        const int h = (int)(rem2 / kRC);
+        const int ch = (int)(rem2 - (int64_t)h * kRC);
+        const int L = clamp_len(a.lens[i], a.max_context);
+        if (L == 0) continue;
+        const int pos = L - 1;
+        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / kBlockTokens];
+        if (block < 0 || block >= a.num_blocks) continue;
+        const int64_t dst = ((block * a.num_kv_heads + h) * kBlockTokens + pos % kBlockTokens) * kRC + ch;
+        const int64_t src = (i * a.num_kv_heads + h) * kRC + ch;
+        const uint4* from = reinterpret_cast<const uint4*>(which == 0 ? a.k_append : a.v_append);
+        uint4* to = const_cast<uint4*>(reinterpret_cast<const uint4*>(which == 0 ? a.k_layer : a.v_layer));
+        to[dst] = from[src];
+    }
+}
+
 template <int G>
 __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
-    const int64_t W = gridDim.x;
+    const int64_t W = a.workers;
     const int64_t w = blockIdx.x;
+    if (w >= W) {   // decode append: the pool side
+        append_scatter_waves(a, w - W, (int64_t)gridDim.x - W);
+        return;
+    }
     const int S = a.num_seqs;
     const int Hkv = a.num_kv_heads;
 
@@ -488,7 +562,14 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         load_q<G>(qb, a, seq, kv, c);
         State st;
         init_state(st);
-        walk<G, kStreamDepth>(st, qb, a.tables + (size_t)seq * a.max_blocks + b, 1, n_here, b, L, c);
+        // the piece that ends with the sequence's last block takes the appended row
+        AppendRow app;
+        app.active = a.k_append != nullptr && b + n_here == nblk;
+        app.tok0 = (nblk - 1) * kBlockTokens;
+        app.j = (L - 1) % kBlockTokens;
+        app.krow = reinterpret_cast<const uint4*>(a.k_append) + ((size_t)seq * Hkv + kv) * kRC;
+        app.vrow = reinterpret_cast<const uint4*>(a.v_append) + ((size_t)seq * Hkv + kv) * kRC;
+        walk<G, kStreamDepth>(st, qb, a.tables + (size_t)seq * a.max_blocks + b, 1, n_here, b, L, c, app);
         const float l_tot = total_l(st);
 
         if (whole) {
@@ -693,8 +774,17 @@ int streamk_workers(int group) {
     return cached[dev][group];
 }
 
-hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
-    dim3 grid((unsigned)workers);
+hipError_t launch_decode_bf16_streamk(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
+    DecodeArgs a = a_in;
+    a.workers = workers;
+    // decode append: a few extra single-wave workgroups store the new rows (about 8 chunks per lane)
+    int64_t extra = 0;
+    if (a.k_append) {
+        const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * kRC;
+        extra = (items + 8 * kWave - 1) / (8 * kWave);
+        extra = extra < 1 ? 1 : (extra > 256 ? 256 : extra);
+    }
+    dim3 grid((unsigned)(workers + extra));
     dim3 fix((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     switch (group) {
         case 1: decode_bf16_streamk_kernel<1><<<grid, kWave, 0, stream>>>(a); break;

@@ -242,11 +242,17 @@ kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int3
     return ok();
 }
 
-kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const void* q,
-                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
-                                 int32_t max_context_len, int32_t partition_size, void* workspace,
-                                 uint64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of paged_attention_decode and paged_attention_decode_append
+// (k_append / v_append null for the former).
+kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, const void* k_append,
+                      const void* v_append, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                      int32_t max_context_len, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+                      void* stream) {
     if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "pool is NULL");
     const kv_pool_desc& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers) return fail(KV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, d.num_layers);
@@ -272,6 +278,9 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
     if (!aligned16(out) || !aligned16(q)) return fail(KV_ERR_INVALID_ARGUMENT, "q/out must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(context_lens)) & 3u)
         return fail(KV_ERR_INVALID_ARGUMENT, "block_tables/context_lens must be 4-byte aligned");
+    const bool append = k_append != nullptr || v_append != nullptr;
+    if (append && (!k_append || !v_append || !aligned16(k_append) || !aligned16(v_append)))
+        return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new must both be non-NULL and 16-byte aligned");
 
     const Plan plan = plan_decode(d, num_seqs, num_q_heads, max_context_len, partition_size);
     kvp::DecodeArgs a;
@@ -306,12 +315,56 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // exp(x) = 2^(x log2 e)
     hipError_t e;
     if (plan.mode == Mode::kBalanced) {
+        // the worker that owns each (sequence, KV head)'s last block writes and uses the new row
+        a.k_append = k_append;
+        a.v_append = v_append;
         e = kvp::launch_decode_bf16_streamk(a, num_q_heads / d.num_kv_heads, plan.workers, static_cast<hipStream_t>(stream));
     } else {
-        e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
+        e = hipSuccess;
+        if (append) {
+            kvp::AppendArgs w;
+            w.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
+            w.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
+            w.k_new = k_append;
+            w.v_new = v_append;
+            w.tables = block_tables;
+            w.lens = context_lens;
+            w.max_blocks = max_blocks_per_seq;
+            w.num_seqs = num_seqs;
+            w.num_blocks = d.num_blocks;
+            w.max_context = max_context_len;
+            w.num_kv_heads = d.num_kv_heads;
+            w.row_chunks = d.head_dim * pool->elem_bytes / 16;
+            e = kvp::launch_append_scatter(w, static_cast<hipStream_t>(stream));
+        }
+        if (e == hipSuccess) e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
     }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const void* q,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                                 int32_t max_context_len, int32_t partition_size, void* workspace,
+                                 uint64_t workspace_bytes, void* stream) {
+    return decode_impl(pool, layer, out, q, nullptr, nullptr, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, max_context_len, partition_size, workspace, workspace_bytes,
+                       stream);
+}
+
+kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out, const void* q, const void* k_new,
+                                        const void* v_new, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                        float scale, int32_t max_context_len, int32_t partition_size,
+                                        void* workspace, uint64_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && (!k_new || !v_new)) return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new is NULL");
+    return decode_impl(pool, layer, out, q, k_new, v_new, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, max_context_len, partition_size, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -24,6 +24,26 @@ struct ScatterArgs {
 
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 
+// Decode append: sequence i's new K/V row (k_new[i], v_new[i], [S][Hkv][D]) goes
+// to position L_i - 1 of its table, i.e. slot table[i][(L_i - 1) / B] * B +
+// (L_i - 1) % B; sequences with L_i = 0 and blocks outside the pool are skipped.
+struct AppendArgs {
+    void* k_layer;
+    void* v_layer;
+    const void* k_new;           // [S][Hkv][D]
+    const void* v_new;
+    const int32_t* tables;       // [S][max_blocks]
+    const int32_t* lens;         // [S]
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t num_blocks;
+    int32_t max_context;         // clamp for lens[i]
+    int32_t num_kv_heads;
+    int32_t row_chunks;          // 16-byte chunks per (token, head) row
+};
+
+hipError_t launch_append_scatter(const AppendArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
     const void* k_layer;
     const void* v_layer;
@@ -34,6 +54,9 @@ struct DecodeArgs {
     float* ws_ml;                // partitions: [S][Hq][max_parts] x (m, l), or null
     float* ws_acc;               // partitions: [S][Hq][max_parts][D]; balanced split: partial records
     int64_t* ws_prefix;          // balanced split: tiles before each sequence, [S + 1]
+    const void* k_append;        // balanced split, decode append: new row per sequence [S][Hkv][D], or null
+    const void* v_append;
+    int32_t workers;             // balanced split: worker waves (the launch adds append waves past them)
     int32_t max_blocks;
     int32_t num_seqs;
     int32_t num_q_heads;

@@ -46,7 +46,45 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
     }
 }
 
+// Decode append without a slot mapping: the slot of sequence i's new row is
+// computed from its table and length on the device, the same formula the
+// host uses ("The write path": block_index * B + offset).  Work items are
+// numbered ((seq * 2 + {K,V}) * num_kv_heads + head) * row_chunks + chunk.
+__global__ __launch_bounds__(kScatterThreads) void append_scatter_kernel(AppendArgs a) {
+    const int64_t per_seq = 2LL * a.num_kv_heads * a.row_chunks;
+    const int64_t total = (int64_t)a.num_seqs * per_seq;
+    const int64_t stride = (int64_t)gridDim.x * kScatterThreads;
+    for (int64_t item = (int64_t)blockIdx.x * kScatterThreads + threadIdx.x; item < total; item += stride) {
+        const int64_t i = item / per_seq;
+        const int64_t rem = item - i * per_seq;
+        const int which = (int)(rem / ((int64_t)a.num_kv_heads * a.row_chunks));
+        const int64_t rem2 = rem - (int64_t)which * a.num_kv_heads * a.row_chunks;
+        const int h = (int)(rem2 / a.row_chunks);
+        const int c = (int)(rem2 - (int64_t)h * a.row_chunks);
+        int L = a.lens[i];
+        L = L < 0 ? 0 : (L > a.max_context ? a.max_context : L);
+        if (L == 0) continue;
+        const int pos = L - 1;
+        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / kBlockTokens];
+        if (block < 0 || block >= a.num_blocks) continue;
+        const int64_t dst_chunk = ((block * a.num_kv_heads + h) * kBlockTokens + pos % kBlockTokens) * a.row_chunks + c;
+        const int64_t src_chunk = (i * a.num_kv_heads + h) * a.row_chunks + c;
+        const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new);
+        uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);
+        dst[dst_chunk] = src[src_chunk];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_append_scatter(const AppendArgs& a, hipStream_t stream) {
+    if (a.num_seqs <= 0) return hipSuccess;
+    const int64_t total = (int64_t)a.num_seqs * 2LL * a.num_kv_heads * a.row_chunks;
+    int64_t blocks = (total + kScatterThreads - 1) / kScatterThreads;
+    if (blocks > 65536) blocks = 65536;
+    append_scatter_kernel<<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(a);
+    return hipGetLastError();
+}
 
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream) {
     if (a.num_tokens <= 0) return hipSuccess;

@@ -30,6 +30,7 @@ KV_BF16 = 1
 EXPORTED = (
     "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
+    "paged_attention_decode_append",
     "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read", "kv_probe_table_walk",
 )
 
@@ -76,6 +77,9 @@ def _load():
     lib.paged_attention_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, P(u64)]
     lib.paged_attention_decode.restype = ctypes.c_int
     lib.paged_attention_decode.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32, vp, u64, vp]
+    lib.paged_attention_decode_append.restype = ctypes.c_int
+    lib.paged_attention_decode_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32,
+                                                  vp, u64, vp]
     lib.kv_probe_copy.restype = ctypes.c_int
     lib.kv_probe_copy.argtypes = [vp, vp, u64, vp]
     lib.kv_probe_read.restype = ctypes.c_int
@@ -246,6 +250,34 @@ class KVPool:
                                           S, Hq, float(scale), int(max_context_len), int(partition_size),
                                           ws_ptr, int(ws_bytes), _stream_handle(stream)),
                "paged_attention_decode")
+
+    def paged_attention_decode_append(self, layer: int, out, q, k_new, v_new, block_tables, context_lens, *,
+                                      scale: float, max_context_len: int, partition_size: int = 0,
+                                      workspace=None, stream=None) -> None:
+        """Append each sequence's new K/V row at position L_i - 1 and attend, in one call."""
+        import torch
+        S, Hq, D = (int(x) for x in q.shape)
+        if tuple(out.shape) != (S, Hq, D) or D != self.head_dim:
+            raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim]")
+        if tuple(k_new.shape) != (S, self.num_kv_heads, D) or tuple(v_new.shape) != (S, self.num_kv_heads, D):
+            raise ValueError("k_new/v_new must be [num_seqs][num_kv_heads][head_dim]")
+        if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+            raise ValueError("one table row and one length per sequence")
+        ws_ptr, ws_bytes = None, 0
+        if workspace is not None:
+            ws_ptr = _dev_ptr(workspace, "workspace")
+            ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib.paged_attention_decode_append(self.handle, int(layer),
+                                                 _dev_ptr(out, "out", self.torch_dtype),
+                                                 _dev_ptr(q, "q", self.torch_dtype),
+                                                 _dev_ptr(k_new, "k_new", self.torch_dtype),
+                                                 _dev_ptr(v_new, "v_new", self.torch_dtype),
+                                                 _dev_ptr(block_tables, "block_tables", torch.int32),
+                                                 int(block_tables.shape[1]),
+                                                 _dev_ptr(context_lens, "context_lens", torch.int32),
+                                                 S, Hq, float(scale), int(max_context_len), int(partition_size),
+                                                 ws_ptr, int(ws_bytes), _stream_handle(stream)),
+               "paged_attention_decode_append")
 
 
 def probe_copy(dst, src, stream=None) -> None:

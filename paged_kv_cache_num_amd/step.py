@@ -71,10 +71,47 @@ class DecodeStep:
         self.v_new = to_device(v_new, dtype, device)
         self.slots_host = kv_build_slot_mapping(write_tables, B, N, write_seq, write_start, write_count)
         self.slot_mapping = to_device(self.slots_host, "i64", device)
+        self._split_appends(k_new, v_new, context_lens, write_tables, B, N, write_seq, write_start, write_count,
+                            dtype, device)
         self.out = torch.empty_like(self.q)
         ws = self.pool.workspace_bytes(self.num_seqs, self.num_q_heads, self.max_context_len,
                                        self.partition_size)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
+
+    def _split_appends(self, k_new, v_new, context_lens, write_tables, B, N, write_seq, write_start, write_count,
+                       dtype, device):
+        """Separate the decode appends (one row per sequence at position L_i - 1,
+        for paged_attention_decode_append) from every other write (for
+        reshape_and_cache).  ``self.can_fuse`` is False when some sequence with
+        L_i > 0 has no such single-row write."""
+        S = self.num_seqs
+        row0 = np.concatenate([[0], np.cumsum(write_count)]).astype(np.int64)
+        seq_row = np.full(S, -1, dtype=np.int64)
+        other = []
+        for k in range(len(write_seq)):
+            i = int(write_seq[k])
+            if (i < S and int(write_count[k]) == 1 and int(write_start[k]) == int(context_lens[i]) - 1
+                    and seq_row[i] < 0):
+                seq_row[i] = row0[k]
+            else:
+                other.append(k)
+        self.can_fuse = bool(all(seq_row[i] >= 0 for i in range(S) if int(context_lens[i]) > 0))
+        ak = np.zeros((S,) + k_new.shape[1:], dtype=k_new.dtype)
+        av = np.zeros_like(ak)
+        has = seq_row >= 0
+        ak[has] = k_new[seq_row[has]]
+        av[has] = v_new[seq_row[has]]
+        self.append_k, self.append_v = to_device(ak, dtype, device), to_device(av, dtype, device)
+        rows = (np.concatenate([np.arange(row0[k], row0[k + 1]) for k in other]).astype(np.int64)
+                if other else np.zeros(0, dtype=np.int64))
+        self.num_other_tokens = int(rows.size)
+        if rows.size:
+            idx = np.asarray(other)
+            slots = kv_build_slot_mapping(write_tables, B, N, np.asarray(write_seq)[idx],
+                                          np.asarray(write_start)[idx], np.asarray(write_count)[idx])
+            self.other_slots = to_device(slots, "i64", device)
+            self.other_k = to_device(np.ascontiguousarray(k_new[rows]), dtype, device)
+            self.other_v = to_device(np.ascontiguousarray(v_new[rows]), dtype, device)
 
     @classmethod
     def from_workload(cls, wl, **kw):
@@ -97,8 +134,23 @@ class DecodeStep:
         self.scatter(stream)
         self.attend(stream)
 
-    def capture(self):
-        """Capture one step (scatter, then attention) in a HIP graph.
+    def run_fused(self, stream=None):
+        """The same step with the decode appends folded into the attention call
+        (paged_attention_decode_append); other writes still go through
+        reshape_and_cache first."""
+        if not self.can_fuse:
+            raise ValueError("some sequence has no single-row write at position L_i - 1")
+        if self.num_other_tokens:
+            self.pool.reshape_and_cache(self.layer, self.other_k, self.other_v, self.other_slots, stream=stream)
+        self.pool.paged_attention_decode_append(self.layer, self.out, self.q, self.append_k, self.append_v,
+                                                self.block_tables, self.context_lens, scale=self.scale,
+                                                max_context_len=self.max_context_len,
+                                                partition_size=self.partition_size, workspace=self.workspace,
+                                                stream=stream)
+
+    def capture(self, fused: bool = False):
+        """Capture one step (scatter, then attention; with ``fused`` the
+        run_fused form) in a HIP graph.
 
         Every launch of the step reads and writes buffers at fixed addresses
         and allocates nothing, so the step can be captured once and replayed;
@@ -107,14 +159,15 @@ class DecodeStep:
         the library (its per-device worker count) happens outside the capture.
         """
         import torch
+        body = self.run_fused if fused else self.run
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            self.run()
+            body()
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            self.run()
+            body()
         return graph
 
     def out_host(self) -> np.ndarray:

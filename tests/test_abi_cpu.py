@@ -196,6 +196,26 @@ def test_decode_argument_checks_return_before_any_launch():
     K.lib.kv_pool_destroy(h)
 
 
+def test_decode_append_argument_checks_return_before_any_launch():
+    st, h = _pool()
+    L = K.lib
+    args = [0, 0x30000000, 0x40000000, 0x70000000, 0x78000000, 0x50000000, 16, 0x60000000, 4, 8, 0.125, 200, 0,
+            None, 0, None]
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[{"k": 3, "v": 4, "S": 8, "Hq": 9, "scale": 10}[k]] = v
+        return L.paged_attention_decode_append(h, *a)
+    assert L.paged_attention_decode_append(None, *args) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(k=None) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(v=None) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(k=0x70000008) == K.KV_ERR_INVALID_ARGUMENT        # misaligned new row
+    assert call(Hq=6) == K.KV_ERR_UNSUPPORTED                      # group of 3, as for the plain call
+    assert call(scale=0.0) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(S=0, k=None, v=None) == K.KV_OK                    # nothing to do, nothing launched
+    K.lib.kv_pool_destroy(h)
+
+
 def test_workspace_size_formula():
     st, h = _pool(head_dim=128, num_kv_heads=8, dtype="bf16")
     out = ctypes.c_uint64(0)
