@@ -195,6 +195,7 @@ def main(argv=None):
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing pass")
     ap.add_argument("--no-identity", action="store_true",
                     help="skip timing the same batch with contiguous (identity-like) block tables")
+    ap.add_argument("--no-copy-blocks", action="store_true", help="skip timing copy-on-write block copies")
     ap.add_argument("--table-walk-probe", type=int, default=0, metavar="N",
                     help="also run the table-walk probe N times in each workgroup ordering (for counter runs)")
     ap.add_argument("--no-fuse", action="store_true",
@@ -394,6 +395,36 @@ def main(argv=None):
         del dense
         torch.cuda.synchronize()
 
+    # Copy-on-write block copies (kv_copy_blocks) on a pool of the same block
+    # shape: 512 disjoint (src, dst) pairs, bytes = read + write of K and V.
+    copy = None
+    if not args.no_copy_blocks:
+        from paged_kv_cache_num_amd import KVPool
+        npairs = 512
+        cpool = KVPool.allocate(num_layers=1, num_blocks=2 * npairs, block_size=wl.block_size,
+                                num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim,
+                                dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16, device="cuda")
+        cpool.k.fill_(1)
+        cpool.v.fill_(2)
+        perm = torch.randperm(2 * npairs, generator=torch.Generator().manual_seed(0)).to(torch.int32)
+        pairs = perm.view(npairs, 2).contiguous().cuda()
+        cus = []
+        for i in range(args.warmup + K):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            cpool.copy_blocks(pairs)
+            b.record()
+            b.synchronize()
+            if i >= args.warmup:
+                cus.append(a.elapsed_time(b) * 1e3)
+        block_bytes = wl.num_kv_heads * wl.block_size * wl.head_dim * (4 if wl.dtype == "f32" else 2)
+        moved = npairs * 2 * block_bytes * 2
+        cp50 = percentile(cus, 0.5)
+        copy = {"pairs": npairs, "bytes_moved": moved, "us_p50": round(cp50, 2),
+                "gbps": round(moved / (cp50 * 1e-6) / 1e9, 1)}
+        del cpool, pairs
+        torch.cuda.synchronize()
+
     table_walk = None
     if args.table_walk_probe:
         from paged_kv_cache_num_amd import probe_table_walk
@@ -452,6 +483,7 @@ def main(argv=None):
         "internal_waste_tokens": int(nbytes["blocks"] * wl.block_size - int(np.sum(wl.context_lens))),
         "identity_tables": identity,
         "table_walk_probe": table_walk,
+        "copy_blocks": copy,
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -144,6 +144,25 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
                             const int64_t* slot_mapping, int64_t num_tokens, void* stream);
 
 /*
+ * GPU step, copy-on-write ([KVC] "Prefix sharing, reference counts, and
+ * copy-on-write"; [PIF] "03 Sharing via copy-on-write"): before a sequence
+ * writes into a block that other tables also name, the block manager takes a
+ * fresh block, has its contents copied, and repoints the writer's table entry.
+ * This call is that device copy: for every pair p, block block_pairs[2p] is
+ * copied to block block_pairs[2p + 1] in every layer of the K and the V tensor
+ * (H_kv * B * D * e contiguous bytes per layer and tensor), bit for bit.
+ *   block_pairs: device, int32 [num_pairs][2] (src, dst), 4-byte aligned.
+ *                A pair naming a block outside [0, num_blocks) is skipped.
+ *   Precondition: no destination appears twice or as a source of another
+ *   pair (the copies run in no particular order).
+ * The refcount check and the table update are host bookkeeping of the block
+ * manager; the library does not keep reference counts.
+ * Errors: KV_ERR_INVALID_ARGUMENT (null handle, negative count, null or
+ * misaligned pairs), KV_ERR_HIP.  num_pairs == 0 queues nothing.
+ */
+kv_status kv_copy_blocks(kv_pool_t pool, const int32_t* block_pairs, int32_t num_pairs, void* stream);
+
+/*
  * Workspace needed by paged_attention_decode for this shape and mode (see
  * partition_size below).  Zero when no workspace is used.  With partitions it
  * holds one fp32 running max, sum and unnormalised output per (sequence,

@@ -158,6 +158,34 @@ class BlockAllocator:
         self.refcount[b] += 1
         return b
 
+    def fork(self, row) -> List[int]:
+        """A child table naming the same blocks (every count goes up by one)."""
+        return [self.share(int(b)) for b in row]
+
+    def cow_for_append(self, row: List[int], pos: int, block_size: int):
+        """The refcount check on the append path ("PagedAttention, Internals
+        First", "03 Sharing via copy-on-write"; aicassindra.com "GPU paged KV
+        cache", "Prefix sharing, reference counts, and copy-on-write").
+
+        Token ``pos`` of the sequence whose table is ``row`` is about to be
+        written.  A fresh block is appended when ``pos`` starts a new block.
+        If its block is named by more than one table, a fresh block is taken,
+        the old count goes down by one and ``row`` is repointed; the
+        ``(src, dst)`` pair of the device copy is returned.  Otherwise (count
+        1: write in place) ``None``.
+        """
+        b = pos // block_size
+        if b == len(row):
+            row.append(self.alloc())
+            return None
+        old = int(row[b])
+        if self.refcount.get(old, 0) > 1:
+            new = self.alloc()
+            self.release(old)
+            row[b] = new
+            return (old, new)
+        return None
+
     def num_free(self) -> int:
         return len(self.free)
 

@@ -112,6 +112,27 @@ def scatter(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np
     return kp, vp
 
 
+def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs):
+    """Copy-on-write block copy, plain numpy (aicassindra.com "GPU paged KV
+    cache", "Prefix sharing, reference counts, and copy-on-write";
+    "PagedAttention, Internals First", "03 Sharing via copy-on-write": the
+    shared block's contents are copied into the writer's fresh block).
+
+    Returns copies of the pools in which block ``dst`` holds what block ``src``
+    held before the call, for every ``(src, dst)`` pair naming two blocks of the
+    pool; pairs naming a block outside it are skipped.  Pools are
+    ``[N][Hkv][B][D]`` or carry a leading layers axis (every layer is copied).
+    """
+    kp, vp = k_pool.copy(), v_pool.copy()
+    n = k_pool.shape[-4]
+    for src, dst in pairs:
+        src, dst = int(src), int(dst)
+        if 0 <= src < n and 0 <= dst < n:
+            kp[..., dst, :, :, :] = k_pool[..., src, :, :, :]
+            vp[..., dst, :, :, :] = v_pool[..., src, :, :, :]
+    return kp, vp
+
+
 def paged_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, dtype: str,
                     block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
                     threads: Optional[int] = None) -> np.ndarray:

@@ -1,0 +1,53 @@
+// Block copy for copy-on-write.
+//
+// aicassindra.com "GPU paged KV cache", "Prefix sharing, reference counts,
+// and copy-on-write", and "PagedAttention, Internals First", "03 Sharing via
+// copy-on-write": a write into a block that more than one table names makes
+// the block manager take a fresh block, copy the shared one into it on the
+// device, and repoint the writer's table entry; only that one (tail) block is
+// ever copied.  This kernel is the device copy: for each (src, dst) pair it
+// copies block src to block dst in every layer of the K and the V tensor.
+//
+// Work items are 16-byte chunks numbered
+//     ((pair * layers + layer) * 2 + {K,V}) * block_chunks + chunk,
+// a (layer, block) run being H_kv * B * D * e contiguous bytes, so
+// neighbouring lanes move neighbouring bytes.  Bit copy, no conversion.
+#include "launch.hpp"
+
+namespace kvp {
+
+namespace {
+
+constexpr int kCopyThreads = 256;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArgs a) {
+    const int64_t per_pair = (int64_t)a.num_layers * 2 * a.block_chunks;
+    const int64_t total = (int64_t)a.num_pairs * per_pair;
+    const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
+    for (int64_t item = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; item < total; item += stride) {
+        const int64_t p = item / per_pair;
+        const int64_t rem = item - p * per_pair;
+        const int64_t run = rem / a.block_chunks;   // layer * 2 + {K,V}
+        const int64_t c = rem - run * a.block_chunks;
+        const int layer = (int)(run >> 1);
+        const int which = (int)(run & 1);
+        const int64_t src = a.pairs[2 * p];
+        const int64_t dst = a.pairs[2 * p + 1];
+        if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) continue;
+        uint4* base = reinterpret_cast<uint4*>((which == 0 ? a.k_base : a.v_base) + (uint64_t)layer * a.layer_bytes);
+        base[dst * a.block_chunks + c] = base[src * a.block_chunks + c];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
+    if (a.num_pairs <= 0) return hipSuccess;
+    const int64_t total = (int64_t)a.num_pairs * a.num_layers * 2 * a.block_chunks;
+    int64_t blocks = (total + kCopyThreads - 1) / kCopyThreads;
+    if (blocks > 65536) blocks = 65536;   // grid-stride loop covers the rest
+    copy_blocks_kernel<<<dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace kvp

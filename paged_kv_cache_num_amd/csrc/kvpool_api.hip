@@ -226,6 +226,27 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
     return ok();
 }
 
+kv_status kv_copy_blocks(kv_pool_t pool, const int32_t* block_pairs, int32_t num_pairs, void* stream) {
+    if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "pool is NULL");
+    if (num_pairs < 0) return fail(KV_ERR_INVALID_ARGUMENT, "num_pairs %d < 0", num_pairs);
+    if (num_pairs == 0) return ok();
+    if (!block_pairs) return fail(KV_ERR_INVALID_ARGUMENT, "block_pairs is NULL");
+    if (reinterpret_cast<uintptr_t>(block_pairs) & 3u) return fail(KV_ERR_INVALID_ARGUMENT, "block_pairs must be 4-byte aligned");
+    const kv_pool_desc& d = pool->desc;
+    kvp::CopyBlocksArgs a;
+    a.k_base = pool->k_base;
+    a.v_base = pool->v_base;
+    a.layer_bytes = pool->layer_bytes;
+    a.pairs = block_pairs;
+    a.num_pairs = num_pairs;
+    a.num_layers = d.num_layers;
+    a.num_blocks = d.num_blocks;
+    a.block_chunks = (int64_t)d.num_kv_heads * d.block_size * d.head_dim * pool->elem_bytes / 16;
+    hipError_t e = kvp::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
+    return ok();
+}
+
 kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int32_t num_q_heads,
                                           int32_t max_context_len, int32_t partition_size, uint64_t* bytes) {
     if (!pool || !bytes) return fail(KV_ERR_INVALID_ARGUMENT, "NULL argument");

@@ -44,6 +44,21 @@ struct AppendArgs {
 
 hipError_t launch_append_scatter(const AppendArgs& a, hipStream_t stream);
 
+// Copy-on-write block copy: block pairs[2p] -> block pairs[2p + 1] in every
+// layer of K and V.  Pairs naming a block outside the pool are skipped.
+struct CopyBlocksArgs {
+    char* k_base;                // layer 0 of the K tensor
+    char* v_base;
+    uint64_t layer_bytes;        // bytes per layer of one tensor
+    const int32_t* pairs;        // [num_pairs][2] (src, dst)
+    int32_t num_pairs;
+    int32_t num_layers;
+    int32_t num_blocks;
+    int64_t block_chunks;        // 16-byte chunks per (layer, block): H_kv * B * D * e / 16
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
     const void* k_layer;
     const void* v_layer;

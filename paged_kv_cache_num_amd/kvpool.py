@@ -30,7 +30,7 @@ KV_BF16 = 1
 EXPORTED = (
     "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
-    "paged_attention_decode_append",
+    "paged_attention_decode_append", "kv_copy_blocks",
     "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read", "kv_probe_table_walk",
 )
 
@@ -77,6 +77,8 @@ def _load():
     lib.paged_attention_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, P(u64)]
     lib.paged_attention_decode.restype = ctypes.c_int
     lib.paged_attention_decode.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32, vp, u64, vp]
+    lib.kv_copy_blocks.restype = ctypes.c_int
+    lib.kv_copy_blocks.argtypes = [vp, vp, i32, vp]
     lib.paged_attention_decode_append.restype = ctypes.c_int
     lib.paged_attention_decode_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32,
                                                   vp, u64, vp]
@@ -250,6 +252,17 @@ class KVPool:
                                           S, Hq, float(scale), int(max_context_len), int(partition_size),
                                           ws_ptr, int(ws_bytes), _stream_handle(stream)),
                "paged_attention_decode")
+
+    def copy_blocks(self, block_pairs, stream=None) -> None:
+        """Copy-on-write device copy: block src -> block dst in every layer of K and V.
+
+        ``block_pairs``: int32 device tensor [num_pairs][2] of (src, dst)."""
+        import torch
+        if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+            raise ValueError("block_pairs must be [num_pairs][2]")
+        n = int(block_pairs.shape[0])
+        ptr = _dev_ptr(block_pairs, "block_pairs", torch.int32) if n else None
+        _check(lib.kv_copy_blocks(self.handle, ptr, n, _stream_handle(stream)), "kv_copy_blocks")
 
     def paged_attention_decode_append(self, layer: int, out, q, k_new, v_new, block_tables, context_lens, *,
                                       scale: float, max_context_len: int, partition_size: int = 0,

@@ -104,3 +104,42 @@ def test_generation_is_deterministic():
     b = kvgen.make_workload("C2", num_seqs=3)
     assert np.array_equal(a.k_pool, b.k_pool) and np.array_equal(a.block_tables, b.block_tables)
     assert np.array_equal(a.q, b.q)
+
+
+def test_fork_then_append_copies_only_the_shared_tail_block():
+    """n samples forked from one prompt cost one prompt plus n tails: only the
+    partially filled tail block is copied, once per writer while it is still
+    shared, and the last holder writes in place ("PagedAttention, Internals
+    First", "03 Sharing via copy-on-write")."""
+    B = 16
+    alloc = kvgen.BlockAllocator(64)
+    parent = [alloc.alloc() for _ in range(7)]          # a 100-token prompt: 6 full blocks + 4 tokens
+    children = [alloc.fork(parent) for _ in range(3)]
+    assert all(alloc.refcount[b] == 4 for b in parent)
+    tail = parent[6]
+    copies = []
+    for row in children + [parent]:
+        pair = alloc.cow_for_append(row, 100, B)
+        if pair is not None:
+            copies.append(pair)
+    assert [src for src, _ in copies] == [tail] * 3     # three copies of the one tail block
+    assert parent[6] == tail and alloc.refcount[tail] == 1
+    assert len({row[6] for row in children + [parent]}) == 4
+    assert all(alloc.refcount[b] == 4 for b in parent[:6])   # the full prompt blocks stay shared
+    # next token of a child lands in its private block: no copy
+    assert alloc.cow_for_append(children[0], 101, B) is None
+    # a position that starts a new block takes a fresh one, no copy
+    row = children[1]
+    for pos in range(101, 112):
+        assert alloc.cow_for_append(row, pos, B) is None
+    assert alloc.cow_for_append(row, 112, B) is None and len(row) == 8
+
+
+def test_full_prompt_blocks_never_copy():
+    """A prompt that fills its last block leaves nothing to copy: every sample's
+    first token opens a private block."""
+    alloc = kvgen.BlockAllocator(300)
+    parent = [alloc.alloc() for _ in range(125)]         # 2000 tokens = 125 full blocks
+    rows = [alloc.fork(parent) for _ in range(3)] + [parent]
+    assert all(alloc.cow_for_append(r, 2000, 16) is None for r in rows)
+    assert all(len(r) == 126 for r in rows) and alloc.refcount[parent[0]] == 4

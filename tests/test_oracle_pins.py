@@ -267,3 +267,38 @@ def test_spec_inputs_are_weak_and_need_variants():
         wlv = kvgen.make_workload("C2", variant=v, num_seqs=4)
         refv = oracle.run_step(wlv)["out"]
         assert not _bf16_gate(np.zeros_like(refv), refv), v
+
+
+# ------------------------------------------------------------ copy-on-write --
+
+def test_attention_through_a_copied_block_is_exact():
+    """A copied block is the same data: attention through a table repointed at
+    the copy equals attention through the original, bit for bit, and the pool
+    differs only at the destination."""
+    rng = np.random.default_rng(11)
+    N, H, B, D = 12, 2, 16, 64
+    kp = rng.standard_normal((N, H, B, D)).astype(np.float32)
+    vp = rng.standard_normal((N, H, B, D)).astype(np.float32)
+    q = rng.standard_normal((1, 4, D)).astype(np.float32)
+    table = np.array([[3, 7, 1, 0]], dtype=np.int32)
+    lens = np.array([53], dtype=np.int32)
+    k2, v2 = oracle.copy_blocks(kp, vp, [(7, 10)])
+    changed = [b for b in range(N) if not (np.array_equal(k2[b], kp[b]) and np.array_equal(v2[b], vp[b]))]
+    assert changed == [10]
+    moved = table.copy()
+    moved[0, 1] = 10
+    a = oracle.paged_attention(q, kp, vp, "f32", table, lens, 0.125)
+    b = oracle.paged_attention(q, k2, v2, "f32", moved, lens, 0.125)
+    assert np.array_equal(a, b)
+
+
+def test_copy_blocks_skips_identity_and_out_of_range_pairs_and_copies_every_layer():
+    rng = np.random.default_rng(12)
+    kp = rng.standard_normal((3, 6, 2, 16, 8)).astype(np.float32)   # [layers][N][H][B][D]
+    vp = rng.standard_normal((3, 6, 2, 16, 8)).astype(np.float32)
+    k2, v2 = oracle.copy_blocks(kp, vp, [(2, 2), (-1, 3), (1, 6), (6, 0)])
+    assert np.array_equal(k2, kp) and np.array_equal(v2, vp)
+    k3, v3 = oracle.copy_blocks(kp, vp, [(4, 1), (0, 5)])
+    for layer in range(3):
+        assert np.array_equal(k3[layer, 1], kp[layer, 4]) and np.array_equal(v3[layer, 5], vp[layer, 0])
+        assert np.array_equal(k3[layer, [0, 2, 3, 4]], kp[layer, [0, 2, 3, 4]])
