@@ -298,7 +298,8 @@ __device__ __forceinline__ void append_into(Tile& t, const AppendRow& app, const
 // in-order load counter lets each block wait for its own tile only.
 template <int G, int D>
 __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* trow, int stride,
-                                     int nk, int b0, int L, const WalkCtx& c, const AppendRow& app) {
+                                     int nk, int b0, int L, const WalkCtx& c, const AppendRow& app,
+                                     bool have_first = false, int tv_first = 0) {
     auto tile_ptrs = [&](int tv, int k, const uint4*& kt, const uint4*& vt) {
         uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(tv, k);
         phys = phys < c.num_blocks ? phys : c.num_blocks - 1;   // stay inside the pool whatever the table says
@@ -309,7 +310,8 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
     uint4 new_k[kKK], new_v;   // the appended row, loaded once the last chunk's first tiles are in flight
     for (int k0 = 0; k0 < nk; k0 += 64) {
         const int nc = min(64, nk - k0);
-        const int tv = c.lane < nc ? trow[(size_t)(k0 + c.lane) * stride] : 0;
+        // the first chunk's entries may have been fetched ahead (entries past nc are never read)
+        const int tv = (k0 == 0 && have_first) ? tv_first : (c.lane < nc ? trow[(size_t)(k0 + c.lane) * stride] : 0);
         Tile tt[D];
         const uint4 *kt, *vt;
 #pragma unroll
@@ -553,6 +555,8 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     int b = (int)(off - (int64_t)kv * nblk);
 
     bool first_piece = true;
+    bool pf_valid = false;   // table entries of the next piece fetched ahead
+    int pf_seq = -1, pf_tv = 0;
     while (t < t_end && seq < S) {
         const int n_here = (int)min((int64_t)(nblk - b), t_end - t);
         const bool whole = (b == 0) && (n_here == nblk);
@@ -569,7 +573,23 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         app.j = (L - 1) % kBlockTokens;
         app.krow = reinterpret_cast<const uint4*>(a.k_append) + ((size_t)seq * Hkv + kv) * kRC;
         app.vrow = reinterpret_cast<const uint4*>(a.v_append) + ((size_t)seq * Hkv + kv) * kRC;
-        walk<G, kStreamDepth>(st, qb, a.tables + (size_t)seq * a.max_blocks + b, 1, n_here, b, L, c, app);
+        // The next piece of this slice, if it starts a new (sequence, KV head),
+        // begins at block 0 of (seq, kv + 1) or of the next sequence: fetch its
+        // first table entries now, so that piece waits for its tiles only.
+        const bool use_pf = pf_valid && pf_seq == seq && b == 0;
+        const int tv_here = pf_tv;
+        pf_valid = false;
+        if (b + n_here == nblk && t + n_here < t_end) {
+            const int nseq = kv + 1 < Hkv ? seq : seq + 1;
+            if (nseq < S) {
+                const int ncap = min(kWave, a.max_blocks);
+                pf_tv = c.lane < ncap ? a.tables[(size_t)nseq * a.max_blocks + c.lane] : 0;
+                pf_seq = nseq;
+                pf_valid = true;
+            }
+        }
+        walk<G, kStreamDepth>(st, qb, a.tables + (size_t)seq * a.max_blocks + b, 1, n_here, b, L, c, app, use_pf,
+                              tv_here);
         const float l_tot = total_l(st);
 
         if (whole) {
