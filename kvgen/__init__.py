@@ -301,7 +301,7 @@ def make_workload(name: str, seed: Optional[int] = None, variant: str = "spec", 
                   num_seqs: Optional[int] = None, poison: bool = False,
                   unshared: bool = False, lengths: Optional[np.ndarray] = None,
                   shape: Optional[Shape] = None, num_blocks: Optional[int] = None,
-                  table_pad: int = 0) -> Workload:
+                  table_pad: int = 0, block_size: Optional[int] = None) -> Workload:
     """Build one seeded workload.
 
     name     one of C1..C5 (or any name when ``shape`` and ``lengths`` are given)
@@ -321,6 +321,8 @@ def make_workload(name: str, seed: Optional[int] = None, variant: str = "spec", 
         if cfg is None:
             raise ValueError(f"unknown config {name}")
         shape = cfg["shape"]
+    if block_size is not None:
+        shape = dataclasses.replace(shape, block_size=int(block_size))
     if seed is None:
         seed = int(name[1:]) if name[1:].isdigit() else 0
     S = num_seqs if num_seqs is not None else (cfg["S"] if cfg else len(lengths))

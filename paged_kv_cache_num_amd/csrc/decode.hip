@@ -319,15 +319,21 @@ hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
 
 }  // namespace
 
-bool decode_shape_supported(int dtype, int head_dim, int group) {
-    return (dtype == 0 || dtype == 1) && (head_dim == 64 || head_dim == 128) &&
-           (group == 1 || group == 2 || group == 4 || group == 8);
+bool decode_shape_supported(int dtype, int head_dim, int group, int block_size) {
+    if (!(dtype == 0 || dtype == 1) || !(head_dim == 64 || head_dim == 128) ||
+        !(group == 1 || group == 2 || group == 4 || group == 8))
+        return false;
+    // the bf16 / head_dim-128 kernels walk 16-token tiles of any block size
+    // 8..128; the vector-unit kernel is built for B = 16
+    if (dtype == 1 && head_dim == 128)
+        return block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128;
+    return block_size == kBlockTokens;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
     if (a.num_seqs <= 0) return hipSuccess;
     const int group = a.num_q_heads / a.num_kv_heads;
-    if (!decode_shape_supported(dtype, head_dim, group)) return hipErrorInvalidValue;
+    if (!decode_shape_supported(dtype, head_dim, group, a.block_size)) return hipErrorInvalidValue;
     if (dtype == 1 && head_dim == 128) {
         hipError_t e = launch_decode_bf16_mfma(a, group, stream);
         if (e != hipSuccess) return e;

@@ -150,7 +150,7 @@ __device__ __forceinline__ void process(State& st, Tile& t, const bf16x8_t (&qb)
                  "+v"(od[2][0]), "+v"(od[2][1]), "+v"(od[3][0]), "+v"(od[3][1]) : : "memory");
     after_v();
 
-    if (tok0 + kBlockTokens > L) {   // last, partially filled block (wave-uniform branch)
+    if (tok0 + kTileTokens > L) {   // last, partially filled tile (wave-uniform branch)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (tok0 + 4 * r + i >= L) {
@@ -217,25 +217,36 @@ struct WalkCtx {
     const uint4* kpool;
     const uint4* vpool;
     size_t head_off;       // kv * tile chunks
-    size_t block_stride;   // num_kv_heads * tile chunks
+    size_t block_stride;   // num_kv_heads * B * 16-byte chunks per row
     uint32_t num_blocks;
+    int max_blocks;        // table entries per sequence
+    bool pair8;            // B = 8: a 16-token tile is two blocks
+    int sub_shift;         // B >= 16: log2(B / 16), tiles per block = 1 << sub_shift
     int k_off, v_off;      // this lane's 16-byte chunk in a K / V tile
     int lane, r, n;
     float sl2;
 };
 
+// kAnyB: the block size comes from the arguments (8..128); otherwise it is 16
+// and every block-size field below is a constant the walk folds away.
+template <bool kAnyB>
 __device__ __forceinline__ WalkCtx make_ctx(const DecodeArgs& a, int kv) {
+    const int B = kAnyB ? a.block_size : kTileTokens;
     WalkCtx c;
     c.lane = threadIdx.x & (kWave - 1);
     c.r = c.lane >> 4;
     c.n = c.lane & 15;
     c.kpool = reinterpret_cast<const uint4*>(a.k_layer);
     c.vpool = reinterpret_cast<const uint4*>(a.v_layer);
-    c.head_off = (size_t)kv * (kBlockTokens * kRC);
-    c.block_stride = (size_t)a.num_kv_heads * (kBlockTokens * kRC);
+    c.head_off = (size_t)kv * ((size_t)B * kRC);
+    c.block_stride = (size_t)a.num_kv_heads * ((size_t)B * kRC);
     c.num_blocks = (uint32_t)a.num_blocks;
-    c.k_off = c.n * kRC + c.r;          // K: token n, chunk 4*kk + r
-    c.v_off = (4 * c.r) * kRC + c.n;    // V: token 4r + i, chunk n
+    c.max_blocks = a.max_blocks;
+    c.pair8 = kAnyB && B == 8;
+    c.sub_shift = kAnyB ? 31 - __builtin_clz(B >= kTileTokens ? B / kTileTokens : 1) : 0;
+    // K: token n, chunk 4*kk + r; V: token 4r + i, chunk n (rows within the lane's block when B = 8)
+    c.k_off = (c.pair8 ? (c.n & 7) : c.n) * kRC + c.r;
+    c.v_off = (c.pair8 ? ((4 * c.r) & 7) : 4 * c.r) * kRC + c.n;
     c.sl2 = a.scale_log2;
     return c;
 }
@@ -286,6 +297,23 @@ __device__ __forceinline__ void append_into(Tile& t, const AppendRow& app, const
         if (4 * c.r + i == app.j) t.v[i] = nv;
 }
 
+// Table entries of tile e (16 tokens) of a sequence whose table row is `row`:
+// for B >= 16 the block holding it (entry e / (B/16)); for B = 8 the two
+// blocks holding its halves (entries 2e and 2e + 1; the second may lie past
+// the row when the tile is the last one, and is then never used).
+__device__ __forceinline__ int2 tile_entries(const int32_t* row, int e, bool valid, const WalkCtx& c) {
+    int2 tv = make_int2(0, 0);
+    if (valid) {
+        if (c.pair8) {
+            tv.x = row[2 * e];
+            if (2 * e + 1 < c.max_blocks) tv.y = row[2 * e + 1];
+        } else {
+            tv.x = row[e >> c.sub_shift];
+        }
+    }
+    return tv;
+}
+
 // Walk nk blocks of one (sequence, KV head): logical blocks b0 + stride*k,
 // k = 0..nk-1, whose table entries start at trow (= row + b0).
 //
@@ -297,26 +325,46 @@ __device__ __forceinline__ void append_into(Tile& t, const AppendRow& app, const
 // an L2 hit) and in the order the tiles are consumed, so the hardware's
 // in-order load counter lets each block wait for its own tile only.
 template <int G, int D>
-__device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* trow, int stride,
+__device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* row, int stride,
                                      int nk, int b0, int L, const WalkCtx& c, const AppendRow& app,
-                                     bool have_first = false, int tv_first = 0) {
-    auto tile_ptrs = [&](int tv, int k, const uint4*& kt, const uint4*& vt) {
-        uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(tv, k);
-        phys = phys < c.num_blocks ? phys : c.num_blocks - 1;   // stay inside the pool whatever the table says
-        const size_t base = (size_t)phys * c.block_stride + c.head_off;
-        kt = c.kpool + base;
-        vt = c.vpool + base;
+                                     bool have_first = false, int tv0_first = 0, int tv1_first = 0) {
+    // Tile k of the current chunk (tile b0 + (k0 + k) * stride of the sequence).
+    // Each lane addresses its own rows: for B = 8 the K rows of tokens 8..15 and
+    // the V rows of lanes r >= 2 come from the second block.
+    int k0 = 0;
+    auto tile_ptrs = [&](int tv0, int tv1, int k, const uint4*& kt, const uint4*& vt) {
+        uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane(tv0, k);
+        p0 = p0 < c.num_blocks ? p0 : c.num_blocks - 1;   // stay inside the pool whatever the table says
+        if (c.pair8) {
+            uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane(tv1, k);
+            p1 = p1 < c.num_blocks ? p1 : c.num_blocks - 1;
+            kt = c.kpool + (size_t)(c.n < 8 ? p0 : p1) * c.block_stride + c.head_off;
+            vt = c.vpool + (size_t)(c.r < 2 ? p0 : p1) * c.block_stride + c.head_off;
+        } else {
+            const int e = b0 + (k0 + k) * stride;
+            const size_t base = (size_t)p0 * c.block_stride + c.head_off +
+                                (size_t)(e & ((1 << c.sub_shift) - 1)) * (kTileTokens * kRC);
+            kt = c.kpool + base;
+            vt = c.vpool + base;
+        }
+    };
+    // the block holding row j of tile k names a block of the pool
+    auto row_in_pool = [&](int tv0, int tv1, int k, int j) -> bool {
+        const int tv = (c.pair8 && j >= 8) ? tv1 : tv0;
+        return (uint32_t)__builtin_amdgcn_readlane(tv, k) < c.num_blocks;
     };
     uint4 new_k[kKK], new_v;   // the appended row, loaded once the last chunk's first tiles are in flight
-    for (int k0 = 0; k0 < nk; k0 += 64) {
+    for (k0 = 0; k0 < nk; k0 += 64) {
         const int nc = min(64, nk - k0);
         // the first chunk's entries may have been fetched ahead (entries past nc are never read)
-        const int tv = (k0 == 0 && have_first) ? tv_first : (c.lane < nc ? trow[(size_t)(k0 + c.lane) * stride] : 0);
+        const int2 tvp = (k0 == 0 && have_first) ? make_int2(tv0_first, tv1_first)
+                                                 : tile_entries(row, b0 + (k0 + c.lane) * stride, c.lane < nc, c);
+        const int tv0 = tvp.x, tv1 = tvp.y;
         Tile tt[D];
         const uint4 *kt, *vt;
 #pragma unroll
         for (int s = 0; s < D; ++s) {
-            tile_ptrs(tv, min(s, nc - 1), kt, vt);
+            tile_ptrs(tv0, tv1, min(s, nc - 1), kt, vt);
             load_k(tt[s], kt, c.k_off);
             asm volatile("" : : : "memory");
             load_v(tt[s], vt, c.v_off);
@@ -334,13 +382,12 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
                 // Past the end a block is a repeat, given a first token of L
                 // so that every position is masked and it adds exact zeros;
                 // running it anyway keeps the loads of every path equal.
-                tile_ptrs(tv, min(k + s + D, nc - 1), kt, vt);
+                tile_ptrs(tv0, tv1, min(k + s + D, nc - 1), kt, vt);
                 __builtin_amdgcn_sched_barrier(0);
-                const int tok = k + s < nc ? (b0 + (k0 + k + s) * stride) * kBlockTokens : L;
-                // wave-uniform: the block holding the new token; a table entry outside
+                const int tok = k + s < nc ? (b0 + (k0 + k + s) * stride) * kTileTokens : L;
+                // wave-uniform: the tile holding the new token; a table entry outside
                 // the pool gets no write (as the scatter skips such a slot)
-                if (app.active && tok == app.tok0 &&
-                    (uint32_t)__builtin_amdgcn_readlane(tv, k + s) < c.num_blocks) {
+                if (app.active && tok == app.tok0 && row_in_pool(tv0, tv1, k + s, app.j)) {
                     append_into(tt[s], app, new_k, new_v, c);
                 }
                 process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2,
@@ -350,7 +397,7 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
     }
 }
 
-template <int G>
+template <int G, bool kAnyB>
 __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int part = blockIdx.x;
@@ -362,12 +409,12 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
     L = __builtin_amdgcn_readfirstlane(L);
     const int nparts = L == 0 ? 1 : (L + a.part_tokens - 1) / a.part_tokens;
     if (part >= nparts) return;
-    const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
-    const int bpp = a.part_tokens / kBlockTokens;
+    const int nblk = (L + kTileTokens - 1) / kTileTokens;   // 16-token tiles
+    const int bpp = a.part_tokens / kTileTokens;
     const int b_begin = part * bpp;
     const int b_end = min(nblk, b_begin + bpp);
 
-    const WalkCtx c = make_ctx(a, kv);
+    const WalkCtx c = make_ctx<kAnyB>(a, kv);
     const int r = c.r, n = c.n;
     bf16x8_t qb[kKK];
     load_q<G>(qb, a, seq, kv, c);
@@ -379,7 +426,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
     AppendRow none;
     none.active = false;
     none.krow = none.vrow = nullptr;
-    walk<G, 2>(st, qb, a.tables + (size_t)seq * a.max_blocks + first, kWaves, nk, first, L, c, none);
+    walk<G, 2>(st, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
     const float l_tot = total_l(st);
 
     // waves of the workgroup merge through LDS
@@ -475,9 +522,9 @@ __device__ __forceinline__ void append_scatter_waves(const DecodeArgs& a, int64_
         const int L = clamp_len(a.lens[i], a.max_context);
         if (L == 0) continue;
         const int pos = L - 1;
-        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / kBlockTokens];
+        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / a.block_size];
         if (block < 0 || block >= a.num_blocks) continue;
-        const int64_t dst = ((block * a.num_kv_heads + h) * kBlockTokens + pos % kBlockTokens) * kRC + ch;
+        const int64_t dst = ((block * a.num_kv_heads + h) * a.block_size + pos % a.block_size) * kRC + ch;
         const int64_t src = (i * a.num_kv_heads + h) * kRC + ch;
         const uint4* from = reinterpret_cast<const uint4*>(which == 0 ? a.k_append : a.v_append);
         uint4* to = const_cast<uint4*>(reinterpret_cast<const uint4*>(which == 0 ? a.k_layer : a.v_layer));
@@ -485,7 +532,7 @@ __device__ __forceinline__ void append_scatter_waves(const DecodeArgs& a, int64_
     }
 }
 
-template <int G>
+template <int G, bool kAnyB>
 __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int64_t W = a.workers;
@@ -514,7 +561,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
         if (ch < nchunks) {
-            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kBlockTokens - 1) / kBlockTokens);
+            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kTileTokens - 1) / kTileTokens);
             int64_t incl = nt;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
@@ -537,7 +584,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
         if (ch < nchunks && seq == S) {
-            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kBlockTokens - 1) / kBlockTokens);
+            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kTileTokens - 1) / kTileTokens);
             const uint64_t bal = __builtin_amdgcn_ballot_w64(nt > 0 && ex_c[ch] <= t && t < ex_c[ch] + nt);
             if (bal) {
                 const int j = __builtin_ctzll(bal);
@@ -549,19 +596,19 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     }
     seq = __builtin_amdgcn_readfirstlane(seq);
     L = __builtin_amdgcn_readfirstlane(L);
-    int nblk = (L + kBlockTokens - 1) / kBlockTokens;
+    int nblk = (L + kTileTokens - 1) / kTileTokens;   // 16-token tiles
     int64_t off = t - seq_first;
     int kv = (int)(off / nblk);
     int b = (int)(off - (int64_t)kv * nblk);
 
     bool first_piece = true;
     bool pf_valid = false;   // table entries of the next piece fetched ahead
-    int pf_seq = -1, pf_tv = 0;
+    int pf_seq = -1, pf_tv0 = 0, pf_tv1 = 0;
     while (t < t_end && seq < S) {
         const int n_here = (int)min((int64_t)(nblk - b), t_end - t);
         const bool whole = (b == 0) && (n_here == nblk);
 
-        const WalkCtx c = make_ctx(a, kv);
+        const WalkCtx c = make_ctx<kAnyB>(a, kv);
         bf16x8_t qb[kKK];
         load_q<G>(qb, a, seq, kv, c);
         State st;
@@ -569,27 +616,31 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         // the piece that ends with the sequence's last block takes the appended row
         AppendRow app;
         app.active = a.k_append != nullptr && b + n_here == nblk;
-        app.tok0 = (nblk - 1) * kBlockTokens;
-        app.j = (L - 1) % kBlockTokens;
+        app.tok0 = (nblk - 1) * kTileTokens;
+        app.j = (L - 1) % kTileTokens;
         app.krow = reinterpret_cast<const uint4*>(a.k_append) + ((size_t)seq * Hkv + kv) * kRC;
         app.vrow = reinterpret_cast<const uint4*>(a.v_append) + ((size_t)seq * Hkv + kv) * kRC;
         // The next piece of this slice, if it starts a new (sequence, KV head),
         // begins at block 0 of (seq, kv + 1) or of the next sequence: fetch its
         // first table entries now, so that piece waits for its tiles only.
         const bool use_pf = pf_valid && pf_seq == seq && b == 0;
-        const int tv_here = pf_tv;
+        const int tv0_here = pf_tv0, tv1_here = pf_tv1;
         pf_valid = false;
         if (b + n_here == nblk && t + n_here < t_end) {
             const int nseq = kv + 1 < Hkv ? seq : seq + 1;
             if (nseq < S) {
-                const int ncap = min(kWave, a.max_blocks);
-                pf_tv = c.lane < ncap ? a.tables[(size_t)nseq * a.max_blocks + c.lane] : 0;
+                // tiles 0..63 of the next sequence's row; a lane whose tile would
+                // need an entry past the row loads nothing (the walk never reads it)
+                const bool ok = c.pair8 ? 2 * c.lane < a.max_blocks : (c.lane >> c.sub_shift) < a.max_blocks;
+                const int2 pf = tile_entries(a.tables + (size_t)nseq * a.max_blocks, c.lane, ok, c);
+                pf_tv0 = pf.x;
+                pf_tv1 = pf.y;
                 pf_seq = nseq;
                 pf_valid = true;
             }
         }
-        walk<G, kStreamDepth>(st, qb, a.tables + (size_t)seq * a.max_blocks + b, 1, n_here, b, L, c, app, use_pf,
-                              tv_here);
+        walk<G, kStreamDepth>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, app, use_pf,
+                              tv0_here, tv1_here);
         const float l_tot = total_l(st);
 
         if (whole) {
@@ -636,7 +687,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                 do {
                     ++seq;
                     L = (seq < S) ? __builtin_amdgcn_readfirstlane(clamp_len(a.lens[seq], a.max_context)) : 0;
-                    nblk = (L + kBlockTokens - 1) / kBlockTokens;
+                    nblk = (L + kTileTokens - 1) / kTileTokens;
                 } while (nblk == 0 && seq < S && t < t_end);
             }
         }
@@ -663,7 +714,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
         for (int h = 0; h < G; ++h) out[h * (kD / 2) + lane] = 0u;
         return;
     }
-    const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
+    const int nblk = (L + kTileTokens - 1) / kTileTokens;   // 16-token tiles
     const int64_t T = a.ws_prefix[a.num_seqs];
     const int64_t W = num_workers;
     const int64_t s0 = a.ws_prefix[seq] + (int64_t)kv * nblk;
@@ -754,7 +805,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
 
 template <int G>
 const void* streamk_kernel_ptr() {
-    return reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G>);
+    return reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, true>);
 }
 
 }  // namespace
@@ -805,12 +856,25 @@ hipError_t launch_decode_bf16_streamk(const DecodeArgs& a_in, int group, int wor
         extra = extra < 1 ? 1 : (extra > 256 ? 256 : extra);
     }
     dim3 grid((unsigned)(workers + extra));
+    const bool any_b = a.block_size != kTileTokens;
     dim3 fix((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     switch (group) {
-        case 1: decode_bf16_streamk_kernel<1><<<grid, kWave, 0, stream>>>(a); break;
-        case 2: decode_bf16_streamk_kernel<2><<<grid, kWave, 0, stream>>>(a); break;
-        case 4: decode_bf16_streamk_kernel<4><<<grid, kWave, 0, stream>>>(a); break;
-        case 8: decode_bf16_streamk_kernel<8><<<grid, kWave, 0, stream>>>(a); break;
+        case 1:
+            if (any_b) decode_bf16_streamk_kernel<1, true><<<grid, kWave, 0, stream>>>(a);
+            else decode_bf16_streamk_kernel<1, false><<<grid, kWave, 0, stream>>>(a);
+            break;
+        case 2:
+            if (any_b) decode_bf16_streamk_kernel<2, true><<<grid, kWave, 0, stream>>>(a);
+            else decode_bf16_streamk_kernel<2, false><<<grid, kWave, 0, stream>>>(a);
+            break;
+        case 4:
+            if (any_b) decode_bf16_streamk_kernel<4, true><<<grid, kWave, 0, stream>>>(a);
+            else decode_bf16_streamk_kernel<4, false><<<grid, kWave, 0, stream>>>(a);
+            break;
+        case 8:
+            if (any_b) decode_bf16_streamk_kernel<8, true><<<grid, kWave, 0, stream>>>(a);
+            else decode_bf16_streamk_kernel<8, false><<<grid, kWave, 0, stream>>>(a);
+            break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
@@ -828,11 +892,24 @@ hipError_t launch_decode_bf16_streamk(const DecodeArgs& a_in, int group, int wor
 hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
     dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     dim3 block(kWaves * kWave);
+    const bool any_b = a.block_size != kTileTokens;
     switch (group) {
-        case 1: decode_bf16_mfma_kernel<1><<<grid, block, 0, stream>>>(a); break;
-        case 2: decode_bf16_mfma_kernel<2><<<grid, block, 0, stream>>>(a); break;
-        case 4: decode_bf16_mfma_kernel<4><<<grid, block, 0, stream>>>(a); break;
-        case 8: decode_bf16_mfma_kernel<8><<<grid, block, 0, stream>>>(a); break;
+        case 1:
+            if (any_b) decode_bf16_mfma_kernel<1, true><<<grid, block, 0, stream>>>(a);
+            else decode_bf16_mfma_kernel<1, false><<<grid, block, 0, stream>>>(a);
+            break;
+        case 2:
+            if (any_b) decode_bf16_mfma_kernel<2, true><<<grid, block, 0, stream>>>(a);
+            else decode_bf16_mfma_kernel<2, false><<<grid, block, 0, stream>>>(a);
+            break;
+        case 4:
+            if (any_b) decode_bf16_mfma_kernel<4, true><<<grid, block, 0, stream>>>(a);
+            else decode_bf16_mfma_kernel<4, false><<<grid, block, 0, stream>>>(a);
+            break;
+        case 8:
+            if (any_b) decode_bf16_mfma_kernel<8, true><<<grid, block, 0, stream>>>(a);
+            else decode_bf16_mfma_kernel<8, false><<<grid, block, 0, stream>>>(a);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

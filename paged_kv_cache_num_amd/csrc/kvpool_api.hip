@@ -92,7 +92,8 @@ Plan plan_decode(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, i
         return p;
     }
     if (partition_size == 0 || partition_size >= max_context_len) {
-        int32_t whole = (int32_t)round_up((uint64_t)(max_context_len > 0 ? max_context_len : 1), (uint64_t)d.block_size);
+        const uint64_t unit = d.block_size > kvp::kTileTokens ? (uint64_t)d.block_size : (uint64_t)kvp::kTileTokens;
+        int32_t whole = (int32_t)round_up((uint64_t)(max_context_len > 0 ? max_context_len : 1), unit);
         p.mode = Mode::kSingle;
         p.part_tokens = partition_size > whole ? partition_size : whole;
         p.max_parts = 1;
@@ -147,8 +148,12 @@ kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, k
     if (s != KV_OK) return s;
     if (!k_base || !v_base) return fail(KV_ERR_INVALID_ARGUMENT, "pool base pointer is NULL");
     if (!aligned16(k_base) || !aligned16(v_base)) return fail(KV_ERR_INVALID_ARGUMENT, "pool base pointers must be 16-byte aligned");
-    if (desc->block_size != kvp::kBlockTokens)
-        return fail(KV_ERR_UNSUPPORTED, "block_size %d: kernels are built for %d", desc->block_size, kvp::kBlockTokens);
+    const int32_t B = desc->block_size;
+    if (B != 8 && B != 16 && B != 32 && B != 64 && B != 128)
+        return fail(KV_ERR_UNSUPPORTED, "block_size %d: kernels are built for 8, 16, 32, 64 and 128", B);
+    if (B != kvp::kBlockTokens && !(desc->dtype == KV_BF16 && desc->head_dim == 128))
+        return fail(KV_ERR_UNSUPPORTED, "block_size %d needs a bf16 pool with head_dim 128 (other pools use %d)", B,
+                    kvp::kBlockTokens);
     if (desc->head_dim != 64 && desc->head_dim != 128)
         return fail(KV_ERR_UNSUPPORTED, "head_dim %d: kernels are built for 64 and 128", desc->head_dim);
     kv_pool* p = new (std::nothrow) kv_pool;
@@ -219,6 +224,7 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
     a.slot_mapping = slot_mapping;
     a.num_tokens = num_tokens;
     a.num_slots = (int64_t)pool->desc.num_blocks * pool->desc.block_size;
+    a.block_size = pool->desc.block_size;
     a.num_kv_heads = pool->desc.num_kv_heads;
     a.row_chunks = pool->desc.head_dim * pool->elem_bytes / 16;
     hipError_t e = kvp::launch_scatter(a, static_cast<hipStream_t>(stream));
@@ -253,9 +259,10 @@ kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int3
     *bytes = 0;
     if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_size < 0)
         return fail(KV_ERR_INVALID_ARGUMENT, "negative size argument");
-    if (partition_size % pool->desc.block_size != 0)
-        return fail(KV_ERR_INVALID_ARGUMENT, "partition_size %d is not a multiple of the block size %d", partition_size,
-                    pool->desc.block_size);
+    const int32_t unit = pool->desc.block_size > kvp::kTileTokens ? pool->desc.block_size : kvp::kTileTokens;
+    if (partition_size % unit != 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "partition_size %d is not a multiple of %d (the block size and the 16-token tile)",
+                    partition_size, unit);
     if (num_q_heads % pool->desc.num_kv_heads != 0)
         return fail(KV_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
                     pool->desc.num_kv_heads);
@@ -283,11 +290,12 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
         return fail(KV_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
                     d.num_kv_heads);
     const int group = num_q_heads / d.num_kv_heads;
-    if (!kvp::decode_shape_supported(d.dtype, d.head_dim, group))
+    if (!kvp::decode_shape_supported(d.dtype, d.head_dim, group, d.block_size))
         return fail(KV_ERR_UNSUPPORTED, "query group size %d: kernels are built for 1, 2, 4 and 8", group);
-    if (partition_size % d.block_size != 0)
-        return fail(KV_ERR_INVALID_ARGUMENT, "partition_size %d is not a multiple of the block size %d", partition_size,
-                    d.block_size);
+    const int32_t unit = d.block_size > kvp::kTileTokens ? d.block_size : kvp::kTileTokens;
+    if (partition_size % unit != 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "partition_size %d is not a multiple of %d (the block size and the 16-token tile)",
+                    partition_size, unit);
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * d.block_size)
         return fail(KV_ERR_INVALID_ARGUMENT, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
                     max_context_len, (long long)max_blocks_per_seq * d.block_size);
@@ -330,6 +338,7 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = d.num_kv_heads;
     a.num_blocks = d.num_blocks;
+    a.block_size = d.block_size;
     a.max_context = max_context_len;
     a.part_tokens = plan.part_tokens;
     a.max_parts = plan.max_parts;
@@ -356,6 +365,7 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
             w.max_context = max_context_len;
             w.num_kv_heads = d.num_kv_heads;
             w.row_chunks = d.head_dim * pool->elem_bytes / 16;
+            w.block_size = d.block_size;
             e = kvp::launch_append_scatter(w, static_cast<hipStream_t>(stream));
         }
         if (e == hipSuccess) e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));

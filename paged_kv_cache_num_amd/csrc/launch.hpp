@@ -6,7 +6,8 @@
 
 namespace kvp {
 
-constexpr int kBlockTokens = 16;   // tokens per KV block the kernels are built for
+constexpr int kBlockTokens = 16;   // block size of the fp32 / head_dim-64 decode kernel
+constexpr int kTileTokens = 16;    // tokens per K/V tile of the bf16 decode kernels (the MFMA height)
 constexpr int kStreamKMaxSeqs = 1024;        // batch size up to which the balanced split is used
 constexpr int kStreamKDefaultWorkers = 1024; // worker count when no device can be queried
 
@@ -18,6 +19,7 @@ struct ScatterArgs {
     const int64_t* slot_mapping; // [T]
     int64_t num_tokens;
     int64_t num_slots;           // num_blocks * block_size
+    int32_t block_size;          // tokens per block
     int32_t num_kv_heads;
     int32_t row_chunks;          // 16-byte chunks per (token, head) row = D * elem / 16
 };
@@ -40,6 +42,7 @@ struct AppendArgs {
     int32_t max_context;         // clamp for lens[i]
     int32_t num_kv_heads;
     int32_t row_chunks;          // 16-byte chunks per (token, head) row
+    int32_t block_size;          // tokens per block
 };
 
 hipError_t launch_append_scatter(const AppendArgs& a, hipStream_t stream);
@@ -77,6 +80,7 @@ struct DecodeArgs {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t num_blocks;
+    int32_t block_size;          // tokens per block: 16 for every kernel; 8..128 for the bf16 ones
     int32_t max_context;         // clamp for lens[i]
     int32_t part_tokens;         // tokens per partition (multiple of 16)
     int32_t max_parts;           // ceil(max_context / part_tokens), >= 1
@@ -85,7 +89,7 @@ struct DecodeArgs {
 
 // dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for a shape without a kernel.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
-bool decode_shape_supported(int dtype, int head_dim, int group);
+bool decode_shape_supported(int dtype, int head_dim, int group, int block_size);
 
 // bf16 pools with head_dim 128: scores on the matrix cores (decode_mfma.hip).
 // Launches the decode kernel only; the caller launches the partition merge.

@@ -34,11 +34,11 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a)
 
         const int64_t slot = a.slot_mapping[t];
         if (slot < 0 || slot >= a.num_slots) continue;   // padding token, or outside the pool
-        const int64_t block = slot / kBlockTokens;
-        const int64_t offset = slot - block * kBlockTokens;
+        const int64_t block = slot / a.block_size;
+        const int64_t offset = slot - block * a.block_size;
 
         // destination row (block, head, offset) in 16-byte chunks
-        const int64_t dst_chunk = ((block * a.num_kv_heads + h) * kBlockTokens + offset) * a.row_chunks + c;
+        const int64_t dst_chunk = ((block * a.num_kv_heads + h) * a.block_size + offset) * a.row_chunks + c;
         const int64_t src_chunk = (t * a.num_kv_heads + h) * a.row_chunks + c;
         const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new);
         uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);
@@ -65,9 +65,9 @@ __global__ __launch_bounds__(kScatterThreads) void append_scatter_kernel(AppendA
         L = L < 0 ? 0 : (L > a.max_context ? a.max_context : L);
         if (L == 0) continue;
         const int pos = L - 1;
-        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / kBlockTokens];
+        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / a.block_size];
         if (block < 0 || block >= a.num_blocks) continue;
-        const int64_t dst_chunk = ((block * a.num_kv_heads + h) * kBlockTokens + pos % kBlockTokens) * a.row_chunks + c;
+        const int64_t dst_chunk = ((block * a.num_kv_heads + h) * a.block_size + pos % a.block_size) * a.row_chunks + c;
         const int64_t src_chunk = (i * a.num_kv_heads + h) * a.row_chunks + c;
         const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new);
         uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);

@@ -216,6 +216,21 @@ def test_decode_append_argument_checks_return_before_any_launch():
     K.lib.kv_pool_destroy(h)
 
 
+def test_block_size_support():
+    """B in {8, 16, 32, 64, 128} for bf16 pools with head_dim 128; B = 16 for the others."""
+    import ctypes
+    for B, dt, d, want in [(8, "bf16", 128, K.KV_OK), (128, "bf16", 128, K.KV_OK),
+                           (24, "bf16", 128, K.KV_ERR_UNSUPPORTED), (256, "bf16", 128, K.KV_ERR_UNSUPPORTED),
+                           (32, "f32", 64, K.KV_ERR_UNSUPPORTED), (32, "bf16", 64, K.KV_ERR_UNSUPPORTED),
+                           (16, "f32", 64, K.KV_OK)]:
+        desc = K.make_desc(1, 8, B, 2, d, dt)
+        h = ctypes.c_void_p()
+        st = K.lib.kv_pool_create(ctypes.byref(desc), 0x10000, 0x20000, ctypes.byref(h))
+        assert st == want, (B, dt, d, st)
+        if st == K.KV_OK:
+            K.lib.kv_pool_destroy(h)
+
+
 def test_workspace_size_formula():
     st, h = _pool(head_dim=128, num_kv_heads=8, dtype="bf16")
     out = ctypes.c_uint64(0)
