@@ -92,14 +92,18 @@ def algorithmic_bytes(wl):
                 kv_unique=kv_unique, kv_logical=kv_logical, blocks=nblk)
 
 
-def traffic_for(config: str, partition: int):
+def traffic_key(config: str, partition: int, block_size: int = 16) -> str:
+    return f"{config}/p{partition}" + ("" if block_size == 16 else f"/B{block_size}")
+
+
+def traffic_for(config: str, partition: int, block_size: int = 16):
     """HBM bytes per decode launch from committed counter runs, or None if stale/absent."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(f"{config}/p{partition}")
+    entry = rec.get(traffic_key(config, partition, block_size))
     if not entry or entry.get("kernel_source_sha256") != kernel_sha():
         return None
     return entry.get("traffic_bytes_per_launch")
@@ -110,7 +114,7 @@ ATTN_KERNEL_MARKERS = ("decode_bf16_streamk_kernel", "streamk_fixup_kernel", "de
 
 
 def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, config: str, partition: int,
-                   command: str) -> dict:
+                   command: str, block_size: int = 16) -> dict:
     """HBM bytes per attention call from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE).
 
     Each counter is scaled by what it reads for the copy probe of copy_mib MiB
@@ -155,7 +159,7 @@ def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, config: str, p
             rec = json.load(f)
     except (OSError, ValueError):
         rec = {}
-    rec[f"{config}/p{partition}"] = entry
+    rec[traffic_key(config, partition, block_size)] = entry
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -191,6 +195,8 @@ def main(argv=None):
     ap.add_argument("--config", default="C2", choices=sorted(WORKLOADS))
     ap.add_argument("--partition", type=int, default=None, help="tokens per partition (0 = single pass)")
     ap.add_argument("--variant", default="spec")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="tokens per block (default: the workload's 16); bf16 workloads take 8..128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing pass")
     ap.add_argument("--no-identity", action="store_true",
@@ -213,7 +219,7 @@ def main(argv=None):
     if args.record_traffic:
         part = DEFAULT_PARTITION[args.config] if args.partition is None else args.partition
         entry = record_traffic(args.record_traffic[0], args.record_traffic[1], args.probe_copy_mib or 1024,
-                               args.config, part, args.record_command)
+                               args.config, part, args.record_command, args.block_size or 16)
         print(json.dumps(entry))
         return 0
 
@@ -235,7 +241,7 @@ def main(argv=None):
     part = DEFAULT_PARTITION[args.config] if args.partition is None else args.partition
 
     print(f"bench: generating {args.config} ({args.variant})", file=sys.stderr, flush=True)
-    wl = kvgen.make_workload(args.config, variant=args.variant)
+    wl = kvgen.make_workload(args.config, variant=args.variant, block_size=args.block_size)
     nbytes = algorithmic_bytes(wl)
     step = DecodeStep.from_workload(wl, partition_size=part)
     torch.cuda.synchronize()
@@ -442,7 +448,7 @@ def main(argv=None):
                 us.append(a.elapsed_time(b) * 1e3)
             table_walk["xcd_grouped_us_p50" if grouped else "default_us_p50"] = round(percentile(us, 0.5), 2)
 
-    traffic = traffic_for(args.config, part)
+    traffic = traffic_for(args.config, part, wl.block_size)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
