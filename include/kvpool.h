@@ -34,6 +34,8 @@
  *   [TMP] aicassindra.com transformer-math "paged attention", "End-to-end
  *         flow" (the step attends over the full history including the token
  *         written this step).
+ *   [LAT] lattice-ai-eng "KV Cache & PagedAttention", "5. Production
+ *         tradeoffs" (an FP8 cache halves cache memory and decode traffic).
  *
  * Conventions for every call:
  *   - Device pointers are borrowed: the caller allocates them and keeps them
@@ -72,17 +74,22 @@ typedef enum kv_status {
 } kv_status;
 
 typedef enum kv_dtype {
-    KV_F32 = 0,    /* IEEE binary32 */
-    KV_BF16 = 1    /* bfloat16 (upper half of binary32); fp32 accumulation, round-to-nearest-even stores */
+    KV_F32 = 0,      /* IEEE binary32 */
+    KV_BF16 = 1,     /* bfloat16 (upper half of binary32); fp32 accumulation, round-to-nearest-even stores */
+    KV_FP8_E4M3 = 2  /* pool holds OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+                      * largest finite 448, 0x7F/0xFF NaN) with one fp32 scale per (block, KV head) for K
+                      * and one for V; a stored value is code * scale.  q, k_new/v_new and the output
+                      * are bf16.  head_dim 128, block_size 16. */
 } kv_dtype;
 
 typedef struct kv_pool_desc {
     int32_t num_layers;     /* >= 1 */
     int32_t num_blocks;     /* physical blocks per layer, >= 1 */
-    int32_t block_size;     /* tokens per block (B); the kernels are built for 16 */
+    int32_t block_size;     /* tokens per block (B): 16; bf16 pools with head_dim 128 also 8, 32, 64, 128 */
     int32_t num_kv_heads;   /* KV heads per layer */
     int32_t head_dim;       /* elements per head row; the kernels are built for 64 and 128 */
-    int32_t dtype;          /* kv_dtype of the pool, of q, of k_new/v_new and of the output */
+    int32_t dtype;          /* kv_dtype of the pool; q, k_new/v_new and the output are in it too
+                             * (bf16 for KV_FP8_E4M3) */
 } kv_pool_desc;
 
 /* Opaque host-side handle: the descriptor and the two base pointers.  Immutable
@@ -102,9 +109,36 @@ kv_status kv_pool_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tensor);
  * Wrap two caller-allocated device buffers of kv_pool_bytes() bytes each as a
  * pool.  No device memory is allocated or touched.  k_base and v_base must be
  * 16-byte aligned.  Errors: KV_ERR_INVALID_ARGUMENT (null, misaligned, bad
- * descriptor), KV_ERR_UNSUPPORTED (block_size != 16, head_dim not 64 or 128).
+ * descriptor, an FP8 dtype: see kv_pool_create_fp8), KV_ERR_UNSUPPORTED
+ * (head_dim not 64 or 128; block_size not 16, or for bf16 pools with head_dim
+ * 128 not one of 8, 16, 32, 64, 128).
  */
 kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, kv_pool_t* out);
+
+/*
+ * FP8 pools (KV_FP8_E4M3): blocks as quantization groups ([PIF] "06 Open
+ * questions": per-block scales ride along with the block, CoW copies included;
+ * [LAT] "5. Production tradeoffs", Quality: FP8 KV halves cache bytes and
+ * decode traffic).  Besides the two code tensors (kv_pool_bytes each, one byte
+ * per element), a pool has two scale tensors, fp32
+ * [num_layers][num_blocks][num_kv_heads], of kv_pool_scale_bytes bytes each.
+ * Scales travel with their block: kv_copy_blocks copies them.  The write that
+ * covers row 0 of a block sets that block's scales to amax / 448 over the rows
+ * it puts there (1.0 when all are zero); later writes into the block keep the
+ * scales and saturate at +-448, so a block is never requantized.  Quantizing
+ * is fp32 division by the scale, then round to the nearest E4M3 value, ties to
+ * the even code.
+ */
+kv_status kv_pool_scale_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tensor);   /* 0 unless FP8 */
+
+/*
+ * kv_pool_create for KV_FP8_E4M3: also wraps the two caller-allocated scale
+ * tensors (4-byte aligned).  Errors: as kv_pool_create; KV_ERR_INVALID_ARGUMENT
+ * when the dtype is not KV_FP8_E4M3 or a scale pointer is null or misaligned;
+ * KV_ERR_UNSUPPORTED unless head_dim is 128 and block_size 16.
+ */
+kv_status kv_pool_create_fp8(const kv_pool_desc* desc, void* k_codes, void* v_codes, float* k_scales,
+                             float* v_scales, kv_pool_t* out);
 
 /* Free the handle (not the buffers).  NULL is accepted. */
 kv_status kv_pool_destroy(kv_pool_t pool);

@@ -55,6 +55,20 @@ kv_status kv_probe_table_walk(const int32_t* block_tables, int32_t max_blocks_pe
                               int32_t max_context_len, int32_t xcd_grouped, void* sink, uint64_t sink_bytes,
                               void* stream);
 
+/*
+ * The E4M3 conversions of the FP8 pool kernels, one element per call site, so
+ * that they can be checked against the format's definition code by code
+ * (kv_pool_create_fp8 in kvpool.h describes the format):
+ *   kv_probe_e4m3_to_bf16: n codes (device, uint8) -> n bfloat16 bit patterns
+ *                          (device, uint16, 2-byte aligned), exact widening;
+ *   kv_probe_f32_to_e4m3:  n fp32 values (device, 4-byte aligned) -> n codes,
+ *                          round to nearest, ties to the even code, +-448
+ *                          saturation, NaN -> 0x7F.
+ * Queued on `stream`.  Errors: KV_ERR_INVALID_ARGUMENT, KV_ERR_HIP.
+ */
+kv_status kv_probe_e4m3_to_bf16(const void* codes, void* out_bf16, int64_t n, void* stream);
+kv_status kv_probe_f32_to_e4m3(const float* x, void* out_codes, int64_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

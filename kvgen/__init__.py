@@ -590,3 +590,61 @@ def privatize_blocks(wl: Workload, *, contiguous: bool = False) -> Workload:
         ext[i, :len(r)] = np.arange(pos, pos + len(r))
         pos += len(r)
     return _rebuild(wl, tables, ext, k, v, "contiguous" if contiguous else "private")
+
+
+# ----------------------------------------------------------------------------
+# FP8 pool contents (codes and block scales as stored, drawn directly)
+# ----------------------------------------------------------------------------
+
+E4M3_NAN_CODE = np.uint8(0x7F)
+# the 254 byte values that are finite E4M3 codes (0x7F and 0xFF are NaN)
+FINITE_E4M3_CODES = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def fp8_codes(shape, seed_seq: np.random.SeedSequence) -> np.ndarray:
+    """Codes drawn uniformly from the finite E4M3 codes, so every exponent,
+    both signs, zeros and subnormals occur."""
+    n = int(np.prod(shape))
+    nchunks = max(1, (n + _CHUNK - 1) // _CHUNK)
+    kids = seed_seq.spawn(nchunks)
+    res = np.empty(n, dtype=np.uint8)
+
+    def work(i):
+        lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        g = np.random.default_rng(kids[i])
+        res[lo:hi] = FINITE_E4M3_CODES[g.integers(0, FINITE_E4M3_CODES.size, size=hi - lo)]
+
+    if nchunks == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return res.reshape(shape)
+
+
+def fp8_pool_state(wl: Workload, *, seed: int = 0, largest: float = 3.0, spread: float = 0.1):
+    """An FP8 pool with the block layout of ``wl``: (k_codes, v_codes, k_scale,
+    v_scale), codes ``uint8 [N][Hkv][B][D]``, scales ``float32 [N][Hkv]``.
+
+    Codes are uniform over the finite codes; scales are lognormal with median
+    ``largest / 448`` (the largest code then stands for about ``largest``,
+    the magnitude of the largest of 128 N(0, 1) values) and log-spread
+    ``spread``.  Wherever ``wl`` holds a NaN stale slot (a poisoned workload),
+    the code is NaN (0x7F) too.
+    """
+    ss = np.random.SeedSequence([seed, 8])
+    s_kc, s_vc, s_ks, s_vs = ss.spawn(4)
+    N, H, B, D = wl.k_pool.shape
+    kc = fp8_codes((N, H, B, D), s_kc)
+    vc = fp8_codes((N, H, B, D), s_vc)
+    med = math.log(largest / 448.0)
+    ks = np.exp(np.random.default_rng(s_ks).normal(med, spread, size=(N, H))).astype(np.float32)
+    vs = np.exp(np.random.default_rng(s_vs).normal(med, spread, size=(N, H))).astype(np.float32)
+    if wl.dtype == BF16:
+        bits = wl.k_pool.view(np.uint16)
+        stale = (bits & np.uint16(0x7FFF)) > np.uint16(0x7F80)
+    else:
+        stale = np.isnan(wl.k_pool)
+    kc[stale] = E4M3_NAN_CODE
+    vc[stale] = E4M3_NAN_CODE
+    return kc, vc, ks, vs

@@ -5,9 +5,10 @@ TEST INFRASTRUCTURE ONLY, like the rest of ``oracle``: only the tests,
 ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg use it.
 
 The pages treat a 16-token block as a natural quantization group whose scales
-travel with it ("PagedAttention, Internals First", "Where this goes next" list,
-"Blocks as quantization groups"; the lattice-ai-eng page, "Production
-considerations": FP8 KV halves cache bytes and decode traffic).  They fix no
+travel with it ("PagedAttention, Internals First", "06 Open questions", the
+paragraph on blocks as quantization groups; lattice-ai-eng "KV Cache &
+PagedAttention", "5. Production tradeoffs", Quality: FP8 KV halves cache bytes
+and decode traffic).  They fix no
 format; this build reads them as:
   * codes: OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
     infinities; 0x7F / 0xFF are NaN; largest finite value 448);

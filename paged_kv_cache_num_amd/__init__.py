@@ -9,7 +9,8 @@ that first use raises ImportError (there is no CPU fallback).  Importing the
 """
 import importlib
 
-_FROM_KVPOOL = ("KV_BF16", "KV_F32", "KVError", "KVPool", "kv_build_slot_mapping", "kv_pool_bytes",
+_FROM_KVPOOL = ("KV_BF16", "KV_F32", "KV_FP8_E4M3", "KVError", "KVPool", "kv_build_slot_mapping", "kv_pool_bytes",
+                "kv_pool_scale_bytes", "probe_e4m3_to_bf16", "probe_f32_to_e4m3",
                 "make_desc", "lib", "LIB_PATH", "EXPORTED", "probe_copy", "probe_read", "probe_table_walk")
 
 __all__ = list(_FROM_KVPOOL) + ["DecodeStep"]

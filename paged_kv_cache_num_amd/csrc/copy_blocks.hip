@@ -11,7 +11,8 @@
 // Work items are 16-byte chunks numbered
 //     ((pair * layers + layer) * 2 + {K,V}) * block_chunks + chunk,
 // a (layer, block) run being H_kv * B * D * e contiguous bytes, so
-// neighbouring lanes move neighbouring bytes.  Bit copy, no conversion.
+// neighbouring lanes move neighbouring bytes.  Bit copy, no conversion.  An
+// FP8 pool's block scales are copied the same way by a second small kernel.
 #include "launch.hpp"
 
 namespace kvp {
@@ -39,6 +40,28 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArg
     }
 }
 
+// FP8 pools: the block scales travel with the block ("PagedAttention,
+// Internals First", "06 Open questions": per-block quantization metadata
+// rides along with the block, across copy-on-write copies too).  Items
+// ((pair * layers + layer) * 2 + {K,V}) * H_kv + head, one fp32 scale each.
+__global__ __launch_bounds__(kCopyThreads) void copy_scales_kernel(CopyBlocksArgs a) {
+    const int64_t per_pair = (int64_t)a.num_layers * 2 * a.num_kv_heads;
+    const int64_t total = (int64_t)a.num_pairs * per_pair;
+    const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
+    const int64_t layer_elems = (int64_t)a.num_blocks * a.num_kv_heads;
+    for (int64_t item = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; item < total; item += stride) {
+        const int64_t p = item / per_pair;
+        const int64_t rem = item - p * per_pair;
+        const int64_t run = rem / a.num_kv_heads;   // layer * 2 + {K,V}
+        const int h = (int)(rem - run * a.num_kv_heads);
+        const int64_t src = a.pairs[2 * p];
+        const int64_t dst = a.pairs[2 * p + 1];
+        if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) continue;
+        float* base = ((run & 1) == 0 ? a.k_scale : a.v_scale) + (run >> 1) * layer_elems;
+        base[dst * a.num_kv_heads + h] = base[src * a.num_kv_heads + h];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
@@ -47,6 +70,12 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
     int64_t blocks = (total + kCopyThreads - 1) / kCopyThreads;
     if (blocks > 65536) blocks = 65536;   // grid-stride loop covers the rest
     copy_blocks_kernel<<<dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.k_scale) return e;
+    const int64_t scales = (int64_t)a.num_pairs * a.num_layers * 2 * a.num_kv_heads;
+    blocks = (scales + kCopyThreads - 1) / kCopyThreads;
+    if (blocks > 65536) blocks = 65536;
+    copy_scales_kernel<<<dim3((unsigned)blocks), dim3(kCopyThreads), 0, stream>>>(a);
     return hipGetLastError();
 }
 

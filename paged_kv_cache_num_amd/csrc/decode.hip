@@ -320,9 +320,11 @@ hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
 }  // namespace
 
 bool decode_shape_supported(int dtype, int head_dim, int group, int block_size) {
-    if (!(dtype == 0 || dtype == 1) || !(head_dim == 64 || head_dim == 128) ||
+    if (!(dtype == 0 || dtype == 1 || dtype == 2) || !(head_dim == 64 || head_dim == 128) ||
         !(group == 1 || group == 2 || group == 4 || group == 8))
         return false;
+    // FP8 pools: the matrix-core kernels, head_dim 128, 16-token blocks
+    if (dtype == 2) return head_dim == 128 && block_size == kTileTokens;
     // the bf16 / head_dim-128 kernels walk 16-token tiles of any block size
     // 8..128; the vector-unit kernel is built for B = 16
     if (dtype == 1 && head_dim == 128)
@@ -336,6 +338,11 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream
     if (!decode_shape_supported(dtype, head_dim, group, a.block_size)) return hipErrorInvalidValue;
     if (dtype == 1 && head_dim == 128) {
         hipError_t e = launch_decode_bf16_mfma(a, group, stream);
+        if (e != hipSuccess) return e;
+        return launch_reduce<1, 128>(a, stream);
+    }
+    if (dtype == 2) {   // bf16 queries and outputs, so the bf16 merge
+        hipError_t e = launch_decode_fp8_mfma(a, group, stream);
         if (e != hipSuccess) return e;
         return launch_reduce<1, 128>(a, stream);
     }

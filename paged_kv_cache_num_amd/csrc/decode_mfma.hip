@@ -30,9 +30,18 @@
 //     are in flight while the current one is computed.
 //   * The walk order and all reductions depend only on logical positions, so
 //     the output is bitwise independent of where the blocks live.
+//   * FP8 pools (E4M3 codes, one fp32 scale per block and KV head for K and
+//     one for V): the same kernels with the codes widened to bfloat16 in
+//     registers (exact: every E4M3 value is a bfloat16 value).  A block's K
+//     scale multiplies its scores; its V scale multiplies the probabilities
+//     that enter P V, while the softmax sum takes them unscaled, so
+//     out = sum_j p_j sv_j v_j / sum_j p_j is what the dequantized cache gives.
+//     A tile moves half the bytes of a bf16 tile, so twice as many are kept
+//     in flight.
 #include <math.h>
 
 #include "device_common.hpp"
+#include "fp8.hpp"
 #include "launch.hpp"
 #include "split.hpp"
 
@@ -46,6 +55,7 @@ constexpr int kRC = kD / 8;        // 16-byte chunks per token row (16)
 constexpr int kKK = kD / 32;       // MFMA steps over head_dim (4)
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max is moved
 constexpr int kStreamDepth = 2;    // tiles in registers per balanced-mode wave
+constexpr int kStreamDepthFp8 = 4; // the same for FP8 tiles (half the bytes)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -78,6 +88,23 @@ struct Tile {
     uint4 v[4];     // V: token 4*r + i, chunk c
 };
 
+// FP8 tile, codes.  K: token n, dims 32r .. 32r+31, so MFMA step kk takes
+// dims 32r + 8kk .. +8 (the queries are loaded in the same order).  V: token
+// 4r + i, dims 8n .. 8n+7, the dims this lane's outputs stand for.
+struct TileF8 {
+    uint4 k[2];
+    uint2 v[4];
+};
+
+template <bool kFp8>
+struct TileOf {
+    typedef Tile type;
+};
+template <>
+struct TileOf<true> {
+    typedef TileF8 type;
+};
+
 // Running state of one wave.  The reference max m is the same in all four
 // rows (blocks are folded in whole), l is this row's share of the softmax
 // sum, and o holds the MFMA accumulators of P V: o[e][j] is the output of
@@ -95,6 +122,16 @@ __device__ __forceinline__ void load_v(Tile& t, const uint4* __restrict__ vt, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) t.v[i] = vt[v_off + i * kRC];
 }
+__device__ __forceinline__ void load_k(TileF8& t, const uint4* __restrict__ kt, int k_off) {
+    t.k[0] = kt[k_off];
+    t.k[1] = kt[k_off + 1];
+}
+// v_off in 8-byte units; a code row is kD / 8 of them
+__device__ __forceinline__ void load_v(TileF8& t, const uint4* __restrict__ vt, int v_off) {
+    const uint2* p = reinterpret_cast<const uint2*>(vt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.v[i] = p[v_off + i * (kD / 8)];
+}
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
@@ -107,10 +144,12 @@ __device__ __forceinline__ bf16x8_t as_operand(uint32_t a, uint32_t b, uint32_t 
     return __builtin_bit_cast(bf16x8_t, make_uint4(a, b, c, d));
 }
 
-// One block: scores on MFMA, lazy online softmax with one reference max per
-// head, P V on MFMA.  The tile's registers are refilled with the next tile as
-// soon as they are consumed: after_k() is called once the K half has been
-// read, after_v() once the V half has.
+// Masking, lazy online softmax with one reference max per head, and P V on
+// MFMA for one tile, from its raw scores s (lane (r, n): tokens 4r..4r+3,
+// head n) and its V operands: ev[w] / od[w] hold dims 8n + 2w / 8n + 2w + 1 of
+// tokens (4r, 4r+1) and (4r+2, 4r+3) as bfloat16 pairs.  vscale multiplies
+// the probabilities that enter P V (an FP8 block's V scale, else 1); the
+// softmax sum takes them unscaled.
 //
 // P V is a 16-head x 16-token by 16-token x 128-dim product, split as P =
 // P_hi + P_lo (a bfloat16 high part and the bfloat16 of the remainder, so the
@@ -120,36 +159,10 @@ __device__ __forceinline__ bf16x8_t as_operand(uint32_t a, uint32_t b, uint32_t 
 // to pair the same token in A and B, so lane (r, n) puts P_hi and P_lo of
 // head n, tokens 4r..4r+3 (already where the score MFMA left them) in its
 // eight A positions and dim 8n + e of the same four tokens, twice, in its
-// eight B positions; that value is already in the lane's own V loads and is
-// only repacked.
-template <int G, class AfterK, class AfterV>
-__device__ __forceinline__ void process(State& st, Tile& t, const bf16x8_t (&qb)[kKK], int tok0, int L,
-                                        int r, int n, float sl2, AfterK after_k, AfterV after_v) {
-    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[kk]), qb[kk], s, 0, 0, 0);
-    // The refills reuse the tile's registers.  An empty asm statement that
-    // consumes the results and clobbers memory keeps the reads before it and
-    // the refill loads after it.
-    asm volatile("" : "+v"(s) : : "memory");
-    after_k();
-
-    // dim 8n + 2w (low halves) and 8n + 2w + 1 (high halves) of tokens 4r..4r+3
-    uint32_t ev[4][2], od[4][2];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = (&t.v[0].x)[w], x1 = (&t.v[1].x)[w], x2 = (&t.v[2].x)[w], x3 = (&t.v[3].x)[w];
-        ev[w][0] = (x0 & 0xFFFFu) | (x1 << 16);
-        ev[w][1] = (x2 & 0xFFFFu) | (x3 << 16);
-        od[w][0] = (x0 >> 16) | (x1 & 0xFFFF0000u);
-        od[w][1] = (x2 >> 16) | (x3 & 0xFFFF0000u);
-    }
-    asm volatile("" : "+v"(ev[0][0]), "+v"(ev[0][1]), "+v"(ev[1][0]), "+v"(ev[1][1]), "+v"(ev[2][0]), "+v"(ev[2][1]),
-                 "+v"(ev[3][0]), "+v"(ev[3][1]), "+v"(od[0][0]), "+v"(od[0][1]), "+v"(od[1][0]), "+v"(od[1][1]),
-                 "+v"(od[2][0]), "+v"(od[2][1]), "+v"(od[3][0]), "+v"(od[3][1]) : : "memory");
-    after_v();
-
+// eight B positions.
+template <int G>
+__device__ __forceinline__ void softmax_pv(State& st, f32x4_t s, uint32_t (&ev)[4][2], uint32_t (&od)[4][2],
+                                           int tok0, int L, int r, int n, float sl2, float vscale) {
     if (tok0 + kTileTokens > L) {   // last, partially filled tile (wave-uniform branch)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -191,6 +204,8 @@ __device__ __forceinline__ void process(State& st, Tile& t, const bf16x8_t (&qb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = n < G ? fast_exp2(fmaf(s[i], sl2, neg_ref)) : 0.0f;
     st.l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] *= vscale;
 
     const uint32_t h01 = bf16_pair(p[0], p[1]);
     const uint32_t h23 = bf16_pair(p[2], p[3]);
@@ -204,6 +219,82 @@ __device__ __forceinline__ void process(State& st, Tile& t, const bf16x8_t (&qb)
         st.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             pa, as_operand(od[w][0], od[w][1], od[w][0], od[w][1]), st.o[2 * w + 1], 0, 0, 0);
     }
+}
+
+// One bf16 tile: scores on MFMA, then softmax_pv.  The tile's registers are
+// refilled with the next tile as soon as they are consumed: after_k() is
+// called once the K half has been read, after_v() once the V half has.  The
+// V operands are already in the lane's own V loads and are only repacked.
+template <int G, class AfterK, class AfterV>
+__device__ __forceinline__ void process(State& st, Tile& t, const bf16x8_t (&qb)[kKK], int tok0, int L,
+                                        int r, int n, float sl2, AfterK after_k, AfterV after_v) {
+    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, t.k[kk]), qb[kk], s, 0, 0, 0);
+    // The refills reuse the tile's registers.  An empty asm statement that
+    // consumes the results and clobbers memory keeps the reads before it and
+    // the refill loads after it.
+    asm volatile("" : "+v"(s) : : "memory");
+    after_k();
+
+    // dim 8n + 2w (low halves) and 8n + 2w + 1 (high halves) of tokens 4r..4r+3
+    uint32_t ev[4][2], od[4][2];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = (&t.v[0].x)[w], x1 = (&t.v[1].x)[w], x2 = (&t.v[2].x)[w], x3 = (&t.v[3].x)[w];
+        ev[w][0] = (x0 & 0xFFFFu) | (x1 << 16);
+        ev[w][1] = (x2 & 0xFFFFu) | (x3 << 16);
+        od[w][0] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+        od[w][1] = (x2 >> 16) | (x3 & 0xFFFF0000u);
+    }
+    asm volatile("" : "+v"(ev[0][0]), "+v"(ev[0][1]), "+v"(ev[1][0]), "+v"(ev[1][1]), "+v"(ev[2][0]), "+v"(ev[2][1]),
+                 "+v"(ev[3][0]), "+v"(ev[3][1]), "+v"(od[0][0]), "+v"(od[0][1]), "+v"(od[1][0]), "+v"(od[1][1]),
+                 "+v"(od[2][0]), "+v"(od[2][1]), "+v"(od[3][0]), "+v"(od[3][1]) : : "memory");
+    after_v();
+    softmax_pv<G>(st, s, ev, od, tok0, L, r, n, sl2, 1.0f);
+}
+
+// One FP8 tile: the codes are widened to bfloat16 operands (two per
+// v_cvt_scalef32_pk_bf16_fp8), the K scale multiplies the raw scores and the
+// V scale goes to softmax_pv.  For V, v_perm_b32 first gathers byte e of the
+// tokens (4r, 4r+1) and of (4r+2, 4r+3) next to each other, so one widening
+// yields the bfloat16 pair softmax_pv expects.
+template <int G, class AfterK, class AfterV>
+__device__ __forceinline__ void process(State& st, TileF8& t, const bf16x8_t (&qb)[kKK], int tok0, int L,
+                                        int r, int n, float sl2, float kscale, float vscale, AfterK after_k,
+                                        AfterV after_v) {
+    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+        const uint32_t d0 = (&t.k[kk >> 1].x)[2 * (kk & 1)];
+        const uint32_t d1 = (&t.k[kk >> 1].x)[2 * (kk & 1) + 1];
+        const bf16x8_t ka = as_operand(e4m3x2_to_bf16x2<false>(d0), e4m3x2_to_bf16x2<true>(d0),
+                                       e4m3x2_to_bf16x2<false>(d1), e4m3x2_to_bf16x2<true>(d1));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kk], s, 0, 0, 0);
+    }
+    asm volatile("" : "+v"(s) : : "memory");
+    after_k();
+
+    uint32_t ev[4][2], od[4][2];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // bytes 2(w&1), 2(w&1)+1 of word w/2 (dims 8n + 2w, 8n + 2w + 1), interleaved over two tokens
+        const uint32_t sel = (w & 1) ? 0x07030602u : 0x05010400u;
+        const uint32_t y01 = __builtin_amdgcn_perm((&t.v[1].x)[w >> 1], (&t.v[0].x)[w >> 1], sel);
+        const uint32_t y23 = __builtin_amdgcn_perm((&t.v[3].x)[w >> 1], (&t.v[2].x)[w >> 1], sel);
+        ev[w][0] = e4m3x2_to_bf16x2<false>(y01);
+        od[w][0] = e4m3x2_to_bf16x2<true>(y01);
+        ev[w][1] = e4m3x2_to_bf16x2<false>(y23);
+        od[w][1] = e4m3x2_to_bf16x2<true>(y23);
+    }
+    asm volatile("" : "+v"(ev[0][0]), "+v"(ev[0][1]), "+v"(ev[1][0]), "+v"(ev[1][1]), "+v"(ev[2][0]), "+v"(ev[2][1]),
+                 "+v"(ev[3][0]), "+v"(ev[3][1]), "+v"(od[0][0]), "+v"(od[0][1]), "+v"(od[1][0]), "+v"(od[1][1]),
+                 "+v"(od[2][0]), "+v"(od[2][1]), "+v"(od[3][0]), "+v"(od[3][1]) : : "memory");
+    after_v();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] *= kscale;
+    softmax_pv<G>(st, s, ev, od, tok0, L, r, n, sl2, vscale);
 }
 
 // End of a walk: lane (r, n) gets the whole softmax sum of head n.
@@ -222,43 +313,61 @@ struct WalkCtx {
     int max_blocks;        // table entries per sequence
     bool pair8;            // B = 8: a 16-token tile is two blocks
     int sub_shift;         // B >= 16: log2(B / 16), tiles per block = 1 << sub_shift
-    int k_off, v_off;      // this lane's 16-byte chunk in a K / V tile
+    int k_off, v_off;      // this lane's K (16-byte units) / V (16-byte, FP8: 8-byte units) offset in a tile
     int lane, r, n;
     float sl2;
+    const float* ksc;      // FP8: scales of KV head kv in block 0; block p's are at p * nkvh
+    const float* vsc;
+    int nkvh;
 };
 
 // kAnyB: the block size comes from the arguments (8..128); otherwise it is 16
 // and every block-size field below is a constant the walk folds away.
-template <bool kAnyB>
+// kFp8: an FP8 pool (block size 16).
+template <bool kAnyB, bool kFp8 = false>
 __device__ __forceinline__ WalkCtx make_ctx(const DecodeArgs& a, int kv) {
     const int B = kAnyB ? a.block_size : kTileTokens;
+    constexpr int kRow = kFp8 ? kD / 16 : kRC;   // 16-byte chunks per token row
     WalkCtx c;
     c.lane = threadIdx.x & (kWave - 1);
     c.r = c.lane >> 4;
     c.n = c.lane & 15;
     c.kpool = reinterpret_cast<const uint4*>(a.k_layer);
     c.vpool = reinterpret_cast<const uint4*>(a.v_layer);
-    c.head_off = (size_t)kv * ((size_t)B * kRC);
-    c.block_stride = (size_t)a.num_kv_heads * ((size_t)B * kRC);
+    c.head_off = (size_t)kv * ((size_t)B * kRow);
+    c.block_stride = (size_t)a.num_kv_heads * ((size_t)B * kRow);
     c.num_blocks = (uint32_t)a.num_blocks;
     c.max_blocks = a.max_blocks;
     c.pair8 = kAnyB && B == 8;
     c.sub_shift = kAnyB ? 31 - __builtin_clz(B >= kTileTokens ? B / kTileTokens : 1) : 0;
-    // K: token n, chunk 4*kk + r; V: token 4r + i, chunk n (rows within the lane's block when B = 8)
-    c.k_off = (c.pair8 ? (c.n & 7) : c.n) * kRC + c.r;
-    c.v_off = (c.pair8 ? ((4 * c.r) & 7) : 4 * c.r) * kRC + c.n;
+    if constexpr (kFp8) {
+        // K: token n, chunks 2r and 2r + 1; V: token 4r + i, 8-byte unit n
+        c.k_off = c.n * kRow + 2 * c.r;
+        c.v_off = 4 * c.r * (kD / 8) + c.n;
+        c.ksc = a.k_scale + kv;
+        c.vsc = a.v_scale + kv;
+        c.nkvh = a.num_kv_heads;
+    } else {
+        // K: token n, chunk 4*kk + r; V: token 4r + i, chunk n (rows within the lane's block when B = 8)
+        c.k_off = (c.pair8 ? (c.n & 7) : c.n) * kRC + c.r;
+        c.v_off = (c.pair8 ? ((4 * c.r) & 7) : 4 * c.r) * kRC + c.n;
+        c.ksc = c.vsc = nullptr;
+        c.nkvh = 0;
+    }
     c.sl2 = a.scale_log2;
     return c;
 }
 
-// B operand: the group's query heads as columns, zero beyond G.
-template <int G>
+// B operand: the group's query heads as columns, zero beyond G.  Step kk
+// takes dims 32kk + 8r .. +8 (bf16 tiles) or 32r + 8kk .. +8 (FP8 tiles), as
+// the K operand does.
+template <int G, bool kFp8 = false>
 __device__ __forceinline__ void load_q(bf16x8_t (&qb)[kKK], const DecodeArgs& a, int seq, int kv, const WalkCtx& c) {
     const uint4* qrow = reinterpret_cast<const uint4*>(a.q) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * kRC;
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) {
         uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (c.n < G) x = qrow[c.n * kRC + kk * 4 + c.r];
+        if (c.n < G) x = qrow[c.n * kRC + (kFp8 ? 4 * c.r + kk : kk * 4 + c.r)];
         qb[kk] = __builtin_bit_cast(bf16x8_t, x);
     }
 }
@@ -324,7 +433,11 @@ __device__ __forceinline__ int2 tile_entries(const int32_t* row, int e, bool val
 // unconditionally (past the end of the chunk the last tile is fetched again,
 // an L2 hit) and in the order the tiles are consumed, so the hardware's
 // in-order load counter lets each block wait for its own tile only.
-template <int G, int D>
+//
+// FP8 tiles also need their block scales: lane k of the chunk loads those of
+// tile k before the first tiles are requested, and tile k reads them from
+// lane k.
+template <int G, int D, bool kFp8 = false>
 __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* row, int stride,
                                      int nk, int b0, int L, const WalkCtx& c, const AppendRow& app,
                                      bool have_first = false, int tv0_first = 0, int tv1_first = 0) {
@@ -360,7 +473,17 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
         const int2 tvp = (k0 == 0 && have_first) ? make_int2(tv0_first, tv1_first)
                                                  : tile_entries(row, b0 + (k0 + c.lane) * stride, c.lane < nc, c);
         const int tv0 = tvp.x, tv1 = tvp.y;
-        Tile tt[D];
+        float ks_l = 1.0f, vs_l = 1.0f;
+        if constexpr (kFp8) {
+            if (c.lane < nc) {
+                uint32_t p = (uint32_t)tv0;
+                p = p < c.num_blocks ? p : c.num_blocks - 1;
+                ks_l = c.ksc[(size_t)p * c.nkvh];
+                vs_l = c.vsc[(size_t)p * c.nkvh];
+            }
+            asm volatile("" : : : "memory");
+        }
+        typename TileOf<kFp8>::type tt[D];
         const uint4 *kt, *vt;
 #pragma unroll
         for (int s = 0; s < D; ++s) {
@@ -370,10 +493,12 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
             load_v(tt[s], vt, c.v_off);
             asm volatile("" : : : "memory");
         }
-        if (app.active && k0 + 64 >= nk) {
+        if constexpr (!kFp8) {
+            if (app.active && k0 + 64 >= nk) {
 #pragma unroll
-            for (int kk = 0; kk < kKK; ++kk) new_k[kk] = app.krow[4 * kk + c.r];
-            new_v = app.vrow[c.n];
+                for (int kk = 0; kk < kKK; ++kk) new_k[kk] = app.krow[4 * kk + c.r];
+                new_v = app.vrow[c.n];
+            }
         }
         for (int k = 0; k < nc; k += D) {
 #pragma unroll
@@ -385,19 +510,25 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
                 tile_ptrs(tv0, tv1, min(k + s + D, nc - 1), kt, vt);
                 __builtin_amdgcn_sched_barrier(0);
                 const int tok = k + s < nc ? (b0 + (k0 + k + s) * stride) * kTileTokens : L;
-                // wave-uniform: the tile holding the new token; a table entry outside
-                // the pool gets no write (as the scatter skips such a slot)
-                if (app.active && tok == app.tok0 && row_in_pool(tv0, tv1, k + s, app.j)) {
-                    append_into(tt[s], app, new_k, new_v, c);
+                if constexpr (kFp8) {
+                    const int ks = min(k + s, nc - 1);
+                    process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2, readlane_f(ks_l, ks), readlane_f(vs_l, ks),
+                               [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off); });
+                } else {
+                    // wave-uniform: the tile holding the new token; a table entry outside
+                    // the pool gets no write (as the scatter skips such a slot)
+                    if (app.active && tok == app.tok0 && row_in_pool(tv0, tv1, k + s, app.j)) {
+                        append_into(tt[s], app, new_k, new_v, c);
+                    }
+                    process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2,
+                               [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off); });
                 }
-                process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2,
-                           [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off); });
             }
         }
     }
 }
 
-template <int G, bool kAnyB>
+template <int G, bool kAnyB, bool kFp8>
 __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int part = blockIdx.x;
@@ -414,10 +545,10 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
     const int b_begin = part * bpp;
     const int b_end = min(nblk, b_begin + bpp);
 
-    const WalkCtx c = make_ctx<kAnyB>(a, kv);
+    const WalkCtx c = make_ctx<kAnyB, kFp8>(a, kv);
     const int r = c.r, n = c.n;
     bf16x8_t qb[kKK];
-    load_q<G>(qb, a, seq, kv, c);
+    load_q<G, kFp8>(qb, a, seq, kv, c);
     State st;
     init_state(st);
 
@@ -426,7 +557,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
     AppendRow none;
     none.active = false;
     none.krow = none.vrow = nullptr;
-    walk<G, 2>(st, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
+    walk<G, kFp8 ? 4 : 2, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
     const float l_tot = total_l(st);
 
     // waves of the workgroup merge through LDS
@@ -532,13 +663,13 @@ __device__ __forceinline__ void append_scatter_waves(const DecodeArgs& a, int64_
     }
 }
 
-template <int G, bool kAnyB>
+template <int G, bool kAnyB, bool kFp8>
 __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int64_t W = a.workers;
     const int64_t w = blockIdx.x;
-    if (w >= W) {   // decode append: the pool side
-        append_scatter_waves(a, w - W, (int64_t)gridDim.x - W);
+    if (w >= W) {   // decode append: the pool side (bf16 pools; FP8 appends run before the launch)
+        if constexpr (!kFp8) append_scatter_waves(a, w - W, (int64_t)gridDim.x - W);
         return;
     }
     const int S = a.num_seqs;
@@ -608,14 +739,14 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         const int n_here = (int)min((int64_t)(nblk - b), t_end - t);
         const bool whole = (b == 0) && (n_here == nblk);
 
-        const WalkCtx c = make_ctx<kAnyB>(a, kv);
+        const WalkCtx c = make_ctx<kAnyB, kFp8>(a, kv);
         bf16x8_t qb[kKK];
-        load_q<G>(qb, a, seq, kv, c);
+        load_q<G, kFp8>(qb, a, seq, kv, c);
         State st;
         init_state(st);
         // the piece that ends with the sequence's last block takes the appended row
         AppendRow app;
-        app.active = a.k_append != nullptr && b + n_here == nblk;
+        app.active = !kFp8 && a.k_append != nullptr && b + n_here == nblk;
         app.tok0 = (nblk - 1) * kTileTokens;
         app.j = (L - 1) % kTileTokens;
         app.krow = reinterpret_cast<const uint4*>(a.k_append) + ((size_t)seq * Hkv + kv) * kRC;
@@ -639,8 +770,8 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                 pf_valid = true;
             }
         }
-        walk<G, kStreamDepth>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, app, use_pf,
-                              tv0_here, tv1_here);
+        walk<G, kFp8 ? kStreamDepthFp8 : kStreamDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1,
+                                                             n_here, b, L, c, app, use_pf, tv0_here, tv1_here);
         const float l_tot = total_l(st);
 
         if (whole) {
@@ -805,7 +936,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
 
 template <int G>
 const void* streamk_kernel_ptr() {
-    return reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, true>);
+    return reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, true, false>);
 }
 
 }  // namespace
@@ -845,35 +976,41 @@ int streamk_workers(int group) {
     return cached[dev][group];
 }
 
-hipError_t launch_decode_bf16_streamk(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
+namespace {
+
+template <bool kFp8>
+hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
     DecodeArgs a = a_in;
     a.workers = workers;
-    // decode append: a few extra single-wave workgroups store the new rows (about 8 chunks per lane)
+    // decode append into a bf16 pool: a few extra single-wave workgroups store
+    // the new rows (about 8 chunks per lane)
     int64_t extra = 0;
-    if (a.k_append) {
+    if (kFp8) {
+        a.k_append = a.v_append = nullptr;
+    } else if (a.k_append) {
         const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * kRC;
         extra = (items + 8 * kWave - 1) / (8 * kWave);
         extra = extra < 1 ? 1 : (extra > 256 ? 256 : extra);
     }
     dim3 grid((unsigned)(workers + extra));
-    const bool any_b = a.block_size != kTileTokens;
+    const bool any_b = !kFp8 && a.block_size != kTileTokens;
     dim3 fix((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     switch (group) {
         case 1:
-            if (any_b) decode_bf16_streamk_kernel<1, true><<<grid, kWave, 0, stream>>>(a);
-            else decode_bf16_streamk_kernel<1, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_bf16_streamk_kernel<1, true, false><<<grid, kWave, 0, stream>>>(a);
+            else decode_bf16_streamk_kernel<1, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 2:
-            if (any_b) decode_bf16_streamk_kernel<2, true><<<grid, kWave, 0, stream>>>(a);
-            else decode_bf16_streamk_kernel<2, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_bf16_streamk_kernel<2, true, false><<<grid, kWave, 0, stream>>>(a);
+            else decode_bf16_streamk_kernel<2, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 4:
-            if (any_b) decode_bf16_streamk_kernel<4, true><<<grid, kWave, 0, stream>>>(a);
-            else decode_bf16_streamk_kernel<4, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_bf16_streamk_kernel<4, true, false><<<grid, kWave, 0, stream>>>(a);
+            else decode_bf16_streamk_kernel<4, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 8:
-            if (any_b) decode_bf16_streamk_kernel<8, true><<<grid, kWave, 0, stream>>>(a);
-            else decode_bf16_streamk_kernel<8, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_bf16_streamk_kernel<8, true, false><<<grid, kWave, 0, stream>>>(a);
+            else decode_bf16_streamk_kernel<8, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         default: return hipErrorInvalidValue;
     }
@@ -889,30 +1026,51 @@ hipError_t launch_decode_bf16_streamk(const DecodeArgs& a_in, int group, int wor
     return hipGetLastError();
 }
 
-hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
+template <bool kFp8>
+hipError_t launch_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
     dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     dim3 block(kWaves * kWave);
-    const bool any_b = a.block_size != kTileTokens;
+    const bool any_b = !kFp8 && a.block_size != kTileTokens;
     switch (group) {
         case 1:
-            if (any_b) decode_bf16_mfma_kernel<1, true><<<grid, block, 0, stream>>>(a);
-            else decode_bf16_mfma_kernel<1, false><<<grid, block, 0, stream>>>(a);
+            if (any_b) decode_bf16_mfma_kernel<1, true, false><<<grid, block, 0, stream>>>(a);
+            else decode_bf16_mfma_kernel<1, false, kFp8><<<grid, block, 0, stream>>>(a);
             break;
         case 2:
-            if (any_b) decode_bf16_mfma_kernel<2, true><<<grid, block, 0, stream>>>(a);
-            else decode_bf16_mfma_kernel<2, false><<<grid, block, 0, stream>>>(a);
+            if (any_b) decode_bf16_mfma_kernel<2, true, false><<<grid, block, 0, stream>>>(a);
+            else decode_bf16_mfma_kernel<2, false, kFp8><<<grid, block, 0, stream>>>(a);
             break;
         case 4:
-            if (any_b) decode_bf16_mfma_kernel<4, true><<<grid, block, 0, stream>>>(a);
-            else decode_bf16_mfma_kernel<4, false><<<grid, block, 0, stream>>>(a);
+            if (any_b) decode_bf16_mfma_kernel<4, true, false><<<grid, block, 0, stream>>>(a);
+            else decode_bf16_mfma_kernel<4, false, kFp8><<<grid, block, 0, stream>>>(a);
             break;
         case 8:
-            if (any_b) decode_bf16_mfma_kernel<8, true><<<grid, block, 0, stream>>>(a);
-            else decode_bf16_mfma_kernel<8, false><<<grid, block, 0, stream>>>(a);
+            if (any_b) decode_bf16_mfma_kernel<8, true, false><<<grid, block, 0, stream>>>(a);
+            else decode_bf16_mfma_kernel<8, false, kFp8><<<grid, block, 0, stream>>>(a);
             break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+    return launch_streamk<false>(a, group, workers, stream);
+}
+
+hipError_t launch_decode_fp8_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+    if (a.block_size != kTileTokens) return hipErrorInvalidValue;
+    return launch_streamk<true>(a, group, workers, stream);
+}
+
+hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
+    return launch_mfma<false>(a, group, stream);
+}
+
+hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
+    if (a.block_size != kTileTokens) return hipErrorInvalidValue;
+    return launch_mfma<true>(a, group, stream);
 }
 
 }  // namespace kvp

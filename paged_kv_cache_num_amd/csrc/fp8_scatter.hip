@@ -1,0 +1,196 @@
+// Write path of FP8 pools: the slot-mapping scatter and the decode append
+// with per-(block, KV head) scales.
+//
+// "PagedAttention, Internals First", "06 Open questions": a block is a natural
+// quantization group, and a scale kept per block travels with it (copy-on-write
+// copies included); sharing a block shares its scale, so a block must never be
+// requantized once other rows depend on that scale.  The scale rule of these
+// kernels: the write that puts row 0 of a block in place sets the block's K
+// and V scales (one per KV head) to amax / 448 over the rows that write puts
+// into the block (1.0 when they are all zero); every other write quantizes
+// with the scale already stored, saturating at +-448.  Quantizing divides by
+// the scale in fp32 and rounds to the nearest E4M3 code, ties to even.
+//
+// The scatter runs two kernels in stream order: fp8_scale_kernel finds the
+// tokens that write row 0 of a block and sets those blocks' scales, then
+// fp8_quantize_kernel writes every token's codes.  Slots are unique (the
+// scatter's precondition), so a block has at most B writers, and when tokens
+// t .. t+B-1 hold its slots B*blk .. B*blk+B-1 in order no other token can
+// write it: that common case needs no search.
+#include <math.h>
+
+#include "device_common.hpp"
+#include "fp8.hpp"
+#include "launch.hpp"
+
+namespace kvp {
+
+namespace {
+
+constexpr int kD8 = 128;                 // head_dim of FP8 pools
+constexpr int kRowWords = kD8 / 2;       // 32-bit words (bf16 pairs) per k_new / v_new row
+constexpr int kRowChunks8 = kD8 / 16;    // 16-byte chunks per code row
+constexpr int kQuantThreads = 256;
+
+__device__ __forceinline__ int64_t readlane64_i(int64_t x, int src) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), src);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ float abs_max2(uint32_t w, float m) {
+    return fmaxf(m, fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w))));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+    return x;
+}
+
+// One wave per workgroup; the token list is taken 64 tokens at a time.
+__global__ __launch_bounds__(kWave) void fp8_scale_kernel(ScatterArgs a) {
+    const int lane = threadIdx.x;
+    const int B = a.block_size;
+    const int H = a.num_kv_heads;
+    const int64_t T = a.num_tokens;
+    const uint32_t* kn = reinterpret_cast<const uint32_t*>(a.k_new);
+    const uint32_t* vn = reinterpret_cast<const uint32_t*>(a.v_new);
+    const uint64_t run_mask = B >= kWave ? ~0ull : ((1ull << B) - 1);
+    for (int64_t c0 = (int64_t)blockIdx.x * kWave; c0 < T; c0 += (int64_t)gridDim.x * kWave) {
+        const int64_t t = c0 + lane;
+        const int64_t slot = t < T ? a.slot_mapping[t] : -1;
+        uint64_t starts = __builtin_amdgcn_ballot_w64(slot >= 0 && slot < a.num_slots && slot % B == 0);
+        while (starts) {
+            const int j = __builtin_ctzll(starts);
+            starts &= starts - 1;
+            const int64_t first = readlane64_i(slot, j);   // slot of row 0
+            const int64_t blk = first / B;
+            // lane i < B: the token writing row i of the block, or -1
+            int64_t tok = -1;
+            const int64_t tl = c0 + j + lane;
+            const bool in_run = lane < B && tl < T && a.slot_mapping[tl] == first + lane;
+            if (__builtin_amdgcn_ballot_w64(in_run) == run_mask) {
+                tok = in_run ? tl : -1;
+            } else {
+                for (int64_t s0 = 0; s0 < T; s0 += kWave) {
+                    const int64_t ts = s0 + lane;
+                    const int64_t sl = ts < T ? a.slot_mapping[ts] : -1;
+                    uint64_t hit = __builtin_amdgcn_ballot_w64(sl >= first && sl < first + B);
+                    while (hit) {
+                        const int jj = __builtin_ctzll(hit);
+                        hit &= hit - 1;
+                        const int row = (int)(readlane64_i(sl, jj) - first);
+                        if (lane == row) tok = s0 + jj;
+                    }
+                }
+            }
+            for (int h = 0; h < H; ++h) {
+                float ak = 0.0f, av = 0.0f;
+                for (int i = 0; i < B && i < kWave; ++i) {
+                    const int64_t ti = readlane64_i(tok, i);
+                    if (ti < 0) continue;
+                    const size_t w = ((size_t)ti * H + h) * kRowWords + lane;   // lane: dims 2*lane, 2*lane+1
+                    ak = abs_max2(kn[w], ak);
+                    av = abs_max2(vn[w], av);
+                }
+                ak = wave_max(ak);
+                av = wave_max(av);
+                if (lane == 0) {
+                    a.k_scale[blk * H + h] = e4m3_block_scale(ak);
+                    a.v_scale[blk * H + h] = e4m3_block_scale(av);
+                }
+            }
+        }
+    }
+}
+
+// One thread per 16 codes: items ((token * 2 + {K,V}) * H + head) * 8 + chunk.
+__global__ __launch_bounds__(kQuantThreads) void fp8_quantize_kernel(ScatterArgs a) {
+    const int H = a.num_kv_heads;
+    const int64_t per_token = 2LL * H * kRowChunks8;
+    const int64_t total = a.num_tokens * per_token;
+    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+    for (int64_t item = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; item < total; item += stride) {
+        const int64_t t = item / per_token;
+        const int64_t rem = item - t * per_token;
+        const int which = (int)(rem / ((int64_t)H * kRowChunks8));
+        const int64_t rem2 = rem - (int64_t)which * H * kRowChunks8;
+        const int h = (int)(rem2 / kRowChunks8);
+        const int c = (int)(rem2 - (int64_t)h * kRowChunks8);
+        const int64_t slot = a.slot_mapping[t];
+        if (slot < 0 || slot >= a.num_slots) continue;
+        const int64_t blk = slot / a.block_size;
+        const int64_t off = slot - blk * a.block_size;
+        const float s = (which == 0 ? a.k_scale : a.v_scale)[blk * H + h];
+        const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new) +
+                           ((t * H + h) * (kD8 / 8) + 2 * c);
+        const uint4 x0 = src[0], x1 = src[1];
+        uint4 o;
+        o.x = bf16x2_to_e4m3x2(x0.x, s) | (bf16x2_to_e4m3x2(x0.y, s) << 16);
+        o.y = bf16x2_to_e4m3x2(x0.z, s) | (bf16x2_to_e4m3x2(x0.w, s) << 16);
+        o.z = bf16x2_to_e4m3x2(x1.x, s) | (bf16x2_to_e4m3x2(x1.y, s) << 16);
+        o.w = bf16x2_to_e4m3x2(x1.z, s) | (bf16x2_to_e4m3x2(x1.w, s) << 16);
+        uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);
+        dst[((blk * H + h) * a.block_size + off) * kRowChunks8 + c] = o;
+    }
+}
+
+// Decode append: one wave per (sequence, {K,V}, KV head), four per workgroup;
+// lane l quantizes dims 2l and 2l + 1.  The row goes to position L - 1; if that
+// is row 0 of its block, this row alone sets the block's scale.
+constexpr int kAppendWaves = 4;
+
+__global__ __launch_bounds__(kAppendWaves * kWave) void fp8_append_kernel(AppendArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int H = a.num_kv_heads;
+    const int64_t item = (int64_t)blockIdx.x * kAppendWaves + threadIdx.x / kWave;   // (seq * 2 + which) * H + h
+    if (item >= (int64_t)a.num_seqs * 2 * H) return;
+    const int64_t seq = item / (2 * H);
+    const int which = (int)((item / H) & 1);
+    const int h = (int)(item - (seq * 2 + which) * H);
+    int L = a.lens[seq];
+    L = L < 0 ? 0 : (L > a.max_context ? a.max_context : L);
+    if (L == 0) return;
+    const int pos = L - 1;
+    const int64_t block = a.tables[seq * a.max_blocks + pos / a.block_size];
+    if (block < 0 || block >= a.num_blocks) return;
+    const int j = pos % a.block_size;
+    const uint32_t w = reinterpret_cast<const uint32_t*>(which == 0 ? a.k_new : a.v_new)[(seq * H + h) * kRowWords + lane];
+    float* sc = (which == 0 ? a.k_scale : a.v_scale) + block * H + h;
+    float s;
+    if (j == 0) {
+        s = e4m3_block_scale(wave_max(abs_max2(w, 0.0f)));
+        if (lane == 0) *sc = s;
+    } else {
+        s = *sc;
+    }
+    uint16_t* dst = reinterpret_cast<uint16_t*>(which == 0 ? a.k_layer : a.v_layer);
+    dst[((block * H + h) * a.block_size + j) * (kD8 / 2) + lane] = (uint16_t)bf16x2_to_e4m3x2(w, s);
+}
+
+}  // namespace
+
+hipError_t launch_scatter_fp8(const ScatterArgs& a, hipStream_t stream) {
+    if (a.num_tokens <= 0) return hipSuccess;
+    int64_t waves = (a.num_tokens + kWave - 1) / kWave;
+    if (waves > 1024) waves = 1024;
+    fp8_scale_kernel<<<dim3((unsigned)waves), dim3(kWave), 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = a.num_tokens * 2LL * a.num_kv_heads * kRowChunks8;
+    int64_t blocks = (total + kQuantThreads - 1) / kQuantThreads;
+    if (blocks > 65536) blocks = 65536;   // grid-stride loop covers the rest
+    fp8_quantize_kernel<<<dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t stream) {
+    if (a.num_seqs <= 0) return hipSuccess;
+    const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads;
+    const int64_t blocks = (items + kAppendWaves - 1) / kAppendWaves;
+    fp8_append_kernel<<<dim3((unsigned)blocks), dim3(kAppendWaves * kWave), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace kvp

@@ -17,6 +17,9 @@ struct kv_pool {
     char* v_base;
     uint64_t layer_bytes;   // bytes of one layer of one tensor
     int32_t elem_bytes;
+    float* k_scale;         // FP8 pools: [layers][blocks][kv_heads] fp32, else null
+    float* v_scale;
+    uint64_t scale_layer;   // scale entries per layer (blocks * kv_heads)
 };
 
 namespace {
@@ -38,7 +41,9 @@ kv_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int elem_bytes_of(int32_t dtype) { return dtype == KV_F32 ? 4 : (dtype == KV_BF16 ? 2 : 0); }
+int elem_bytes_of(int32_t dtype) {
+    return dtype == KV_F32 ? 4 : (dtype == KV_BF16 ? 2 : (dtype == KV_FP8_E4M3 ? 1 : 0));
+}
 
 bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
     if (a != 0 && b > UINT64_MAX / a) return false;
@@ -80,7 +85,8 @@ Plan plan_decode(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, i
     Plan p;
     memset(&p, 0, sizeof p);
     const int group = num_q_heads / d.num_kv_heads;
-    if (partition_size == 0 && d.dtype == KV_BF16 && d.head_dim == 128 && num_seqs <= kvp::kStreamKMaxSeqs) {
+    if (partition_size == 0 && (d.dtype == KV_BF16 || d.dtype == KV_FP8_E4M3) && d.head_dim == 128 &&
+        num_seqs <= kvp::kStreamKMaxSeqs) {
         p.mode = Mode::kBalanced;
         p.workers = kvp::streamk_workers(group);
         p.part_tokens = 0;
@@ -140,7 +146,24 @@ kv_status kv_pool_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tensor) {
     return ok();
 }
 
-kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, kv_pool_t* out) {
+kv_status kv_pool_scale_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tensor) {
+    if (!bytes_per_tensor) return fail(KV_ERR_INVALID_ARGUMENT, "bytes_per_tensor is NULL");
+    *bytes_per_tensor = 0;
+    kv_status s = check_desc(desc);
+    if (s != KV_OK) return s;
+    if (desc->dtype != KV_FP8_E4M3) return ok();
+    uint64_t v = 4;
+    if (!mul_ok(v, (uint64_t)desc->num_kv_heads, &v) || !mul_ok(v, (uint64_t)desc->num_blocks, &v) ||
+        !mul_ok(v, (uint64_t)desc->num_layers, &v))
+        return fail(KV_ERR_INVALID_ARGUMENT, "scale size overflows 64 bits");
+    *bytes_per_tensor = v;
+    return ok();
+}
+
+namespace {
+
+kv_status create_pool(const kv_pool_desc* desc, void* k_base, void* v_base, float* k_scales, float* v_scales,
+                      kv_pool_t* out) {
     if (!out) return fail(KV_ERR_INVALID_ARGUMENT, "out is NULL");
     *out = nullptr;
     uint64_t total = 0;
@@ -148,6 +171,10 @@ kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, k
     if (s != KV_OK) return s;
     if (!k_base || !v_base) return fail(KV_ERR_INVALID_ARGUMENT, "pool base pointer is NULL");
     if (!aligned16(k_base) || !aligned16(v_base)) return fail(KV_ERR_INVALID_ARGUMENT, "pool base pointers must be 16-byte aligned");
+    const bool fp8 = desc->dtype == KV_FP8_E4M3;
+    if (fp8 && (!k_scales || !v_scales ||
+                ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & 3u)))
+        return fail(KV_ERR_INVALID_ARGUMENT, "FP8 scale tensors must be non-NULL and 4-byte aligned");
     const int32_t B = desc->block_size;
     if (B != 8 && B != 16 && B != 32 && B != 64 && B != 128)
         return fail(KV_ERR_UNSUPPORTED, "block_size %d: kernels are built for 8, 16, 32, 64 and 128", B);
@@ -156,6 +183,7 @@ kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, k
                     kvp::kBlockTokens);
     if (desc->head_dim != 64 && desc->head_dim != 128)
         return fail(KV_ERR_UNSUPPORTED, "head_dim %d: kernels are built for 64 and 128", desc->head_dim);
+    if (fp8 && desc->head_dim != 128) return fail(KV_ERR_UNSUPPORTED, "FP8 pools are built for head_dim 128");
     kv_pool* p = new (std::nothrow) kv_pool;
     if (!p) return fail(KV_ERR_INVALID_ARGUMENT, "out of host memory");
     p->desc = *desc;
@@ -163,8 +191,30 @@ kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, k
     p->v_base = static_cast<char*>(v_base);
     p->layer_bytes = total / (uint64_t)desc->num_layers;
     p->elem_bytes = elem_bytes_of(desc->dtype);
+    p->k_scale = fp8 ? k_scales : nullptr;
+    p->v_scale = fp8 ? v_scales : nullptr;
+    p->scale_layer = (uint64_t)desc->num_blocks * (uint64_t)desc->num_kv_heads;
     *out = p;
     return ok();
+}
+
+}  // namespace
+
+kv_status kv_pool_create(const kv_pool_desc* desc, void* k_base, void* v_base, kv_pool_t* out) {
+    if (desc && desc->dtype == KV_FP8_E4M3) {
+        if (out) *out = nullptr;
+        return fail(KV_ERR_INVALID_ARGUMENT, "FP8 pools carry scale tensors: create them with kv_pool_create_fp8");
+    }
+    return create_pool(desc, k_base, v_base, nullptr, nullptr, out);
+}
+
+kv_status kv_pool_create_fp8(const kv_pool_desc* desc, void* k_codes, void* v_codes, float* k_scales,
+                             float* v_scales, kv_pool_t* out) {
+    if (desc && desc->dtype != KV_FP8_E4M3) {
+        if (out) *out = nullptr;
+        return fail(KV_ERR_INVALID_ARGUMENT, "kv_pool_create_fp8 needs dtype KV_FP8_E4M3");
+    }
+    return create_pool(desc, k_codes, v_codes, k_scales, v_scales, out);
 }
 
 kv_status kv_pool_destroy(kv_pool_t pool) {
@@ -217,6 +267,7 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
     if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) return fail(KV_ERR_INVALID_ARGUMENT, "slot_mapping must be 8-byte aligned");
     kvp::ScatterArgs a;
+    memset(&a, 0, sizeof a);
     a.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
     a.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
     a.k_new = k_new;
@@ -227,7 +278,14 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
     a.block_size = pool->desc.block_size;
     a.num_kv_heads = pool->desc.num_kv_heads;
     a.row_chunks = pool->desc.head_dim * pool->elem_bytes / 16;
-    hipError_t e = kvp::launch_scatter(a, static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (pool->desc.dtype == KV_FP8_E4M3) {
+        a.k_scale = pool->k_scale + (uint64_t)layer * pool->scale_layer;
+        a.v_scale = pool->v_scale + (uint64_t)layer * pool->scale_layer;
+        e = kvp::launch_scatter_fp8(a, static_cast<hipStream_t>(stream));
+    } else {
+        e = kvp::launch_scatter(a, static_cast<hipStream_t>(stream));
+    }
     if (e != hipSuccess) return hip_fail(e, "scatter launch");
     return ok();
 }
@@ -240,6 +298,7 @@ kv_status kv_copy_blocks(kv_pool_t pool, const int32_t* block_pairs, int32_t num
     if (reinterpret_cast<uintptr_t>(block_pairs) & 3u) return fail(KV_ERR_INVALID_ARGUMENT, "block_pairs must be 4-byte aligned");
     const kv_pool_desc& d = pool->desc;
     kvp::CopyBlocksArgs a;
+    memset(&a, 0, sizeof a);
     a.k_base = pool->k_base;
     a.v_base = pool->v_base;
     a.layer_bytes = pool->layer_bytes;
@@ -248,6 +307,9 @@ kv_status kv_copy_blocks(kv_pool_t pool, const int32_t* block_pairs, int32_t num
     a.num_layers = d.num_layers;
     a.num_blocks = d.num_blocks;
     a.block_chunks = (int64_t)d.num_kv_heads * d.block_size * d.head_dim * pool->elem_bytes / 16;
+    a.k_scale = pool->k_scale;   // null unless FP8
+    a.v_scale = pool->v_scale;
+    a.num_kv_heads = d.num_kv_heads;
     hipError_t e = kvp::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "copy_blocks launch");
     return ok();
@@ -343,16 +405,23 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
     a.part_tokens = plan.part_tokens;
     a.max_parts = plan.max_parts;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // exp(x) = 2^(x log2 e)
+    const bool fp8 = d.dtype == KV_FP8_E4M3;
+    if (fp8) {
+        a.k_scale = pool->k_scale + (uint64_t)layer * pool->scale_layer;
+        a.v_scale = pool->v_scale + (uint64_t)layer * pool->scale_layer;
+    }
     hipError_t e;
-    if (plan.mode == Mode::kBalanced) {
+    if (plan.mode == Mode::kBalanced && !fp8) {
         // the worker that owns each (sequence, KV head)'s last block writes and uses the new row
         a.k_append = k_append;
         a.v_append = v_append;
         e = kvp::launch_decode_bf16_streamk(a, num_q_heads / d.num_kv_heads, plan.workers, static_cast<hipStream_t>(stream));
     } else {
+        // the new rows first (FP8: quantized, with the scale of a block they open), then the decode
         e = hipSuccess;
         if (append) {
             kvp::AppendArgs w;
+            memset(&w, 0, sizeof w);
             w.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
             w.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
             w.k_new = k_append;
@@ -366,9 +435,21 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
             w.num_kv_heads = d.num_kv_heads;
             w.row_chunks = d.head_dim * pool->elem_bytes / 16;
             w.block_size = d.block_size;
-            e = kvp::launch_append_scatter(w, static_cast<hipStream_t>(stream));
+            if (fp8) {
+                w.k_scale = pool->k_scale + (uint64_t)layer * pool->scale_layer;
+                w.v_scale = pool->v_scale + (uint64_t)layer * pool->scale_layer;
+                e = kvp::launch_append_fp8(w, static_cast<hipStream_t>(stream));
+            } else {
+                e = kvp::launch_append_scatter(w, static_cast<hipStream_t>(stream));
+            }
         }
-        if (e == hipSuccess) e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
+        if (e == hipSuccess) {
+            if (plan.mode == Mode::kBalanced)
+                e = kvp::launch_decode_fp8_streamk(a, num_q_heads / d.num_kv_heads, plan.workers,
+                                                   static_cast<hipStream_t>(stream));
+            else
+                e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
+        }
     }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();

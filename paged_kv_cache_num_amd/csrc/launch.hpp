@@ -22,9 +22,14 @@ struct ScatterArgs {
     int32_t block_size;          // tokens per block
     int32_t num_kv_heads;
     int32_t row_chunks;          // 16-byte chunks per (token, head) row = D * elem / 16
+    float* k_scale;              // FP8 pools: the layer's scales [num_blocks][Hkv], else null
+    float* v_scale;
 };
 
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
+// FP8 pools (head_dim 128, bf16 k_new / v_new): the scales of blocks whose row
+// 0 is written, then the quantized rows (fp8_scatter.hip).
+hipError_t launch_scatter_fp8(const ScatterArgs& a, hipStream_t stream);
 
 // Decode append: sequence i's new K/V row (k_new[i], v_new[i], [S][Hkv][D]) goes
 // to position L_i - 1 of its table, i.e. slot table[i][(L_i - 1) / B] * B +
@@ -43,9 +48,12 @@ struct AppendArgs {
     int32_t num_kv_heads;
     int32_t row_chunks;          // 16-byte chunks per (token, head) row
     int32_t block_size;          // tokens per block
+    float* k_scale;              // FP8 pools: the layer's scales [num_blocks][Hkv], else null
+    float* v_scale;
 };
 
 hipError_t launch_append_scatter(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t stream);
 
 // Copy-on-write block copy: block pairs[2p] -> block pairs[2p + 1] in every
 // layer of K and V.  Pairs naming a block outside the pool are skipped.
@@ -58,6 +66,9 @@ struct CopyBlocksArgs {
     int32_t num_layers;
     int32_t num_blocks;
     int64_t block_chunks;        // 16-byte chunks per (layer, block): H_kv * B * D * e / 16
+    float* k_scale;              // FP8 pools: layer 0 of the scale tensors [layers][num_blocks][H_kv], else null
+    float* v_scale;
+    int32_t num_kv_heads;
 };
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
@@ -74,6 +85,8 @@ struct DecodeArgs {
     int64_t* ws_prefix;          // balanced split: tiles before each sequence, [S + 1]
     const void* k_append;        // balanced split, decode append: new row per sequence [S][Hkv][D], or null
     const void* v_append;
+    const float* k_scale;        // FP8 pools: the layer's block scales [num_blocks][Hkv]
+    const float* v_scale;
     int32_t workers;             // balanced split: worker waves (the launch adds append waves past them)
     int32_t max_blocks;
     int32_t num_seqs;
@@ -87,17 +100,21 @@ struct DecodeArgs {
     float scale_log2;            // softmax scale * log2(e)
 };
 
-// dtype: 0 fp32, 1 bf16.  Returns hipErrorInvalidValue for a shape without a kernel.
+// dtype: 0 fp32, 1 bf16, 2 FP8 E4M3.  Returns hipErrorInvalidValue for a shape without a kernel.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 bool decode_shape_supported(int dtype, int head_dim, int group, int block_size);
 
 // bf16 pools with head_dim 128: scores on the matrix cores (decode_mfma.hip).
 // Launches the decode kernel only; the caller launches the partition merge.
 hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t stream);
+// The same kernels reading an FP8 pool (codes widened to bf16, block scales
+// applied to the scores and the probabilities); block size 16.
+hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, int group, hipStream_t stream);
 
 // bf16 / head_dim 128, balanced split over `workers` single-wave workers plus
 // the fix-up of split (sequence, KV head) pairs; no partition merge needed.
 hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
+hipError_t launch_decode_fp8_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
 // Worker count for the balanced split on the current device (resident waves).
 int streamk_workers(int group);
 

@@ -2,6 +2,7 @@
 // calibrate HBM byte counters and as the achievable-bandwidth reference.
 #include <hip/hip_runtime.h>
 
+#include "fp8.hpp"
 #include "kvpool_probe.h"
 #include "launch.hpp"
 #include "split.hpp"
@@ -106,7 +107,47 @@ __global__ __launch_bounds__(64) void table_walk_kernel(const int32_t* __restric
     if (lane == 0) sink[w] = acc;
 }
 
+// E4M3 conversions as the FP8 pool kernels do them.  Widening: thread i takes
+// codes 2i and 2i + 1 as one 16-bit word, in the low half of the operand for
+// even i and the high half for odd i, so both word selects are exercised.
+__global__ __launch_bounds__(256) void e4m3_widen_kernel(const uint8_t* __restrict__ codes, uint16_t* __restrict__ out,
+                                                         int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (2 * i >= n) return;
+    const bool second = 2 * i + 1 < n;
+    const uint32_t w = (uint32_t)codes[2 * i] | (second ? (uint32_t)codes[2 * i + 1] << 8 : 0u);
+    const uint32_t r = (i & 1) ? kvp::e4m3x2_to_bf16x2<true>(w << 16) : kvp::e4m3x2_to_bf16x2<false>(w);
+    out[2 * i] = (uint16_t)r;
+    if (second) out[2 * i + 1] = (uint16_t)(r >> 16);
+}
+
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ x, uint8_t* __restrict__ out,
+                                                          int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) out[i] = (uint8_t)kvp::f32_to_e4m3(x[i]);
+}
+
 }  // namespace
+
+extern "C" kv_status kv_probe_e4m3_to_bf16(const void* codes, void* out_bf16, int64_t n, void* stream) {
+    if (n < 0 || (n > 0 && (!codes || !out_bf16)) || (reinterpret_cast<uintptr_t>(out_bf16) & 1u))
+        return KV_ERR_INVALID_ARGUMENT;
+    if (n == 0) return KV_OK;
+    const int64_t threads = (n + 1) / 2;
+    if ((threads + 255) / 256 > 0x7FFFFFFF) return KV_ERR_INVALID_ARGUMENT;
+    e4m3_widen_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint8_t*>(codes), static_cast<uint16_t*>(out_bf16), n);
+    return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
+
+extern "C" kv_status kv_probe_f32_to_e4m3(const float* x, void* out_codes, int64_t n, void* stream) {
+    if (n < 0 || (n > 0 && (!x || !out_codes)) || (reinterpret_cast<uintptr_t>(x) & 3u)) return KV_ERR_INVALID_ARGUMENT;
+    if (n == 0) return KV_OK;
+    if ((n + 255) / 256 > 0x7FFFFFFF) return KV_ERR_INVALID_ARGUMENT;
+    e4m3_encode_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        x, static_cast<uint8_t*>(out_codes), n);
+    return hipGetLastError() == hipSuccess ? KV_OK : KV_ERR_HIP;
+}
 
 extern "C" kv_status kv_probe_table_walk(const int32_t* block_tables, int32_t max_blocks_per_seq,
                                          const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,

@@ -25,13 +25,16 @@ KV_ERR_OUT_OF_RANGE = -5
 
 KV_F32 = 0
 KV_BF16 = 1
+KV_FP8_E4M3 = 2
 
 # every entry point include/kvpool.h declares
 EXPORTED = (
-    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_build_slot_mapping",
+    "kv_pool_bytes", "kv_pool_scale_bytes", "kv_pool_create", "kv_pool_create_fp8", "kv_pool_destroy",
+    "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
     "paged_attention_decode_append", "kv_copy_blocks",
     "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read", "kv_probe_table_walk",
+    "kv_probe_e4m3_to_bf16", "kv_probe_f32_to_e4m3",
 )
 
 
@@ -67,6 +70,10 @@ def _load():
     lib.kv_pool_bytes.argtypes = [P(kv_pool_desc), P(u64)]
     lib.kv_pool_create.restype = ctypes.c_int
     lib.kv_pool_create.argtypes = [P(kv_pool_desc), vp, vp, P(vp)]
+    lib.kv_pool_scale_bytes.restype = ctypes.c_int
+    lib.kv_pool_scale_bytes.argtypes = [P(kv_pool_desc), P(u64)]
+    lib.kv_pool_create_fp8.restype = ctypes.c_int
+    lib.kv_pool_create_fp8.argtypes = [P(kv_pool_desc), vp, vp, vp, vp, P(vp)]
     lib.kv_pool_destroy.restype = ctypes.c_int
     lib.kv_pool_destroy.argtypes = [vp]
     lib.kv_build_slot_mapping.restype = ctypes.c_int
@@ -88,6 +95,10 @@ def _load():
     lib.kv_probe_read.argtypes = [vp, u64, vp, vp]
     lib.kv_probe_table_walk.restype = ctypes.c_int
     lib.kv_probe_table_walk.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, u64, vp]
+    lib.kv_probe_e4m3_to_bf16.restype = ctypes.c_int
+    lib.kv_probe_e4m3_to_bf16.argtypes = [vp, vp, i64, vp]
+    lib.kv_probe_f32_to_e4m3.restype = ctypes.c_int
+    lib.kv_probe_f32_to_e4m3.argtypes = [vp, vp, i64, vp]
     return lib
 
 
@@ -104,12 +115,14 @@ def _check(status: int, where: str) -> None:
 
 
 def dtype_code(dtype) -> int:
-    """'f32' / 'bf16' / torch.float32 / torch.bfloat16 -> kv_dtype."""
+    """'f32' / 'bf16' / 'fp8' / torch.float32 / torch.bfloat16 -> kv_dtype."""
     s = str(dtype)
     if s in ("f32", "torch.float32", "float32"):
         return KV_F32
     if s in ("bf16", "torch.bfloat16", "bfloat16"):
         return KV_BF16
+    if s in ("fp8", "e4m3", "fp8_e4m3"):
+        return KV_FP8_E4M3
     raise ValueError(f"unsupported dtype {dtype}")
 
 
@@ -122,6 +135,12 @@ def make_desc(num_layers: int, num_blocks: int, block_size: int, num_kv_heads: i
 def kv_pool_bytes(desc: kv_pool_desc) -> int:
     out = ctypes.c_uint64(0)
     _check(lib.kv_pool_bytes(ctypes.byref(desc), ctypes.byref(out)), "kv_pool_bytes")
+    return int(out.value)
+
+
+def kv_pool_scale_bytes(desc: kv_pool_desc) -> int:
+    out = ctypes.c_uint64(0)
+    _check(lib.kv_pool_scale_bytes(ctypes.byref(desc), ctypes.byref(out)), "kv_pool_scale_bytes")
     return int(out.value)
 
 
@@ -162,33 +181,57 @@ def _dev_ptr(t, name: str, dtype=None) -> int:
 
 
 class KVPool:
-    """A paged K/V pool: two caller-owned device tensors wrapped by the C handle.
+    """A paged K/V pool: caller-owned device tensors wrapped by the C handle.
 
     ``k`` and ``v`` are device tensors of ``kv_pool_bytes(desc)`` bytes each,
-    viewed as ``[num_layers][num_blocks][num_kv_heads][block_size][head_dim]``.
+    viewed as ``[num_layers][num_blocks][num_kv_heads][block_size][head_dim]``:
+    float32 or bfloat16 values, or, for an FP8 pool, uint8 E4M3 codes.  An FP8
+    pool also takes ``k_scale`` / ``v_scale``, float32
+    ``[num_layers][num_blocks][num_kv_heads]``; its q, k_new / v_new and
+    outputs are bfloat16 (``torch_dtype``).
     """
 
     def __init__(self, k, v, *, num_layers: int, num_blocks: int, block_size: int,
-                 num_kv_heads: int, head_dim: int):
+                 num_kv_heads: int, head_dim: int, k_scale=None, v_scale=None):
         import torch
-        self.desc = make_desc(num_layers, num_blocks, block_size, num_kv_heads, head_dim, k.dtype)
+        self.fp8 = k.dtype == torch.uint8
+        self.desc = make_desc(num_layers, num_blocks, block_size, num_kv_heads, head_dim,
+                              "fp8" if self.fp8 else k.dtype)
         need = kv_pool_bytes(self.desc)
         for name, t in (("k", k), ("v", v)):
             if t.dtype != k.dtype or t.numel() * t.element_size() != need:
                 raise ValueError(f"{name} pool must hold {need} bytes of {k.dtype}")
         self.k, self.v = k, v
-        self.torch_dtype = k.dtype
+        self.k_scale, self.v_scale = k_scale, v_scale
+        self.torch_dtype = torch.bfloat16 if self.fp8 else k.dtype
         self._h = ctypes.c_void_p(0)
-        _check(lib.kv_pool_create(ctypes.byref(self.desc), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                                  ctypes.byref(self._h)), "kv_pool_create")
+        if self.fp8:
+            sneed = kv_pool_scale_bytes(self.desc)
+            for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+                if t is None or t.dtype != torch.float32 or t.numel() * 4 != sneed:
+                    raise ValueError(f"{name} must be a float32 tensor of {sneed} bytes")
+            _check(lib.kv_pool_create_fp8(ctypes.byref(self.desc), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                          _dev_ptr(k_scale, "k_scale"), _dev_ptr(v_scale, "v_scale"),
+                                          ctypes.byref(self._h)), "kv_pool_create_fp8")
+        else:
+            _check(lib.kv_pool_create(ctypes.byref(self.desc), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                      ctypes.byref(self._h)), "kv_pool_create")
         self.num_layers, self.num_blocks, self.block_size = num_layers, num_blocks, block_size
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
 
     @classmethod
     def allocate(cls, *, num_layers: int, num_blocks: int, block_size: int, num_kv_heads: int,
                  head_dim: int, dtype, device="cuda"):
+        """dtype: torch.float32, torch.bfloat16, or "fp8" (uint8 codes plus float32 scales)."""
         import torch
         shape = (num_layers, num_blocks, num_kv_heads, block_size, head_dim)
+        if str(dtype) in ("fp8", "e4m3", "fp8_e4m3"):
+            k = torch.empty(shape, dtype=torch.uint8, device=device)
+            v = torch.empty(shape, dtype=torch.uint8, device=device)
+            ks = torch.ones(shape[:3], dtype=torch.float32, device=device)
+            vs = torch.ones(shape[:3], dtype=torch.float32, device=device)
+            return cls(k, v, num_layers=num_layers, num_blocks=num_blocks, block_size=block_size,
+                       num_kv_heads=num_kv_heads, head_dim=head_dim, k_scale=ks, v_scale=vs)
         k = torch.empty(shape, dtype=dtype, device=device)
         v = torch.empty(shape, dtype=dtype, device=device)
         return cls(k, v, num_layers=num_layers, num_blocks=num_blocks, block_size=block_size,
@@ -321,3 +364,21 @@ def probe_table_walk(block_tables, context_lens, num_kv_heads: int, max_context_
                                    int(num_kv_heads), int(max_context_len), 1 if xcd_grouped else 0,
                                    _dev_ptr(sink, "sink"), sink.numel() * sink.element_size(),
                                    _stream_handle(stream)), "kv_probe_table_walk")
+
+
+def probe_e4m3_to_bf16(codes, out, stream=None) -> None:
+    """Test hook: widen uint8 E4M3 codes to bfloat16 (out: int16/bfloat16 tensor, same length)."""
+    import torch
+    if codes.dtype != torch.uint8 or out.numel() != codes.numel() or out.element_size() != 2:
+        raise TypeError("codes: uint8; out: 2-byte elements, same count")
+    _check(lib.kv_probe_e4m3_to_bf16(_dev_ptr(codes, "codes"), _dev_ptr(out, "out"), codes.numel(),
+                                     _stream_handle(stream)), "kv_probe_e4m3_to_bf16")
+
+
+def probe_f32_to_e4m3(x, out, stream=None) -> None:
+    """Test hook: fp32 values to E4M3 codes as the FP8 write path rounds them."""
+    import torch
+    if x.dtype != torch.float32 or out.dtype != torch.uint8 or out.numel() != x.numel():
+        raise TypeError("x: float32; out: uint8, same count")
+    _check(lib.kv_probe_f32_to_e4m3(_dev_ptr(x, "x"), _dev_ptr(out, "out"), x.numel(), _stream_handle(stream)),
+           "kv_probe_f32_to_e4m3")

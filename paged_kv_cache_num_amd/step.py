@@ -40,15 +40,23 @@ def to_host(t, dtype: str) -> np.ndarray:
 
 
 class DecodeStep:
-    def __init__(self, *, k_pool: np.ndarray, v_pool: np.ndarray, dtype: str,
+    """``dtype`` is the type of q, k_new / v_new and the output.  The pool holds
+    the same type, or, with ``fp8_pool = (k_codes, v_codes, k_scale, v_scale)``
+    (uint8 ``[N][Hkv][B][D]``, float32 ``[N][Hkv]``), E4M3 codes with block
+    scales; dtype is then "bf16" and k_pool / v_pool are not used."""
+
+    def __init__(self, *, k_pool: Optional[np.ndarray], v_pool: Optional[np.ndarray], dtype: str,
                  block_tables: np.ndarray, context_lens: np.ndarray, q: np.ndarray,
                  k_new: np.ndarray, v_new: np.ndarray, write_tables: np.ndarray,
                  write_seq: np.ndarray, write_start: np.ndarray, write_count: np.ndarray,
                  num_layers: int = 1, layer: int = 0, partition_size: int = 0,
                  scale: Optional[float] = None, max_context_len: Optional[int] = None,
-                 device="cuda"):
+                 fp8_pool=None, device="cuda"):
         import torch
-        N, Hkv, B, D = k_pool.shape
+        self.fp8 = fp8_pool is not None
+        if self.fp8 and dtype != "bf16":
+            raise ValueError("FP8 pools take bf16 queries and rows")
+        N, Hkv, B, D = (fp8_pool[0] if self.fp8 else k_pool).shape
         self.dtype, self.layer, self.partition_size = dtype, int(layer), int(partition_size)
         self.num_seqs, self.num_q_heads = int(q.shape[0]), int(q.shape[1])
         self.scale = float(scale) if scale is not None else 1.0 / math.sqrt(D)
@@ -56,14 +64,20 @@ class DecodeStep:
                                    else (context_lens.max() if context_lens.size else 0))
         self.pool = KVPool.allocate(num_layers=num_layers, num_blocks=N, block_size=B,
                                     num_kv_heads=Hkv, head_dim=D,
-                                    dtype=torch.float32 if dtype == "f32" else torch.bfloat16,
+                                    dtype="fp8" if self.fp8 else (torch.float32 if dtype == "f32" else torch.bfloat16),
                                     device=device)
         # every layer but the working one is filled with the same stale contents
-        kd, vd = to_device(k_pool, dtype, device), to_device(v_pool, dtype, device)
-        for li in range(num_layers):
-            self.pool.k[li].copy_(kd)
-            self.pool.v[li].copy_(vd)
-        del kd, vd
+        if self.fp8:
+            kc, vc, ks, vs = fp8_pool
+            parts = [(self.pool.k, to_device(kc, "u8", device)), (self.pool.v, to_device(vc, "u8", device)),
+                     (self.pool.k_scale, to_device(ks, "f32", device)),
+                     (self.pool.v_scale, to_device(vs, "f32", device))]
+        else:
+            parts = [(self.pool.k, to_device(k_pool, dtype, device)), (self.pool.v, to_device(v_pool, dtype, device))]
+        for dst, src in parts:
+            for li in range(num_layers):
+                dst[li].copy_(src)
+        del parts
         self.block_tables = to_device(np.ascontiguousarray(block_tables, dtype=np.int32), "i32", device)
         self.context_lens = to_device(np.ascontiguousarray(context_lens, dtype=np.int32), "i32", device)
         self.q = to_device(q, dtype, device)
@@ -115,6 +129,8 @@ class DecodeStep:
 
     @classmethod
     def from_workload(cls, wl, **kw):
+        """kw may carry ``fp8_pool`` (see the class docstring): the step then
+        runs on that FP8 pool with ``wl``'s tables, queries and rows."""
         kw.setdefault("partition_size", wl.partition_size)
         return cls(k_pool=wl.k_pool, v_pool=wl.v_pool, dtype=wl.dtype, block_tables=wl.block_tables,
                    context_lens=wl.context_lens, q=wl.q, k_new=wl.k_new, v_new=wl.v_new,
@@ -174,5 +190,12 @@ class DecodeStep:
         return to_host(self.out, self.dtype)
 
     def pool_host(self, layer: Optional[int] = None):
+        """K and V of one layer in storage form (FP8 pools: the uint8 codes)."""
         li = self.layer if layer is None else layer
-        return to_host(self.pool.k[li], self.dtype), to_host(self.pool.v[li], self.dtype)
+        dt = "u8" if self.fp8 else self.dtype
+        return to_host(self.pool.k[li], dt), to_host(self.pool.v[li], dt)
+
+    def scales_host(self, layer: Optional[int] = None):
+        """FP8 pools: the K and V block scales of one layer, float32 [N][Hkv]."""
+        li = self.layer if layer is None else layer
+        return to_host(self.pool.k_scale[li], "f32"), to_host(self.pool.v_scale[li], "f32")

@@ -285,3 +285,69 @@ def test_status_strings():
                        (-3, "KV_ERR_WORKSPACE_TOO_SMALL"), (-4, "KV_ERR_HIP"), (-5, "KV_ERR_OUT_OF_RANGE")]:
         assert K.lib.kv_status_string(code).decode() == name
     assert K.lib.kv_status_string(42).decode() == "KV_ERR_UNKNOWN"
+
+
+# ------------------------------------------------------------------ FP8 pools --
+
+def _fp8_pool(**kw):
+    d = _desc(**dict(dict(head_dim=128, num_kv_heads=2, dtype="fp8"), **kw))
+    h = ctypes.c_void_p(0)
+    st = K.lib.kv_pool_create_fp8(ctypes.byref(d), 0x10000, 0x20000, 0x30000, 0x40000, ctypes.byref(h))
+    return st, h
+
+
+def test_fp8_pool_sizes():
+    """Codes are one byte per element; scales one fp32 per (layer, block, KV head) and tensor."""
+    d = _desc(num_layers=3, num_blocks=10, block_size=16, num_kv_heads=8, head_dim=128, dtype="fp8")
+    assert kvp.kv_pool_bytes(d) == 3 * 10 * 16 * 8 * 128
+    assert K.kv_pool_scale_bytes(d) == 3 * 10 * 8 * 4
+    # the bf16 pool of the same shape is twice the code bytes and has no scales
+    d16 = _desc(num_layers=3, num_blocks=10, block_size=16, num_kv_heads=8, head_dim=128, dtype="bf16")
+    assert kvp.kv_pool_bytes(d16) == 2 * kvp.kv_pool_bytes(d)
+    assert K.kv_pool_scale_bytes(d16) == 0
+
+
+def test_fp8_pool_create_checks():
+    st, h = _fp8_pool()
+    assert st == K.KV_OK and h.value
+    K.lib.kv_pool_destroy(h)
+    # an FP8 descriptor needs the FP8 entry point, and that entry point an FP8 descriptor
+    d = _desc(head_dim=128, dtype="fp8")
+    h = ctypes.c_void_p(0)
+    assert K.lib.kv_pool_create(ctypes.byref(d), 0x10000, 0x20000, ctypes.byref(h)) == K.KV_ERR_INVALID_ARGUMENT
+    d16 = _desc(head_dim=128, dtype="bf16")
+    assert K.lib.kv_pool_create_fp8(ctypes.byref(d16), 0x10000, 0x20000, 0x30000, 0x40000,
+                                    ctypes.byref(h)) == K.KV_ERR_INVALID_ARGUMENT
+    # scales: non-null, 4-byte aligned
+    assert K.lib.kv_pool_create_fp8(ctypes.byref(d), 0x10000, 0x20000, None, 0x40000,
+                                    ctypes.byref(h)) == K.KV_ERR_INVALID_ARGUMENT
+    assert K.lib.kv_pool_create_fp8(ctypes.byref(d), 0x10000, 0x20000, 0x30002, 0x40000,
+                                    ctypes.byref(h)) == K.KV_ERR_INVALID_ARGUMENT
+    # built for head_dim 128 and 16-token blocks
+    assert _fp8_pool(head_dim=64)[0] == K.KV_ERR_UNSUPPORTED
+    assert _fp8_pool(block_size=32)[0] == K.KV_ERR_UNSUPPORTED
+
+
+def test_fp8_decode_argument_checks():
+    st, h = _fp8_pool()
+    assert st == K.KV_OK
+    assert _decode(h, Hq=6) == K.KV_ERR_UNSUPPORTED                # group of 3
+    assert _decode(h, part=24) == K.KV_ERR_INVALID_ARGUMENT        # not a multiple of 16
+    assert _decode(h, part=64) == K.KV_ERR_WORKSPACE_TOO_SMALL
+    # the balanced split is used for FP8 pools too: a workspace is needed with partition_size 0
+    need = ctypes.c_uint64(0)
+    assert K.lib.paged_attention_workspace_bytes(h, 4, 8, 200, 0, ctypes.byref(need)) == K.KV_OK
+    assert need.value > 0
+    assert _decode(h) == K.KV_ERR_WORKSPACE_TOO_SMALL
+    assert _decode(h, S=0) == K.KV_OK
+    K.lib.kv_pool_destroy(h)
+
+
+def test_fp8_probe_argument_checks():
+    L = K.lib
+    assert L.kv_probe_e4m3_to_bf16(None, 0x2000, 4, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_e4m3_to_bf16(0x1000, 0x2001, 4, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_e4m3_to_bf16(0x1000, 0x2000, -1, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_e4m3_to_bf16(None, None, 0, None) == K.KV_OK
+    assert L.kv_probe_f32_to_e4m3(0x1002, 0x2000, 4, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert L.kv_probe_f32_to_e4m3(None, None, 0, None) == K.KV_OK
