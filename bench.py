@@ -41,7 +41,8 @@ METRIC = "paged decode attention achieved HBM GB/s (% of peak) + decode tokens/s
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_num_amd/csrc/decode.hip", "paged_kv_cache_num_amd/csrc/decode_mfma.hip",
-                  "paged_kv_cache_num_amd/csrc/device_common.hpp", "paged_kv_cache_num_amd/csrc/split.hpp"]
+                  "paged_kv_cache_num_amd/csrc/device_common.hpp", "paged_kv_cache_num_amd/csrc/split.hpp",
+                  "paged_kv_cache_num_amd/csrc/fp8.hpp"]
 
 WORKLOADS = {
     "C1": "tiny fp32 paged decode: 4 sequences, lengths {17,33,100,200}, 8 query / 2 KV heads, head_dim 64, block 16, 64-block pool",
@@ -62,17 +63,21 @@ def kernel_sha() -> str:
     return h.hexdigest()
 
 
-def algorithmic_bytes(wl):
+def algorithmic_bytes(wl, fp8: bool = False):
     """Bytes the step must move at minimum.
 
     attention: every distinct (physical block, token) K and V row once, plus q
     in and the output out, plus the table entries and lengths read;
     scatter: new K/V rows read and written, plus the slot mapping.
     Split-partition partial states are not counted.
+    FP8 pools: rows are one byte per element plus, per distinct block, its K
+    and V scales (8 bytes per KV head); the scatter reads bf16 rows, writes
+    codes and reads each written row's two scales.
     """
     import numpy as np
     B, Hkv, D, e = wl.block_size, wl.num_kv_heads, wl.head_dim, wl.elem_bytes
-    row = 2 * Hkv * D * e                      # K and V of one token, all KV heads
+    e_pool = 1 if fp8 else e
+    row = 2 * Hkv * D * e_pool                 # K and V of one token, all KV heads
     used = {}
     for i, L in enumerate(wl.context_lens):
         L = int(L)
@@ -81,29 +86,33 @@ def algorithmic_bytes(wl):
             phys = int(wl.block_tables[i, b])
             tokens = min(B, L - b * B)
             used[phys] = max(used.get(phys, 0), tokens)
-    kv_unique = sum(used.values()) * row
+    kv_unique = sum(used.values()) * row + (len(used) * 8 * Hkv if fp8 else 0)
     kv_logical = int(np.sum(wl.context_lens)) * row
     nblk = int(sum(-(-int(L) // B) for L in wl.context_lens))
     qo = 2 * wl.num_seqs * wl.num_q_heads * D * e
     attn = kv_unique + qo + 4 * nblk + 4 * wl.num_seqs
     T = wl.num_write_tokens
-    scatter = 2 * T * row + 8 * T
+    if fp8:
+        scatter = T * 2 * Hkv * D * (e + 1) + 8 * T + 8 * Hkv * T
+    else:
+        scatter = 2 * T * row + 8 * T
     return dict(attn=attn, attn_logical=kv_logical + qo + 4 * nblk + 4 * wl.num_seqs, scatter=scatter,
                 kv_unique=kv_unique, kv_logical=kv_logical, blocks=nblk)
 
 
-def traffic_key(config: str, partition: int, block_size: int = 16) -> str:
-    return f"{config}/p{partition}" + ("" if block_size == 16 else f"/B{block_size}")
+def traffic_key(config: str, partition: int, block_size: int = 16, kv_dtype: str = "bf16") -> str:
+    return (f"{config}/p{partition}" + ("" if block_size == 16 else f"/B{block_size}")
+            + ("" if kv_dtype == "bf16" else f"/{kv_dtype}"))
 
 
-def traffic_for(config: str, partition: int, block_size: int = 16):
+def traffic_for(config: str, partition: int, block_size: int = 16, kv_dtype: str = "bf16"):
     """HBM bytes per decode launch from committed counter runs, or None if stale/absent."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get(traffic_key(config, partition, block_size))
+    entry = rec.get(traffic_key(config, partition, block_size, kv_dtype))
     if not entry or entry.get("kernel_source_sha256") != kernel_sha():
         return None
     return entry.get("traffic_bytes_per_launch")
@@ -114,7 +123,7 @@ ATTN_KERNEL_MARKERS = ("decode_bf16_streamk_kernel", "streamk_fixup_kernel", "de
 
 
 def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, config: str, partition: int,
-                   command: str, block_size: int = 16) -> dict:
+                   command: str, block_size: int = 16, kv_dtype: str = "bf16") -> dict:
     """HBM bytes per attention call from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE).
 
     Each counter is scaled by what it reads for the copy probe of copy_mib MiB
@@ -159,7 +168,7 @@ def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, config: str, p
             rec = json.load(f)
     except (OSError, ValueError):
         rec = {}
-    rec[traffic_key(config, partition, block_size)] = entry
+    rec[traffic_key(config, partition, block_size, kv_dtype)] = entry
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -187,6 +196,52 @@ def cpu_baseline(wl, bytes_total):
             "tokens_per_s_per_layer": round(wl.num_seqs / dt, 3)}
 
 
+def cpu_baseline_fp8(wl, state, nseq: int = 16):
+    """The FP8 oracle (oracle/fp8.py: scatter with block scales, fp64 attention
+    over the dequantized pool) on the first ``nseq`` sequences of the batch,
+    their blocks gathered into a pool of their own first (outside the timing)."""
+    import dataclasses
+
+    import numpy as np
+
+    import oracle
+    import oracle.fp8 as ofp8
+    B = wl.block_size
+    S = min(nseq, wl.num_seqs)
+    lens = wl.context_lens[:S]
+    rows = [wl.block_tables[i, :-(-int(L) // B)] for i, L in enumerate(lens)]
+    blocks = np.unique(np.concatenate(rows)) if rows else np.zeros(0, dtype=np.int32)
+    where = {int(b): j for j, b in enumerate(blocks)}
+    tables = np.zeros((S, max(1, max(len(r) for r in rows))), dtype=np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = [where[int(b)] for b in r]
+    sub_state = tuple(a[blocks] for a in state)
+    # the sample's decode writes: one row per sequence at L - 1
+    keep = [k for k in range(len(wl.write_seq)) if wl.write_seq[k] < S and wl.write_count[k] == 1]
+    row0 = np.concatenate([[0], np.cumsum(wl.write_count)])
+    tok = np.array([row0[k] for k in keep], dtype=np.int64)
+    sub = dataclasses.replace(wl, context_lens=lens, block_tables=tables, extra_tables=tables[:0],
+                              write_seq=wl.write_seq[keep], write_start=wl.write_start[keep],
+                              write_count=wl.write_count[keep], q=wl.q[:S], k_new=wl.k_new[tok],
+                              v_new=wl.v_new[tok], k_pool=wl.k_pool[blocks], v_pool=wl.v_pool[blocks],
+                              num_blocks=int(blocks.size))
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):      # numpy's BLAS on one thread: the figure is per core
+        t0 = time.perf_counter()
+        slots = oracle.slot_mapping(sub.block_tables, B, sub.num_blocks, sub.write_seq, sub.write_start,
+                                    sub.write_count)
+        kc, vc, ks, vs = ofp8.scatter(*sub_state, sub.k_new, sub.v_new, slots, B)
+        ofp8.paged_attention(sub.q, kc, vc, ks, vs, sub.block_tables, sub.context_lens, scale)
+        dt = time.perf_counter() - t0
+    nb = algorithmic_bytes(sub, fp8=True)
+    return {"value": round((nb["attn"] + nb["scatter"]) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the first {S} of {wl.num_seqs} sequences of the {wl.name} step with their blocks: "
+                      "FP8 slot mapping, scatter with block scales and fp64 attention (numpy)",
+            "tokens_per_s_per_layer": round(S / dt, 3)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +252,9 @@ def main(argv=None):
     ap.add_argument("--variant", default="spec")
     ap.add_argument("--block-size", type=int, default=None,
                     help="tokens per block (default: the workload's 16); bf16 workloads take 8..128")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="pool storage: the workload's bf16, or E4M3 codes with per-(block, KV head) scales "
+                         "(q, new rows and outputs stay bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing pass")
     ap.add_argument("--no-identity", action="store_true",
@@ -219,7 +277,7 @@ def main(argv=None):
     if args.record_traffic:
         part = DEFAULT_PARTITION[args.config] if args.partition is None else args.partition
         entry = record_traffic(args.record_traffic[0], args.record_traffic[1], args.probe_copy_mib or 1024,
-                               args.config, part, args.record_command, args.block_size or 16)
+                               args.config, part, args.record_command, args.block_size or 16, args.kv_dtype)
         print(json.dumps(entry))
         return 0
 
@@ -242,8 +300,21 @@ def main(argv=None):
 
     print(f"bench: generating {args.config} ({args.variant})", file=sys.stderr, flush=True)
     wl = kvgen.make_workload(args.config, variant=args.variant, block_size=args.block_size)
-    nbytes = algorithmic_bytes(wl)
-    step = DecodeStep.from_workload(wl, partition_size=part)
+    fp8 = args.kv_dtype == "fp8"
+    if fp8 and (wl.dtype != "bf16" or wl.head_dim != 128 or wl.block_size != 16):
+        print("bench.py: FP8 pools are built for bf16 workloads with head_dim 128 and block size 16",
+              file=sys.stderr)
+        return 2
+
+    def fp8_state(w):
+        # codes and block scales drawn directly; the largest code stands for about 3 sigma of the
+        # workload's values (N(0, 1/128) for the spec variant)
+        sigma = 1.0 / math.sqrt(w.head_dim) if args.variant == "spec" else 1.0
+        return kvgen.fp8_pool_state(w, seed=w.info.get("seed") or 0, largest=3.0 * sigma) if fp8 else None
+
+    nbytes = algorithmic_bytes(wl, fp8=fp8)
+    state = fp8_state(wl)
+    step = DecodeStep.from_workload(wl, partition_size=part, fp8_pool=state)
     torch.cuda.synchronize()
 
     # achievable HBM read rate on this machine: a plain 16-byte-load read of 2 GiB (larger than the caches)
@@ -374,7 +445,8 @@ def main(argv=None):
     # ratio is what the indirection costs.
     identity = None
     if not args.no_identity:
-        dense = DecodeStep.from_workload(kvgen.privatize_blocks(wl, contiguous=True), partition_size=part)
+        dense_wl = kvgen.privatize_blocks(wl, contiguous=True)
+        dense = DecodeStep.from_workload(dense_wl, partition_size=part, fp8_pool=fp8_state(dense_wl))
         for _ in range(args.warmup):
             dense.attend()
         torch.cuda.synchronize()
@@ -409,7 +481,8 @@ def main(argv=None):
         npairs = 512
         cpool = KVPool.allocate(num_layers=1, num_blocks=2 * npairs, block_size=wl.block_size,
                                 num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim,
-                                dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16, device="cuda")
+                                dtype="fp8" if fp8 else (torch.float32 if wl.dtype == "f32" else torch.bfloat16),
+                                device="cuda")
         cpool.k.fill_(1)
         cpool.v.fill_(2)
         perm = torch.randperm(2 * npairs, generator=torch.Generator().manual_seed(0)).to(torch.int32)
@@ -423,7 +496,9 @@ def main(argv=None):
             b.synchronize()
             if i >= args.warmup:
                 cus.append(a.elapsed_time(b) * 1e3)
-        block_bytes = wl.num_kv_heads * wl.block_size * wl.head_dim * (4 if wl.dtype == "f32" else 2)
+        block_bytes = wl.num_kv_heads * wl.block_size * wl.head_dim * (1 if fp8 else (4 if wl.dtype == "f32" else 2))
+        if fp8:
+            block_bytes += 4 * wl.num_kv_heads          # the block's scale per KV head
         moved = npairs * 2 * block_bytes * 2
         cp50 = percentile(cus, 0.5)
         copy = {"pairs": npairs, "bytes_moved": moved, "us_p50": round(cp50, 2),
@@ -448,7 +523,7 @@ def main(argv=None):
                 us.append(a.elapsed_time(b) * 1e3)
             table_walk["xcd_grouped_us_p50" if grouped else "default_us_p50"] = round(percentile(us, 0.5), 2)
 
-    traffic = traffic_for(args.config, part, wl.block_size)
+    traffic = traffic_for(args.config, part, wl.block_size, args.kv_dtype)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -470,6 +545,7 @@ def main(argv=None):
                    "num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "partition_size": part,
                    "context_tokens": int(np.sum(wl.context_lens)), "scatter_tokens": wl.num_write_tokens,
+                   "kv_dtype": "fp8_e4m3 codes + fp32 scale per (block, KV head)" if fp8 else wl.dtype,
                    "seed": wl.info.get("seed")},
         "tokens_per_s_per_layer": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -493,7 +569,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, step_bytes)
+        result["cpu_baseline"] = cpu_baseline_fp8(wl, state) if fp8 else cpu_baseline(wl, step_bytes)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -167,7 +167,13 @@ kv_status kv_build_slot_mapping(const int32_t* block_tables, int32_t num_rows,
  * and v_new[t][h][:] to row (slot / B, h, slot % B) of layer `layer` of the K
  * and V pools, for every KV head h.  Tokens with a negative slot (padding) or a
  * slot past the pool are skipped.  A bit-exact copy.
- *   k_new, v_new:   device, [num_tokens][num_kv_heads][head_dim], pool dtype, 16-byte aligned
+ * FP8 pools: k_new / v_new are bf16; first every block whose row 0 one of the
+ * tokens writes gets its K and V scales (per KV head) from the rows this call
+ * puts into that block, then every row is quantized with its block's scale
+ * (the rule under kv_pool_scale_bytes).  Rows should be finite (a NaN or an
+ * infinity gives an unspecified result for its block).  Two kernels in
+ * stream order.
+ *   k_new, v_new:   device, [num_tokens][num_kv_heads][head_dim], pool dtype (bf16 for FP8), 16-byte aligned
  *   slot_mapping:   device, int64 [num_tokens]
  * Precondition: non-negative slots are unique (two tokens for one slot race).
  * num_tokens == 0 queues nothing.  Errors: KV_ERR_INVALID_ARGUMENT (null
@@ -184,7 +190,8 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
  * fresh block, has its contents copied, and repoints the writer's table entry.
  * This call is that device copy: for every pair p, block block_pairs[2p] is
  * copied to block block_pairs[2p + 1] in every layer of the K and the V tensor
- * (H_kv * B * D * e contiguous bytes per layer and tensor), bit for bit.
+ * (H_kv * B * D * e contiguous bytes per layer and tensor), bit for bit; in an
+ * FP8 pool the block's K and V scales of every layer are copied too.
  *   block_pairs: device, int32 [num_pairs][2] (src, dst), 4-byte aligned.
  *                A pair naming a block outside [0, num_blocks) is skipped.
  *   Precondition: no destination appears twice or as a source of another
@@ -219,13 +226,15 @@ kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int3
  * j over the first L_i = context_lens[i] logical tokens of sequence i, where
  * K_i[j] / V_i[j] are row (block_tables[i][j / B], kv, j % B) of layer `layer`.
  * L_i counts the token written this step.  L_i == 0 gives a zero output.
- *   out, q:        device, [num_seqs][num_q_heads][head_dim], pool dtype, 16-byte aligned
+ * FP8 pools: K_i[j] and V_i[j] are the codes times their block's K / V scale
+ * for head kv; q and out are bf16.
+ *   out, q:        device, [num_seqs][num_q_heads][head_dim], pool dtype (bf16 for FP8), 16-byte aligned
  *   block_tables:  device, int32 [num_seqs][max_blocks_per_seq]; entries at
  *                  b >= ceil(L_i / B) are never read
  *   context_lens:  device, int32 [num_seqs], each in [0, max_context_len]
  *   max_context_len: host bound on every L_i (sizes the grid); <= max_blocks_per_seq * B
- *   partition_size: 0 = the library balances the work itself.  For bf16 pools
- *                  with head_dim 128 and at most 1024 sequences, the
+ *   partition_size: 0 = the library balances the work itself.  For bf16 and FP8
+ *                  pools with head_dim 128 and at most 1024 sequences, the
  *                  (sequence, KV head, block) tiles of the whole batch are cut
  *                  into equal contiguous slices, one per resident wave, and
  *                  a second kernel merges the (sequence, KV head) pairs that
@@ -255,7 +264,7 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
  * new row to position L_i - 1 (slot table[i][(L_i - 1) / B] * B + (L_i - 1) % B,
  * [KVC] "The write path: slot mapping and scatter") for every i with L_i > 0,
  * followed by paged_attention_decode with the same arguments.
- *   k_new, v_new: device, [num_seqs][H_kv][D] in the pool dtype, 16-byte aligned:
+ *   k_new, v_new: device, [num_seqs][H_kv][D] in the pool dtype (bf16 for FP8), 16-byte aligned:
  *                 the K/V row of the token each sequence writes this step
  *                 (rows of sequences with L_i = 0 are not read).
  *   Every other argument, and every error, as for paged_attention_decode.
@@ -264,7 +273,9 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
  * copy-on-write).  In the balanced mode the wave that reads that block writes
  * the row into the pool and uses it directly (one kernel, no separate scatter);
  * other modes run a small scatter kernel first.  A block index outside the pool
- * is skipped, as by reshape_and_cache.
+ * is skipped, as by reshape_and_cache.  FP8 pools always run a small append
+ * kernel first (the row is quantized; a row at position 0 of its block sets
+ * that block's scales from itself alone), then the decode.
  */
 kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out, const void* q,
                                         const void* k_new, const void* v_new, const int32_t* block_tables,

@@ -36,8 +36,8 @@
 //     scale multiplies its scores; its V scale multiplies the probabilities
 //     that enter P V, while the softmax sum takes them unscaled, so
 //     out = sum_j p_j sv_j v_j / sum_j p_j is what the dequantized cache gives.
-//     A tile moves half the bytes of a bf16 tile, so twice as many are kept
-//     in flight.
+//     Two tiles in flight per wave, as for bf16: deeper pipelines (4, 6, 8
+//     FP8 tiles) measured slower on the 8B- and 70B-shaped batches.
 #include <math.h>
 
 #include "device_common.hpp"
@@ -55,7 +55,6 @@ constexpr int kRC = kD / 8;        // 16-byte chunks per token row (16)
 constexpr int kKK = kD / 32;       // MFMA steps over head_dim (4)
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max is moved
 constexpr int kStreamDepth = 2;    // tiles in registers per balanced-mode wave
-constexpr int kStreamDepthFp8 = 4; // the same for FP8 tiles (half the bytes)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -557,7 +556,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
     AppendRow none;
     none.active = false;
     none.krow = none.vrow = nullptr;
-    walk<G, kFp8 ? 4 : 2, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
+    walk<G, 2, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
     const float l_tot = total_l(st);
 
     // waves of the workgroup merge through LDS
@@ -770,8 +769,8 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                 pf_valid = true;
             }
         }
-        walk<G, kFp8 ? kStreamDepthFp8 : kStreamDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1,
-                                                             n_here, b, L, c, app, use_pf, tv0_here, tv1_here);
+        walk<G, kStreamDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, app, use_pf,
+                                    tv0_here, tv1_here);
         const float l_tot = total_l(st);
 
         if (whole) {
