@@ -220,10 +220,14 @@ __device__ __forceinline__ void softmax_pv(State& st, f32x4_t s, uint32_t (&ev)[
     }
 }
 
-// One bf16 tile: scores on MFMA, then softmax_pv.  The tile's registers are
-// refilled with the next tile as soon as they are consumed: after_k() is
-// called once the K half has been read, after_v() once the V half has.  The
-// V operands are already in the lane's own V loads and are only repacked.
+// One bf16 tile: scores on MFMA, then the steps of softmax_pv written out in
+// place (with a V scale of 1).  The tile's registers are refilled with the
+// next tile as soon as they are consumed: after_k() is called once the K half
+// has been read, after_v() once the V half has.  The V operands are already
+// in the lane's own V loads and are only repacked.  Kept as one body: with
+// softmax_pv called here the bf16 walk took 264 registers instead of 254, so
+// a second wave no longer fit on a SIMD beside a worker and the decode-append
+// waves of the balanced kernel could not run alongside the workers.
 template <int G, class AfterK, class AfterV>
 __device__ __forceinline__ void process(State& st, Tile& t, const bf16x8_t (&qb)[kKK], int tok0, int L,
                                         int r, int n, float sl2, AfterK after_k, AfterV after_v) {
@@ -251,7 +255,61 @@ __device__ __forceinline__ void process(State& st, Tile& t, const bf16x8_t (&qb)
                  "+v"(ev[3][0]), "+v"(ev[3][1]), "+v"(od[0][0]), "+v"(od[0][1]), "+v"(od[1][0]), "+v"(od[1][1]),
                  "+v"(od[2][0]), "+v"(od[2][1]), "+v"(od[3][0]), "+v"(od[3][1]) : : "memory");
     after_v();
-    softmax_pv<G>(st, s, ev, od, tok0, L, r, n, sl2, 1.0f);
+
+    if (tok0 + kTileTokens > L) {   // last, partially filled tile (wave-uniform branch)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (tok0 + 4 * r + i >= L) {
+                s[i] = -INFINITY;
+                // stale slots may hold NaN; P is 0 there
+                const uint32_t keep = (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    ev[w][i >> 1] &= keep;
+                    od[w][i >> 1] &= keep;
+                }
+            }
+        }
+    }
+
+    // This row's max of head n.  The reference m is shared by the four rows
+    // (their P meet in one MFMA), so it only moves, to the block max over all
+    // rows, when some row would exceed it by more than 2^kLazy.
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * sl2;
+    const bool row_need = (n < G) && (mx > st.m + kLazy);
+    if (__builtin_amdgcn_ballot_w64(row_need)) {   // rare after the first block
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const bool need = (n < G) && (mx > st.m + kLazy);
+        const float m_new = need ? mx : st.m;
+        const float corr = need ? fast_exp2(st.m - m_new) : 1.0f;   // 0 when nothing was seen yet
+        st.l *= corr;
+        st.m = m_new;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float cj = __shfl(corr, 4 * r + j, kWave);   // head 4r + j (rows agree)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st.o[e][j] *= cj;
+        }
+    }
+    const float neg_ref = -safe_ref(st.m);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = n < G ? fast_exp2(fmaf(s[i], sl2, neg_ref)) : 0.0f;
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+
+    const uint32_t h01 = bf16_pair(p[0], p[1]);
+    const uint32_t h23 = bf16_pair(p[2], p[3]);
+    const uint32_t l01 = bf16_pair(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
+    const uint32_t l23 = bf16_pair(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    const bf16x8_t pa = as_operand(h01, h23, l01, l23);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        st.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pa, as_operand(ev[w][0], ev[w][1], ev[w][0], ev[w][1]), st.o[2 * w], 0, 0, 0);
+        st.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pa, as_operand(od[w][0], od[w][1], od[w][0], od[w][1]), st.o[2 * w + 1], 0, 0, 0);
+    }
 }
 
 // One FP8 tile: the codes are widened to bfloat16 operands (two per
@@ -405,6 +463,37 @@ __device__ __forceinline__ void append_into(Tile& t, const AppendRow& app, const
         if (4 * c.r + i == app.j) t.v[i] = nv;
 }
 
+// FP8 tiles: the new row is quantized here exactly as the pool-side waves
+// quantize it (fp8_store_row: lane l takes dims 2l and 2l + 1 of the bf16 row,
+// kw for K and vw for V, so both sides compute the same codes and scales),
+// then the codes move to the lanes that hold the row in the tile layout: K
+// dims 32r + 4m .. +3 (m = 0..7) from lane 16r + 2m, V dims 8n .. 8n+7 from
+// lanes 4n and 4n + 2.  When the row is row 0 of its block (j == 0) it alone
+// sets the block's scales, which then replace the scales read for the tile
+// (the pool side writes them concurrently).
+__device__ __forceinline__ void append_into_fp8(TileF8& t, const AppendRow& app, uint32_t kw, uint32_t vw,
+                                                const WalkCtx& c, float& kscale, float& vscale) {
+    if (app.j == 0) {   // wave-uniform
+        kscale = e4m3_block_scale(wave_max(abs_max2(kw, 0.0f)));
+        vscale = e4m3_block_scale(wave_max(abs_max2(vw, 0.0f)));
+    }
+    const uint32_t k2 = bf16x2_to_e4m3x2(kw, kscale);   // codes of dims 2l, 2l + 1
+    const uint32_t v2 = bf16x2_to_e4m3x2(vw, vscale);
+    const uint32_t k4 = k2 | ((uint32_t)__shfl_down((int)k2, 1, kWave) << 16);   // even lanes: dims 2l .. 2l+3
+    const uint32_t v4 = v2 | ((uint32_t)__shfl_down((int)v2, 1, kWave) << 16);
+    uint32_t kd[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) kd[m] = (uint32_t)__shfl((int)k4, 16 * c.r + 2 * m, kWave);
+    const uint2 vd = make_uint2((uint32_t)__shfl((int)v4, 4 * c.n, kWave), (uint32_t)__shfl((int)v4, 4 * c.n + 2, kWave));
+    if (c.n == app.j) {
+        t.k[0] = make_uint4(kd[0], kd[1], kd[2], kd[3]);
+        t.k[1] = make_uint4(kd[4], kd[5], kd[6], kd[7]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * c.r + i == app.j) t.v[i] = vd;
+}
+
 // Table entries of tile e (16 tokens) of a sequence whose table row is `row`:
 // for B >= 16 the block holding it (entry e / (B/16)); for B = 8 the two
 // blocks holding its halves (entries 2e and 2e + 1; the second may lie past
@@ -466,6 +555,7 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
         return (uint32_t)__builtin_amdgcn_readlane(tv, k) < c.num_blocks;
     };
     uint4 new_k[kKK], new_v;   // the appended row, loaded once the last chunk's first tiles are in flight
+    uint32_t new_kw = 0, new_vw = 0;   // FP8: dims 2l, 2l + 1 of the appended row
     for (k0 = 0; k0 < nk; k0 += 64) {
         const int nc = min(64, nk - k0);
         // the first chunk's entries may have been fetched ahead (entries past nc are never read)
@@ -492,8 +582,11 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
             load_v(tt[s], vt, c.v_off);
             asm volatile("" : : : "memory");
         }
-        if constexpr (!kFp8) {
-            if (app.active && k0 + 64 >= nk) {
+        if (app.active && k0 + 64 >= nk) {
+            if constexpr (kFp8) {
+                new_kw = reinterpret_cast<const uint32_t*>(app.krow)[c.lane];
+                new_vw = reinterpret_cast<const uint32_t*>(app.vrow)[c.lane];
+            } else {
 #pragma unroll
                 for (int kk = 0; kk < kKK; ++kk) new_k[kk] = app.krow[4 * kk + c.r];
                 new_v = app.vrow[c.n];
@@ -511,7 +604,11 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
                 const int tok = k + s < nc ? (b0 + (k0 + k + s) * stride) * kTileTokens : L;
                 if constexpr (kFp8) {
                     const int ks = min(k + s, nc - 1);
-                    process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2, readlane_f(ks_l, ks), readlane_f(vs_l, ks),
+                    float ksc = readlane_f(ks_l, ks), vsc = readlane_f(vs_l, ks);
+                    if (app.active && tok == app.tok0 && row_in_pool(tv0, tv1, k + s, app.j)) {
+                        append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc, vsc);
+                    }
+                    process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2, ksc, vsc,
                                [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off); });
                 } else {
                     // wave-uniform: the tile holding the new token; a table entry outside
@@ -662,13 +759,40 @@ __device__ __forceinline__ void append_scatter_waves(const DecodeArgs& a, int64_
     }
 }
 
+// The same for FP8 pools: one (sequence, {K,V}, KV head) row per wave and
+// step, quantized with its block's scale; a row at position 0 of its block
+// sets that scale first (fp8_store_row).
+__device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x, int64_t nx) {
+    const int lane = threadIdx.x;
+    const int H = a.num_kv_heads;
+    const int64_t items = (int64_t)a.num_seqs * 2 * H;
+    for (int64_t item = x; item < items; item += nx) {
+        const int64_t i = item / (2 * H);
+        const int which = (int)((item / H) & 1);
+        const int h = (int)(item - (i * 2 + which) * H);
+        const int L = clamp_len(a.lens[i], a.max_context);
+        if (L == 0) continue;
+        const int pos = L - 1;
+        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / kTileTokens];
+        if (block < 0 || block >= a.num_blocks) continue;
+        const int j = pos % kTileTokens;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(which == 0 ? a.k_append : a.v_append) +
+                              (i * H + h) * (kD / 2);
+        uint16_t* dst = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(which == 0 ? a.k_layer : a.v_layer)) +
+                        ((block * H + h) * kTileTokens + j) * (kD / 2);
+        float* scale = const_cast<float*>(which == 0 ? a.k_scale : a.v_scale) + block * H + h;
+        fp8_store_row(src, dst, scale, j == 0, lane);
+    }
+}
+
 template <int G, bool kAnyB, bool kFp8>
 __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int64_t W = a.workers;
     const int64_t w = blockIdx.x;
-    if (w >= W) {   // decode append: the pool side (bf16 pools; FP8 appends run before the launch)
-        if constexpr (!kFp8) append_scatter_waves(a, w - W, (int64_t)gridDim.x - W);
+    if (w >= W) {   // decode append: the pool side
+        if constexpr (kFp8) append_fp8_waves(a, w - W, (int64_t)gridDim.x - W);
+        else append_scatter_waves(a, w - W, (int64_t)gridDim.x - W);
         return;
     }
     const int S = a.num_seqs;
@@ -745,7 +869,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         init_state(st);
         // the piece that ends with the sequence's last block takes the appended row
         AppendRow app;
-        app.active = !kFp8 && a.k_append != nullptr && b + n_here == nblk;
+        app.active = a.k_append != nullptr && b + n_here == nblk;
         app.tok0 = (nblk - 1) * kTileTokens;
         app.j = (L - 1) % kTileTokens;
         app.krow = reinterpret_cast<const uint4*>(a.k_append) + ((size_t)seq * Hkv + kv) * kRC;
@@ -981,14 +1105,13 @@ template <bool kFp8>
 hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
     DecodeArgs a = a_in;
     a.workers = workers;
-    // decode append into a bf16 pool: a few extra single-wave workgroups store
-    // the new rows (about 8 chunks per lane)
+    // decode append: a few extra single-wave workgroups store the new rows
+    // (bf16: about 8 chunks per lane; FP8: about 4 rows per wave)
     int64_t extra = 0;
-    if (kFp8) {
-        a.k_append = a.v_append = nullptr;
-    } else if (a.k_append) {
-        const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * kRC;
-        extra = (items + 8 * kWave - 1) / (8 * kWave);
+    if (a.k_append) {
+        const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * (kFp8 ? 1 : kRC);
+        const int64_t per_wave = kFp8 ? 4 : 8 * kWave;
+        extra = (items + per_wave - 1) / per_wave;
         extra = extra < 1 ? 1 : (extra > 256 ? 256 : extra);
     }
     dim3 grid((unsigned)(workers + extra));

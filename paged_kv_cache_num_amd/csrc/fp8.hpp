@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.hpp"
+
 namespace kvp {
 
 constexpr float kE4M3Max = 448.0f;
@@ -28,23 +30,22 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 // the format's bit fields: above 2^-6 the fp32 exponent is re-biased and the
 // mantissa rounded from 23 to 3 bits (a carry out of the mantissa moves to
 // the next binade, which is the next code); below 2^-6 the values are the
-// multiples of 2^-9, so the code is x * 2^9 rounded to an integer.
+// multiples of 2^-9, so the code is x * 2^9 rounded to an integer.  Both
+// candidates are computed and selected, without branches.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
     const uint32_t u = __float_as_uint(x);
     const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return 0x7Fu;               // NaN
-    if (a >= 0x43E00000u) return sign | 0x7Eu;       // >= 448
-    if (a < 0x3C800000u) {                           // < 2^-6: subnormal codes 0..8
-        const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);   // exact scaling, then ties to even
-        return sign | (uint32_t)q;
-    }
-    const uint32_t e = (a >> 23) - 120u;              // E4M3 biased exponent, 1..15
+    // below 2^-6: subnormal codes 0..8 (the input clamped so the conversion stays in range)
+    const uint32_t sub = (uint32_t)__builtin_rintf(fminf(__uint_as_float(a), 0.015625f) * 512.0f);
+    // from 2^-6: biased exponent 1..15 and three mantissa bits, round to nearest even
     const uint32_t m = a & 0x7FFFFFu;
-    uint32_t code = (e << 3) | (m >> 20);
-    const uint32_t rest = m & 0xFFFFFu;               // the 20 dropped mantissa bits
+    const uint32_t rest = m & 0xFFFFFu;                // the 20 dropped mantissa bits
+    uint32_t code = (((a >> 23) - 120u) << 3) | (m >> 20);
     code += (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) ? 1u : 0u;
-    return sign | code;
+    uint32_t r = a < 0x3C800000u ? sub : code;         // 2^-6
+    r = a >= 0x43E00000u ? 0x7Eu : r;                  // >= 448
+    return a > 0x7F800000u ? 0x7Fu : (sign | r);       // NaN
 }
 
 // Quantize a packed bfloat16 pair with a block scale: two codes in the low 16
@@ -57,5 +58,33 @@ __device__ __forceinline__ uint32_t bf16x2_to_e4m3x2(uint32_t w, float scale) {
 
 // Block scale from the largest magnitude of the rows that set it.
 __device__ __forceinline__ float e4m3_block_scale(float amax) { return amax > 0.0f ? amax / kE4M3Max : 1.0f; }
+
+// max(m, |lo|, |hi|) of a packed bfloat16 pair.
+__device__ __forceinline__ float abs_max2(uint32_t w, float m) {
+    return fmaxf(m, fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w))));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+    return x;
+}
+
+// One wave writes one new head row (128 bf16 values, lane l: dims 2l and
+// 2l + 1) into an FP8 pool row `dst` (128 codes).  When the row is row 0 of
+// its block (`opens`), it alone sets the block's scale first; otherwise the
+// stored scale is used.
+__device__ __forceinline__ void fp8_store_row(const uint32_t* __restrict__ src, uint16_t* dst, float* scale,
+                                              bool opens, int lane) {
+    const uint32_t w = src[lane];
+    float s;
+    if (opens) {
+        s = e4m3_block_scale(wave_max(abs_max2(w, 0.0f)));
+        if (lane == 0) *scale = s;
+    } else {
+        s = *scale;
+    }
+    dst[lane] = (uint16_t)bf16x2_to_e4m3x2(w, s);
+}
 
 }  // namespace kvp

@@ -38,16 +38,6 @@ __device__ __forceinline__ int64_t readlane64_i(int64_t x, int src) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ float abs_max2(uint32_t w, float m) {
-    return fmaxf(m, fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w))));
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-    return x;
-}
-
 // One wave per (16-token chunk, KV head): grid (chunks, H), grid-stride over
 // the chunks, so a wave usually has at most one block to open.  The wave finds
 // the tokens of its chunk that write row 0 of a block, lists the block's
@@ -179,17 +169,10 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void fp8_append_kernel(Append
     const int64_t block = a.tables[seq * a.max_blocks + pos / a.block_size];
     if (block < 0 || block >= a.num_blocks) return;
     const int j = pos % a.block_size;
-    const uint32_t w = reinterpret_cast<const uint32_t*>(which == 0 ? a.k_new : a.v_new)[(seq * H + h) * kRowWords + lane];
-    float* sc = (which == 0 ? a.k_scale : a.v_scale) + block * H + h;
-    float s;
-    if (j == 0) {
-        s = e4m3_block_scale(wave_max(abs_max2(w, 0.0f)));
-        if (lane == 0) *sc = s;
-    } else {
-        s = *sc;
-    }
-    uint16_t* dst = reinterpret_cast<uint16_t*>(which == 0 ? a.k_layer : a.v_layer);
-    dst[((block * H + h) * a.block_size + j) * (kD8 / 2) + lane] = (uint16_t)bf16x2_to_e4m3x2(w, s);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(which == 0 ? a.k_new : a.v_new) + (seq * H + h) * kRowWords;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(which == 0 ? a.k_layer : a.v_layer) +
+                    ((block * H + h) * a.block_size + j) * (kD8 / 2);
+    fp8_store_row(src, dst, (which == 0 ? a.k_scale : a.v_scale) + block * H + h, j == 0, lane);
 }
 
 }  // namespace

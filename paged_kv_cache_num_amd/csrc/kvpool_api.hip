@@ -411,11 +411,14 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
         a.v_scale = pool->v_scale + (uint64_t)layer * pool->scale_layer;
     }
     hipError_t e;
-    if (plan.mode == Mode::kBalanced && !fp8) {
-        // the worker that owns each (sequence, KV head)'s last block writes and uses the new row
+    if (plan.mode == Mode::kBalanced) {
+        // the worker that owns each (sequence, KV head)'s last block uses the new row
+        // (FP8: quantized in registers); extra waves of the same launch store it
         a.k_append = k_append;
         a.v_append = v_append;
-        e = kvp::launch_decode_bf16_streamk(a, num_q_heads / d.num_kv_heads, plan.workers, static_cast<hipStream_t>(stream));
+        const int group = num_q_heads / d.num_kv_heads;
+        e = fp8 ? kvp::launch_decode_fp8_streamk(a, group, plan.workers, static_cast<hipStream_t>(stream))
+                : kvp::launch_decode_bf16_streamk(a, group, plan.workers, static_cast<hipStream_t>(stream));
     } else {
         // the new rows first (FP8: quantized, with the scale of a block they open), then the decode
         e = hipSuccess;
@@ -443,13 +446,7 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
                 e = kvp::launch_append_scatter(w, static_cast<hipStream_t>(stream));
             }
         }
-        if (e == hipSuccess) {
-            if (plan.mode == Mode::kBalanced)
-                e = kvp::launch_decode_fp8_streamk(a, num_q_heads / d.num_kv_heads, plan.workers,
-                                                   static_cast<hipStream_t>(stream));
-            else
-                e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
-        }
+        if (e == hipSuccess) e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
     }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();
