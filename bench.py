@@ -260,6 +260,7 @@ def main(argv=None):
     ap.add_argument("--no-identity", action="store_true",
                     help="skip timing the same batch with contiguous (identity-like) block tables")
     ap.add_argument("--no-copy-blocks", action="store_true", help="skip timing copy-on-write block copies")
+    ap.add_argument("--no-swap", action="store_true", help="skip timing swap of the batch's blocks to host and back")
     ap.add_argument("--table-walk-probe", type=int, default=0, metavar="N",
                     help="also run the table-walk probe N times in each workgroup ordering (for counter runs)")
     ap.add_argument("--no-fuse", action="store_true",
@@ -506,6 +507,41 @@ def main(argv=None):
         del cpool, pairs
         torch.cuda.synchronize()
 
+    # Swap (kv_swap_out / kv_swap_in): every block the batch's tables name, out
+    # to pinned host memory and back into the same blocks; bytes = the pool
+    # bytes of those blocks each way.  Reference: one DMA copy of the same
+    # byte count between a contiguous device buffer and pinned host memory.
+    swap = None
+    if not args.no_swap:
+        nb = [-(-int(L) // wl.block_size) for L in wl.context_lens]
+        blist = np.unique(np.concatenate([wl.block_tables[i, :n] for i, n in enumerate(nb)])).astype(np.int32)
+        blocks_dev = torch.from_numpy(blist).cuda()
+        nbytes_swap = step.pool.swap_bytes(blist.size)
+        host = torch.empty(nbytes_swap, dtype=torch.uint8).pin_memory()
+        dev = torch.empty(nbytes_swap, dtype=torch.uint8, device="cuda")
+        times = {"out": [], "in": [], "dma_d2h": [], "dma_h2d": []}
+        for i in range(3 + 10):
+            for key, fn in (("out", lambda: step.pool.swap_out(blocks_dev, host)),
+                            ("in", lambda: step.pool.swap_in(blocks_dev, host)),
+                            ("dma_d2h", lambda: host.copy_(dev, non_blocking=True)),
+                            ("dma_h2d", lambda: dev.copy_(host, non_blocking=True))):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                b.synchronize()
+                if i >= 3:
+                    times[key].append(a.elapsed_time(b) * 1e3)
+        swap = {"blocks": int(blist.size), "bytes_each_way": nbytes_swap}
+        for key, us in times.items():
+            p50 = percentile(us, 0.5)
+            swap[f"{key}_us_p50"] = round(p50, 1)
+            swap[f"{key}_gbps"] = round(nbytes_swap / (p50 * 1e-6) / 1e9, 2)
+        print(f"bench: swap {nbytes_swap / 2**20:.0f} MiB: out {swap['out_gbps']} GB/s, in {swap['in_gbps']} GB/s "
+              f"(DMA {swap['dma_d2h_gbps']} / {swap['dma_h2d_gbps']})", file=sys.stderr, flush=True)
+        del host, dev, blocks_dev
+        torch.cuda.synchronize()
+
     table_walk = None
     if args.table_walk_probe:
         from paged_kv_cache_num_amd import probe_table_walk
@@ -566,6 +602,7 @@ def main(argv=None):
         "identity_tables": identity,
         "table_walk_probe": table_walk,
         "copy_blocks": copy,
+        "swap": swap,
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)

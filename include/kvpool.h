@@ -204,6 +204,42 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
 kv_status kv_copy_blocks(kv_pool_t pool, const int32_t* block_pairs, int32_t num_pairs, void* stream);
 
 /*
+ * Swap to and from host memory ([KVC] "Reclaiming memory: swap versus
+ * recompute": a preempted sequence's blocks are copied to pinned host memory
+ * and back on resume, twice its KV bytes over the host link; [PIF] "05
+ * Preemption and the scheduler contract").  Freeing the blocks in between and
+ * choosing victims is the block manager's host bookkeeping, not done here.
+ *
+ * The host buffer holds one record of kv_swap_bytes(pool, 1, ...) bytes per
+ * listed block, in list order: for each layer, the block's K run then its V
+ * run (H_kv * B * D * e bytes each, the pool's bytes unchanged); for FP8 pools
+ * then, for each layer, the block's K scales then its V scales (H_kv fp32
+ * each); zero padding to a multiple of 16 bytes.
+ *
+ *   kv_swap_bytes: host bytes for num_blocks blocks (num_blocks >= 0).
+ *   kv_swap_out:   GPU step: copy blocks[i] (device int32 list, 4-byte aligned)
+ *                  of every layer to record i of host_buf.
+ *   kv_swap_in:    GPU step: copy record i of host_buf to block blocks[i] of
+ *                  every layer (the blocks may differ from those swapped out;
+ *                  the caller then repoints the table entries).
+ * host_buf must be pinned host memory that the device can address
+ * (hipHostMalloc; torch's pin_memory), 16-byte aligned, with host_bytes at
+ * least kv_swap_bytes(pool, num_blocks); the kernels read and write it
+ * directly over the host link, one launch per call, and the caller keeps it
+ * alive until the stream has passed the call.  A list entry outside
+ * [0, num_blocks) is skipped (its record is left as it was, or not read).
+ * Precondition for kv_swap_in: no block listed twice.  Bit-exact both ways.
+ * Errors: KV_ERR_INVALID_ARGUMENT (null or misaligned pointer, negative count,
+ * host buffer too small, not pinned or without a device mapping), KV_ERR_HIP.
+ * num_blocks == 0 queues nothing.
+ */
+kv_status kv_swap_bytes(kv_pool_t pool, int32_t num_blocks, uint64_t* bytes);
+kv_status kv_swap_out(kv_pool_t pool, const int32_t* blocks, int32_t num_blocks, void* host_buf,
+                      uint64_t host_bytes, void* stream);
+kv_status kv_swap_in(kv_pool_t pool, const int32_t* blocks, int32_t num_blocks, const void* host_buf,
+                     uint64_t host_bytes, void* stream);
+
+/*
  * Workspace needed by paged_attention_decode for this shape and mode (see
  * partition_size below).  Zero when no workspace is used.  With partitions it
  * holds one fp32 running max, sum and unnormalised output per (sequence,

@@ -178,3 +178,75 @@ def run_step(wl, scale: Optional[float] = None, threads: Optional[int] = None,
         out = paged_attention(wl.q[seqs], kp, vp, wl.dtype, wl.block_tables[seqs],
                               wl.context_lens[seqs], scale, threads)
     return dict(slots=slots, k_pool=kp, v_pool=vp, out=out)
+
+
+def swap_record_bytes(num_layers: int, run_bytes: int, num_kv_heads: int = 0, fp8: bool = False) -> int:
+    """Host bytes of one swapped block: its K and V runs of every layer, then
+    (FP8) its K and V scales of every layer, padded to a multiple of 16."""
+    rec = 2 * num_layers * run_bytes + (2 * num_layers * num_kv_heads * 4 if fp8 else 0)
+    return -(-rec // 16) * 16
+
+
+def swap_out(k_pool: np.ndarray, v_pool: np.ndarray, blocks, k_scale=None, v_scale=None) -> np.ndarray:
+    """Swap to host (aicassindra.com "GPU paged KV cache", "Reclaiming memory:
+    swap versus recompute"; "PagedAttention, Internals First", "05 Preemption
+    and the scheduler contract": the victim's blocks are copied to host memory
+    and back on resume), plain numpy.
+
+    Pools are ``[layers][N][Hkv][B][D]`` (any dtype), FP8 scales
+    ``[layers][N][Hkv]`` float32.  Returns the host buffer as bytes: one record
+    per listed block, in list order, holding for each layer the block's K then
+    V bytes, then for each layer its K then V scales, zero-padded to 16 bytes.
+    A listed index outside the pool leaves its record zero.
+    """
+    L, N = k_pool.shape[0], k_pool.shape[1]
+    fp8 = k_scale is not None
+    H = k_pool.shape[2]
+    run = k_pool[0, 0].nbytes
+    rec = swap_record_bytes(L, run, H, fp8)
+    out = np.zeros((len(blocks), rec), dtype=np.uint8)
+    for i, b in enumerate(blocks):
+        b = int(b)
+        if not 0 <= b < N:
+            continue
+        parts = []
+        for layer in range(L):
+            parts += [k_pool[layer, b].tobytes(), v_pool[layer, b].tobytes()]
+        if fp8:
+            for layer in range(L):
+                parts += [np.asarray(k_scale[layer, b], dtype=np.float32).tobytes(),
+                          np.asarray(v_scale[layer, b], dtype=np.float32).tobytes()]
+        data = b"".join(parts)
+        out[i, :len(data)] = np.frombuffer(data, dtype=np.uint8)
+    return out.reshape(-1)
+
+
+def swap_in(k_pool: np.ndarray, v_pool: np.ndarray, blocks, host: np.ndarray, k_scale=None, v_scale=None):
+    """Inverse of swap_out: record i of ``host`` goes back to block ``blocks[i]``
+    of every layer.  Returns new pools (and new scales for FP8 pools); indices
+    outside the pool are skipped."""
+    kp, vp = k_pool.copy(), v_pool.copy()
+    fp8 = k_scale is not None
+    ks = k_scale.copy() if fp8 else None
+    vs = v_scale.copy() if fp8 else None
+    L, N, H = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    run = k_pool[0, 0].nbytes
+    rec = swap_record_bytes(L, run, H, fp8)
+    host = np.asarray(host, dtype=np.uint8).reshape(-1, rec)
+    tile = k_pool.shape[2:]
+    for i, b in enumerate(blocks):
+        b = int(b)
+        if not 0 <= b < N:
+            continue
+        r = host[i]
+        pos = 0
+        for layer in range(L):
+            kp[layer, b] = np.frombuffer(r[pos:pos + run].tobytes(), dtype=k_pool.dtype).reshape(tile)
+            vp[layer, b] = np.frombuffer(r[pos + run:pos + 2 * run].tobytes(), dtype=v_pool.dtype).reshape(tile)
+            pos += 2 * run
+        if fp8:
+            for layer in range(L):
+                ks[layer, b] = np.frombuffer(r[pos:pos + 4 * H].tobytes(), dtype=np.float32)
+                vs[layer, b] = np.frombuffer(r[pos + 4 * H:pos + 8 * H].tobytes(), dtype=np.float32)
+                pos += 8 * H
+    return (kp, vp, ks, vs) if fp8 else (kp, vp)

@@ -315,6 +315,89 @@ kv_status kv_copy_blocks(kv_pool_t pool, const int32_t* block_pairs, int32_t num
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Host record of one swapped block: the 2 * layers runs, then FP8 scales, padded to 16 bytes.
+uint64_t swap_record_bytes(const kv_pool* p) {
+    const kv_pool_desc& d = p->desc;
+    const uint64_t run = (uint64_t)d.num_kv_heads * d.block_size * d.head_dim * p->elem_bytes;
+    uint64_t rec = 2ull * d.num_layers * run;
+    if (p->k_scale) rec += 2ull * d.num_layers * d.num_kv_heads * 4u;
+    return round_up(rec, 16u);
+}
+
+kv_status swap_impl(kv_pool_t pool, const int32_t* blocks, int32_t num_blocks, const void* host, uint64_t host_bytes,
+                    bool out, void* stream) {
+    const char* what = out ? "kv_swap_out" : "kv_swap_in";
+    if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "%s: pool is NULL", what);
+    if (num_blocks < 0) return fail(KV_ERR_INVALID_ARGUMENT, "%s: num_blocks %d < 0", what, num_blocks);
+    if (num_blocks == 0) return ok();
+    if (!blocks || (reinterpret_cast<uintptr_t>(blocks) & 3u))
+        return fail(KV_ERR_INVALID_ARGUMENT, "%s: blocks must be a non-NULL, 4-byte aligned device pointer", what);
+    if (!host || !aligned16(host)) return fail(KV_ERR_INVALID_ARGUMENT, "%s: host buffer must be non-NULL and 16-byte aligned", what);
+    const uint64_t rec = swap_record_bytes(pool);
+    if (host_bytes < rec * (uint64_t)num_blocks)
+        return fail(KV_ERR_INVALID_ARGUMENT, "%s: host buffer of %llu bytes, %llu needed", what,
+                    (unsigned long long)host_bytes, (unsigned long long)(rec * (uint64_t)num_blocks));
+    // the kernels address the host buffer through its device mapping: it must be pinned host memory
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof attr);
+    hipError_t e = hipPointerGetAttributes(&attr, host);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(KV_ERR_INVALID_ARGUMENT, "%s: the host buffer is not pinned host memory (hipHostMalloc)", what);
+    }
+    void* mapped = nullptr;
+    e = hipHostGetDevicePointer(&mapped, const_cast<void*>(host), 0);
+    if (e != hipSuccess || !mapped) {
+        (void)hipGetLastError();
+        return fail(KV_ERR_INVALID_ARGUMENT, "%s: the host buffer has no device mapping", what);
+    }
+    const kv_pool_desc& d = pool->desc;
+    kvp::SwapArgs a;
+    memset(&a, 0, sizeof a);
+    a.k_base = pool->k_base;
+    a.v_base = pool->v_base;
+    a.layer_bytes = pool->layer_bytes;
+    a.run_bytes = (uint64_t)d.num_kv_heads * d.block_size * d.head_dim * pool->elem_bytes;
+    a.k_scale = pool->k_scale;
+    a.v_scale = pool->v_scale;
+    a.blocks = blocks;
+    a.host = static_cast<char*>(mapped);
+    a.block_bytes = rec;
+    a.num_list = num_blocks;
+    a.num_layers = d.num_layers;
+    a.num_blocks = d.num_blocks;
+    a.num_kv_heads = d.num_kv_heads;
+    e = kvp::launch_swap(a, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, what);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_swap_bytes(kv_pool_t pool, int32_t num_blocks, uint64_t* bytes) {
+    if (!pool || !bytes) return fail(KV_ERR_INVALID_ARGUMENT, "NULL argument");
+    *bytes = 0;
+    if (num_blocks < 0) return fail(KV_ERR_INVALID_ARGUMENT, "num_blocks %d < 0", num_blocks);
+    *bytes = swap_record_bytes(pool) * (uint64_t)num_blocks;
+    return ok();
+}
+
+kv_status kv_swap_out(kv_pool_t pool, const int32_t* blocks, int32_t num_blocks, void* host, uint64_t host_bytes,
+                      void* stream) {
+    return swap_impl(pool, blocks, num_blocks, host, host_bytes, true, stream);
+}
+
+kv_status kv_swap_in(kv_pool_t pool, const int32_t* blocks, int32_t num_blocks, const void* host, uint64_t host_bytes,
+                     void* stream) {
+    return swap_impl(pool, blocks, num_blocks, host, host_bytes, false, stream);
+}
+
 kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int32_t num_q_heads,
                                           int32_t max_context_len, int32_t partition_size, uint64_t* bytes) {
     if (!pool || !bytes) return fail(KV_ERR_INVALID_ARGUMENT, "NULL argument");

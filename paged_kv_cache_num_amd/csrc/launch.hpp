@@ -73,6 +73,26 @@ struct CopyBlocksArgs {
 
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 
+// Swap: blocks[0..num_list) of every layer (and FP8 scales) to / from a host
+// buffer the device can address, block_bytes per listed block.
+struct SwapArgs {
+    char* k_base;                // layer 0 of the K tensor
+    char* v_base;
+    uint64_t layer_bytes;
+    uint64_t run_bytes;          // one (layer, block) run of one tensor: H_kv * B * D * e
+    float* k_scale;              // FP8: layer 0 of the scale tensors, else null
+    float* v_scale;
+    const int32_t* blocks;       // device, [num_list]
+    char* host;                  // device address of the host buffer
+    uint64_t block_bytes;        // host record per listed block (multiple of 16)
+    int32_t num_list;
+    int32_t num_layers;
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+};
+
+hipError_t launch_swap(const SwapArgs& a, bool out, hipStream_t stream);
+
 struct DecodeArgs {
     const void* k_layer;
     const void* v_layer;

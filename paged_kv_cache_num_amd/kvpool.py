@@ -32,7 +32,7 @@ EXPORTED = (
     "kv_pool_bytes", "kv_pool_scale_bytes", "kv_pool_create", "kv_pool_create_fp8", "kv_pool_destroy",
     "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
-    "paged_attention_decode_append", "kv_copy_blocks",
+    "paged_attention_decode_append", "kv_copy_blocks", "kv_swap_bytes", "kv_swap_out", "kv_swap_in",
     "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read", "kv_probe_table_walk",
     "kv_probe_e4m3_to_bf16", "kv_probe_f32_to_e4m3",
 )
@@ -86,6 +86,12 @@ def _load():
     lib.paged_attention_decode.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32, vp, u64, vp]
     lib.kv_copy_blocks.restype = ctypes.c_int
     lib.kv_copy_blocks.argtypes = [vp, vp, i32, vp]
+    lib.kv_swap_bytes.restype = ctypes.c_int
+    lib.kv_swap_bytes.argtypes = [vp, i32, P(u64)]
+    lib.kv_swap_out.restype = ctypes.c_int
+    lib.kv_swap_out.argtypes = [vp, vp, i32, vp, u64, vp]
+    lib.kv_swap_in.restype = ctypes.c_int
+    lib.kv_swap_in.argtypes = [vp, vp, i32, vp, u64, vp]
     lib.paged_attention_decode_append.restype = ctypes.c_int
     lib.paged_attention_decode_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32,
                                                   vp, u64, vp]
@@ -306,6 +312,31 @@ class KVPool:
         n = int(block_pairs.shape[0])
         ptr = _dev_ptr(block_pairs, "block_pairs", torch.int32) if n else None
         _check(lib.kv_copy_blocks(self.handle, ptr, n, _stream_handle(stream)), "kv_copy_blocks")
+
+    def swap_bytes(self, num_blocks: int) -> int:
+        """Host bytes that swapping out ``num_blocks`` blocks takes."""
+        out = ctypes.c_uint64(0)
+        _check(lib.kv_swap_bytes(self.handle, int(num_blocks), ctypes.byref(out)), "kv_swap_bytes")
+        return int(out.value)
+
+    def _swap(self, fn, name, blocks, host, stream):
+        import torch
+        if blocks.dim() != 1:
+            raise ValueError("blocks must be a 1-D int32 device tensor")
+        if not isinstance(host, torch.Tensor) or host.is_cuda or not host.is_contiguous():
+            raise TypeError("host buffer must be a contiguous host tensor (pinned: pin_memory=True)")
+        n = int(blocks.shape[0])
+        bptr = _dev_ptr(blocks, "blocks", torch.int32) if n else None
+        _check(fn(self.handle, bptr, n, host.data_ptr() if host.numel() else None,
+                  host.numel() * host.element_size(), _stream_handle(stream)), name)
+
+    def swap_out(self, blocks, host, stream=None) -> None:
+        """Copy the listed blocks (every layer, FP8 scales too) into pinned host memory."""
+        self._swap(lib.kv_swap_out, "kv_swap_out", blocks, host, stream)
+
+    def swap_in(self, blocks, host, stream=None) -> None:
+        """Copy host records back into the listed blocks (every layer)."""
+        self._swap(lib.kv_swap_in, "kv_swap_in", blocks, host, stream)
 
     def paged_attention_decode_append(self, layer: int, out, q, k_new, v_new, block_tables, context_lens, *,
                                       scale: float, max_context_len: int, partition_size: int = 0,

@@ -351,3 +351,60 @@ def test_fp8_probe_argument_checks():
     assert L.kv_probe_e4m3_to_bf16(None, None, 0, None) == K.KV_OK
     assert L.kv_probe_f32_to_e4m3(0x1002, 0x2000, 4, None) == K.KV_ERR_INVALID_ARGUMENT
     assert L.kv_probe_f32_to_e4m3(None, None, 0, None) == K.KV_OK
+
+
+# -------------------------------------------------------------------- swap --
+
+def test_swap_bytes_reproduce_the_pages_figures():
+    """A 4K-token 70B-class sequence swaps 1.25 GiB each way; a block of the
+    8B-class pool is 2 MiB; at 25 GB/s a trip takes about 50 ms."""
+    g = GOLDEN["swap_4k_70b"]
+    d = _desc(num_layers=g["layers"], num_blocks=300, block_size=g["block_size"], num_kv_heads=g["kv_heads"],
+              head_dim=g["head_dim"], dtype="bf16")
+    h = ctypes.c_void_p(0)
+    assert K.lib.kv_pool_create(ctypes.byref(d), 0x10000, 0x20000, ctypes.byref(h)) == K.KV_OK
+    out = ctypes.c_uint64(0)
+    assert K.lib.kv_swap_bytes(h, g["tokens"] // g["block_size"], ctypes.byref(out)) == K.KV_OK
+    assert out.value == g["expected_gib_each_way"] * 2**30
+    seconds = out.value / (g["link_gb_per_s"] * 1e9)
+    assert abs(seconds * 1e3 - g["expected_ms_each_way"]) / g["expected_ms_each_way"] < 0.1
+    K.lib.kv_pool_destroy(h)
+    b = GOLDEN["kv_bytes_per_token_8b"]
+    d8 = _desc(num_layers=b["layers"], num_blocks=10, block_size=b["block_size"], num_kv_heads=b["kv_heads"],
+               head_dim=b["head_dim"], dtype="bf16")
+    assert K.lib.kv_pool_create(ctypes.byref(d8), 0x10000, 0x20000, ctypes.byref(h)) == K.KV_OK
+    assert K.lib.kv_swap_bytes(h, 1, ctypes.byref(out)) == K.KV_OK
+    assert out.value == b["expected_block_bytes"]
+    K.lib.kv_pool_destroy(h)
+
+
+def test_swap_bytes_match_the_oracle_record_for_fp8_pools():
+    for layers, heads in [(1, 1), (3, 8), (2, 3)]:
+        st, h = _fp8_pool(num_layers=layers, num_kv_heads=heads)
+        assert st == K.KV_OK
+        out = ctypes.c_uint64(0)
+        assert K.lib.kv_swap_bytes(h, 5, ctypes.byref(out)) == K.KV_OK
+        assert out.value == 5 * oracle.swap_record_bytes(layers, heads * 16 * 128, heads, fp8=True)
+        assert out.value % 16 == 0
+        K.lib.kv_pool_destroy(h)
+
+
+def test_swap_argument_checks_return_before_any_launch():
+    st, h = _pool(head_dim=128, dtype="bf16")
+    L = K.lib
+    need = ctypes.c_uint64(0)
+    assert L.kv_swap_bytes(h, 4, ctypes.byref(need)) == K.KV_OK
+    buf = np.zeros(need.value + 16, dtype=np.uint8)
+    host = (buf.ctypes.data + 15) // 16 * 16
+    for fn in (L.kv_swap_out, L.kv_swap_in):
+        assert fn(None, 0x1000, 4, host, need.value, None) == K.KV_ERR_INVALID_ARGUMENT
+        assert fn(h, 0x1000, -1, host, need.value, None) == K.KV_ERR_INVALID_ARGUMENT
+        assert fn(h, None, 4, host, need.value, None) == K.KV_ERR_INVALID_ARGUMENT
+        assert fn(h, 0x1002, 4, host, need.value, None) == K.KV_ERR_INVALID_ARGUMENT
+        assert fn(h, 0x1000, 4, host + 8, need.value, None) == K.KV_ERR_INVALID_ARGUMENT
+        assert fn(h, 0x1000, 4, host, need.value - 16, None) == K.KV_ERR_INVALID_ARGUMENT
+        # ordinary (pageable) host memory is refused: the kernels need a pinned, mapped buffer
+        assert fn(h, 0x1000, 4, host, need.value, None) == K.KV_ERR_INVALID_ARGUMENT
+        assert b"pinned" in L.kv_last_error_message() or b"mapping" in L.kv_last_error_message()
+        assert fn(h, None, 0, None, 0, None) == K.KV_OK
+    K.lib.kv_pool_destroy(h)
