@@ -151,7 +151,7 @@ def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, config: str, p
             raise SystemExit(f"no copy-probe dispatch in {path}")
         factor = known / (statistics.median(copy) * 1024.0)
         attn = {name: statistics.mean(vs) for name, vs in k.items()
-                if any(m in name for m in ATTN_KERNEL_MARKERS)}
+                if "kvp::" in name and any(m in name for m in ATTN_KERNEL_MARKERS)}
         res[counter] = {"factor": round(factor, 4),
                         "kib_per_dispatch": {n.replace("(anonymous namespace)::", "").split("(")[0][-60:]: round(v, 1)
                                              for n, v in attn.items()},
