@@ -961,7 +961,10 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     const int kv = blockIdx.x;
     const int seq = blockIdx.y;
     const int lane = threadIdx.x;
+    // the length and the two prefix sums are independent: one memory round trip for all three
     const int L = clamp_len(a.lens[seq], a.max_context);
+    const int64_t T = a.ws_prefix[a.num_seqs];
+    const int64_t first_tile = a.ws_prefix[seq];
     uint32_t* out = reinterpret_cast<uint32_t*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * (kD / 2);
     if (L == 0) {
 #pragma unroll
@@ -969,9 +972,8 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
         return;
     }
     const int nblk = (L + kTileTokens - 1) / kTileTokens;   // 16-token tiles
-    const int64_t T = a.ws_prefix[a.num_seqs];
     const int64_t W = num_workers;
-    const int64_t s0 = a.ws_prefix[seq] + (int64_t)kv * nblk;
+    const int64_t s0 = first_tile + (int64_t)kv * nblk;
     const int64_t w0 = worker_of(s0, T, W);
     const int64_t w1 = worker_of(s0 + nblk - 1, T, W);
     if (w0 == w1) return;   // written by its worker
@@ -1057,37 +1059,42 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     }
 }
 
-template <int G>
+template <int G, bool kFp8>
 const void* streamk_kernel_ptr() {
-    return reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, true, false>);
+    return kFp8 ? reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, false, true>)
+                : reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, true, false>);
 }
 
 }  // namespace
 
-int streamk_workers(int group) {
-    // One worker wave per SIMD (four per compute unit).  With two resident
-    // waves per SIMD the older one wins the SIMD's issue arbitration: equal
-    // slices then finish about 1.5x apart, and the second half of the kernel
-    // runs with one wave per SIMD anyway.  One wave per SIMD keeps all
+int streamk_workers(int group, bool fp8) {
+    // bf16 tiles: one worker wave per SIMD (four per compute unit).  With two
+    // resident waves per SIMD the older one wins the SIMD's issue arbitration:
+    // equal slices then finish about 1.5x apart, and the second half of the
+    // kernel runs with one wave per SIMD anyway.  One wave per SIMD keeps all
     // workers at the same pace (timed per worker with the chip's realtime
     // counter) and is 4 % faster end to end on the 8B and 70B shapes.
+    // FP8 tiles carry half the bytes for the same arithmetic, so a wave's
+    // compute is a larger share of its time; a second wave per SIMD hides it
+    // (8B shape: call 60.9 -> 60.3 us warm, 74.8 -> 69.8 us cold; 70B shape:
+    // 201 -> 188 us).
     constexpr int kMaxDev = 16;
-    constexpr int kWavesPerCU = 4;
-    static int cached[kMaxDev][9] = {};
+    const int waves_per_cu = fp8 ? 8 : 4;
+    static int cached[kMaxDev][2][9] = {};
     if (group < 1 || group > 8) return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
         (void)hipGetLastError();
         return kStreamKDefaultWorkers;
     }
-    if (cached[dev][group]) return cached[dev][group];
+    if (cached[dev][fp8][group]) return cached[dev][fp8][group];
     int cus = 0, per_cu = 0;
     const void* fn = nullptr;
     switch (group) {
-        case 1: fn = streamk_kernel_ptr<1>(); break;
-        case 2: fn = streamk_kernel_ptr<2>(); break;
-        case 4: fn = streamk_kernel_ptr<4>(); break;
-        case 8: fn = streamk_kernel_ptr<8>(); break;
+        case 1: fn = fp8 ? streamk_kernel_ptr<1, true>() : streamk_kernel_ptr<1, false>(); break;
+        case 2: fn = fp8 ? streamk_kernel_ptr<2, true>() : streamk_kernel_ptr<2, false>(); break;
+        case 4: fn = fp8 ? streamk_kernel_ptr<4, true>() : streamk_kernel_ptr<4, false>(); break;
+        case 8: fn = fp8 ? streamk_kernel_ptr<8, true>() : streamk_kernel_ptr<8, false>(); break;
         default: return 0;
     }
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -1095,8 +1102,8 @@ int streamk_workers(int group) {
         (void)hipGetLastError();
         return kStreamKDefaultWorkers;
     }
-    cached[dev][group] = cus * min(per_cu, kWavesPerCU);
-    return cached[dev][group];
+    cached[dev][fp8][group] = cus * min(per_cu, waves_per_cu);
+    return cached[dev][fp8][group];
 }
 
 namespace {

@@ -88,7 +88,7 @@ Plan plan_decode(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, i
     if (partition_size == 0 && (d.dtype == KV_BF16 || d.dtype == KV_FP8_E4M3) && d.head_dim == 128 &&
         num_seqs <= kvp::kStreamKMaxSeqs) {
         p.mode = Mode::kBalanced;
-        p.workers = kvp::streamk_workers(group);
+        p.workers = kvp::streamk_workers(group, d.dtype == KV_FP8_E4M3);
         p.part_tokens = 0;
         p.max_parts = 1;
         p.ws_first = round_up((uint64_t)(num_seqs + 1) * 8u, 256u);

@@ -135,7 +135,8 @@ hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, int group, hipStream_t st
 // the fix-up of split (sequence, KV head) pairs; no partition merge needed.
 hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
 hipError_t launch_decode_fp8_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
-// Worker count for the balanced split on the current device (resident waves).
-int streamk_workers(int group);
+// Worker count for the balanced split on the current device (resident waves:
+// one per SIMD for bf16 tiles, two for FP8 tiles).
+int streamk_workers(int group, bool fp8);
 
 }  // namespace kvp

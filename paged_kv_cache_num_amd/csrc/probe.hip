@@ -157,7 +157,7 @@ extern "C" kv_status kv_probe_table_walk(const int32_t* block_tables, int32_t ma
         max_blocks_per_seq <= 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvp::kBlockTokens ||
         (reinterpret_cast<uintptr_t>(sink) & 3u))
         return KV_ERR_INVALID_ARGUMENT;
-    const int workers = kvp::streamk_workers(4);
+    const int workers = kvp::streamk_workers(4, false);
     if (workers <= 0 || workers % 8 != 0 || sink_bytes < (uint64_t)workers * 4u) return KV_ERR_INVALID_ARGUMENT;
     if (num_seqs == 0) return KV_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
