@@ -277,8 +277,12 @@ kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int3
  *                  straddle slices; other shapes walk each context in one
  *                  workgroup per (sequence, KV head).
  *                  > 0: a multiple of B; each context is cut into partitions
- *                  of that many tokens, each handled by its own workgroup,
- *                  and a second kernel merges them (log-sum-exp rescale).
+ *                  of that many tokens, each computed whole by one wave (for
+ *                  bf16 and FP8 pools with head_dim 128 and at most 1024
+ *                  sequences the partitions of the whole batch are shared out
+ *                  to one resident wave per SIMD; otherwise one workgroup per
+ *                  partition), and a second kernel merges them (log-sum-exp
+ *                  rescale).
  *   scale:         softmax scale, finite and > 0
  *   workspace:     device, >= paged_attention_workspace_bytes(...) bytes, 16-byte
  *                  aligned; may be NULL when that size is 0.  Its contents on

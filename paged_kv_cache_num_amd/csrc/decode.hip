@@ -254,33 +254,82 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_kernel(DecodeArgs
 
 // Merge the partitions of one (sequence, query head): with M the largest
 // partition max, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+// Four waves per (sequence, head): every thread takes part in the max over
+// the partitions, then wave w sums partitions w, w + 4, ... with kMergeU of
+// them in flight per lane (lane: dims 2l, 2l + 1), and the four partial sums
+// meet in LDS.  A long context has hundreds of partitions (128K tokens in
+// 512-token partitions: 256), so the partitions are not walked one load at a
+// time.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeU = 8;
+
 template <int DT, int D>
-__global__ __launch_bounds__(kWave) void reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeWaves * kWave) void reduce_kernel(DecodeArgs a) {
     const int h = blockIdx.x;
     const int seq = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid & (kWave - 1);
     int L = a.lens[seq];
     L = L < 0 ? 0 : (L > a.max_context ? a.max_context : L);
-    const int nparts = L == 0 ? 1 : (L + a.part_tokens - 1) / a.part_tokens;
+    const size_t row = (size_t)seq * a.num_q_heads + h;
+    if (L == 0) {   // nothing to attend to: zeros (also written by the per-partition kernels)
+        for (int d = tid * 2; d < D; d += kMergeWaves * kWave * 2) {
+            if constexpr (DT == 1) reinterpret_cast<uint32_t*>(a.out)[(row * D + d) / 2] = 0u;
+            else reinterpret_cast<float2*>(a.out)[(row * D + d) / 2] = make_float2(0.0f, 0.0f);
+        }
+        return;
+    }
+    const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
     if (nparts <= 1) return;   // the decode kernel wrote this row itself
 
-    const size_t row = (size_t)seq * a.num_q_heads + h;
     const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row * a.max_parts;
+    __shared__ float sm_red[kMergeWaves];
     float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[p].x);
+    for (int p = tid; p < nparts; p += kMergeWaves * kWave) M = fmaxf(M, ml[p].x);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+    if (lane == 0) sm_red[wave] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, sm_red[w]);
     const float Ms = safe_max(M);
 
-    const int d = threadIdx.x * 2;
-    if (d >= D) return;
+    const float2* acc = reinterpret_cast<const float2*>(a.ws_acc) + (row * a.max_parts) * (D / 2) + lane;
+    const bool active = lane * 2 < D;
     float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
-    const float2* acc = reinterpret_cast<const float2*>(a.ws_acc) + (row * a.max_parts) * (D / 2) + threadIdx.x;
-    for (int p = 0; p < nparts; ++p) {
-        const float2 mlp = ml[p];
-        const float f = fast_exp2(mlp.x - Ms);
-        den = fmaf(mlp.y, f, den);
-        const float2 x = acc[(size_t)p * (D / 2)];
-        n0 = fmaf(x.x, f, n0);
-        n1 = fmaf(x.y, f, n1);
+    for (int p0 = wave; p0 < nparts; p0 += kMergeWaves * kMergeU) {
+        float2 mlu[kMergeU], xu[kMergeU];
+#pragma unroll
+        for (int u = 0; u < kMergeU; ++u) {
+            const int p = p0 + u * kMergeWaves;
+            const bool live = p < nparts;
+            mlu[u] = live ? ml[p] : make_float2(-INFINITY, 0.0f);
+            xu[u] = (live && active) ? acc[(size_t)p * (D / 2)] : make_float2(0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeU; ++u) {
+            const float f = fast_exp2(mlu[u].x - Ms);   // 0 for a missing partition
+            den = fmaf(mlu[u].y, f, den);
+            n0 = fmaf(xu[u].x, f, n0);
+            n1 = fmaf(xu[u].y, f, n1);
+        }
     }
+    __shared__ float sm_den[kMergeWaves];
+    __shared__ float2 sm_n[kMergeWaves][kWave];
+    if (lane == 0) sm_den[wave] = den;
+    sm_n[wave][lane] = make_float2(n0, n1);
+    __syncthreads();
+    if (wave != 0 || !active) return;
+    den = 0.0f;
+    n0 = n1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+        den += sm_den[w];
+        n0 += sm_n[w][lane].x;
+        n1 += sm_n[w][lane].y;
+    }
+    const int d = lane * 2;
     const float o0 = den > 0.0f ? n0 / den : 0.0f;
     const float o1 = den > 0.0f ? n1 / den : 0.0f;
     if constexpr (DT == 1) {
@@ -293,7 +342,7 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(DecodeArgs a) {
 template <int DT, int D>
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t stream) {
     if (a.max_parts <= 1) return hipSuccess;
-    reduce_kernel<DT, D><<<dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(kWave), 0, stream>>>(a);
+    reduce_kernel<DT, D><<<dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(kMergeWaves * kWave), 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -318,6 +367,10 @@ hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_partition_merge_bf16(const DecodeArgs& a, hipStream_t stream) {
+    return launch_reduce<1, 128>(a, stream);
+}
 
 bool decode_shape_supported(int dtype, int head_dim, int group, int block_size) {
     if (!(dtype == 0 || dtype == 1 || dtype == 2) || !(head_dim == 64 || head_dim == 128) ||

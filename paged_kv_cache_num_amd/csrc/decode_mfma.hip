@@ -948,6 +948,146 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fixed partitions, persistent: the (sequence, KV head, partition) items of
+// the whole batch, in that order, go to the same single-wave workers as the
+// balanced split.  Worker w takes every item whose first tile lies in its
+// tile slice [slice_start(w), slice_start(w + 1)) and walks it whole, so each
+// partition's state comes from one wave, as the partition merge expects, and
+// the workers' loads differ by at most one partition.  A one-workgroup-per-
+// partition grid instead pays the latency of a table load and of the first
+// tiles for every partition, and launches a workgroup for every slot of the
+// (max partitions, KV heads, sequences) grid, most of them empty when lengths
+// vary (70B-shaped batch: 874 us in that form).  Sequences of length 0 are
+// written by the merge kernel.
+// ---------------------------------------------------------------------------
+template <int G, bool kAnyB, bool kFp8>
+__global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x;
+    const int64_t W = gridDim.x;
+    const int64_t w = blockIdx.x;
+    const int S = a.num_seqs;
+    const int Hkv = a.num_kv_heads;
+    const int pt = a.part_tokens / kTileTokens;   // tiles per partition
+
+    // tiles per sequence and their exclusive prefix sums, as in the balanced split
+    constexpr int kMaxChunks = kStreamKMaxSeqs / kWave;
+    const int nchunks = (S + kWave - 1) / kWave;
+    int len_c[kMaxChunks];
+#pragma unroll
+    for (int ch = 0; ch < kMaxChunks; ++ch) {
+        const int i = ch * kWave + lane;
+        len_c[ch] = (ch < nchunks && i < S) ? clamp_len(a.lens[i], a.max_context) : 0;
+    }
+    int64_t ex_c[kMaxChunks];
+    int64_t T = 0;
+#pragma unroll
+    for (int ch = 0; ch < kMaxChunks; ++ch) {
+        if (ch < nchunks) {
+            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kTileTokens - 1) / kTileTokens);
+            int64_t incl = nt;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int64_t y = __shfl_up(incl, off, kWave);
+                if (lane >= off) incl += y;
+            }
+            ex_c[ch] = T + incl - nt;
+            T += __shfl(incl, kWave - 1, kWave);
+        }
+    }
+    const int64_t t_lo = slice_start(w, T, W);
+    const int64_t t_hi = slice_start(w + 1, T, W);
+    if (t_lo >= t_hi) return;
+
+    int seq = S, L = 0;
+    int64_t seq_first = 0;
+#pragma unroll
+    for (int ch = 0; ch < kMaxChunks; ++ch) {
+        if (ch < nchunks && seq == S) {
+            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kTileTokens - 1) / kTileTokens);
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(nt > 0 && ex_c[ch] <= t_lo && t_lo < ex_c[ch] + nt);
+            if (bal) {
+                const int j = __builtin_ctzll(bal);
+                seq = ch * kWave + j;
+                seq_first = readlane64(ex_c[ch], j);
+                L = __builtin_amdgcn_readlane(len_c[ch], j);
+            }
+        }
+    }
+    seq = __builtin_amdgcn_readfirstlane(seq);
+    L = __builtin_amdgcn_readfirstlane(L);
+    int nblk = (L + kTileTokens - 1) / kTileTokens;
+    const int64_t off = t_lo - seq_first;
+    int kv = (int)(off / nblk);
+    int b = (int)(off - (int64_t)kv * nblk);
+    b = (b + pt - 1) / pt * pt;   // the first partition that starts in this slice
+
+    AppendRow none;
+    none.active = false;
+    none.krow = none.vrow = nullptr;
+    while (seq < S) {
+        if (b >= nblk) {   // past this (sequence, KV head): the next one with tiles
+            b = 0;
+            if (++kv == Hkv) {
+                kv = 0;
+                do {
+                    seq_first += (int64_t)Hkv * nblk;
+                    ++seq;
+                    L = (seq < S) ? __builtin_amdgcn_readfirstlane(clamp_len(a.lens[seq], a.max_context)) : 0;
+                    nblk = (L + kTileTokens - 1) / kTileTokens;
+                } while (nblk == 0 && seq < S);
+                if (seq >= S) break;
+            }
+            continue;
+        }
+        if (seq_first + (int64_t)kv * nblk + b >= t_hi) break;   // the next worker's partition
+        const int n_here = min(pt, nblk - b);
+        const int part = b / pt;
+        const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+
+        const WalkCtx c = make_ctx<kAnyB, kFp8>(a, kv);
+        bf16x8_t qb[kKK];
+        load_q<G, kFp8>(qb, a, seq, kv, c);
+        State st;
+        init_state(st);
+        walk<G, kStreamDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, none);
+        const float l_tot = total_l(st);
+
+        if (nparts == 1) {   // the whole context: the output itself
+            uint4* orow = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * kRC;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * c.r + j;
+                const float lh = __shfl(l_tot, h & 15, kWave);
+                if (h < G) {
+                    const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+                    uint4 o;
+                    o.x = pack_bf16x2(st.o[0][j] * inv, st.o[1][j] * inv);
+                    o.y = pack_bf16x2(st.o[2][j] * inv, st.o[3][j] * inv);
+                    o.z = pack_bf16x2(st.o[4][j] * inv, st.o[5][j] * inv);
+                    o.w = pack_bf16x2(st.o[6][j] * inv, st.o[7][j] * inv);
+                    orow[h * kRC + c.n] = o;
+                }
+            }
+        } else {   // this partition's (m, l, unnormalised output) for the merge kernel
+            const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * c.r + j;
+                if (h < G) {
+                    const size_t slot = (row0 + h) * a.max_parts + part;
+                    float4* dst = reinterpret_cast<float4*>(a.ws_acc + slot * kD + c.n * 8);
+                    dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
+                    dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
+                }
+            }
+            if (c.r == 0 && c.n < G)
+                reinterpret_cast<float2*>(a.ws_ml)[(row0 + c.n) * a.max_parts + part] = make_float2(st.m, l_tot);
+        }
+        b += pt;
+    }
+}
+
 // Fix-up for one (sequence, KV head): zeros for an empty sequence; nothing if
 // one slice held it whole; otherwise the log-sum-exp merge of the partial
 // states its slices left.  With fewer tiles than workers some slices are
@@ -1156,6 +1296,32 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
 }
 
 template <bool kFp8>
+hipError_t launch_partitions(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+    dim3 grid((unsigned)workers);
+    const bool any_b = !kFp8 && a.block_size != kTileTokens;
+    switch (group) {
+        case 1:
+            if (any_b) decode_partitions_kernel<1, true, false><<<grid, kWave, 0, stream>>>(a);
+            else decode_partitions_kernel<1, false, kFp8><<<grid, kWave, 0, stream>>>(a);
+            break;
+        case 2:
+            if (any_b) decode_partitions_kernel<2, true, false><<<grid, kWave, 0, stream>>>(a);
+            else decode_partitions_kernel<2, false, kFp8><<<grid, kWave, 0, stream>>>(a);
+            break;
+        case 4:
+            if (any_b) decode_partitions_kernel<4, true, false><<<grid, kWave, 0, stream>>>(a);
+            else decode_partitions_kernel<4, false, kFp8><<<grid, kWave, 0, stream>>>(a);
+            break;
+        case 8:
+            if (any_b) decode_partitions_kernel<8, true, false><<<grid, kWave, 0, stream>>>(a);
+            else decode_partitions_kernel<8, false, kFp8><<<grid, kWave, 0, stream>>>(a);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <bool kFp8>
 hipError_t launch_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
     dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     dim3 block(kWaves * kWave);
@@ -1200,6 +1366,15 @@ hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t s
 hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
     if (a.block_size != kTileTokens) return hipErrorInvalidValue;
     return launch_mfma<true>(a, group, stream);
+}
+
+hipError_t launch_decode_bf16_partitions(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+    return launch_partitions<false>(a, group, workers, stream);
+}
+
+hipError_t launch_decode_fp8_partitions(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+    if (a.block_size != kTileTokens) return hipErrorInvalidValue;
+    return launch_partitions<true>(a, group, workers, stream);
 }
 
 }  // namespace kvp

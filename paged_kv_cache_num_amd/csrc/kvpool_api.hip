@@ -108,6 +108,9 @@ Plan plan_decode(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, i
     p.mode = Mode::kPartitions;
     p.part_tokens = partition_size;
     p.max_parts = (max_context_len + partition_size - 1) / partition_size;
+    // bf16 / FP8 pools with head_dim 128: the partitions run on the balanced split's workers
+    if ((d.dtype == KV_BF16 || d.dtype == KV_FP8_E4M3) && d.head_dim == 128 && num_seqs <= kvp::kStreamKMaxSeqs)
+        p.workers = kvp::streamk_workers(group, d.dtype == KV_FP8_E4M3);
     // (m, l) pairs first, then the fp32 partial outputs at a 256-byte boundary
     const uint64_t entries = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)p.max_parts;
     p.ws_first = round_up(entries * 8u, 256u);
@@ -529,7 +532,16 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
                 e = kvp::launch_append_scatter(w, static_cast<hipStream_t>(stream));
             }
         }
-        if (e == hipSuccess) e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
+        if (e == hipSuccess) {
+            if (plan.mode == Mode::kPartitions && plan.workers > 0) {
+                const int group = num_q_heads / d.num_kv_heads;
+                e = fp8 ? kvp::launch_decode_fp8_partitions(a, group, plan.workers, static_cast<hipStream_t>(stream))
+                        : kvp::launch_decode_bf16_partitions(a, group, plan.workers, static_cast<hipStream_t>(stream));
+                if (e == hipSuccess) e = kvp::launch_partition_merge_bf16(a, static_cast<hipStream_t>(stream));
+            } else {
+                e = kvp::launch_decode(a, d.dtype, d.head_dim, static_cast<hipStream_t>(stream));
+            }
+        }
     }
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();

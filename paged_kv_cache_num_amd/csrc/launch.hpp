@@ -135,6 +135,13 @@ hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, int group, hipStream_t st
 // the fix-up of split (sequence, KV head) pairs; no partition merge needed.
 hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
 hipError_t launch_decode_fp8_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
+// head_dim 128, at most kStreamKMaxSeqs sequences, partition_size > 0: the
+// (sequence, KV head, partition) items on the balanced split's workers, one
+// wave per item; the caller launches the partition merge.
+hipError_t launch_decode_bf16_partitions(const DecodeArgs& a, int group, int workers, hipStream_t stream);
+hipError_t launch_decode_fp8_partitions(const DecodeArgs& a, int group, int workers, hipStream_t stream);
+// the partition merge for bf16 outputs (decode.hip)
+hipError_t launch_partition_merge_bf16(const DecodeArgs& a, hipStream_t stream);
 // Worker count for the balanced split on the current device (resident waves:
 // one per SIMD for bf16 tiles, two for FP8 tiles).
 int streamk_workers(int group, bool fp8);

@@ -343,3 +343,31 @@ def test_8b_batch_pool_exact_and_sampled_sequences():
         worst = max(worst, float(np.abs(out[i] - want[0]).max()))
     say(f"  C2 fp8 sampled: max |gpu - oracle| = {worst:.3e}")
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fused,partition", [(False, 0), (True, 0), (False, 512), (True, 512)])
+def test_graph_replays_match_eager_steps(fused, partition):
+    """A captured FP8 step (scatter + attention, or the fused append) gives the
+    eager step's output and pool bits on every replay, with eager work between
+    the replays (the FP8 write path rewrites the same codes and scales each time)."""
+    import torch
+    from paged_kv_cache_num_amd import DecodeStep
+    wl = kvgen.custom_workload(lengths=[700, 1, 16, 2049, 300, 33], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                               dtype="bf16", seed=67, variant="sharp", poison=True, table_pad=1)
+    state = kvgen.fp8_pool_state(wl, seed=17)
+    step = DecodeStep.from_workload(wl, fp8_pool=state, partition_size=partition)
+    (step.run_fused if fused else step.run)()
+    torch.cuda.synchronize()
+    eager = step.out_host().copy()
+    pool = [a.copy() for a in step.pool_host() + step.scales_host()]
+    graph = step.capture(fused=fused)
+    for i in range(4):
+        step.out.fill_(0)
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        del junk
+        assert np.array_equal(step.out_host(), eager), f"replay {i}: output differs from the eager step"
+        for g, w in zip(step.pool_host() + step.scales_host(), pool):
+            assert g.tobytes() == w.tobytes(), f"replay {i}: pool differs"
