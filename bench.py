@@ -390,6 +390,7 @@ def main(argv=None):
     # batch allows it.
     launch = "eager"
     graph_ms = {}
+    graph_gpu_us = {}
     if not args.eager:
         forms = [False] + ([True] if step.can_fuse and not args.no_fuse else [])
         for fused in forms:
@@ -402,6 +403,17 @@ def main(argv=None):
             torch.cuda.synchronize()
             t1 = time.perf_counter()
             graph_ms[fused] = (t1 - t0) * 1e3 / K
+            # the same replays one at a time between events on the stream: the GPU's own time for one
+            # replayed step, without the host's submission of the next one
+            g_us = []
+            for _ in range(min(K, 50)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                graph.replay()
+                b.record()
+                b.synchronize()
+                g_us.append(a.elapsed_time(b) * 1e3)
+            graph_gpu_us[fused] = percentile(g_us, 0.5)
             del graph
             print(f"bench: timed {K} graph replays ({'fused append' if fused else 'scatter + attention'}), "
                   f"{graph_ms[fused] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
@@ -572,6 +584,7 @@ def main(argv=None):
         "eager_ms_per_step": round(eager_ms_per_step, 5),
         "graph_two_call_ms_per_step": round(graph_ms[False], 5) if False in graph_ms else None,
         "graph_fused_ms_per_step": round(graph_ms[True], 5) if True in graph_ms else None,
+        "graph_step_gpu_us_p50": {("fused" if f else "two_call"): round(v, 2) for f, v in graph_gpu_us.items()},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

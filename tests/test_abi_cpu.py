@@ -408,3 +408,12 @@ def test_swap_argument_checks_return_before_any_launch():
         assert b"pinned" in L.kv_last_error_message() or b"mapping" in L.kv_last_error_message()
         assert fn(h, None, 0, None, 0, None) == K.KV_OK
     K.lib.kv_pool_destroy(h)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs the hot path on one GPU; --gpus above 1 exits with a message."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
