@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kCopyThreads) void read_kernel(const uint4* __restr
     const uint64_t stride = (uint64_t)gridDim.x * kCopyThreads;
     uint32_t acc = 0;
     for (uint64_t i = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x; i < n; i += stride) {
-        const uint4 x = src[i];
+        const uint4 x = src[i];   // a plain (allocating) load: reading evicts what the caches held
         acc ^= x.x ^ x.y ^ x.z ^ x.w;
     }
     // fold the wave, then one word per workgroup
