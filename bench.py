@@ -56,10 +56,16 @@ DEFAULT_PARTITION = {"C1": 0, "C2": 0, "C3": 0, "C4": 0, "C5": 512}
 
 
 def kernel_sha() -> str:
+    """sha256 of the decode sources' code: comments and blank space removed, so a
+    comment edit does not invalidate the recorded traffic while any code change does."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
