@@ -1,5 +1,5 @@
-// Paged decode attention for bf16 pools with head_dim 128: q.k on the matrix
-// cores, online softmax and the value pass on the vector ALUs.
+// Paged decode attention for bf16 and FP8 pools with head_dim 128: both
+// products on the matrix cores, the online softmax on the vector ALUs.
 //
 // What is computed is the same as decode.hip (aicassindra.com "GPU paged KV
 // cache", "Inside the paged attention kernel"; "PagedAttention, Internals
@@ -20,14 +20,21 @@
 //     rescaled); otherwise exponentials use the old max, which changes no
 //     result beyond rounding because output = sum(p v) / sum(p) for any
 //     common reference.
-//   * Values.  Lane (r, c) reads the 16-byte chunk c (dims 8c..8c+7) of tokens
-//     4r..4r+3 of the V tile and accumulates p * v for every head of the
-//     group; p comes from lane (r, h) of the same 16-lane row through a DPP
-//     row broadcast.
-//   * Memory.  Each wave walks every 4th block of its partition.  The
-//     partition's block-table entries are fetched with one vector load per 64
-//     blocks and read out with readlane; the K and V tiles of the next block
-//     are in flight while the current one is computed.
+//   * Values.  P V runs as eight more MFMAs per tile (see softmax_pv): P is
+//     already where the score MFMA left it, and each lane's V operands are
+//     repacked from its own V loads (tokens 4r..4r+3, dims 8n..8n+7).
+//   * Work.  The tiles of one (sequence, KV head) are walked by one wave at a
+//     time.  With partition_size 0 the tiles of the whole batch are cut into
+//     equal slices, one per worker wave, and a fix-up merges the (sequence,
+//     KV head) pairs that straddle slices (decode_bf16_streamk_kernel); with
+//     fixed partitions the partitions go to the same workers whole
+//     (decode_partitions_kernel); above 1024 sequences one 4-wave workgroup
+//     takes each partition (decode_bf16_mfma_kernel).
+//   * Memory.  Block-table entries are fetched with one vector load per 64
+//     tiles and read out with readlane; two tiles are held in registers, the
+//     next one in flight while the current one is computed, and each half of
+//     a tile's registers is refilled as soon as it has been read.  V tiles of
+//     bf16 pools are loaded with the streaming hint (keep_v_cached).
 //   * The walk order and all reductions depend only on logical positions, so
 //     the output is bitwise independent of where the blocks live.
 //   * FP8 pools (E4M3 codes, one fp32 scale per block and KV head for K and
