@@ -13,6 +13,9 @@
  *                                     attention, online softmax, optional split
  *                                     of the context into partitions merged by
  *                                     a second kernel).
+ * Beside them: the decode append folded into the attention call, the
+ * copy-on-write block copy, FP8 pools with per-block scales, and swap of
+ * blocks to pinned host memory and back.
  *
  * Sources (page title, section):
  *   [KVC] aicassindra.com "GPU paged KV cache":
