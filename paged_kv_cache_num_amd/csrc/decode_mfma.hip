@@ -47,6 +47,8 @@
 //     FP8 tiles) measured slower on the 8B- and 70B-shaped batches.
 #include <math.h>
 
+#include <atomic>
+
 #include "device_common.hpp"
 #include "fp8.hpp"
 #include "launch.hpp"
@@ -1267,14 +1269,16 @@ int streamk_workers(int group, bool fp8) {
     // 201 -> 188 us).
     constexpr int kMaxDev = 16;
     const int waves_per_cu = fp8 ? 8 : 4;
-    static int cached[kMaxDev][2][9] = {};
+    // per (device, pool type, group); several host threads may fill it at once with the same value
+    static std::atomic<int> cached[kMaxDev][2][9];
     if (group < 1 || group > 8) return 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
         (void)hipGetLastError();
         return kStreamKDefaultWorkers;
     }
-    if (cached[dev][fp8][group]) return cached[dev][fp8][group];
+    const int known = cached[dev][fp8][group].load(std::memory_order_relaxed);
+    if (known) return known;
     int cus = 0, per_cu = 0;
     const void* fn = nullptr;
     switch (group) {
@@ -1289,8 +1293,9 @@ int streamk_workers(int group, bool fp8) {
         (void)hipGetLastError();
         return kStreamKDefaultWorkers;
     }
-    cached[dev][fp8][group] = cus * min(per_cu, waves_per_cu);
-    return cached[dev][fp8][group];
+    const int workers = cus * min(per_cu, waves_per_cu);
+    cached[dev][fp8][group].store(workers, std::memory_order_relaxed);
+    return workers;
 }
 
 namespace {
