@@ -31,9 +31,9 @@
 //     (decode_partitions_kernel); above 1024 sequences one 4-wave workgroup
 //     takes each partition (decode_bf16_mfma_kernel).
 //   * Memory.  Block-table entries are fetched with one vector load per 64
-//     tiles and read out with readlane; two tiles are held in registers, the
-//     next one in flight while the current one is computed, and each half of
-//     a tile's registers is refilled as soon as it has been read.  V tiles of
+//     tiles and read out with readlane; a worker wave holds one tile in
+//     registers (fixed partitions: two), and each half of a tile's registers
+//     is refilled with the next tile as soon as it has been read.  V tiles of
 //     bf16 pools are loaded with the streaming hint (keep_v_cached).
 //   * The walk order and all reductions depend only on logical positions, so
 //     the output is bitwise independent of where the blocks live.
@@ -43,8 +43,9 @@
 //     scale multiplies its scores; its V scale multiplies the probabilities
 //     that enter P V, while the softmax sum takes them unscaled, so
 //     out = sum_j p_j sv_j v_j / sum_j p_j is what the dequantized cache gives.
-//     Two tiles in flight per wave, as for bf16: deeper pipelines (4, 6, 8
-//     FP8 tiles) measured slower on the 8B- and 70B-shaped batches.
+//     One tile in registers per worker wave, as for bf16: deeper pipelines
+//     (2, 4, 6, 8 FP8 tiles) measured slower on the 8B- and 70B-shaped
+//     batches.
 #include <math.h>
 
 #include <atomic>
@@ -63,7 +64,15 @@ constexpr int kD = 128;            // head_dim this kernel is built for
 constexpr int kRC = kD / 8;        // 16-byte chunks per token row (16)
 constexpr int kKK = kD / 32;       // MFMA steps over head_dim (4)
 constexpr float kLazy = 8.0f;      // log2 headroom before the running max is moved
-constexpr int kStreamDepth = 2;    // tiles in registers per balanced-mode wave
+// Tiles in registers per worker wave.  Balanced split: one (the next tile's
+// loads go out as soon as each half of the current one is read).  With two,
+// the 8B- and 70B-shaped batches ran 1.5-4% slower for bf16 tiles and 2.5-6%
+// slower for FP8 tiles, as a plain gather of the same tiles in the same
+// slices does: more requests in flight per wave than the memory system turns
+// into bandwidth.  Fixed partitions, whose walks are short: two (one measured
+// 2% slower on the long-context batch).
+constexpr int kBalancedDepth = 1;
+constexpr int kPartitionDepth = 2;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -423,6 +432,28 @@ __device__ __forceinline__ bool keep_v_cached(const DecodeArgs& a, int seq, int 
     return shared;
 }
 
+// The same test for a piece whose first table entries are fetched ahead (lane
+// 0 of tv0 holds the entry of its first tile): the neighbours' entries are
+// fetched with them, lane 0 the previous sequence's and lane 1 the next one's,
+// so the piece starts without a round trip for the test.
+template <bool kFp8>
+__device__ __forceinline__ int neighbour_entries(const DecodeArgs& a, int seq, int tile, const WalkCtx& c) {
+    int x = 0;
+    if (!kFp8) {
+        const int entry = c.pair8 ? 2 * tile : tile >> c.sub_shift;
+        if (c.lane == 0 && seq > 0) x = a.tables[(size_t)(seq - 1) * a.max_blocks + entry];
+        if (c.lane == 1 && seq + 1 < a.num_seqs) x = a.tables[(size_t)(seq + 1) * a.max_blocks + entry];
+    }
+    return x;
+}
+template <bool kFp8>
+__device__ __forceinline__ bool keep_v_fetched(int tv0, int nb, int seq, int num_seqs) {
+    if (kFp8) return true;
+    const int mine = __builtin_amdgcn_readlane(tv0, 0);
+    return (seq > 0 && __builtin_amdgcn_readlane(nb, 0) == mine) ||
+           (seq + 1 < num_seqs && __builtin_amdgcn_readlane(nb, 1) == mine);
+}
+
 // kAnyB: the block size comes from the arguments (8..128); otherwise it is 16
 // and every block-size field below is a constant the walk folds away.
 // kFp8: an FP8 pool (block size 16).
@@ -571,10 +602,10 @@ __device__ __forceinline__ int2 tile_entries(const int32_t* row, int e, bool val
 // FP8 tiles also need their block scales: lane k of the chunk loads those of
 // tile k before the first tiles are requested, and tile k reads them from
 // lane k.
-template <int G, int D, bool kFp8 = false>
-__device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* row, int stride,
-                                     int nk, int b0, int L, const WalkCtx& c, const AppendRow& app,
-                                     bool have_first = false, int tv0_first = 0, int tv1_first = 0) {
+template <int G, int D, bool kFp8, bool kKeepV>
+__device__ __forceinline__ void walk_policy(State& st, const bf16x8_t (&qb)[kKK], const int32_t* row, int stride,
+                                            int nk, int b0, int L, const WalkCtx& c, const AppendRow& app,
+                                            bool have_first, int tv0_first, int tv1_first) {
     // Tile k of the current chunk (tile b0 + (k0 + k) * stride of the sequence).
     // Each lane addresses its own rows: for B = 8 the K rows of tokens 8..15 and
     // the V rows of lanes r >= 2 come from the second block.
@@ -625,7 +656,7 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
             tile_ptrs(tv0, tv1, min(s, nc - 1), kt, vt);
             load_k(tt[s], kt, c.k_off);
             asm volatile("" : : : "memory");
-            load_v(tt[s], vt, c.v_off, c.keep_v);
+            load_v(tt[s], vt, c.v_off, kKeepV);
             asm volatile("" : : : "memory");
         }
         if (app.active && k0 + 64 >= nk) {
@@ -655,7 +686,7 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
                         append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc, vsc);
                     }
                     process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2, ksc, vsc,
-                               [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off, c.keep_v); });
+                               [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off, kKeepV); });
                 } else {
                     // wave-uniform: the tile holding the new token; a table entry outside
                     // the pool gets no write (as the scatter skips such a slot)
@@ -663,11 +694,24 @@ __device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const
                         append_into(tt[s], app, new_k, new_v, c);
                     }
                     process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2,
-                               [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off, c.keep_v); });
+                               [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off, kKeepV); });
                 }
             }
         }
     }
+}
+
+// The walk with the cache policy of its V loads fixed at compile time: a
+// runtime choice inside the loop put a branch around every V refill, and that
+// cost 1.3 us per call on the 8B-shaped batch and 10 us on the 70B-shaped one.
+template <int G, int D, bool kFp8 = false>
+__device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* row, int stride,
+                                     int nk, int b0, int L, const WalkCtx& c, const AppendRow& app,
+                                     bool have_first = false, int tv0_first = 0, int tv1_first = 0) {
+    if (kFp8 || c.keep_v)
+        walk_policy<G, D, kFp8, true>(st, qb, row, stride, nk, b0, L, c, app, have_first, tv0_first, tv1_first);
+    else
+        walk_policy<G, D, kFp8, false>(st, qb, row, stride, nk, b0, L, c, app, have_first, tv0_first, tv1_first);
 }
 
 template <int G, bool kAnyB, bool kFp8>
@@ -904,13 +948,14 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
 
     bool first_piece = true;
     bool pf_valid = false;   // table entries of the next piece fetched ahead
-    int pf_seq = -1, pf_tv0 = 0, pf_tv1 = 0;
+    int pf_seq = -1, pf_tv0 = 0, pf_tv1 = 0, pf_nb = 0;
     while (t < t_end && seq < S) {
         const int n_here = (int)min((int64_t)(nblk - b), t_end - t);
         const bool whole = (b == 0) && (n_here == nblk);
 
         WalkCtx c = make_ctx<kAnyB, kFp8>(a, kv);
-        c.keep_v = keep_v_cached<kFp8>(a, seq, b, c);
+        const bool use_pf = pf_valid && pf_seq == seq && b == 0;
+        c.keep_v = use_pf ? keep_v_fetched<kFp8>(pf_tv0, pf_nb, seq, S) : keep_v_cached<kFp8>(a, seq, b, c);
         bf16x8_t qb[kKK];
         load_q<G, kFp8>(qb, a, seq, kv, c);
         State st;
@@ -925,7 +970,6 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         // The next piece of this slice, if it starts a new (sequence, KV head),
         // begins at block 0 of (seq, kv + 1) or of the next sequence: fetch its
         // first table entries now, so that piece waits for its tiles only.
-        const bool use_pf = pf_valid && pf_seq == seq && b == 0;
         const int tv0_here = pf_tv0, tv1_here = pf_tv1;
         pf_valid = false;
         if (b + n_here == nblk && t + n_here < t_end) {
@@ -937,12 +981,13 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                 const int2 pf = tile_entries(a.tables + (size_t)nseq * a.max_blocks, c.lane, ok, c);
                 pf_tv0 = pf.x;
                 pf_tv1 = pf.y;
+                pf_nb = neighbour_entries<kFp8>(a, nseq, 0, c);
                 pf_seq = nseq;
                 pf_valid = true;
             }
         }
-        walk<G, kStreamDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, app, use_pf,
-                                    tv0_here, tv1_here);
+        walk<G, kBalancedDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, app, use_pf,
+                                      tv0_here, tv1_here);
         const float l_tot = total_l(st);
 
         if (whole) {
@@ -1073,6 +1118,8 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
     AppendRow none;
     none.active = false;
     none.krow = none.vrow = nullptr;
+    bool pf_valid = false;   // table entries of the next partition fetched ahead
+    int pf_kv = -1, pf_b = -1, pf_tv0 = 0, pf_tv1 = 0, pf_nb = 0;
     while (seq < S) {
         if (b >= nblk) {   // past this (sequence, KV head): the next one with tiles
             b = 0;
@@ -1094,12 +1141,36 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
         const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
 
         WalkCtx c = make_ctx<kAnyB, kFp8>(a, kv);
-        c.keep_v = keep_v_cached<kFp8>(a, seq, b, c);
+        const bool use_pf = pf_valid && pf_kv == kv && pf_b == b;   // pf_valid only within one sequence
+        const int tv0_here = pf_tv0, tv1_here = pf_tv1;
+        c.keep_v = use_pf ? keep_v_fetched<kFp8>(pf_tv0, pf_nb, seq, S) : keep_v_cached<kFp8>(a, seq, b, c);
+        // The next partition, when it lies in this sequence and in this slice:
+        // fetch its first table entries now, so that it waits for its tiles only.
+        pf_valid = false;
+        {
+            int nb = b + pt, nkv = kv;
+            if (nb >= nblk) {
+                nb = 0;
+                ++nkv;
+            }
+            if (nkv < Hkv && seq_first + (int64_t)nkv * nblk + nb < t_hi) {
+                const int e = nb + c.lane;
+                const bool ok = (c.pair8 ? 2 * e : e >> c.sub_shift) < a.max_blocks;
+                const int2 pf = tile_entries(a.tables + (size_t)seq * a.max_blocks, e, ok, c);
+                pf_tv0 = pf.x;
+                pf_tv1 = pf.y;
+                pf_nb = neighbour_entries<kFp8>(a, seq, nb, c);
+                pf_kv = nkv;
+                pf_b = nb;
+                pf_valid = true;
+            }
+        }
         bf16x8_t qb[kKK];
         load_q<G, kFp8>(qb, a, seq, kv, c);
         State st;
         init_state(st);
-        walk<G, kStreamDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, none);
+        walk<G, kPartitionDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, none, use_pf,
+                                       tv0_here, tv1_here);
         const float l_tot = total_l(st);
 
         if (nparts == 1) {   // the whole context: the output itself
