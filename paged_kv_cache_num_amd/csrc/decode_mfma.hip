@@ -395,6 +395,7 @@ struct WalkCtx {
     const uint4* kpool;
     const uint4* vpool;
     size_t head_off;       // kv * tile chunks
+    size_t head_stride;    // chunks between the tiles of consecutive KV heads in a block
     size_t block_stride;   // num_kv_heads * B * 16-byte chunks per row
     uint32_t num_blocks;
     int max_blocks;        // table entries per sequence
@@ -467,7 +468,8 @@ __device__ __forceinline__ WalkCtx make_ctx(const DecodeArgs& a, int kv) {
     c.n = c.lane & 15;
     c.kpool = reinterpret_cast<const uint4*>(a.k_layer);
     c.vpool = reinterpret_cast<const uint4*>(a.v_layer);
-    c.head_off = (size_t)kv * ((size_t)B * kRow);
+    c.head_stride = (size_t)B * kRow;
+    c.head_off = (size_t)kv * c.head_stride;
     c.block_stride = (size_t)a.num_kv_heads * ((size_t)B * kRow);
     c.num_blocks = (uint32_t)a.num_blocks;
     c.max_blocks = a.max_blocks;
@@ -588,43 +590,73 @@ __device__ __forceinline__ int2 tile_entries(const int32_t* row, int e, bool val
     return tv;
 }
 
+// The walk that follows on the same wave, when its first table entries are
+// already in registers: the last refills of a walk then fetch its first tiles
+// instead of repeating a tile, so that it starts with them in flight.
+struct NextWalk {
+    bool valid;
+    int tv0, tv1;          // lane j: table entries of its tile j (tv1: B = 8's second block)
+    int e0;                // its first 16-token tile in its sequence
+    size_t head_off;       // its KV head's offset in a block (16-byte units)
+    int count;             // its tiles (at least 1)
+};
+
+__device__ __forceinline__ NextWalk no_next_walk() {
+    NextWalk n;
+    n.valid = false;
+    n.tv0 = n.tv1 = n.e0 = 0;
+    n.head_off = 0;
+    n.count = 1;
+    return n;
+}
+
 // Walk nk blocks of one (sequence, KV head): logical blocks b0 + stride*k,
 // k = 0..nk-1, whose table entries start at trow (= row + b0).
 //
 // Table entries come 64 at a time from one vector load.  Within such a chunk
-// D tiles are held in registers: while block k is computed, blocks k+1 ..
-// k+D-1 are in flight, and block k's registers are refilled with block k+D
-// as soon as each half has been read.  Every tile load is issued
-// unconditionally (past the end of the chunk the last tile is fetched again,
-// an L2 hit) and in the order the tiles are consumed, so the hardware's
-// in-order load counter lets each block wait for its own tile only.
+// D tiles are held in registers (tt, owned by the caller): while block k is
+// computed, blocks k+1 .. k+D-1 are in flight, and block k's registers are
+// refilled with block k+D as soon as each half has been read.  Every tile
+// load is issued unconditionally and in the order the tiles are consumed, so
+// the hardware's in-order load counter lets each block wait for its own tile
+// only.  Past the end of a chunk a refill fetches the chunk's last tile again
+// (an L2 hit), except past the end of the walk when the next walk of this
+// wave is known (nxt): then the refills fetch that walk's first D tiles, and
+// the caller starts it with primed = true (its tiles already requested).
 //
 // FP8 tiles also need their block scales: lane k of the chunk loads those of
 // tile k before the first tiles are requested, and tile k reads them from
 // lane k.
 template <int G, int D, bool kFp8, bool kKeepV>
-__device__ __forceinline__ void walk_policy(State& st, const bf16x8_t (&qb)[kKK], const int32_t* row, int stride,
-                                            int nk, int b0, int L, const WalkCtx& c, const AppendRow& app,
-                                            bool have_first, int tv0_first, int tv1_first) {
+__device__ __forceinline__ void walk_policy(State& st, typename TileOf<kFp8>::type (&tt)[D], bool primed,
+                                            const bf16x8_t (&qb)[kKK], const int32_t* row, int stride, int nk,
+                                            int b0, int L, const WalkCtx& c, const AppendRow& app, bool have_first,
+                                            int tv0_first, int tv1_first, const NextWalk& nxt) {
     // Tile k of the current chunk (tile b0 + (k0 + k) * stride of the sequence).
     // Each lane addresses its own rows: for B = 8 the K rows of tokens 8..15 and
     // the V rows of lanes r >= 2 come from the second block.
     int k0 = 0;
-    auto tile_ptrs = [&](int tv0, int tv1, int k, const uint4*& kt, const uint4*& vt) {
-        uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane(tv0, k);
+    auto ptrs_of = [&](uint32_t p0, uint32_t p1, int e, size_t head_off, const uint4*& kt, const uint4*& vt) {
         p0 = p0 < c.num_blocks ? p0 : c.num_blocks - 1;   // stay inside the pool whatever the table says
         if (c.pair8) {
-            uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane(tv1, k);
             p1 = p1 < c.num_blocks ? p1 : c.num_blocks - 1;
-            kt = c.kpool + (size_t)(c.n < 8 ? p0 : p1) * c.block_stride + c.head_off;
-            vt = c.vpool + (size_t)(c.r < 2 ? p0 : p1) * c.block_stride + c.head_off;
+            kt = c.kpool + (size_t)(c.n < 8 ? p0 : p1) * c.block_stride + head_off;
+            vt = c.vpool + (size_t)(c.r < 2 ? p0 : p1) * c.block_stride + head_off;
         } else {
-            const int e = b0 + (k0 + k) * stride;
-            const size_t base = (size_t)p0 * c.block_stride + c.head_off +
+            const size_t base = (size_t)p0 * c.block_stride + head_off +
                                 (size_t)(e & ((1 << c.sub_shift) - 1)) * (kTileTokens * kRC);
             kt = c.kpool + base;
             vt = c.vpool + base;
         }
+    };
+    auto tile_ptrs = [&](int tv0, int tv1, int k, const uint4*& kt, const uint4*& vt) {
+        ptrs_of((uint32_t)__builtin_amdgcn_readlane(tv0, k), c.pair8 ? (uint32_t)__builtin_amdgcn_readlane(tv1, k) : 0u,
+                b0 + (k0 + k) * stride, c.head_off, kt, vt);
+    };
+    // tile j of the next walk
+    auto next_ptrs = [&](int j, const uint4*& kt, const uint4*& vt) {
+        ptrs_of((uint32_t)__builtin_amdgcn_readlane(nxt.tv0, j),
+                c.pair8 ? (uint32_t)__builtin_amdgcn_readlane(nxt.tv1, j) : 0u, nxt.e0 + j, nxt.head_off, kt, vt);
     };
     // the block holding row j of tile k names a block of the pool
     auto row_in_pool = [&](int tv0, int tv1, int k, int j) -> bool {
@@ -635,6 +667,8 @@ __device__ __forceinline__ void walk_policy(State& st, const bf16x8_t (&qb)[kKK]
     uint32_t new_kw = 0, new_vw = 0;   // FP8: dims 2l, 2l + 1 of the appended row
     for (k0 = 0; k0 < nk; k0 += 64) {
         const int nc = min(64, nk - k0);
+        const bool last_chunk = k0 + 64 >= nk;
+        const int nc_pad = (nc + D - 1) / D * D;   // tiles the loop below runs, masked ones included
         // the first chunk's entries may have been fetched ahead (entries past nc are never read)
         const int2 tvp = (k0 == 0 && have_first) ? make_int2(tv0_first, tv1_first)
                                                  : tile_entries(row, b0 + (k0 + c.lane) * stride, c.lane < nc, c);
@@ -649,17 +683,18 @@ __device__ __forceinline__ void walk_policy(State& st, const bf16x8_t (&qb)[kKK]
             }
             asm volatile("" : : : "memory");
         }
-        typename TileOf<kFp8>::type tt[D];
         const uint4 *kt, *vt;
+        if (!(k0 == 0 && primed)) {
 #pragma unroll
-        for (int s = 0; s < D; ++s) {
-            tile_ptrs(tv0, tv1, min(s, nc - 1), kt, vt);
-            load_k(tt[s], kt, c.k_off);
-            asm volatile("" : : : "memory");
-            load_v(tt[s], vt, c.v_off, kKeepV);
-            asm volatile("" : : : "memory");
+            for (int s = 0; s < D; ++s) {
+                tile_ptrs(tv0, tv1, min(s, nc - 1), kt, vt);
+                load_k(tt[s], kt, c.k_off);
+                asm volatile("" : : : "memory");
+                load_v(tt[s], vt, c.v_off, kKeepV);
+                asm volatile("" : : : "memory");
+            }
         }
-        if (app.active && k0 + 64 >= nk) {
+        if (app.active && last_chunk) {
             if constexpr (kFp8) {
                 new_kw = reinterpret_cast<const uint32_t*>(app.krow)[c.lane];
                 new_vw = reinterpret_cast<const uint32_t*>(app.vrow)[c.lane];
@@ -669,14 +704,20 @@ __device__ __forceinline__ void walk_policy(State& st, const bf16x8_t (&qb)[kKK]
                 new_v = app.vrow[c.n];
             }
         }
+        const bool to_next = last_chunk && nxt.valid;
         for (int k = 0; k < nc; k += D) {
 #pragma unroll
             for (int s = 0; s < D; ++s) {
                 // tt[s] holds block k + s; it is refilled with block k + s + D.
                 // Past the end a block is a repeat, given a first token of L
                 // so that every position is masked and it adds exact zeros;
-                // running it anyway keeps the loads of every path equal.
-                tile_ptrs(tv0, tv1, min(k + s + D, nc - 1), kt, vt);
+                // running it anyway keeps the loads of every path equal.  The
+                // refills of the last D slots fetch the next walk's tiles 0..D-1.
+                const int idx = k + s + D;
+                if (to_next && idx >= nc_pad)
+                    next_ptrs(min(idx - nc_pad, nxt.count - 1), kt, vt);
+                else
+                    tile_ptrs(tv0, tv1, min(idx, nc - 1), kt, vt);
                 __builtin_amdgcn_sched_barrier(0);
                 const int tok = k + s < nc ? (b0 + (k0 + k + s) * stride) * kTileTokens : L;
                 if constexpr (kFp8) {
@@ -704,15 +745,21 @@ __device__ __forceinline__ void walk_policy(State& st, const bf16x8_t (&qb)[kKK]
 // The walk with the cache policy of its V loads fixed at compile time: a
 // runtime choice inside the loop put a branch around every V refill, and that
 // cost 1.3 us per call on the 8B-shaped batch and 10 us on the 70B-shaped one.
-template <int G, int D, bool kFp8 = false>
-__device__ __forceinline__ void walk(State& st, const bf16x8_t (&qb)[kKK], const int32_t* row, int stride,
-                                     int nk, int b0, int L, const WalkCtx& c, const AppendRow& app,
-                                     bool have_first = false, int tv0_first = 0, int tv1_first = 0) {
+// Returns whether tt now holds the first tiles of nxt.
+template <int G, int D, bool kFp8>
+__device__ __forceinline__ bool walk(State& st, typename TileOf<kFp8>::type (&tt)[D], bool primed,
+                                     const bf16x8_t (&qb)[kKK], const int32_t* row, int stride, int nk, int b0,
+                                     int L, const WalkCtx& c, const AppendRow& app, bool have_first = false,
+                                     int tv0_first = 0, int tv1_first = 0, const NextWalk& nxt = no_next_walk()) {
     if (kFp8 || c.keep_v)
-        walk_policy<G, D, kFp8, true>(st, qb, row, stride, nk, b0, L, c, app, have_first, tv0_first, tv1_first);
+        walk_policy<G, D, kFp8, true>(st, tt, primed, qb, row, stride, nk, b0, L, c, app, have_first, tv0_first,
+                                      tv1_first, nxt);
     else
-        walk_policy<G, D, kFp8, false>(st, qb, row, stride, nk, b0, L, c, app, have_first, tv0_first, tv1_first);
+        walk_policy<G, D, kFp8, false>(st, tt, primed, qb, row, stride, nk, b0, L, c, app, have_first, tv0_first,
+                                       tv1_first, nxt);
+    return nk > 0 && nxt.valid;
 }
+
 
 template <int G, bool kAnyB, bool kFp8>
 __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(DecodeArgs a) {
@@ -744,7 +791,8 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
     AppendRow none;
     none.active = false;
     none.krow = none.vrow = nullptr;
-    walk<G, 2, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
+    typename TileOf<kFp8>::type tt[2];
+    walk<G, 2, kFp8>(st, tt, false, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
     const float l_tot = total_l(st);
 
     // waves of the workgroup merge through LDS
@@ -949,6 +997,10 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     bool first_piece = true;
     bool pf_valid = false;   // table entries of the next piece fetched ahead
     int pf_seq = -1, pf_tv0 = 0, pf_tv1 = 0, pf_nb = 0;
+    // tiles in registers; `primed`: they hold the first tiles of the piece fetched ahead
+    static_assert(kBalancedDepth == 1, "a next piece is only known to have one tile");
+    typename TileOf<kFp8>::type tt[kBalancedDepth];
+    bool primed = false;
     while (t < t_end && seq < S) {
         const int n_here = (int)min((int64_t)(nblk - b), t_end - t);
         const bool whole = (b == 0) && (n_here == nblk);
@@ -972,6 +1024,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         // first table entries now, so that piece waits for its tiles only.
         const int tv0_here = pf_tv0, tv1_here = pf_tv1;
         pf_valid = false;
+        NextWalk nxt = no_next_walk();
         if (b + n_here == nblk && t + n_here < t_end) {
             const int nseq = kv + 1 < Hkv ? seq : seq + 1;
             if (nseq < S) {
@@ -984,10 +1037,18 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                 pf_nb = neighbour_entries<kFp8>(a, nseq, 0, c);
                 pf_seq = nseq;
                 pf_valid = true;
+                // its first tile is fetched by this walk's last refill (wasted if
+                // nseq turns out to be empty: the piece after it is then another one)
+                nxt.valid = true;
+                nxt.tv0 = pf.x;
+                nxt.tv1 = pf.y;
+                nxt.e0 = 0;
+                nxt.head_off = (size_t)(kv + 1 < Hkv ? kv + 1 : 0) * c.head_stride;
+                nxt.count = 1;
             }
         }
-        walk<G, kBalancedDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, app, use_pf,
-                                      tv0_here, tv1_here);
+        primed = walk<G, kBalancedDepth, kFp8>(st, tt, primed && use_pf, qb, a.tables + (size_t)seq * a.max_blocks, 1,
+                                               n_here, b, L, c, app, use_pf, tv0_here, tv1_here, nxt);
         const float l_tot = total_l(st);
 
         if (whole) {
@@ -1120,6 +1181,9 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
     none.krow = none.vrow = nullptr;
     bool pf_valid = false;   // table entries of the next partition fetched ahead
     int pf_kv = -1, pf_b = -1, pf_tv0 = 0, pf_tv1 = 0, pf_nb = 0;
+    // tiles in registers; `primed`: they hold the first tiles of the partition fetched ahead
+    typename TileOf<kFp8>::type tt[kPartitionDepth];
+    bool primed = false;
     while (seq < S) {
         if (b >= nblk) {   // past this (sequence, KV head): the next one with tiles
             b = 0;
@@ -1147,6 +1211,7 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
         // The next partition, when it lies in this sequence and in this slice:
         // fetch its first table entries now, so that it waits for its tiles only.
         pf_valid = false;
+        NextWalk nxt = no_next_walk();
         {
             int nb = b + pt, nkv = kv;
             if (nb >= nblk) {
@@ -1163,14 +1228,21 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
                 pf_kv = nkv;
                 pf_b = nb;
                 pf_valid = true;
+                // its first tiles are fetched by this walk's last refills
+                nxt.valid = true;
+                nxt.tv0 = pf.x;
+                nxt.tv1 = pf.y;
+                nxt.e0 = nb;
+                nxt.head_off = (size_t)nkv * c.head_stride;
+                nxt.count = min(64, min(pt, nblk - nb));   // its first chunk
             }
         }
         bf16x8_t qb[kKK];
         load_q<G, kFp8>(qb, a, seq, kv, c);
         State st;
         init_state(st);
-        walk<G, kPartitionDepth, kFp8>(st, qb, a.tables + (size_t)seq * a.max_blocks, 1, n_here, b, L, c, none, use_pf,
-                                       tv0_here, tv1_here);
+        primed = walk<G, kPartitionDepth, kFp8>(st, tt, primed && use_pf, qb, a.tables + (size_t)seq * a.max_blocks,
+                                                1, n_here, b, L, c, none, use_pf, tv0_here, tv1_here, nxt);
         const float l_tot = total_l(st);
 
         if (nparts == 1) {   // the whole context: the output itself
