@@ -254,14 +254,14 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void decode_kernel(DecodeArgs
 
 // Merge the partitions of one (sequence, query head): with M the largest
 // partition max, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
-// Four waves per (sequence, head): every thread takes part in the max over
-// the partitions, then wave w sums partitions w, w + 4, ... with kMergeU of
-// them in flight per lane (lane: dims 2l, 2l + 1), and the four partial sums
-// meet in LDS.  A long context has hundreds of partitions (128K tokens in
-// 512-token partitions: 256), so the partitions are not walked one load at a
-// time.
-constexpr int kMergeWaves = 4;
-constexpr int kMergeU = 8;
+// Eight waves per (sequence, head), one pass: wave w takes partitions w,
+// w + 8, ... kMergeU of them in flight per lane (lane: dims 2l, 2l + 1),
+// keeping its own running max (what it summed so far is rescaled when a batch
+// raises it); the eight partial states then meet in LDS.  A long context has
+// hundreds of partitions (128K tokens in 512-token partitions: 256), so each
+// wave takes them in one or two batches of loads rather than one at a time.
+constexpr int kMergeWaves = 8;
+constexpr int kMergeU = 16;
 
 template <int DT, int D>
 __global__ __launch_bounds__(kMergeWaves * kWave) void reduce_kernel(DecodeArgs a) {
@@ -284,20 +284,9 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void reduce_kernel(DecodeArgs 
     if (nparts <= 1) return;   // the decode kernel wrote this row itself
 
     const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + row * a.max_parts;
-    __shared__ float sm_red[kMergeWaves];
-    float M = -INFINITY;
-    for (int p = tid; p < nparts; p += kMergeWaves * kWave) M = fmaxf(M, ml[p].x);
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
-    if (lane == 0) sm_red[wave] = M;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, sm_red[w]);
-    const float Ms = safe_max(M);
-
     const float2* acc = reinterpret_cast<const float2*>(a.ws_acc) + (row * a.max_parts) * (D / 2) + lane;
     const bool active = lane * 2 < D;
-    float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
+    float M = -INFINITY, den = 0.0f, n0 = 0.0f, n1 = 0.0f;
     for (int p0 = wave; p0 < nparts; p0 += kMergeWaves * kMergeU) {
         float2 mlu[kMergeU], xu[kMergeU];
 #pragma unroll
@@ -307,6 +296,15 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void reduce_kernel(DecodeArgs 
             mlu[u] = live ? ml[p] : make_float2(-INFINITY, 0.0f);
             xu[u] = (live && active) ? acc[(size_t)p * (D / 2)] : make_float2(0.0f, 0.0f);
         }
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < kMergeU; ++u) mb = fmaxf(mb, mlu[u].x);
+        const float corr = fast_exp2(M - safe_max(mb));   // 0 for the first batch
+        den *= corr;
+        n0 *= corr;
+        n1 *= corr;
+        M = mb;
+        const float Ms = safe_max(M);
 #pragma unroll
         for (int u = 0; u < kMergeU; ++u) {
             const float f = fast_exp2(mlu[u].x - Ms);   // 0 for a missing partition
@@ -315,19 +313,28 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void reduce_kernel(DecodeArgs 
             n1 = fmaf(xu[u].y, f, n1);
         }
     }
+    __shared__ float sm_m[kMergeWaves];
     __shared__ float sm_den[kMergeWaves];
     __shared__ float2 sm_n[kMergeWaves][kWave];
-    if (lane == 0) sm_den[wave] = den;
+    if (lane == 0) {
+        sm_m[wave] = M;
+        sm_den[wave] = den;
+    }
     sm_n[wave][lane] = make_float2(n0, n1);
     __syncthreads();
     if (wave != 0 || !active) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, sm_m[w]);
+    const float Mts = safe_max(Mt);
     den = 0.0f;
     n0 = n1 = 0.0f;
 #pragma unroll
     for (int w = 0; w < kMergeWaves; ++w) {
-        den += sm_den[w];
-        n0 += sm_n[w][lane].x;
-        n1 += sm_n[w][lane].y;
+        const float f = fast_exp2(sm_m[w] - Mts);   // 0 for a wave that had no partition
+        den = fmaf(sm_den[w], f, den);
+        n0 = fmaf(sm_n[w][lane].x, f, n0);
+        n1 = fmaf(sm_n[w][lane].y, f, n1);
     }
     const int d = lane * 2;
     const float o0 = den > 0.0f ? n0 / den : 0.0f;

@@ -1319,9 +1319,12 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
         return (w == w0 && st < s0) ? 2 * w + 1 : 2 * w;
     };
 
-    // Records are taken 64 at a time: lane j holds the (m, l) pairs of record
-    // j0 + j; all lanes read two dims of each record's outputs, kU records'
-    // loads in flight together and issued before the (m, l) reduction.
+    // Records are taken 64 at a time, lane j holding the (m, l) pairs of record
+    // j0 + j.  Per block of records: the block's max of each head (a wave
+    // reduction), each lane's weight 2^(m_j - M) and the denominator (a wave
+    // sum); every lane then sums two dims of every head over the records in
+    // order, kU records' loads in flight at a time, and stops after the last
+    // record (a wave-uniform test: most pairs have two or three records).
     constexpr int kU = 8;
     float M[G], den[G], n0[G], n1[G];
 #pragma unroll
@@ -1333,7 +1336,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     for (int j0 = 0; j0 < nrec; j0 += kWave) {
         const int cnt = min(kWave, nrec - j0);
         const int64_t slot = lane < cnt ? slot_of(j0 + lane) : -1;
-        float m_j[G], l_j[G];
+        float m_j[G], l_j[G], f_j[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             m_j[h] = -INFINITY;
@@ -1349,37 +1352,40 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
         }
         for (int jj = 0; jj < cnt; jj += kU) {
             float2 x[kU][G];
-            bool live[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int64_t sl = readlane64(slot, min(jj + u, cnt - 1));
-                live[u] = (jj + u < cnt) && sl >= 0;
-                const float* rec = record_ptr<G>(a, live[u] ? sl : 0);
+                const bool live = jj + u < cnt && sl >= 0;   // wave-uniform
+                const float* rec = record_ptr<G>(a, live ? sl : 0);
 #pragma unroll
                 for (int h = 0; h < G; ++h)
-                    x[u][h] = live[u] ? *reinterpret_cast<const float2*>(rec + h * kD + d) : make_float2(0.0f, 0.0f);
+                    x[u][h] = live ? *reinterpret_cast<const float2*>(rec + h * kD + d) : make_float2(0.0f, 0.0f);
             }
-            // running reference: rescale what was summed so far when the max moves
+            if (jj == 0) {   // the block's weights, while the first loads are in flight
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float mb = -INFINITY;
+                for (int h = 0; h < G; ++h) {
+                    const float m_new = fmaxf(M[h], wave_max(m_j[h]));
+                    const float corr = fast_exp2(M[h] - safe_ref(m_new));   // 0 for the first block
+                    n0[h] *= corr;
+                    n1[h] *= corr;
+                    den[h] *= corr;
+                    M[h] = m_new;
+                    f_j[h] = slot >= 0 ? fast_exp2(m_j[h] - safe_ref(m_new)) : 0.0f;
+                    float w = l_j[h] * f_j[h];
 #pragma unroll
-                for (int u = 0; u < kU; ++u) mb = fmaxf(mb, readlane_f(m_j[h], min(jj + u, cnt - 1)));
-                const float m_new = fmaxf(M[h], mb);
-                const float corr = fast_exp2(M[h] - safe_ref(m_new));
-                n0[h] *= corr;
-                n1[h] *= corr;
-                den[h] *= corr;
-                M[h] = m_new;
+                    for (int off = kWave / 2; off > 0; off >>= 1) w += __shfl_xor(w, off, kWave);
+                    den[h] += w;
+                }
+            }
 #pragma unroll
-                for (int u = 0; u < kU; ++u) {
-                    const int src = min(jj + u, cnt - 1);
-                    const float mj = readlane_f(m_j[h], src);
-                    const float lj = readlane_f(l_j[h], src);
-                    const float f = live[u] ? fast_exp2(mj - safe_ref(M[h])) : 0.0f;
-                    den[h] = fmaf(lj, f, den[h]);
-                    n0[h] = fmaf(x[u][h].x, f, n0[h]);
-                    n1[h] = fmaf(x[u][h].y, f, n1[h]);
+            for (int u = 0; u < kU; ++u) {
+                if (jj + u < cnt) {   // wave-uniform
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float f = readlane_f(f_j[h], jj + u);
+                        n0[h] = fmaf(x[u][h].x, f, n0[h]);
+                        n1[h] = fmaf(x[u][h].y, f, n1[h]);
+                    }
                 }
             }
         }
