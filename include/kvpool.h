@@ -181,7 +181,7 @@ kv_status kv_build_slot_mapping(const int32_t* block_tables, int32_t num_rows,
  * Precondition: non-negative slots are unique (two tokens for one slot race).
  * num_tokens == 0 queues nothing.  Errors: KV_ERR_INVALID_ARGUMENT (null
  * handle or pointer, misalignment, layer out of range, num_tokens < 0),
- * KV_ERR_HIP.
+ * KV_ERR_UNSUPPORTED (num_kv_heads above 2^20), KV_ERR_HIP.
  */
 kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, const void* v_new,
                             const int64_t* slot_mapping, int64_t num_tokens, void* stream);

@@ -120,32 +120,33 @@ __global__ __launch_bounds__(kWave) void fp8_scale_kernel(ScatterArgs a) {
 
 // One thread per 16 codes: items ((token * 2 + {K,V}) * H + head) * 8 + chunk.
 __global__ __launch_bounds__(kQuantThreads) void fp8_quantize_kernel(ScatterArgs a) {
+    // workgroup y: one token at a time (its slot read once); x: its K and V
+    // code chunks ({K,V} * H + head) * kRowChunks8 + chunk, in 32 bits
     const int H = a.num_kv_heads;
-    const int64_t per_token = 2LL * H * kRowChunks8;
-    const int64_t total = a.num_tokens * per_token;
-    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-    for (int64_t item = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; item < total; item += stride) {
-        const int64_t t = item / per_token;
-        const int64_t rem = item - t * per_token;
-        const int which = (int)(rem / ((int64_t)H * kRowChunks8));
-        const int64_t rem2 = rem - (int64_t)which * H * kRowChunks8;
-        const int h = (int)(rem2 / kRowChunks8);
-        const int c = (int)(rem2 - (int64_t)h * kRowChunks8);
+    const int per_head = H * kRowChunks8;
+    for (int64_t t = blockIdx.y; t < a.num_tokens; t += gridDim.y) {
         const int64_t slot = a.slot_mapping[t];
         if (slot < 0 || slot >= a.num_slots) continue;
         const int64_t blk = slot / a.block_size;
-        const int64_t off = slot - blk * a.block_size;
-        const float s = (which == 0 ? a.k_scale : a.v_scale)[blk * H + h];
-        const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new) +
-                           ((t * H + h) * (kD8 / 8) + 2 * c);
-        const uint4 x0 = src[0], x1 = src[1];
-        uint4 o;
-        o.x = bf16x2_to_e4m3x2(x0.x, s) | (bf16x2_to_e4m3x2(x0.y, s) << 16);
-        o.y = bf16x2_to_e4m3x2(x0.z, s) | (bf16x2_to_e4m3x2(x0.w, s) << 16);
-        o.z = bf16x2_to_e4m3x2(x1.x, s) | (bf16x2_to_e4m3x2(x1.y, s) << 16);
-        o.w = bf16x2_to_e4m3x2(x1.z, s) | (bf16x2_to_e4m3x2(x1.w, s) << 16);
-        uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);
-        dst[((blk * H + h) * a.block_size + off) * kRowChunks8 + c] = o;
+        const int off = (int)(slot - blk * a.block_size);
+        for (int item = blockIdx.x * kQuantThreads + threadIdx.x; item < 2 * per_head;
+             item += gridDim.x * kQuantThreads) {
+            const int which = item >= per_head;
+            const int rem = item - which * per_head;
+            const int h = rem / kRowChunks8;
+            const int c = rem - h * kRowChunks8;
+            const float s = (which == 0 ? a.k_scale : a.v_scale)[blk * H + h];
+            const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new) +
+                               ((t * H + h) * (kD8 / 8) + 2 * c);
+            const uint4 x0 = src[0], x1 = src[1];
+            uint4 o;
+            o.x = bf16x2_to_e4m3x2(x0.x, s) | (bf16x2_to_e4m3x2(x0.y, s) << 16);
+            o.y = bf16x2_to_e4m3x2(x0.z, s) | (bf16x2_to_e4m3x2(x0.w, s) << 16);
+            o.z = bf16x2_to_e4m3x2(x1.x, s) | (bf16x2_to_e4m3x2(x1.y, s) << 16);
+            o.w = bf16x2_to_e4m3x2(x1.z, s) | (bf16x2_to_e4m3x2(x1.w, s) << 16);
+            uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);
+            dst[((blk * H + h) * a.block_size + off) * kRowChunks8 + c] = o;
+        }
     }
 }
 
@@ -185,10 +186,9 @@ hipError_t launch_scatter_fp8(const ScatterArgs& a, hipStream_t stream) {
     fp8_scale_kernel<<<dim3((unsigned)chunks, (unsigned)a.num_kv_heads), dim3(kWave), 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t total = a.num_tokens * 2LL * a.num_kv_heads * kRowChunks8;
-    int64_t blocks = (total + kQuantThreads - 1) / kQuantThreads;
-    if (blocks > 65536) blocks = 65536;   // grid-stride loop covers the rest
-    fp8_quantize_kernel<<<dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream>>>(a);
+    const unsigned gx = (unsigned)((2 * a.num_kv_heads * kRowChunks8 + kQuantThreads - 1) / kQuantThreads);
+    const unsigned gy = (unsigned)(a.num_tokens < 65535 ? a.num_tokens : 65535);   // grid-stride over the rest
+    fp8_quantize_kernel<<<dim3(gx, gy), dim3(kQuantThreads), 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -269,6 +269,8 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
     if (!k_new || !v_new || !slot_mapping) return fail(KV_ERR_INVALID_ARGUMENT, "NULL device pointer");
     if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) return fail(KV_ERR_INVALID_ARGUMENT, "slot_mapping must be 8-byte aligned");
+    if (pool->desc.num_kv_heads > (1 << 20))   // the kernels number a token's chunks in 32 bits
+        return fail(KV_ERR_UNSUPPORTED, "num_kv_heads %d above 2^20", pool->desc.num_kv_heads);
     kvp::ScatterArgs a;
     memset(&a, 0, sizeof a);
     a.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;

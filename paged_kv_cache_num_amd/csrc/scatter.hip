@@ -6,11 +6,12 @@
 // computed for it; head_dim is innermost, so each row is a contiguous,
 // vectorisable store even though the destinations are scattered.
 //
-// One thread moves one 16-byte chunk.  Work items are numbered
-//     ((token * 2 + {K,V}) * num_kv_heads + head) * row_chunks + chunk
-// so neighbouring lanes read neighbouring bytes of k_new / v_new and write
-// neighbouring bytes of one destination row (a 128-512 byte run).  The copy is
-// bit-exact: data moves as 32-bit words and is never converted.
+// One thread moves one 16-byte chunk; a workgroup takes one token, whose
+// chunks are numbered ({K,V} * num_kv_heads + head) * row_chunks + chunk, so
+// neighbouring lanes read neighbouring bytes of k_new / v_new and write
+// neighbouring bytes of one destination row (a 128-512 byte run).  The
+// token's slot is read once per workgroup and the chunk indices are 32-bit.
+// The copy is bit-exact: data moves as 32-bit words and is never converted.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -21,35 +22,33 @@ namespace {
 constexpr int kScatterThreads = 256;
 
 __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(ScatterArgs a) {
-    const int64_t chunks_per_token = 2LL * a.num_kv_heads * a.row_chunks;
-    const int64_t total = a.num_tokens * chunks_per_token;
-    const int64_t stride = (int64_t)gridDim.x * kScatterThreads;
-    for (int64_t item = (int64_t)blockIdx.x * kScatterThreads + threadIdx.x; item < total; item += stride) {
-        const int64_t t = item / chunks_per_token;
-        const int64_t rem = item - t * chunks_per_token;
-        const int which = (int)(rem / ((int64_t)a.num_kv_heads * a.row_chunks));   // 0: K, 1: V
-        const int64_t rem2 = rem - (int64_t)which * a.num_kv_heads * a.row_chunks;
-        const int h = (int)(rem2 / a.row_chunks);
-        const int c = (int)(rem2 - (int64_t)h * a.row_chunks);
-
+    // workgroup y: one token at a time (its slot is a wave-uniform value read
+    // once); x: the token's K and V chunks, numbered
+    // ({K,V} * num_kv_heads + head) * row_chunks + chunk (32-bit: the host
+    // allows at most 2^20 KV heads of at most 32 chunks)
+    const int per_head = a.num_kv_heads * a.row_chunks;
+    const int per_token = 2 * per_head;
+    for (int64_t t = blockIdx.y; t < a.num_tokens; t += gridDim.y) {
         const int64_t slot = a.slot_mapping[t];
         if (slot < 0 || slot >= a.num_slots) continue;   // padding token, or outside the pool
         const int64_t block = slot / a.block_size;
-        const int64_t offset = slot - block * a.block_size;
-
-        // destination row (block, head, offset) in 16-byte chunks
-        const int64_t dst_chunk = ((block * a.num_kv_heads + h) * a.block_size + offset) * a.row_chunks + c;
-        const int64_t src_chunk = (t * a.num_kv_heads + h) * a.row_chunks + c;
-        const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new);
-        uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);
-        dst[dst_chunk] = src[src_chunk];
+        const int offset = (int)(slot - block * a.block_size);
+        for (int item = blockIdx.x * kScatterThreads + threadIdx.x; item < per_token;
+             item += gridDim.x * kScatterThreads) {
+            const int which = item >= per_head;   // 0: K, 1: V
+            const int rem = item - which * per_head;
+            const int h = rem / a.row_chunks;
+            const int c = rem - h * a.row_chunks;
+            // destination row (block, head, offset) in 16-byte chunks
+            const int64_t dst_chunk = ((block * a.num_kv_heads + h) * a.block_size + offset) * a.row_chunks + c;
+            const int64_t src_chunk = (t * a.num_kv_heads + h) * a.row_chunks + c;
+            const uint4* src = reinterpret_cast<const uint4*>(which == 0 ? a.k_new : a.v_new);
+            uint4* dst = reinterpret_cast<uint4*>(which == 0 ? a.k_layer : a.v_layer);
+            dst[dst_chunk] = src[src_chunk];
+        }
     }
 }
 
-// Decode append without a slot mapping: the slot of sequence i's new row is
-// computed from its table and length on the device, the same formula the
-// host uses ("The write path": block_index * B + offset).  Work items are
-// numbered ((seq * 2 + {K,V}) * num_kv_heads + head) * row_chunks + chunk.
 __global__ __launch_bounds__(kScatterThreads) void append_scatter_kernel(AppendArgs a) {
     const int64_t per_seq = 2LL * a.num_kv_heads * a.row_chunks;
     const int64_t total = (int64_t)a.num_seqs * per_seq;
@@ -88,10 +87,10 @@ hipError_t launch_append_scatter(const AppendArgs& a, hipStream_t stream) {
 
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream) {
     if (a.num_tokens <= 0) return hipSuccess;
-    const int64_t total = a.num_tokens * 2LL * a.num_kv_heads * a.row_chunks;
-    int64_t blocks = (total + kScatterThreads - 1) / kScatterThreads;
-    if (blocks > 65536) blocks = 65536;   // grid-stride loop covers the rest
-    scatter_kernel<<<dim3((unsigned)blocks), dim3(kScatterThreads), 0, stream>>>(a);
+    const int per_token = 2 * a.num_kv_heads * a.row_chunks;
+    const unsigned gx = (unsigned)((per_token + kScatterThreads - 1) / kScatterThreads);
+    const unsigned gy = (unsigned)(a.num_tokens < 65535 ? a.num_tokens : 65535);   // grid-stride over the rest
+    scatter_kernel<<<dim3(gx, gy), dim3(kScatterThreads), 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -278,6 +278,11 @@ def test_scatter_argument_checks():
     assert L.reshape_and_cache(h, 0, 0x1000, 0x2000, 0x3000, -1, None) == K.KV_ERR_INVALID_ARGUMENT
     assert L.reshape_and_cache(h, 0, 0x1000, 0x2000, 0x3000, 0, None) == K.KV_OK
     K.lib.kv_pool_destroy(h)
+    # the scatter numbers a token's chunks in 32 bits: at most 2^20 KV heads
+    st, big = _pool(num_kv_heads=(1 << 20) + 1, num_blocks=1)
+    assert st == K.KV_OK
+    assert L.reshape_and_cache(big, 0, 0x1000, 0x2000, 0x3000, 4, None) == K.KV_ERR_UNSUPPORTED
+    K.lib.kv_pool_destroy(big)
 
 
 def test_status_strings():
