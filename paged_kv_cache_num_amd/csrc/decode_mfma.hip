@@ -33,8 +33,11 @@
 //   * Memory.  Block-table entries are fetched with one vector load per 64
 //     tiles and read out with readlane; a worker wave holds one tile in
 //     registers (fixed partitions: two), and each half of a tile's registers
-//     is refilled with the next tile as soon as it has been read.  V tiles of
-//     bf16 pools are loaded with the streaming hint (keep_v_cached).
+//     is refilled with the next tile as soon as it has been read, across the
+//     end of a walk too: the next piece's table entries are fetched while
+//     the current one runs, and its first tiles replace the current walk's
+//     last refills.  V tiles of bf16 pools are loaded with the streaming hint
+//     (keep_v_cached).
 //   * The walk order and all reductions depend only on logical positions, so
 //     the output is bitwise independent of where the blocks live.
 //   * FP8 pools (E4M3 codes, one fp32 scale per block and KV head for K and
