@@ -279,6 +279,8 @@ def main(argv=None):
     ap.add_argument("--no-identity", action="store_true",
                     help="skip timing the same batch with contiguous (identity-like) block tables")
     ap.add_argument("--no-copy-blocks", action="store_true", help="skip timing copy-on-write block copies")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="batches with a shared prompt: time only the plain call, not paged_attention_decode_shared")
     ap.add_argument("--no-swap", action="store_true", help="skip timing swap of the batch's blocks to host and back")
     ap.add_argument("--table-walk-probe", type=int, default=0, metavar="N",
                     help="also run the table-walk probe N times in each workgroup ordering (for counter runs)")
@@ -451,6 +453,63 @@ def main(argv=None):
             assert torch.equal(step.out.view(torch.int16) if step.out.dtype == torch.bfloat16 else step.out,
                                ref_out.view(torch.int16) if ref_out.dtype == torch.bfloat16 else ref_out), \
                 "fused step output differs from scatter + attention"
+
+    # A batch whose sequences share a prompt (the prefix-sharing workload: its
+    # block manager knows the 128 shared blocks): the same step with
+    # paged_attention_decode_shared, checked against the plain call's output
+    # and timed the same ways; the faster form is the headline.
+    shared = None
+    head_step = step
+    roofline_kernel = "paged_attention_decode"
+    sb = int(wl.info.get("shared_prefix_blocks") or 0)
+    if sb and not fp8 and part == 0 and wl.dtype == "bf16" and not args.no_shared:
+        sstep = DecodeStep.from_workload(wl, partition_size=0, shared_blocks=sb)
+        for _ in range(args.warmup):
+            sstep.run()
+        step.run()
+        sstep.run()
+        torch.cuda.synchronize()
+        diff = float((sstep.out.float() - step.out.float()).abs().max())
+        assert diff <= 2e-2, f"shared-prefix call differs from the plain call by {diff}"
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            sstep.scatter()
+            sev[i][0].record()
+            sstep.attend()
+            sev[i][1].record()
+        torch.cuda.synchronize()
+        sh_us = [a.elapsed_time(b) * 1e3 for a, b in sev]
+        sh_mean = sum(sh_us) / K
+        sh_graph_ms = None
+        if not args.eager:
+            graph = sstep.capture()
+            graph.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(K):
+                graph.replay()
+            torch.cuda.synchronize()
+            sh_graph_ms = (time.perf_counter() - t0) * 1e3 / K
+            del graph
+        shared = {"shared_blocks": sb, "attn_us_mean": round(sh_mean, 2),
+                  "attn_us_p50": round(percentile(sh_us, 0.5), 2),
+                  "achieved_gbps": round(nbytes["attn"] / (sh_mean * 1e-6) / 1e9, 1),
+                  "frac": round(nbytes["attn"] / (sh_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                  "graph_ms_per_step": round(sh_graph_ms, 5) if sh_graph_ms is not None else None,
+                  "plain_attn_us_mean": round(attn_mean, 2), "plain_ms_per_step": round(ms_per_step, 5),
+                  "max_abs_diff_vs_plain": diff}
+        print(f"bench: shared-prefix call {sh_mean:.1f} us (plain {attn_mean:.1f} us)", file=sys.stderr, flush=True)
+        faster = sh_graph_ms < ms_per_step if sh_graph_ms is not None else sh_mean < attn_mean
+        if faster:
+            if sh_graph_ms is not None:
+                ms_per_step = sh_graph_ms
+                launch = "hip_graph, scatter + shared-prefix attention"
+            attn_us, attn_mean = sh_us, sh_mean
+            achieved = nbytes["attn"] / (attn_mean * 1e-6) / 1e9
+            head_step = sstep
+            roofline_kernel = "paged_attention_decode_shared"
+        else:
+            del sstep
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     cold = None
@@ -462,7 +521,7 @@ def main(argv=None):
             probe_read(big, sink)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            step.attend()
+            head_step.attend()
             b.record()
             b.synchronize()
             cold_us.append(a.elapsed_time(b) * 1e3)
@@ -617,7 +676,7 @@ def main(argv=None):
                    "seed": wl.info.get("seed")},
         "tokens_per_s_per_layer": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": roofline_kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": nbytes["attn"],
                      "launch_us_mean": round(attn_mean, 2), "launch_us_p10": round(percentile(attn_us, 0.1), 2),
@@ -632,6 +691,7 @@ def main(argv=None):
         "blocks_per_seq_mean": round(nbytes["blocks"] / max(1, wl.num_seqs), 2),
         "internal_waste_tokens": int(nbytes["blocks"] * wl.block_size - int(np.sum(wl.context_lens))),
         "identity_tables": identity,
+        "shared_prefix": shared,
         "table_walk_probe": table_walk,
         "copy_blocks": copy,
         "swap": swap,

@@ -316,9 +316,10 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
  * copy-on-write).  In the balanced mode the wave that reads that block writes
  * the row into the pool and uses it directly (one kernel, no separate scatter);
  * other modes run a small scatter kernel first.  A block index outside the pool
- * is skipped, as by reshape_and_cache.  FP8 pools always run a small append
- * kernel first (the row is quantized; a row at position 0 of its block sets
- * that block's scales from itself alone), then the decode.
+ * is skipped, as by reshape_and_cache.  FP8 pools: the row is quantized (a row
+ * at position 0 of its block sets that block's scales from itself alone); in
+ * the balanced mode the attention kernel does it, other modes run a small
+ * append kernel first.
  */
 kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out, const void* q,
                                         const void* k_new, const void* v_new, const int32_t* block_tables,
@@ -326,6 +327,45 @@ kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out
                                         int32_t num_q_heads, float scale, int32_t max_context_len,
                                         int32_t partition_size, void* workspace, uint64_t workspace_bytes,
                                         void* stream);
+
+/*
+ * GPU step, a batch with a common prefix ([KVC] "Prefix sharing, reference
+ * counts, and copy-on-write"; [PIF] "03 Sharing via copy-on-write"): the same
+ * result as paged_attention_decode with partition_size 0, up to rounding
+ * order, when the first shared_blocks entries of every sequence's table name
+ * the same blocks (the block manager's shared, reference-counted prompt).
+ * Each (block, KV head) tile of that prefix is then read once for up to
+ * sixteen query heads of several sequences together, instead of once per
+ * sequence; the rest of each context goes through the balanced split; a
+ * third kernel merges the two.
+ *   shared_blocks: host, >= 0; 0 runs paged_attention_decode with
+ *                  partition_size 0.  shared_blocks * B <= max_context_len and
+ *                  <= max_blocks_per_seq * B.
+ *   workspace:     device, >= paged_attention_shared_workspace_bytes(...)
+ *                  bytes, 16-byte aligned; contents on entry do not matter.
+ *   Every other argument as for paged_attention_decode.
+ * Preconditions (device data, not checked): block_tables[i][b] ==
+ * block_tables[0][b] for every i and b < shared_blocks, and L_i >=
+ * shared_blocks * B for every i (a sequence with L_i == 0 still gives zeros).
+ * The prefix is read through sequence 0's table row.  Built for bf16 pools
+ * with head_dim 128 and block size 16 and at most 1024 sequences
+ * (KV_ERR_UNSUPPORTED otherwise); no decode-append form.  Errors as for
+ * paged_attention_decode.
+ */
+kv_status paged_attention_decode_shared(kv_pool_t pool, int32_t layer, void* out, const void* q,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                        float scale, int32_t max_context_len, int32_t shared_blocks,
+                                        void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * Host: workspace bytes paged_attention_decode_shared needs for these sizes
+ * (shared_blocks 0: those of paged_attention_decode with partition_size 0).
+ * Errors: KV_ERR_INVALID_ARGUMENT, KV_ERR_UNSUPPORTED, as for the call.
+ */
+kv_status paged_attention_shared_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t max_context_len, int32_t max_blocks_per_seq,
+                                                 int32_t shared_blocks, uint64_t* bytes);
 
 /* Static name of a status code ("KV_OK", ...); never NULL. */
 const char* kv_status_string(kv_status status);

@@ -428,7 +428,7 @@ template <bool kFp8>
 __device__ __forceinline__ bool keep_v_cached(const DecodeArgs& a, int seq, int tile, const WalkCtx& c) {
     if (kFp8) return true;   // FP8 tiles: the hint measured no different (8B, 70B, long-context batches)
     const int entry = c.pair8 ? 2 * tile : tile >> c.sub_shift;
-    const int32_t* t = a.tables + (size_t)seq * a.max_blocks + entry;
+    const int32_t* t = a.tables + (size_t)seq * a.max_blocks + a.shared_tiles + entry;
     const int32_t mine = t[0];
     bool shared = false;
     if (seq > 0) shared = shared || t[-(ptrdiff_t)a.max_blocks] == mine;
@@ -445,8 +445,8 @@ __device__ __forceinline__ int neighbour_entries(const DecodeArgs& a, int seq, i
     int x = 0;
     if (!kFp8) {
         const int entry = c.pair8 ? 2 * tile : tile >> c.sub_shift;
-        if (c.lane == 0 && seq > 0) x = a.tables[(size_t)(seq - 1) * a.max_blocks + entry];
-        if (c.lane == 1 && seq + 1 < a.num_seqs) x = a.tables[(size_t)(seq + 1) * a.max_blocks + entry];
+        if (c.lane == 0 && seq > 0) x = a.tables[(size_t)(seq - 1) * a.max_blocks + a.shared_tiles + entry];
+        if (c.lane == 1 && seq + 1 < a.num_seqs) x = a.tables[(size_t)(seq + 1) * a.max_blocks + a.shared_tiles + entry];
     }
     return x;
 }
@@ -860,6 +860,18 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
     return L < 0 ? 0 : (L > max_context ? max_context : L);
 }
 
+// Tokens of sequence i that the balanced walk covers: its context past a
+// shared prefix (all of it when there is none).
+__device__ __forceinline__ int walk_len(const DecodeArgs& a, int i) {
+    const int L = clamp_len(a.lens[i], a.max_context) - a.shared_tiles * kTileTokens;
+    return L > 0 ? L : 0;
+}
+
+// Table row of sequence i from the first tile the balanced walk covers.
+__device__ __forceinline__ const int32_t* walk_row(const DecodeArgs& a, int i) {
+    return a.tables + (size_t)i * a.max_blocks + a.shared_tiles;
+}
+
 // Partial state of one (sequence, KV head) piece: the unnormalised output of
 // each head, then m and l of each head, padded so every record starts on a
 // 16-byte boundary.
@@ -950,7 +962,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
         const int i = ch * kWave + lane;
-        len_c[ch] = (ch < nchunks && i < S) ? clamp_len(a.lens[i], a.max_context) : 0;
+        len_c[ch] = (ch < nchunks && i < S) ? walk_len(a, i) : 0;
     }
     int64_t ex_c[kMaxChunks];
     int64_t T = 0;
@@ -1033,8 +1045,9 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
             if (nseq < S) {
                 // tiles 0..63 of the next sequence's row; a lane whose tile would
                 // need an entry past the row loads nothing (the walk never reads it)
-                const bool ok = c.pair8 ? 2 * c.lane < a.max_blocks : (c.lane >> c.sub_shift) < a.max_blocks;
-                const int2 pf = tile_entries(a.tables + (size_t)nseq * a.max_blocks, c.lane, ok, c);
+                const int row_len = a.max_blocks - a.shared_tiles;
+                const bool ok = c.pair8 ? 2 * c.lane < row_len : (c.lane >> c.sub_shift) < row_len;
+                const int2 pf = tile_entries(walk_row(a, nseq), c.lane, ok, c);
                 pf_tv0 = pf.x;
                 pf_tv1 = pf.y;
                 pf_nb = neighbour_entries<kFp8>(a, nseq, 0, c);
@@ -1050,11 +1063,26 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                 nxt.count = 1;
             }
         }
-        primed = walk<G, kBalancedDepth, kFp8>(st, tt, primed && use_pf, qb, a.tables + (size_t)seq * a.max_blocks, 1,
-                                               n_here, b, L, c, app, use_pf, tv0_here, tv1_here, nxt);
+        primed = walk<G, kBalancedDepth, kFp8>(st, tt, primed && use_pf, qb, walk_row(a, seq), 1, n_here, b, L, c,
+                                               app, use_pf, tv0_here, tv1_here, nxt);
         const float l_tot = total_l(st);
 
-        if (whole) {
+        if (whole && a.shared_tiles > 0) {   // after a shared prefix: a state for the fix-up to merge
+            const int slots = a.prefix_parts + 1;
+            const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * c.r + j;
+                if (h < G) {
+                    float4* dst = reinterpret_cast<float4*>(a.ws_pacc + ((row0 + h) * slots + a.prefix_parts) * kD +
+                                                            c.n * 8);
+                    dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
+                    dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
+                }
+            }
+            if (c.r == 0 && c.n < G)
+                reinterpret_cast<float2*>(a.ws_pml)[(row0 + c.n) * slots + a.prefix_parts] = make_float2(st.m, l_tot);
+        } else if (whole) {
             uint4* orow = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * kRC;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -1097,7 +1125,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                 kv = 0;
                 do {
                     ++seq;
-                    L = (seq < S) ? __builtin_amdgcn_readfirstlane(clamp_len(a.lens[seq], a.max_context)) : 0;
+                    L = (seq < S) ? __builtin_amdgcn_readfirstlane(walk_len(a, seq)) : 0;
                     nblk = (L + kTileTokens - 1) / kTileTokens;
                 } while (nblk == 0 && seq < S && t < t_end);
             }
@@ -1283,6 +1311,73 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Shared prefix (paged_attention_decode_shared).  The caller's block manager
+// knows that the first shared_tiles table entries of every sequence name the
+// same blocks (a common prompt: [KVC] "Prefix sharing, reference counts, and
+// copy-on-write", [PIF] "03 Sharing via copy-on-write"), so each (block, KV
+// head) tile of the prefix is read once for sixteen query columns instead of
+// once per sequence: the G query heads of 16 / G consecutive sequences fill
+// the score MFMA's sixteen columns and the P V MFMA's sixteen rows, which one
+// sequence's G heads leave mostly zero.  Wave (column block qb, KV head kv,
+// part p) walks prefix tiles [p PT, (p + 1) PT) of sequence 0's table row and
+// leaves each column's (m, l, unnormalised output) in slot p of the prefix
+// states; neighbouring workgroups take different KV heads (and XCDs), so the
+// waves of one XCD share a KV head's prefix tiles in its L2.  The fix-up
+// merges these states with the balanced walk of what follows the prefix.
+// ---------------------------------------------------------------------------
+constexpr int kPrefixDepth = 2;   // prefix tiles are mostly cache hits: two in flight per wave
+
+template <int G>
+__global__ __launch_bounds__(kWave) void decode_prefix_kernel(DecodeArgs a) {
+    constexpr int kSeqs = 16 / G;   // sequences per column block
+    const int Hkv = a.num_kv_heads;
+    const int kv = blockIdx.x % Hkv;
+    const int qb = blockIdx.x / Hkv;
+    const int p = blockIdx.y;
+    const int b0 = p * a.prefix_part_tiles;
+    const int nk = min(a.prefix_part_tiles, a.shared_tiles - b0);   // >= 1: the host sizes the parts
+
+    WalkCtx c = make_ctx<false, false>(a, kv);
+    c.keep_v = true;   // every column block reads these tiles
+    // column n: query head n % G of sequence qb * kSeqs + n / G (zero past the batch)
+    const int col_seq = qb * kSeqs + c.n / G;
+    const bool col_ok = col_seq < a.num_seqs;
+    const size_t col_row = (size_t)(col_ok ? col_seq : 0) * a.num_q_heads + (size_t)kv * G + c.n % G;
+    bf16x8_t qb_op[kKK];
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.q) + col_row * kRC;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (col_ok) x = qrow[kk * 4 + c.r];
+        qb_op[kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+    State st;
+    init_state(st);
+    AppendRow none;
+    none.active = false;
+    none.krow = none.vrow = nullptr;
+    typename TileOf<false>::type tt[kPrefixDepth];
+    // every sequence covers the whole prefix: no position is masked
+    walk<16, kPrefixDepth, false>(st, tt, false, qb_op, a.tables, 1, nk, b0, a.shared_tiles * kTileTokens, c, none);
+    const float l_tot = total_l(st);
+
+    // lane (r, n): outputs of columns 4r .. 4r+3, dims 8n .. 8n+7; (m, l) of column n
+    const int slots = a.prefix_parts + 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = 4 * c.r + j;
+        const int sq = qb * kSeqs + col / G;
+        if (sq < a.num_seqs) {
+            const size_t row = (size_t)sq * a.num_q_heads + (size_t)kv * G + col % G;
+            float4* dst = reinterpret_cast<float4*>(a.ws_pacc + (row * slots + p) * kD + c.n * 8);
+            dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
+            dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
+        }
+    }
+    if (c.r == 0 && col_ok) reinterpret_cast<float2*>(a.ws_pml)[col_row * slots + p] = make_float2(st.m, l_tot);
+}
+
 // Fix-up for one (sequence, KV head): zeros for an empty sequence; nothing if
 // one slice held it whole; otherwise the log-sum-exp merge of the partial
 // states its slices left.  With fewer tiles than workers some slices are
@@ -1297,22 +1392,26 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     const int seq = blockIdx.y;
     const int lane = threadIdx.x;
     // the length and the two prefix sums are independent: one memory round trip for all three
-    const int L = clamp_len(a.lens[seq], a.max_context);
+    const int L_all = clamp_len(a.lens[seq], a.max_context);
     const int64_t T = a.ws_prefix[a.num_seqs];
     const int64_t first_tile = a.ws_prefix[seq];
     uint32_t* out = reinterpret_cast<uint32_t*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * (kD / 2);
-    if (L == 0) {
+    if (L_all == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) out[h * (kD / 2) + lane] = 0u;
         return;
     }
+    // with a shared prefix the balanced walk covered only the tokens after it
+    const bool shared = a.shared_tiles > 0;
+    const int L = shared ? (L_all > a.shared_tiles * kTileTokens ? L_all - a.shared_tiles * kTileTokens : 0) : L_all;
     const int nblk = (L + kTileTokens - 1) / kTileTokens;   // 16-token tiles
     const int64_t W = num_workers;
     const int64_t s0 = first_tile + (int64_t)kv * nblk;
-    const int64_t w0 = worker_of(s0, T, W);
-    const int64_t w1 = worker_of(s0 + nblk - 1, T, W);
-    if (w0 == w1) return;   // written by its worker
-    const int nrec = (int)(w1 - w0 + 1);
+    const int64_t w0 = nblk > 0 ? worker_of(s0, T, W) : 0;
+    const int64_t w1 = nblk > 0 ? worker_of(s0 + nblk - 1, T, W) : 0;
+    if (w0 == w1 && !shared) return;   // written by its worker
+    // records of the slices that split the walk (none when one slice held it whole)
+    const int nrec = (nblk > 0 && w0 != w1) ? (int)(w1 - w0 + 1) : 0;
 
     // record slot of worker w0 + j, or -1 for an empty slice
     auto slot_of = [&](int j) -> int64_t {
@@ -1336,6 +1435,46 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
         den[h] = n0[h] = n1[h] = 0.0f;
     }
     const int d = lane * 2;
+    if (shared) {
+        // the prefix parts, then (when one slice held the rest whole) its state,
+        // in slot order; each lane two dims of every head
+        const int slots = a.prefix_parts + 1;
+        const int nslot = a.prefix_parts + (nblk > 0 && w0 == w1 ? 1 : 0);
+        const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G;
+        constexpr int kUP = 32 / G;   // slots in flight per batch (128 registers of loads)
+        for (int p0 = 0; p0 < nslot; p0 += kUP) {
+            float2 ml[kUP][G], x[kUP][G];
+#pragma unroll
+            for (int u = 0; u < kUP; ++u) {
+                const bool live = p0 + u < nslot;   // wave-uniform
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const size_t slot = (row0 + h) * slots + (live ? p0 + u : 0);
+                    ml[u][h] = live ? reinterpret_cast<const float2*>(a.ws_pml)[slot] : make_float2(-INFINITY, 0.0f);
+                    x[u][h] = live ? *reinterpret_cast<const float2*>(a.ws_pacc + slot * kD + d)
+                                   : make_float2(0.0f, 0.0f);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float mb = M[h];
+#pragma unroll
+                for (int u = 0; u < kUP; ++u) mb = fmaxf(mb, ml[u][h].x);
+                const float corr = fast_exp2(M[h] - safe_ref(mb));   // 0 for the first batch
+                n0[h] *= corr;
+                n1[h] *= corr;
+                den[h] *= corr;
+                M[h] = mb;
+#pragma unroll
+                for (int u = 0; u < kUP; ++u) {
+                    const float f = fast_exp2(ml[u][h].x - safe_ref(mb));   // 0 for an absent slot
+                    den[h] = fmaf(ml[u][h].y, f, den[h]);
+                    n0[h] = fmaf(x[u][h].x, f, n0[h]);
+                    n1[h] = fmaf(x[u][h].y, f, n1[h]);
+                }
+            }
+        }
+    }
     for (int j0 = 0; j0 < nrec; j0 += kWave) {
         const int cnt = min(kWave, nrec - j0);
         const int64_t slot = lane < cnt ? slot_of(j0 + lane) : -1;
@@ -1553,6 +1692,24 @@ hipError_t launch_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_bf16_shared(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+    if (a.shared_tiles <= 0 || a.prefix_parts <= 0 || a.prefix_part_tiles <= 0 || a.block_size != kTileTokens ||
+        (int64_t)(a.prefix_parts - 1) * a.prefix_part_tiles >= a.shared_tiles || !a.ws_pml || !a.ws_pacc || a.k_append)
+        return hipErrorInvalidValue;
+    const unsigned blocks = (unsigned)(((int64_t)a.num_seqs * group + 15) / 16 * a.num_kv_heads);
+    dim3 grid(blocks, (unsigned)a.prefix_parts);
+    switch (group) {
+        case 1: decode_prefix_kernel<1><<<grid, kWave, 0, stream>>>(a); break;
+        case 2: decode_prefix_kernel<2><<<grid, kWave, 0, stream>>>(a); break;
+        case 4: decode_prefix_kernel<4><<<grid, kWave, 0, stream>>>(a); break;
+        case 8: decode_prefix_kernel<8><<<grid, kWave, 0, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_streamk<false>(a, group, workers, stream);
+}
 
 hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
     return launch_streamk<false>(a, group, workers, stream);

@@ -118,6 +118,50 @@ Plan plan_decode(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, i
     return p;
 }
 
+// A shared-prefix call: the balanced plan, then the prefix states
+// [S][Hq][parts + 1] x (m, l) and x head_dim.  The prefix is cut into parts
+// so that the prefix kernel runs about two waves per worker of the balanced
+// split, every part non-empty.
+struct SharedPlan {
+    Plan base;
+    int32_t parts;
+    int32_t part_tiles;
+    uint64_t pml_off, pacc_off, total;
+};
+
+SharedPlan plan_shared(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                       int32_t shared_blocks) {
+    SharedPlan sp;
+    memset(&sp, 0, sizeof sp);
+    sp.base = plan_decode(d, num_seqs, num_q_heads, max_context_len, 0);
+    const int64_t group = num_q_heads / d.num_kv_heads;
+    const int64_t column_blocks = ((int64_t)num_seqs * group + 15) / 16 * d.num_kv_heads;
+    const int64_t want = (2 * (int64_t)sp.base.workers + column_blocks - 1) / (column_blocks > 0 ? column_blocks : 1);
+    int64_t parts = want < 1 ? 1 : (want > shared_blocks ? shared_blocks : want);
+    sp.part_tiles = (int32_t)((shared_blocks + parts - 1) / parts);
+    sp.parts = (int32_t)((shared_blocks + sp.part_tiles - 1) / sp.part_tiles);
+    const uint64_t states = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)(sp.parts + 1);
+    sp.pml_off = round_up(sp.base.ws_total, 256u);
+    sp.pacc_off = sp.pml_off + round_up(states * 8u, 256u);
+    sp.total = sp.pacc_off + states * (uint64_t)d.head_dim * 4u;
+    return sp;
+}
+
+// Shapes the shared-prefix kernels cover.
+kv_status check_shared(const kv_pool_desc& d, int32_t num_seqs, int32_t max_context_len, int32_t max_blocks_per_seq,
+                       int32_t shared_blocks) {
+    if (shared_blocks < 0) return fail(KV_ERR_INVALID_ARGUMENT, "shared_blocks %d < 0", shared_blocks);
+    if (shared_blocks == 0) return KV_OK;
+    if (d.dtype != KV_BF16 || d.head_dim != 128 || d.block_size != kvp::kTileTokens)
+        return fail(KV_ERR_UNSUPPORTED, "a shared prefix needs a bf16 pool with head_dim 128 and block size 16");
+    if (num_seqs > kvp::kStreamKMaxSeqs)
+        return fail(KV_ERR_UNSUPPORTED, "a shared prefix is handled for at most %d sequences", kvp::kStreamKMaxSeqs);
+    if (shared_blocks > max_blocks_per_seq || (int64_t)shared_blocks * d.block_size > max_context_len)
+        return fail(KV_ERR_INVALID_ARGUMENT, "shared_blocks %d exceeds max_blocks_per_seq %d or max_context_len %d / %d",
+                    shared_blocks, max_blocks_per_seq, max_context_len, d.block_size);
+    return KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -430,7 +474,7 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
                       const void* v_append, const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                       int32_t max_context_len, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-                      void* stream) {
+                      void* stream, int32_t shared_blocks = 0) {
     if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "pool is NULL");
     const kv_pool_desc& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers) return fail(KV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, d.num_layers);
@@ -461,13 +505,20 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
     if (append && (!k_append || !v_append || !aligned16(k_append) || !aligned16(v_append)))
         return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new must both be non-NULL and 16-byte aligned");
 
-    const Plan plan = plan_decode(d, num_seqs, num_q_heads, max_context_len, partition_size);
+    if (shared_blocks > 0) {
+        const kv_status st = check_shared(d, num_seqs, max_context_len, max_blocks_per_seq, shared_blocks);
+        if (st != KV_OK) return st;
+    }
+    const SharedPlan sp = shared_blocks > 0 ? plan_shared(d, num_seqs, num_q_heads, max_context_len, shared_blocks)
+                                            : SharedPlan{};
+    const Plan plan = shared_blocks > 0 ? sp.base : plan_decode(d, num_seqs, num_q_heads, max_context_len, partition_size);
+    const uint64_t ws_needed = shared_blocks > 0 ? sp.total : plan.ws_total;
     kvp::DecodeArgs a;
     memset(&a, 0, sizeof a);
-    if (plan.ws_total > 0) {
-        if (!workspace || workspace_bytes < plan.ws_total)
+    if (ws_needed > 0) {
+        if (!workspace || workspace_bytes < ws_needed)
             return fail(KV_ERR_WORKSPACE_TOO_SMALL, "workspace of %llu bytes given, %llu needed",
-                        (unsigned long long)workspace_bytes, (unsigned long long)plan.ws_total);
+                        (unsigned long long)workspace_bytes, (unsigned long long)ws_needed);
         if (!aligned16(workspace)) return fail(KV_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
         char* ws = static_cast<char*>(workspace);
         if (plan.mode == Mode::kBalanced) {
@@ -476,6 +527,10 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
             a.ws_ml = reinterpret_cast<float*>(ws);
         }
         a.ws_acc = reinterpret_cast<float*>(ws + plan.ws_first);
+        if (shared_blocks > 0) {
+            a.ws_pml = reinterpret_cast<float*>(ws + sp.pml_off);
+            a.ws_pacc = reinterpret_cast<float*>(ws + sp.pacc_off);
+        }
     }
     a.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
     a.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
@@ -499,7 +554,13 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
         a.v_scale = pool->v_scale + (uint64_t)layer * pool->scale_layer;
     }
     hipError_t e;
-    if (plan.mode == Mode::kBalanced) {
+    if (shared_blocks > 0) {
+        a.shared_tiles = shared_blocks;   // block size 16: one tile per block
+        a.prefix_parts = sp.parts;
+        a.prefix_part_tiles = sp.part_tiles;
+        e = kvp::launch_decode_bf16_shared(a, num_q_heads / d.num_kv_heads, plan.workers,
+                                           static_cast<hipStream_t>(stream));
+    } else if (plan.mode == Mode::kBalanced) {
         // the worker that owns each (sequence, KV head)'s last block uses the new row
         // (FP8: quantized in registers); extra waves of the same launch store it
         a.k_append = k_append;
@@ -561,6 +622,34 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
     return decode_impl(pool, layer, out, q, nullptr, nullptr, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, scale, max_context_len, partition_size, workspace, workspace_bytes,
                        stream);
+}
+
+kv_status paged_attention_decode_shared(kv_pool_t pool, int32_t layer, void* out, const void* q,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                        float scale, int32_t max_context_len, int32_t shared_blocks, void* workspace,
+                                        uint64_t workspace_bytes, void* stream) {
+    if (shared_blocks < 0) return fail(KV_ERR_INVALID_ARGUMENT, "shared_blocks %d < 0", shared_blocks);
+    return decode_impl(pool, layer, out, q, nullptr, nullptr, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, max_context_len, 0, workspace, workspace_bytes, stream,
+                       shared_blocks);
+}
+
+kv_status paged_attention_shared_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int32_t num_q_heads,
+                                                 int32_t max_context_len, int32_t max_blocks_per_seq,
+                                                 int32_t shared_blocks, uint64_t* bytes) {
+    if (!pool || !bytes) return fail(KV_ERR_INVALID_ARGUMENT, "NULL argument");
+    *bytes = 0;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_blocks_per_seq <= 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "negative size argument");
+    if (num_q_heads % pool->desc.num_kv_heads != 0)
+        return fail(KV_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                    pool->desc.num_kv_heads);
+    const kv_status st = check_shared(pool->desc, num_seqs, max_context_len, max_blocks_per_seq, shared_blocks);
+    if (st != KV_OK) return st;
+    *bytes = shared_blocks > 0 ? plan_shared(pool->desc, num_seqs, num_q_heads, max_context_len, shared_blocks).total
+                               : plan_decode(pool->desc, num_seqs, num_q_heads, max_context_len, 0).ws_total;
+    return ok();
 }
 
 kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out, const void* q, const void* k_new,

@@ -32,7 +32,8 @@ EXPORTED = (
     "kv_pool_bytes", "kv_pool_scale_bytes", "kv_pool_create", "kv_pool_create_fp8", "kv_pool_destroy",
     "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
-    "paged_attention_decode_append", "kv_copy_blocks", "kv_swap_bytes", "kv_swap_out", "kv_swap_in",
+    "paged_attention_decode_append", "paged_attention_decode_shared", "paged_attention_shared_workspace_bytes",
+    "kv_copy_blocks", "kv_swap_bytes", "kv_swap_out", "kv_swap_in",
     "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read", "kv_probe_table_walk",
     "kv_probe_e4m3_to_bf16", "kv_probe_f32_to_e4m3",
 )
@@ -92,6 +93,10 @@ def _load():
     lib.kv_swap_out.argtypes = [vp, vp, i32, vp, u64, vp]
     lib.kv_swap_in.restype = ctypes.c_int
     lib.kv_swap_in.argtypes = [vp, vp, i32, vp, u64, vp]
+    lib.paged_attention_decode_shared.restype = ctypes.c_int
+    lib.paged_attention_decode_shared.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32, vp, u64, vp]
+    lib.paged_attention_shared_workspace_bytes.restype = ctypes.c_int
+    lib.paged_attention_shared_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i32, P(u64)]
     lib.paged_attention_decode_append.restype = ctypes.c_int
     lib.paged_attention_decode_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32,
                                                   vp, u64, vp]
@@ -301,6 +306,40 @@ class KVPool:
                                           S, Hq, float(scale), int(max_context_len), int(partition_size),
                                           ws_ptr, int(ws_bytes), _stream_handle(stream)),
                "paged_attention_decode")
+
+    def shared_workspace_bytes(self, num_seqs: int, num_q_heads: int, max_context_len: int,
+                               max_blocks_per_seq: int, shared_blocks: int) -> int:
+        out = ctypes.c_uint64(0)
+        _check(lib.paged_attention_shared_workspace_bytes(self.handle, int(num_seqs), int(num_q_heads),
+                                                          int(max_context_len), int(max_blocks_per_seq),
+                                                          int(shared_blocks), ctypes.byref(out)),
+               "paged_attention_shared_workspace_bytes")
+        return int(out.value)
+
+    def paged_attention_decode_shared(self, layer: int, out, q, block_tables, context_lens, *,
+                                      scale: float, max_context_len: int, shared_blocks: int,
+                                      workspace=None, stream=None) -> None:
+        """paged_attention_decode for a batch whose first ``shared_blocks``
+        table entries are common to every sequence (see the C header)."""
+        import torch
+        S, Hq, D = (int(x) for x in q.shape)
+        if tuple(out.shape) != (S, Hq, D) or D != self.head_dim:
+            raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim]")
+        if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+            raise ValueError("one table row and one length per sequence")
+        ws_ptr, ws_bytes = None, 0
+        if workspace is not None:
+            ws_ptr = _dev_ptr(workspace, "workspace")
+            ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib.paged_attention_decode_shared(self.handle, int(layer),
+                                                 _dev_ptr(out, "out", self.torch_dtype),
+                                                 _dev_ptr(q, "q", self.torch_dtype),
+                                                 _dev_ptr(block_tables, "block_tables", torch.int32),
+                                                 int(block_tables.shape[1]),
+                                                 _dev_ptr(context_lens, "context_lens", torch.int32),
+                                                 S, Hq, float(scale), int(max_context_len), int(shared_blocks),
+                                                 ws_ptr, int(ws_bytes), _stream_handle(stream)),
+               "paged_attention_decode_shared")
 
     def copy_blocks(self, block_pairs, stream=None) -> None:
         """Copy-on-write device copy: block src -> block dst in every layer of K and V.

@@ -51,7 +51,7 @@ class DecodeStep:
                  write_seq: np.ndarray, write_start: np.ndarray, write_count: np.ndarray,
                  num_layers: int = 1, layer: int = 0, partition_size: int = 0,
                  scale: Optional[float] = None, max_context_len: Optional[int] = None,
-                 fp8_pool=None, device="cuda"):
+                 fp8_pool=None, shared_blocks: int = 0, device="cuda"):
         import torch
         self.fp8 = fp8_pool is not None
         if self.fp8 and dtype != "bf16":
@@ -88,8 +88,17 @@ class DecodeStep:
         self._split_appends(k_new, v_new, context_lens, write_tables, B, N, write_seq, write_start, write_count,
                             dtype, device)
         self.out = torch.empty_like(self.q)
-        ws = self.pool.workspace_bytes(self.num_seqs, self.num_q_heads, self.max_context_len,
-                                       self.partition_size)
+        # shared_blocks > 0: attend() runs paged_attention_decode_shared (the first
+        # shared_blocks table entries of every sequence are the same blocks)
+        self.shared_blocks = int(shared_blocks)
+        if self.shared_blocks and self.partition_size:
+            raise ValueError("a shared prefix goes with partition_size 0")
+        if self.shared_blocks:
+            ws = self.pool.shared_workspace_bytes(self.num_seqs, self.num_q_heads, self.max_context_len,
+                                                  int(block_tables.shape[1]), self.shared_blocks)
+        else:
+            ws = self.pool.workspace_bytes(self.num_seqs, self.num_q_heads, self.max_context_len,
+                                           self.partition_size)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
 
     def _split_appends(self, k_new, v_new, context_lens, write_tables, B, N, write_seq, write_start, write_count,
@@ -141,6 +150,13 @@ class DecodeStep:
         self.pool.reshape_and_cache(self.layer, self.k_new, self.v_new, self.slot_mapping, stream=stream)
 
     def attend(self, stream=None):
+        if self.shared_blocks:
+            self.pool.paged_attention_decode_shared(self.layer, self.out, self.q, self.block_tables,
+                                                    self.context_lens, scale=self.scale,
+                                                    max_context_len=self.max_context_len,
+                                                    shared_blocks=self.shared_blocks, workspace=self.workspace,
+                                                    stream=stream)
+            return
         self.pool.paged_attention_decode(self.layer, self.out, self.q, self.block_tables, self.context_lens,
                                          scale=self.scale, max_context_len=self.max_context_len,
                                          partition_size=self.partition_size, workspace=self.workspace,
@@ -156,6 +172,8 @@ class DecodeStep:
         reshape_and_cache first."""
         if not self.can_fuse:
             raise ValueError("some sequence has no single-row write at position L_i - 1")
+        if self.shared_blocks:
+            raise ValueError("the shared-prefix call has no decode-append form")
         if self.num_other_tokens:
             self.pool.reshape_and_cache(self.layer, self.other_k, self.other_v, self.other_slots, stream=stream)
         self.pool.paged_attention_decode_append(self.layer, self.out, self.q, self.append_k, self.append_v,

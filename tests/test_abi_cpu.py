@@ -422,3 +422,51 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def _shared(h, **kw):
+    a = dict(layer=0, out=0x30000000, q=0x40000000, tables=0x50000000, mb=256, lens=0x60000000, S=4, Hq=32,
+             scale=0.125, max_ctx=4096, shared=128, ws=None, ws_bytes=0)
+    a.update(kw)
+    return K.lib.paged_attention_decode_shared(h, a["layer"], a["out"], a["q"], a["tables"], a["mb"], a["lens"],
+                                               a["S"], a["Hq"], a["scale"], a["max_ctx"], a["shared"], a["ws"],
+                                               a["ws_bytes"], None)
+
+
+def _shared_ws(h, S=4, Hq=32, max_ctx=4096, mb=256, shared=128):
+    out = ctypes.c_uint64(0)
+    st = K.lib.paged_attention_shared_workspace_bytes(h, S, Hq, max_ctx, mb, shared, ctypes.byref(out))
+    return st, int(out.value)
+
+
+def test_shared_prefix_argument_checks_return_before_any_launch():
+    # a bf16 pool with head_dim 128 and block size 16, as the shared-prefix kernels need
+    st, h = _pool(num_kv_heads=8, head_dim=128, dtype="bf16", num_blocks=1024)
+    assert st == K.KV_OK
+    assert _shared(None) == K.KV_ERR_INVALID_ARGUMENT
+    assert _shared(h, shared=-1) == K.KV_ERR_INVALID_ARGUMENT
+    assert _shared(h, shared=257) == K.KV_ERR_INVALID_ARGUMENT           # past max_blocks_per_seq
+    assert _shared(h, shared=129, max_ctx=2063) == K.KV_ERR_INVALID_ARGUMENT   # past max_context_len / B
+    assert _shared(h, Hq=24) == K.KV_ERR_UNSUPPORTED                     # group of 3
+    assert _shared(h, S=0) == K.KV_OK                                    # nothing to do
+    st, need = _shared_ws(h)
+    assert st == K.KV_OK and need > 0
+    assert _shared(h, ws=0x70000000, ws_bytes=need - 1) == K.KV_ERR_WORKSPACE_TOO_SMALL
+    assert _shared(h, ws=0x70000008, ws_bytes=need) == K.KV_ERR_INVALID_ARGUMENT   # misaligned
+    # shared_blocks 0: the plain call's workspace
+    st, plain = _shared_ws(h, shared=0)
+    want = ctypes.c_uint64(0)
+    assert K.lib.paged_attention_workspace_bytes(h, 4, 32, 4096, 0, ctypes.byref(want)) == K.KV_OK
+    assert st == K.KV_OK and plain == want.value
+    # the prefix states come on top of the balanced split's workspace
+    assert need > plain
+    assert _shared_ws(h, shared=-1)[0] == K.KV_ERR_INVALID_ARGUMENT
+    K.lib.kv_pool_destroy(h)
+    # other pools: unsupported
+    for kw in (dict(), dict(num_kv_heads=8, head_dim=64, dtype="bf16"),
+               dict(num_kv_heads=8, head_dim=128, dtype="bf16", block_size=32)):
+        st, h = _pool(**kw)
+        assert st == K.KV_OK
+        assert _shared(h, Hq=8 * (kw.get("num_kv_heads", 2) // 2)) == K.KV_ERR_UNSUPPORTED
+        assert _shared_ws(h, Hq=8 * (kw.get("num_kv_heads", 2) // 2))[0] == K.KV_ERR_UNSUPPORTED
+        K.lib.kv_pool_destroy(h)
