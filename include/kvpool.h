@@ -336,8 +336,8 @@ kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out
  * the same blocks (the block manager's shared, reference-counted prompt).
  * Each (block, KV head) tile of that prefix is then read once for up to
  * sixteen query heads of several sequences together, instead of once per
- * sequence; the rest of each context goes through the balanced split; a
- * third kernel merges the two.
+ * sequence, by extra waves of the balanced split's launch; the rest of each
+ * context goes through the balanced split; a second kernel merges the two.
  *   shared_blocks: host, >= 0; 0 runs paged_attention_decode with
  *                  partition_size 0.  shared_blocks * B <= max_context_len and
  *                  <= max_blocks_per_seq * B.

@@ -939,12 +939,90 @@ __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Shared prefix (paged_attention_decode_shared).  The caller's block manager
+// knows that the first shared_tiles table entries of every sequence name the
+// same blocks (a common prompt: [KVC] "Prefix sharing, reference counts, and
+// copy-on-write", [PIF] "03 Sharing via copy-on-write"), so each (block, KV
+// head) tile of the prefix is read once for sixteen query columns instead of
+// once per sequence: the G query heads of 16 / G consecutive sequences fill
+// the score MFMA's sixteen columns and the P V MFMA's sixteen rows, which one
+// sequence's G heads leave mostly zero.  Wave (column block qb, KV head kv,
+// part p) walks prefix tiles [p PT, (p + 1) PT) of sequence 0's table row and
+// leaves each column's (m, l, unnormalised output) in slot p of the prefix
+// states; the fix-up merges them with the balanced walk of what follows the
+// prefix.  The prefix waves are workgroups of the balanced kernel's own
+// launch, past its workers, so the prefix walk, served mostly from L2, runs
+// beside the walk of the private tiles, served from HBM; prefix wave idx
+// takes KV head idx mod H_kv, so with eight KV heads the waves of one XCD
+// share one head's prefix tiles in its L2.
+// ---------------------------------------------------------------------------
+constexpr int kPrefixDepth = 2;   // prefix tiles are mostly cache hits: two in flight per wave
+
+template <int G>
+__device__ void prefix_wave(const DecodeArgs& a, int64_t idx) {
+    constexpr int kSeqs = 16 / G;   // sequences per column block
+    const int Hkv = a.num_kv_heads;
+    const int blocks = (a.num_seqs * G + 15) / 16;
+    const int kv = (int)(idx % Hkv);
+    const int qb = (int)((idx / Hkv) % blocks);
+    const int p = (int)(idx / ((int64_t)Hkv * blocks));
+    const int b0 = p * a.prefix_part_tiles;
+    const int nk = min(a.prefix_part_tiles, a.shared_tiles - b0);   // >= 1: the host sizes the parts
+
+    WalkCtx c = make_ctx<false, false>(a, kv);
+    c.keep_v = true;   // every column block reads these tiles
+    // column n: query head n % G of sequence qb * kSeqs + n / G (zero past the batch)
+    const int col_seq = qb * kSeqs + c.n / G;
+    const bool col_ok = col_seq < a.num_seqs;
+    const size_t col_row = (size_t)(col_ok ? col_seq : 0) * a.num_q_heads + (size_t)kv * G + c.n % G;
+    bf16x8_t qb_op[kKK];
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.q) + col_row * kRC;
+#pragma unroll
+    for (int kk = 0; kk < kKK; ++kk) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (col_ok) x = qrow[kk * 4 + c.r];
+        qb_op[kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+    State st;
+    init_state(st);
+    AppendRow none;
+    none.active = false;
+    none.krow = none.vrow = nullptr;
+    typename TileOf<false>::type tt[kPrefixDepth];
+    // every sequence covers the whole prefix: no position is masked
+    walk<16, kPrefixDepth, false>(st, tt, false, qb_op, a.tables, 1, nk, b0, a.shared_tiles * kTileTokens, c, none);
+    const float l_tot = total_l(st);
+
+    // lane (r, n): outputs of columns 4r .. 4r+3, dims 8n .. 8n+7; (m, l) of column n
+    const int slots = a.prefix_parts + 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = 4 * c.r + j;
+        const int sq = qb * kSeqs + col / G;
+        if (sq < a.num_seqs) {
+            const size_t row = (size_t)sq * a.num_q_heads + (size_t)kv * G + col % G;
+            float4* dst = reinterpret_cast<float4*>(a.ws_pacc + (row * slots + p) * kD + c.n * 8);
+            dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
+            dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
+        }
+    }
+    if (c.r == 0 && col_ok) reinterpret_cast<float2*>(a.ws_pml)[col_row * slots + p] = make_float2(st.m, l_tot);
+}
+
 template <int G, bool kAnyB, bool kFp8>
 __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a) {
     const int lane = threadIdx.x;
     const int64_t W = a.workers;
     const int64_t w = blockIdx.x;
-    if (w >= W) {   // decode append: the pool side
+    if (w >= W) {
+        if constexpr (!kFp8 && !kAnyB) {
+            if (a.shared_tiles > 0) {   // a shared prefix: its walks
+                prefix_wave<G>(a, w - W);
+                return;
+            }
+        }
+        // decode append: the pool side
         if constexpr (kFp8) append_fp8_waves(a, w - W, (int64_t)gridDim.x - W);
         else append_scatter_waves(a, w - W, (int64_t)gridDim.x - W);
         return;
@@ -1311,72 +1389,6 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
     }
 }
 
-// ---------------------------------------------------------------------------
-// Shared prefix (paged_attention_decode_shared).  The caller's block manager
-// knows that the first shared_tiles table entries of every sequence name the
-// same blocks (a common prompt: [KVC] "Prefix sharing, reference counts, and
-// copy-on-write", [PIF] "03 Sharing via copy-on-write"), so each (block, KV
-// head) tile of the prefix is read once for sixteen query columns instead of
-// once per sequence: the G query heads of 16 / G consecutive sequences fill
-// the score MFMA's sixteen columns and the P V MFMA's sixteen rows, which one
-// sequence's G heads leave mostly zero.  Wave (column block qb, KV head kv,
-// part p) walks prefix tiles [p PT, (p + 1) PT) of sequence 0's table row and
-// leaves each column's (m, l, unnormalised output) in slot p of the prefix
-// states; neighbouring workgroups take different KV heads (and XCDs), so the
-// waves of one XCD share a KV head's prefix tiles in its L2.  The fix-up
-// merges these states with the balanced walk of what follows the prefix.
-// ---------------------------------------------------------------------------
-constexpr int kPrefixDepth = 2;   // prefix tiles are mostly cache hits: two in flight per wave
-
-template <int G>
-__global__ __launch_bounds__(kWave) void decode_prefix_kernel(DecodeArgs a) {
-    constexpr int kSeqs = 16 / G;   // sequences per column block
-    const int Hkv = a.num_kv_heads;
-    const int kv = blockIdx.x % Hkv;
-    const int qb = blockIdx.x / Hkv;
-    const int p = blockIdx.y;
-    const int b0 = p * a.prefix_part_tiles;
-    const int nk = min(a.prefix_part_tiles, a.shared_tiles - b0);   // >= 1: the host sizes the parts
-
-    WalkCtx c = make_ctx<false, false>(a, kv);
-    c.keep_v = true;   // every column block reads these tiles
-    // column n: query head n % G of sequence qb * kSeqs + n / G (zero past the batch)
-    const int col_seq = qb * kSeqs + c.n / G;
-    const bool col_ok = col_seq < a.num_seqs;
-    const size_t col_row = (size_t)(col_ok ? col_seq : 0) * a.num_q_heads + (size_t)kv * G + c.n % G;
-    bf16x8_t qb_op[kKK];
-    const uint4* qrow = reinterpret_cast<const uint4*>(a.q) + col_row * kRC;
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) {
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (col_ok) x = qrow[kk * 4 + c.r];
-        qb_op[kk] = __builtin_bit_cast(bf16x8_t, x);
-    }
-    State st;
-    init_state(st);
-    AppendRow none;
-    none.active = false;
-    none.krow = none.vrow = nullptr;
-    typename TileOf<false>::type tt[kPrefixDepth];
-    // every sequence covers the whole prefix: no position is masked
-    walk<16, kPrefixDepth, false>(st, tt, false, qb_op, a.tables, 1, nk, b0, a.shared_tiles * kTileTokens, c, none);
-    const float l_tot = total_l(st);
-
-    // lane (r, n): outputs of columns 4r .. 4r+3, dims 8n .. 8n+7; (m, l) of column n
-    const int slots = a.prefix_parts + 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = 4 * c.r + j;
-        const int sq = qb * kSeqs + col / G;
-        if (sq < a.num_seqs) {
-            const size_t row = (size_t)sq * a.num_q_heads + (size_t)kv * G + col % G;
-            float4* dst = reinterpret_cast<float4*>(a.ws_pacc + (row * slots + p) * kD + c.n * 8);
-            dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
-            dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
-        }
-    }
-    if (c.r == 0 && col_ok) reinterpret_cast<float2*>(a.ws_pml)[col_row * slots + p] = make_float2(st.m, l_tot);
-}
 
 // Fix-up for one (sequence, KV head): zeros for an empty sequence; nothing if
 // one slice held it whole; otherwise the log-sum-exp merge of the partial
@@ -1598,7 +1610,9 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
     // decode append: a few extra single-wave workgroups store the new rows
     // (bf16: about 8 chunks per lane; FP8: about 4 rows per wave)
     int64_t extra = 0;
-    if (a.k_append) {
+    if (a.shared_tiles > 0) {   // the prefix walks: (column block, KV head, part)
+        extra = ((int64_t)a.num_seqs * group + 15) / 16 * a.num_kv_heads * a.prefix_parts;
+    } else if (a.k_append) {
         const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * (kFp8 ? 1 : kRC);
         const int64_t per_wave = kFp8 ? 4 : 8 * kWave;
         extra = (items + per_wave - 1) / per_wave;
@@ -1697,18 +1711,8 @@ hipError_t launch_decode_bf16_shared(const DecodeArgs& a, int group, int workers
     if (a.shared_tiles <= 0 || a.prefix_parts <= 0 || a.prefix_part_tiles <= 0 || a.block_size != kTileTokens ||
         (int64_t)(a.prefix_parts - 1) * a.prefix_part_tiles >= a.shared_tiles || !a.ws_pml || !a.ws_pacc || a.k_append)
         return hipErrorInvalidValue;
-    const unsigned blocks = (unsigned)(((int64_t)a.num_seqs * group + 15) / 16 * a.num_kv_heads);
-    dim3 grid(blocks, (unsigned)a.prefix_parts);
-    switch (group) {
-        case 1: decode_prefix_kernel<1><<<grid, kWave, 0, stream>>>(a); break;
-        case 2: decode_prefix_kernel<2><<<grid, kWave, 0, stream>>>(a); break;
-        case 4: decode_prefix_kernel<4><<<grid, kWave, 0, stream>>>(a); break;
-        case 8: decode_prefix_kernel<8><<<grid, kWave, 0, stream>>>(a); break;
-        default: return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_streamk<false>(a, group, workers, stream);
+    if (group != 1 && group != 2 && group != 4 && group != 8) return hipErrorInvalidValue;
+    return launch_streamk<false>(a, group, workers, stream);   // the prefix walks run as extra waves
 }
 
 hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream) {

@@ -120,7 +120,7 @@ struct DecodeArgs {
     float scale_log2;            // softmax scale * log2(e)
     // Shared prefix (paged_attention_decode_shared, bf16, block size 16): the
     // first shared_tiles table entries of every sequence name the same blocks.
-    // The prefix kernel leaves (m, l, output) per (sequence, query head) and
+    // The prefix waves leave (m, l, output) per (sequence, query head) and
     // part in slots 0 .. prefix_parts-1 of ws_pml / ws_pacc ([S][Hq][parts + 1]
     // x (m, l) and x head_dim); the balanced kernel walks only the tiles past
     // the prefix and leaves a (sequence, KV head) it covers whole in slot
@@ -146,8 +146,8 @@ hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, int group, hipStream_t st
 // bf16 / head_dim 128, balanced split over `workers` single-wave workers plus
 // the fix-up of split (sequence, KV head) pairs; no partition merge needed.
 hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
-// The same with a shared prefix (a.shared_tiles > 0): the prefix kernel, the
-// balanced decode of what follows the prefix, the fix-up merging both.
+// The same with a shared prefix (a.shared_tiles > 0): prefix waves beside the
+// balanced decode of what follows the prefix, then the fix-up merging both.
 hipError_t launch_decode_bf16_shared(const DecodeArgs& a, int group, int workers, hipStream_t stream);
 hipError_t launch_decode_fp8_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream);
 // head_dim 128, at most kStreamKMaxSeqs sequences, partition_size > 0: the
