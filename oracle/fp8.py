@@ -53,7 +53,8 @@ _POS_VALUES = e4m3_decode(_POS_CODES)                  # increasing
 def e4m3_encode(x) -> np.ndarray:
     """float32 value -> E4M3 code: round to nearest, ties to the even code,
     saturate at +-448 (NaN -> 0x7F)."""
-    v = np.asarray(x, dtype=np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):   # signalling NaN inputs widen to NaN quietly
+        v = np.asarray(x, dtype=np.float32).astype(np.float64)
     a = np.abs(v)
     i = np.clip(np.searchsorted(_POS_VALUES, a), 1, len(_POS_VALUES) - 1)   # a in [values[i-1], values[i]]
     lo, hi = _POS_VALUES[i - 1], _POS_VALUES[i]
