@@ -82,7 +82,7 @@ typedef enum kv_dtype {
     KV_FP8_E4M3 = 2  /* pool holds OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
                       * largest finite 448, 0x7F/0xFF NaN) with one fp32 scale per (block, KV head) for K
                       * and one for V; a stored value is code * scale.  q, k_new/v_new and the output
-                      * are bf16.  head_dim 128, block_size 16. */
+                      * are bf16.  head_dim 128, block_size 8, 16, 32, 64 or 128. */
 } kv_dtype;
 
 typedef struct kv_pool_desc {
@@ -138,7 +138,8 @@ kv_status kv_pool_scale_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tens
  * kv_pool_create for KV_FP8_E4M3: also wraps the two caller-allocated scale
  * tensors (4-byte aligned).  Errors: as kv_pool_create; KV_ERR_INVALID_ARGUMENT
  * when the dtype is not KV_FP8_E4M3 or a scale pointer is null or misaligned;
- * KV_ERR_UNSUPPORTED unless head_dim is 128 and block_size 16.
+ * KV_ERR_UNSUPPORTED unless head_dim is 128 and block_size one of 8, 16, 32,
+ * 64, 128.
  */
 kv_status kv_pool_create_fp8(const kv_pool_desc* desc, void* k_codes, void* v_codes, float* k_scales,
                              float* v_scales, kv_pool_t* out);

@@ -383,11 +383,10 @@ bool decode_shape_supported(int dtype, int head_dim, int group, int block_size) 
     if (!(dtype == 0 || dtype == 1 || dtype == 2) || !(head_dim == 64 || head_dim == 128) ||
         !(group == 1 || group == 2 || group == 4 || group == 8))
         return false;
-    // FP8 pools: the matrix-core kernels, head_dim 128, 16-token blocks
-    if (dtype == 2) return head_dim == 128 && block_size == kTileTokens;
-    // the bf16 / head_dim-128 kernels walk 16-token tiles of any block size
-    // 8..128; the vector-unit kernel is built for B = 16
-    if (dtype == 1 && head_dim == 128)
+    // the bf16 and FP8 / head_dim-128 kernels (matrix cores) walk 16-token
+    // tiles of any block size 8..128; the vector-unit kernel is built for B = 16
+    if (dtype == 2 && head_dim != 128) return false;
+    if ((dtype == 1 || dtype == 2) && head_dim == 128)
         return block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128;
     return block_size == kBlockTokens;
 }

@@ -46,7 +46,9 @@
 //     scale multiplies its scores; its V scale multiplies the probabilities
 //     that enter P V, while the softmax sum takes them unscaled, so
 //     out = sum_j p_j sv_j v_j / sum_j p_j is what the dequantized cache gives.
-//     One tile in registers per worker wave, as for bf16: deeper pipelines
+//     Any block size 8..128: with 8-token blocks a tile's two halves are two
+//     blocks, and the lanes holding tokens 8..15 (rows r = 2, 3) take the
+//     second block's scales.  One tile in registers per worker wave, as for bf16: deeper pipelines
 //     (2, 4, 6, 8 FP8 tiles) measured slower on the 8B- and 70B-shaped
 //     batches.
 #include <math.h>
@@ -460,7 +462,7 @@ __device__ __forceinline__ bool keep_v_fetched(int tv0, int nb, int seq, int num
 
 // kAnyB: the block size comes from the arguments (8..128); otherwise it is 16
 // and every block-size field below is a constant the walk folds away.
-// kFp8: an FP8 pool (block size 16).
+// kFp8: an FP8 pool.
 template <bool kAnyB, bool kFp8 = false>
 __device__ __forceinline__ WalkCtx make_ctx(const DecodeArgs& a, int kv) {
     const int B = kAnyB ? a.block_size : kTileTokens;
@@ -480,8 +482,9 @@ __device__ __forceinline__ WalkCtx make_ctx(const DecodeArgs& a, int kv) {
     c.sub_shift = kAnyB ? 31 - __builtin_clz(B >= kTileTokens ? B / kTileTokens : 1) : 0;
     if constexpr (kFp8) {
         // K: token n, chunks 2r and 2r + 1; V: token 4r + i, 8-byte unit n
-        c.k_off = c.n * kRow + 2 * c.r;
-        c.v_off = 4 * c.r * (kD / 8) + c.n;
+        // (rows within the lane's block when B = 8)
+        c.k_off = (c.pair8 ? (c.n & 7) : c.n) * kRow + 2 * c.r;
+        c.v_off = (c.pair8 ? ((4 * c.r) & 7) : 4 * c.r) * (kD / 8) + c.n;
         c.ksc = a.k_scale + kv;
         c.vsc = a.v_scale + kv;
         c.nkvh = a.num_kv_heads;
@@ -528,7 +531,8 @@ __device__ __forceinline__ void init_state(State& st) {
 struct AppendRow {
     bool active;
     int tok0;             // first token of the block holding position L - 1
-    int j;                // (L - 1) % B
+    int j;                // (L - 1) % 16: the row within its 16-token tile
+    bool opens;           // (L - 1) % B == 0: the row is row 0 of its block
     const uint4* krow;    // the new K row (16 chunks)
     const uint4* vrow;
 };
@@ -550,12 +554,13 @@ __device__ __forceinline__ void append_into(Tile& t, const AppendRow& app, const
 // kw for K and vw for V, so both sides compute the same codes and scales),
 // then the codes move to the lanes that hold the row in the tile layout: K
 // dims 32r + 4m .. +3 (m = 0..7) from lane 16r + 2m, V dims 8n .. 8n+7 from
-// lanes 4n and 4n + 2.  When the row is row 0 of its block (j == 0) it alone
-// sets the block's scales, which then replace the scales read for the tile
-// (the pool side writes them concurrently).
+// lanes 4n and 4n + 2.  When the row is row 0 of its block (app.opens) it
+// alone sets the block's scales, which then replace the scales read for the
+// block (the pool side writes them concurrently).  kscale / vscale are the
+// scales of the block holding the row (with 8-token blocks, the tile's half).
 __device__ __forceinline__ void append_into_fp8(TileF8& t, const AppendRow& app, uint32_t kw, uint32_t vw,
                                                 const WalkCtx& c, float& kscale, float& vscale) {
-    if (app.j == 0) {   // wave-uniform
+    if (app.opens) {   // wave-uniform
         kscale = e4m3_block_scale(wave_max(abs_max2(kw, 0.0f)));
         vscale = e4m3_block_scale(wave_max(abs_max2(vw, 0.0f)));
     }
@@ -639,6 +644,7 @@ __device__ __forceinline__ void walk_policy(State& st, typename TileOf<kFp8>::ty
     // Each lane addresses its own rows: for B = 8 the K rows of tokens 8..15 and
     // the V rows of lanes r >= 2 come from the second block.
     int k0 = 0;
+    constexpr int kRowChunks = kFp8 ? kD / 16 : kRC;   // 16-byte chunks per token row
     auto ptrs_of = [&](uint32_t p0, uint32_t p1, int e, size_t head_off, const uint4*& kt, const uint4*& vt) {
         p0 = p0 < c.num_blocks ? p0 : c.num_blocks - 1;   // stay inside the pool whatever the table says
         if (c.pair8) {
@@ -647,7 +653,7 @@ __device__ __forceinline__ void walk_policy(State& st, typename TileOf<kFp8>::ty
             vt = c.vpool + (size_t)(c.r < 2 ? p0 : p1) * c.block_stride + head_off;
         } else {
             const size_t base = (size_t)p0 * c.block_stride + head_off +
-                                (size_t)(e & ((1 << c.sub_shift) - 1)) * (kTileTokens * kRC);
+                                (size_t)(e & ((1 << c.sub_shift) - 1)) * (kTileTokens * kRowChunks);
             kt = c.kpool + base;
             vt = c.vpool + base;
         }
@@ -676,13 +682,19 @@ __device__ __forceinline__ void walk_policy(State& st, typename TileOf<kFp8>::ty
         const int2 tvp = (k0 == 0 && have_first) ? make_int2(tv0_first, tv1_first)
                                                  : tile_entries(row, b0 + (k0 + c.lane) * stride, c.lane < nc, c);
         const int tv0 = tvp.x, tv1 = tvp.y;
-        float ks_l = 1.0f, vs_l = 1.0f;
+        float ks_l = 1.0f, vs_l = 1.0f, ks_l1 = 1.0f, vs_l1 = 1.0f;
         if constexpr (kFp8) {
             if (c.lane < nc) {
                 uint32_t p = (uint32_t)tv0;
                 p = p < c.num_blocks ? p : c.num_blocks - 1;
                 ks_l = c.ksc[(size_t)p * c.nkvh];
                 vs_l = c.vsc[(size_t)p * c.nkvh];
+                if (c.pair8) {   // tokens 8..15 of the tile
+                    uint32_t p1 = (uint32_t)tv1;
+                    p1 = p1 < c.num_blocks ? p1 : c.num_blocks - 1;
+                    ks_l1 = c.ksc[(size_t)p1 * c.nkvh];
+                    vs_l1 = c.vsc[(size_t)p1 * c.nkvh];
+                }
             }
             asm volatile("" : : : "memory");
         }
@@ -726,10 +738,20 @@ __device__ __forceinline__ void walk_policy(State& st, typename TileOf<kFp8>::ty
                 if constexpr (kFp8) {
                     const int ks = min(k + s, nc - 1);
                     float ksc = readlane_f(ks_l, ks), vsc = readlane_f(vs_l, ks);
-                    if (app.active && tok == app.tok0 && row_in_pool(tv0, tv1, k + s, app.j)) {
-                        append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc, vsc);
+                    float ksc1 = ksc, vsc1 = vsc;   // B = 8: the scales of tokens 8..15
+                    if (c.pair8) {
+                        ksc1 = readlane_f(ks_l1, ks);
+                        vsc1 = readlane_f(vs_l1, ks);
                     }
-                    process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2, ksc, vsc,
+                    if (app.active && tok == app.tok0 && row_in_pool(tv0, tv1, k + s, app.j)) {
+                        if (c.pair8 && app.j >= 8)
+                            append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc1, vsc1);
+                        else
+                            append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc, vsc);
+                    }
+                    // lane (r, n) holds the scores and probabilities of tokens 4r .. 4r+3
+                    const bool second = c.pair8 && c.r >= 2;
+                    process<G>(st, tt[s], qb, tok, L, c.r, c.n, c.sl2, second ? ksc1 : ksc, second ? vsc1 : vsc,
                                [&] { load_k(tt[s], kt, c.k_off); }, [&] { load_v(tt[s], vt, c.v_off, kKeepV); });
                 } else {
                     // wave-uniform: the tile holding the new token; a table entry outside
@@ -793,6 +815,7 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
     const int nk = first < b_end ? (b_end - first + kWaves - 1) / kWaves : 0;
     AppendRow none;
     none.active = false;
+    none.opens = false;
     none.krow = none.vrow = nullptr;
     typename TileOf<kFp8>::type tt[2];
     walk<G, 2, kFp8>(st, tt, false, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
@@ -927,13 +950,13 @@ __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x,
         const int L = clamp_len(a.lens[i], a.max_context);
         if (L == 0) continue;
         const int pos = L - 1;
-        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / kTileTokens];
+        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / a.block_size];
         if (block < 0 || block >= a.num_blocks) continue;
-        const int j = pos % kTileTokens;
+        const int j = pos % a.block_size;
         const uint32_t* src = reinterpret_cast<const uint32_t*>(which == 0 ? a.k_append : a.v_append) +
                               (i * H + h) * (kD / 2);
         uint16_t* dst = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(which == 0 ? a.k_layer : a.v_layer)) +
-                        ((block * H + h) * kTileTokens + j) * (kD / 2);
+                        ((block * H + h) * a.block_size + j) * (kD / 2);
         float* scale = const_cast<float*>(which == 0 ? a.k_scale : a.v_scale) + block * H + h;
         fp8_store_row(src, dst, scale, j == 0, lane);
     }
@@ -988,6 +1011,7 @@ __device__ void prefix_wave(const DecodeArgs& a, int64_t idx) {
     init_state(st);
     AppendRow none;
     none.active = false;
+    none.opens = false;
     none.krow = none.vrow = nullptr;
     typename TileOf<false>::type tt[kPrefixDepth];
     // every sequence covers the whole prefix: no position is masked
@@ -1110,6 +1134,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         app.active = a.k_append != nullptr && b + n_here == nblk;
         app.tok0 = (nblk - 1) * kTileTokens;
         app.j = (L - 1) % kTileTokens;
+        app.opens = (L - 1) % (kAnyB ? a.block_size : kTileTokens) == 0;
         app.krow = reinterpret_cast<const uint4*>(a.k_append) + ((size_t)seq * Hkv + kv) * kRC;
         app.vrow = reinterpret_cast<const uint4*>(a.v_append) + ((size_t)seq * Hkv + kv) * kRC;
         // The next piece of this slice, if it starts a new (sequence, KV head),
@@ -1287,6 +1312,7 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
 
     AppendRow none;
     none.active = false;
+    none.opens = false;
     none.krow = none.vrow = nullptr;
     bool pf_valid = false;   // table entries of the next partition fetched ahead
     int pf_kv = -1, pf_b = -1, pf_tv0 = 0, pf_tv1 = 0, pf_nb = 0;
@@ -1619,23 +1645,23 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
         extra = extra < 1 ? 1 : (extra > 256 ? 256 : extra);
     }
     dim3 grid((unsigned)(workers + extra));
-    const bool any_b = !kFp8 && a.block_size != kTileTokens;
+    const bool any_b = a.block_size != kTileTokens;
     dim3 fix((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     switch (group) {
         case 1:
-            if (any_b) decode_bf16_streamk_kernel<1, true, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_bf16_streamk_kernel<1, true, kFp8><<<grid, kWave, 0, stream>>>(a);
             else decode_bf16_streamk_kernel<1, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 2:
-            if (any_b) decode_bf16_streamk_kernel<2, true, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_bf16_streamk_kernel<2, true, kFp8><<<grid, kWave, 0, stream>>>(a);
             else decode_bf16_streamk_kernel<2, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 4:
-            if (any_b) decode_bf16_streamk_kernel<4, true, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_bf16_streamk_kernel<4, true, kFp8><<<grid, kWave, 0, stream>>>(a);
             else decode_bf16_streamk_kernel<4, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 8:
-            if (any_b) decode_bf16_streamk_kernel<8, true, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_bf16_streamk_kernel<8, true, kFp8><<<grid, kWave, 0, stream>>>(a);
             else decode_bf16_streamk_kernel<8, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         default: return hipErrorInvalidValue;
@@ -1655,22 +1681,22 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
 template <bool kFp8>
 hipError_t launch_partitions(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
     dim3 grid((unsigned)workers);
-    const bool any_b = !kFp8 && a.block_size != kTileTokens;
+    const bool any_b = a.block_size != kTileTokens;
     switch (group) {
         case 1:
-            if (any_b) decode_partitions_kernel<1, true, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_partitions_kernel<1, true, kFp8><<<grid, kWave, 0, stream>>>(a);
             else decode_partitions_kernel<1, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 2:
-            if (any_b) decode_partitions_kernel<2, true, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_partitions_kernel<2, true, kFp8><<<grid, kWave, 0, stream>>>(a);
             else decode_partitions_kernel<2, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 4:
-            if (any_b) decode_partitions_kernel<4, true, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_partitions_kernel<4, true, kFp8><<<grid, kWave, 0, stream>>>(a);
             else decode_partitions_kernel<4, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         case 8:
-            if (any_b) decode_partitions_kernel<8, true, false><<<grid, kWave, 0, stream>>>(a);
+            if (any_b) decode_partitions_kernel<8, true, kFp8><<<grid, kWave, 0, stream>>>(a);
             else decode_partitions_kernel<8, false, kFp8><<<grid, kWave, 0, stream>>>(a);
             break;
         default: return hipErrorInvalidValue;
@@ -1682,22 +1708,22 @@ template <bool kFp8>
 hipError_t launch_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
     dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     dim3 block(kWaves * kWave);
-    const bool any_b = !kFp8 && a.block_size != kTileTokens;
+    const bool any_b = a.block_size != kTileTokens;
     switch (group) {
         case 1:
-            if (any_b) decode_bf16_mfma_kernel<1, true, false><<<grid, block, 0, stream>>>(a);
+            if (any_b) decode_bf16_mfma_kernel<1, true, kFp8><<<grid, block, 0, stream>>>(a);
             else decode_bf16_mfma_kernel<1, false, kFp8><<<grid, block, 0, stream>>>(a);
             break;
         case 2:
-            if (any_b) decode_bf16_mfma_kernel<2, true, false><<<grid, block, 0, stream>>>(a);
+            if (any_b) decode_bf16_mfma_kernel<2, true, kFp8><<<grid, block, 0, stream>>>(a);
             else decode_bf16_mfma_kernel<2, false, kFp8><<<grid, block, 0, stream>>>(a);
             break;
         case 4:
-            if (any_b) decode_bf16_mfma_kernel<4, true, false><<<grid, block, 0, stream>>>(a);
+            if (any_b) decode_bf16_mfma_kernel<4, true, kFp8><<<grid, block, 0, stream>>>(a);
             else decode_bf16_mfma_kernel<4, false, kFp8><<<grid, block, 0, stream>>>(a);
             break;
         case 8:
-            if (any_b) decode_bf16_mfma_kernel<8, true, false><<<grid, block, 0, stream>>>(a);
+            if (any_b) decode_bf16_mfma_kernel<8, true, kFp8><<<grid, block, 0, stream>>>(a);
             else decode_bf16_mfma_kernel<8, false, kFp8><<<grid, block, 0, stream>>>(a);
             break;
         default: return hipErrorInvalidValue;
@@ -1720,7 +1746,6 @@ hipError_t launch_decode_bf16_streamk(const DecodeArgs& a, int group, int worker
 }
 
 hipError_t launch_decode_fp8_streamk(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
-    if (a.block_size != kTileTokens) return hipErrorInvalidValue;
     return launch_streamk<true>(a, group, workers, stream);
 }
 
@@ -1729,7 +1754,6 @@ hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t s
 }
 
 hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
-    if (a.block_size != kTileTokens) return hipErrorInvalidValue;
     return launch_mfma<true>(a, group, stream);
 }
 
@@ -1738,7 +1762,6 @@ hipError_t launch_decode_bf16_partitions(const DecodeArgs& a, int group, int wor
 }
 
 hipError_t launch_decode_fp8_partitions(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
-    if (a.block_size != kTileTokens) return hipErrorInvalidValue;
     return launch_partitions<true>(a, group, workers, stream);
 }
 

@@ -40,12 +40,13 @@ __device__ __forceinline__ int64_t readlane64_i(int64_t x, int src) {
 
 // One wave per (16-token chunk, KV head): grid (chunks, H), grid-stride over
 // the chunks, so a wave usually has at most one block to open.  The wave finds
-// the tokens of its chunk that write row 0 of a block, lists the block's
-// writers in lanes 0..15 (from the run that follows the token, else by
-// searching the whole mapping, 512 slots per step) and takes the amax of head
-// h's K and V rows over them (lane l: dims 2l and 2l + 1), all 32 row loads in
-// flight at once.
-constexpr int kB8 = 16;        // block size of FP8 pools
+// the tokens of its chunk that write row 0 of a block and takes the amax of
+// head h's K and V rows (lane l: dims 2l and 2l + 1) over every row this call
+// writes into that block, sixteen rows at a time: lanes 0..15 list the writers
+// of rows g .. g+15 (from the run that follows the token, else by searching
+// the whole mapping, 512 slots per step), and their 32 row loads go out
+// together.
+constexpr int kRowGroup = 16;  // block rows gathered per round (all of them for 8-token blocks)
 constexpr int kScaleChunk = 16;
 constexpr int kSearchUnroll = 8;
 
@@ -53,59 +54,64 @@ __global__ __launch_bounds__(kWave) void fp8_scale_kernel(ScatterArgs a) {
     const int lane = threadIdx.x;
     const int H = a.num_kv_heads;
     const int h = blockIdx.y;
+    const int B = a.block_size;
+    const int R = B < kRowGroup ? B : kRowGroup;   // rows per round
+    const uint64_t run_mask = (1ull << R) - 1;
     const int64_t T = a.num_tokens;
     const uint32_t* kn = reinterpret_cast<const uint32_t*>(a.k_new);
     const uint32_t* vn = reinterpret_cast<const uint32_t*>(a.v_new);
-    constexpr uint64_t kRunMask = (1ull << kB8) - 1;
     for (int64_t c0 = (int64_t)blockIdx.x * kScaleChunk; c0 < T; c0 += (int64_t)gridDim.x * kScaleChunk) {
         const int64_t t = c0 + lane;
         const int64_t slot = (lane < kScaleChunk && t < T) ? a.slot_mapping[t] : -1;
-        uint64_t starts = __builtin_amdgcn_ballot_w64(slot >= 0 && slot < a.num_slots && slot % kB8 == 0);
+        uint64_t starts = __builtin_amdgcn_ballot_w64(slot >= 0 && slot < a.num_slots && slot % B == 0);
         while (starts) {
             const int j = __builtin_ctzll(starts);
             starts &= starts - 1;
             const int64_t first = readlane64_i(slot, j);   // slot of row 0
-            const int64_t blk = first / kB8;
-            // lane i < 16: the token writing row i of the block, or -1
-            int64_t tok = -1;
-            const int64_t tl = c0 + j + lane;
-            const bool in_run = lane < kB8 && tl < T && a.slot_mapping[tl] == first + lane;
-            if (__builtin_amdgcn_ballot_w64(in_run) == kRunMask) {
-                tok = in_run ? tl : -1;
-            } else {
-                for (int64_t s0 = 0; s0 < T; s0 += kSearchUnroll * kWave) {
-                    int64_t sl[kSearchUnroll];
+            const int64_t blk = first / B;
+            float ak = 0.0f, av = 0.0f;
+            for (int g = 0; g < B; g += R) {
+                // lane i < R: the token writing row g + i of the block, or -1
+                int64_t tok = -1;
+                const int64_t tl = c0 + j + g + lane;
+                const bool in_run = lane < R && tl < T && a.slot_mapping[tl] == first + g + lane;
+                if (__builtin_amdgcn_ballot_w64(in_run) == run_mask) {
+                    tok = in_run ? tl : -1;
+                } else {
+                    const int64_t lo = first + g;
+                    for (int64_t s0 = 0; s0 < T; s0 += kSearchUnroll * kWave) {
+                        int64_t sl[kSearchUnroll];
 #pragma unroll
-                    for (int u = 0; u < kSearchUnroll; ++u) {
-                        const int64_t ts = s0 + u * kWave + lane;
-                        sl[u] = ts < T ? a.slot_mapping[ts] : -1;
-                    }
+                        for (int u = 0; u < kSearchUnroll; ++u) {
+                            const int64_t ts = s0 + u * kWave + lane;
+                            sl[u] = ts < T ? a.slot_mapping[ts] : -1;
+                        }
 #pragma unroll
-                    for (int u = 0; u < kSearchUnroll; ++u) {
-                        uint64_t hit = __builtin_amdgcn_ballot_w64(sl[u] >= first && sl[u] < first + kB8);
-                        while (hit) {
-                            const int jj = __builtin_ctzll(hit);
-                            hit &= hit - 1;
-                            const int row = (int)(readlane64_i(sl[u], jj) - first);
-                            if (lane == row) tok = s0 + u * kWave + jj;
+                        for (int u = 0; u < kSearchUnroll; ++u) {
+                            uint64_t hit = __builtin_amdgcn_ballot_w64(sl[u] >= lo && sl[u] < lo + R);
+                            while (hit) {
+                                const int jj = __builtin_ctzll(hit);
+                                hit &= hit - 1;
+                                const int row = (int)(readlane64_i(sl[u], jj) - lo);
+                                if (lane == row) tok = s0 + u * kWave + jj;
+                            }
                         }
                     }
                 }
-            }
-            uint32_t wk[kB8], wv[kB8];
+                uint32_t wk[kRowGroup], wv[kRowGroup];
 #pragma unroll
-            for (int i = 0; i < kB8; ++i) {
-                const int64_t ti = readlane64_i(tok, i);
-                const size_t w = ((size_t)(ti < 0 ? 0 : ti) * H + h) * kRowWords + lane;
-                wk[i] = kn[w];
-                wv[i] = vn[w];
-            }
-            float ak = 0.0f, av = 0.0f;
+                for (int i = 0; i < kRowGroup; ++i) {
+                    const int64_t ti = readlane64_i(tok, i);
+                    const size_t w = ((size_t)(ti < 0 ? 0 : ti) * H + h) * kRowWords + lane;
+                    wk[i] = kn[w];
+                    wv[i] = vn[w];
+                }
 #pragma unroll
-            for (int i = 0; i < kB8; ++i) {
-                if (readlane64_i(tok, i) >= 0) {
-                    ak = abs_max2(wk[i], ak);
-                    av = abs_max2(wv[i], av);
+                for (int i = 0; i < kRowGroup; ++i) {
+                    if (readlane64_i(tok, i) >= 0) {
+                        ak = abs_max2(wk[i], ak);
+                        av = abs_max2(wv[i], av);
+                    }
                 }
             }
             ak = wave_max(ak);
@@ -180,7 +186,9 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void fp8_append_kernel(Append
 
 hipError_t launch_scatter_fp8(const ScatterArgs& a, hipStream_t stream) {
     if (a.num_tokens <= 0) return hipSuccess;
-    if (a.block_size != kB8 || a.num_kv_heads <= 0 || a.num_kv_heads > 65535) return hipErrorInvalidValue;
+    if ((a.block_size != 8 && a.block_size != 16 && a.block_size != 32 && a.block_size != 64 &&
+         a.block_size != 128) || a.num_kv_heads <= 0 || a.num_kv_heads > 65535)
+        return hipErrorInvalidValue;
     int64_t chunks = (a.num_tokens + kScaleChunk - 1) / kScaleChunk;
     if (chunks > 8192) chunks = 8192;   // grid-stride over the rest
     fp8_scale_kernel<<<dim3((unsigned)chunks, (unsigned)a.num_kv_heads), dim3(kWave), 0, stream>>>(a);

@@ -227,9 +227,9 @@ kv_status create_pool(const kv_pool_desc* desc, void* k_base, void* v_base, floa
     const int32_t B = desc->block_size;
     if (B != 8 && B != 16 && B != 32 && B != 64 && B != 128)
         return fail(KV_ERR_UNSUPPORTED, "block_size %d: kernels are built for 8, 16, 32, 64 and 128", B);
-    if (B != kvp::kBlockTokens && !(desc->dtype == KV_BF16 && desc->head_dim == 128))
-        return fail(KV_ERR_UNSUPPORTED, "block_size %d needs a bf16 pool with head_dim 128 (other pools use %d)", B,
-                    kvp::kBlockTokens);
+    if (B != kvp::kBlockTokens && !((desc->dtype == KV_BF16 || fp8) && desc->head_dim == 128))
+        return fail(KV_ERR_UNSUPPORTED, "block_size %d needs a bf16 or FP8 pool with head_dim 128 (other pools use %d)",
+                    B, kvp::kBlockTokens);
     if (desc->head_dim != 64 && desc->head_dim != 128)
         return fail(KV_ERR_UNSUPPORTED, "head_dim %d: kernels are built for 64 and 128", desc->head_dim);
     if (fp8 && desc->head_dim != 128) return fail(KV_ERR_UNSUPPORTED, "FP8 pools are built for head_dim 128");

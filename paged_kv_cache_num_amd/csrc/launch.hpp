@@ -140,7 +140,7 @@ bool decode_shape_supported(int dtype, int head_dim, int group, int block_size);
 // Launches the decode kernel only; the caller launches the partition merge.
 hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int group, hipStream_t stream);
 // The same kernels reading an FP8 pool (codes widened to bf16, block scales
-// applied to the scores and the probabilities); block size 16.
+// applied to the scores and the probabilities); block sizes 8..128.
 hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, int group, hipStream_t stream);
 
 // bf16 / head_dim 128, balanced split over `workers` single-wave workers plus

@@ -328,9 +328,14 @@ def test_fp8_pool_create_checks():
                                     ctypes.byref(h)) == K.KV_ERR_INVALID_ARGUMENT
     assert K.lib.kv_pool_create_fp8(ctypes.byref(d), 0x10000, 0x20000, 0x30002, 0x40000,
                                     ctypes.byref(h)) == K.KV_ERR_INVALID_ARGUMENT
-    # built for head_dim 128 and 16-token blocks
+    # built for head_dim 128 and the block sizes of the bf16 / head_dim-128 pools
     assert _fp8_pool(head_dim=64)[0] == K.KV_ERR_UNSUPPORTED
-    assert _fp8_pool(block_size=32)[0] == K.KV_ERR_UNSUPPORTED
+    for B in (8, 16, 32, 64, 128):
+        st, h = _fp8_pool(block_size=B)
+        assert st == K.KV_OK, B
+        K.lib.kv_pool_destroy(h)
+    for B in (4, 24, 256):
+        assert _fp8_pool(block_size=B)[0] == K.KV_ERR_UNSUPPORTED, B
 
 
 def test_fp8_decode_argument_checks():

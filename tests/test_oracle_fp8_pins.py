@@ -72,6 +72,29 @@ def test_scale_rule_first_write_sets_it_later_writes_keep_it():
     assert np.array_equal(ks3, ks2) and (kc3[1, :, 4, :] == 0x7E).all()
 
 
+@pytest.mark.parametrize("B", [8, 128])
+def test_scale_rule_covers_every_row_a_write_puts_into_a_block(B):
+    """At any block size the write that fills row 0 sets the scale from all the
+    rows it puts into that block (a prefill chunk filling it whole), and a row
+    that opens the next block alone sets that block's scale from itself."""
+    N, H, D = 4, 1, 8
+    kc = np.zeros((N, H, B, D), np.uint8)
+    ks = np.zeros((N, H), np.float32)
+    rows = np.full((B + 1, H, D), 0.5, np.float32)
+    rows[B - 1, 0, 3] = -96.0                  # the block's last row holds its largest magnitude
+    rows[B, 0, :] = 2.0                        # row 0 of the next block, written by the same call
+    bits = kvgen.f32_to_bf16_bits(rows)
+    slots = np.concatenate([np.arange(2 * B, 3 * B), [B]])     # block 2 whole, then row 0 of block 1
+    kc2, _, ks2, _ = fp8.scatter(kc, kc, ks, ks, bits, bits, slots, B)
+    assert ks2[2, 0] == np.float32(96.0 / 448.0)
+    assert ks2[1, 0] == np.float32(2.0 / 448.0)
+    assert ks2[0, 0] == 0 and ks2[3, 0] == 0
+    assert kc2[2, 0, B - 1, 3] == 0xFE                         # -96 is -448 x scale: the largest code
+    assert (kc2[1, 0, 0, :] == 0x7E).all()                     # 2.0 alone: +448 x scale
+    # 0.5 / (96 / 448) = 2.333..: the nearest E4M3 value is 2.25 (0x41)
+    assert (kc2[2, 0, :B - 1, :] == 0x41).all()
+
+
 def test_attention_matches_the_c_oracle_on_exact_values():
     """Codes times power-of-two scales are exact in bf16, so the FP8 path and the
     bf16 C oracle see the same numbers."""
