@@ -348,9 +348,11 @@ kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out
  * Preconditions (device data, not checked): block_tables[i][b] ==
  * block_tables[0][b] for every i and b < shared_blocks, and L_i >=
  * shared_blocks * B for every i (a sequence with L_i == 0 still gives zeros).
- * The prefix is read through sequence 0's table row.  Built for bf16 pools
- * with head_dim 128 and block size 16 and at most 1024 sequences
- * (KV_ERR_UNSUPPORTED otherwise); no decode-append form.  Errors as for
+ * The prefix is read through sequence 0's table row, in whole 16-token tiles
+ * (with 8-token blocks an odd last prefix block is read per sequence, as the
+ * rest of the context is; a prefix of one 8-token block runs the plain call).
+ * Built for bf16 pools with head_dim 128, block sizes 8 to 128, and at most
+ * 1024 sequences (KV_ERR_UNSUPPORTED otherwise); no decode-append form.  Errors as for
  * paged_attention_decode.
  */
 kv_status paged_attention_decode_shared(kv_pool_t pool, int32_t layer, void* out, const void* q,

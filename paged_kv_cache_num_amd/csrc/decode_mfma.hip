@@ -430,7 +430,7 @@ template <bool kFp8>
 __device__ __forceinline__ bool keep_v_cached(const DecodeArgs& a, int seq, int tile, const WalkCtx& c) {
     if (kFp8) return true;   // FP8 tiles: the hint measured no different (8B, 70B, long-context batches)
     const int entry = c.pair8 ? 2 * tile : tile >> c.sub_shift;
-    const int32_t* t = a.tables + (size_t)seq * a.max_blocks + a.shared_tiles + entry;
+    const int32_t* t = a.tables + (size_t)seq * a.max_blocks + a.shared_entries + entry;
     const int32_t mine = t[0];
     bool shared = false;
     if (seq > 0) shared = shared || t[-(ptrdiff_t)a.max_blocks] == mine;
@@ -447,8 +447,8 @@ __device__ __forceinline__ int neighbour_entries(const DecodeArgs& a, int seq, i
     int x = 0;
     if (!kFp8) {
         const int entry = c.pair8 ? 2 * tile : tile >> c.sub_shift;
-        if (c.lane == 0 && seq > 0) x = a.tables[(size_t)(seq - 1) * a.max_blocks + a.shared_tiles + entry];
-        if (c.lane == 1 && seq + 1 < a.num_seqs) x = a.tables[(size_t)(seq + 1) * a.max_blocks + a.shared_tiles + entry];
+        if (c.lane == 0 && seq > 0) x = a.tables[(size_t)(seq - 1) * a.max_blocks + a.shared_entries + entry];
+        if (c.lane == 1 && seq + 1 < a.num_seqs) x = a.tables[(size_t)(seq + 1) * a.max_blocks + a.shared_entries + entry];
     }
     return x;
 }
@@ -892,7 +892,7 @@ __device__ __forceinline__ int walk_len(const DecodeArgs& a, int i) {
 
 // Table row of sequence i from the first tile the balanced walk covers.
 __device__ __forceinline__ const int32_t* walk_row(const DecodeArgs& a, int i) {
-    return a.tables + (size_t)i * a.max_blocks + a.shared_tiles;
+    return a.tables + (size_t)i * a.max_blocks + a.shared_entries;
 }
 
 // Partial state of one (sequence, KV head) piece: the unnormalised output of
@@ -982,7 +982,7 @@ __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x,
 // ---------------------------------------------------------------------------
 constexpr int kPrefixDepth = 2;   // prefix tiles are mostly cache hits: two in flight per wave
 
-template <int G>
+template <int G, bool kAnyB>
 __device__ void prefix_wave(const DecodeArgs& a, int64_t idx) {
     constexpr int kSeqs = 16 / G;   // sequences per column block
     const int Hkv = a.num_kv_heads;
@@ -993,7 +993,7 @@ __device__ void prefix_wave(const DecodeArgs& a, int64_t idx) {
     const int b0 = p * a.prefix_part_tiles;
     const int nk = min(a.prefix_part_tiles, a.shared_tiles - b0);   // >= 1: the host sizes the parts
 
-    WalkCtx c = make_ctx<false, false>(a, kv);
+    WalkCtx c = make_ctx<kAnyB, false>(a, kv);
     c.keep_v = true;   // every column block reads these tiles
     // column n: query head n % G of sequence qb * kSeqs + n / G (zero past the batch)
     const int col_seq = qb * kSeqs + c.n / G;
@@ -1040,9 +1040,9 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     const int64_t W = a.workers;
     const int64_t w = blockIdx.x;
     if (w >= W) {
-        if constexpr (!kFp8 && !kAnyB) {
+        if constexpr (!kFp8) {
             if (a.shared_tiles > 0) {   // a shared prefix: its walks
-                prefix_wave<G>(a, w - W);
+                prefix_wave<G, kAnyB>(a, w - W);
                 return;
             }
         }
@@ -1148,7 +1148,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
             if (nseq < S) {
                 // tiles 0..63 of the next sequence's row; a lane whose tile would
                 // need an entry past the row loads nothing (the walk never reads it)
-                const int row_len = a.max_blocks - a.shared_tiles;
+                const int row_len = a.max_blocks - a.shared_entries;
                 const bool ok = c.pair8 ? 2 * c.lane < row_len : (c.lane >> c.sub_shift) < row_len;
                 const int2 pf = tile_entries(walk_row(a, nseq), c.lane, ok, c);
                 pf_tv0 = pf.x;
@@ -1577,10 +1577,11 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     }
 }
 
+// The any-block-size instantiation: it holds the most registers of the
+// kernels a pool type can launch, so its occupancy bounds them all.
 template <int G, bool kFp8>
 const void* streamk_kernel_ptr() {
-    return kFp8 ? reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, false, true>)
-                : reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, true, false>);
+    return reinterpret_cast<const void*>(&decode_bf16_streamk_kernel<G, true, kFp8>);
 }
 
 }  // namespace
@@ -1734,7 +1735,8 @@ hipError_t launch_mfma(const DecodeArgs& a, int group, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_bf16_shared(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
-    if (a.shared_tiles <= 0 || a.prefix_parts <= 0 || a.prefix_part_tiles <= 0 || a.block_size != kTileTokens ||
+    if (a.shared_tiles <= 0 || a.prefix_parts <= 0 || a.prefix_part_tiles <= 0 ||
+        a.shared_entries != (int32_t)((int64_t)a.shared_tiles * kTileTokens / a.block_size) ||
         (int64_t)(a.prefix_parts - 1) * a.prefix_part_tiles >= a.shared_tiles || !a.ws_pml || !a.ws_pacc || a.k_append)
         return hipErrorInvalidValue;
     if (group != 1 && group != 2 && group != 4 && group != 8) return hipErrorInvalidValue;

@@ -131,17 +131,24 @@ struct SharedPlan {
     uint64_t pml_off, pacc_off, total;
 };
 
+// 16-token tiles the prefix waves take for a prefix of shared_blocks blocks:
+// whole tiles only (with 8-token blocks an odd last block goes to the
+// per-sequence walks, which read it like any other block).
+int32_t shared_tiles_of(const kv_pool_desc& d, int32_t shared_blocks) {
+    return (int32_t)((int64_t)shared_blocks * d.block_size / kvp::kTileTokens);
+}
+
 SharedPlan plan_shared(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                       int32_t shared_blocks) {
+                       int32_t shared_tiles) {
     SharedPlan sp;
     memset(&sp, 0, sizeof sp);
     sp.base = plan_decode(d, num_seqs, num_q_heads, max_context_len, 0);
     const int64_t group = num_q_heads / d.num_kv_heads;
     const int64_t column_blocks = ((int64_t)num_seqs * group + 15) / 16 * d.num_kv_heads;
     const int64_t want = ((int64_t)sp.base.workers / 2 + column_blocks - 1) / (column_blocks > 0 ? column_blocks : 1);
-    int64_t parts = want < 1 ? 1 : (want > shared_blocks ? shared_blocks : want);
-    sp.part_tiles = (int32_t)((shared_blocks + parts - 1) / parts);
-    sp.parts = (int32_t)((shared_blocks + sp.part_tiles - 1) / sp.part_tiles);
+    int64_t parts = want < 1 ? 1 : (want > shared_tiles ? shared_tiles : want);
+    sp.part_tiles = (int32_t)((shared_tiles + parts - 1) / parts);
+    sp.parts = (int32_t)((shared_tiles + sp.part_tiles - 1) / sp.part_tiles);
     const uint64_t states = (uint64_t)num_seqs * (uint64_t)num_q_heads * (uint64_t)(sp.parts + 1);
     sp.pml_off = round_up(sp.base.ws_total, 256u);
     sp.pacc_off = sp.pml_off + round_up(states * 8u, 256u);
@@ -154,8 +161,8 @@ kv_status check_shared(const kv_pool_desc& d, int32_t num_seqs, int32_t max_cont
                        int32_t shared_blocks) {
     if (shared_blocks < 0) return fail(KV_ERR_INVALID_ARGUMENT, "shared_blocks %d < 0", shared_blocks);
     if (shared_blocks == 0) return KV_OK;
-    if (d.dtype != KV_BF16 || d.head_dim != 128 || d.block_size != kvp::kTileTokens)
-        return fail(KV_ERR_UNSUPPORTED, "a shared prefix needs a bf16 pool with head_dim 128 and block size 16");
+    if (d.dtype != KV_BF16 || d.head_dim != 128)
+        return fail(KV_ERR_UNSUPPORTED, "a shared prefix needs a bf16 pool with head_dim 128");
     if (num_seqs > kvp::kStreamKMaxSeqs)
         return fail(KV_ERR_UNSUPPORTED, "a shared prefix is handled for at most %d sequences", kvp::kStreamKMaxSeqs);
     if (shared_blocks > max_blocks_per_seq || (int64_t)shared_blocks * d.block_size > max_context_len)
@@ -511,10 +518,10 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
         const kv_status st = check_shared(d, num_seqs, max_context_len, max_blocks_per_seq, shared_blocks);
         if (st != KV_OK) return st;
     }
-    const SharedPlan sp = shared_blocks > 0 ? plan_shared(d, num_seqs, num_q_heads, max_context_len, shared_blocks)
-                                            : SharedPlan{};
-    const Plan plan = shared_blocks > 0 ? sp.base : plan_decode(d, num_seqs, num_q_heads, max_context_len, partition_size);
-    const uint64_t ws_needed = shared_blocks > 0 ? sp.total : plan.ws_total;
+    const int32_t stiles = shared_blocks > 0 ? shared_tiles_of(d, shared_blocks) : 0;   // 0: the plain call
+    const SharedPlan sp = stiles > 0 ? plan_shared(d, num_seqs, num_q_heads, max_context_len, stiles) : SharedPlan{};
+    const Plan plan = stiles > 0 ? sp.base : plan_decode(d, num_seqs, num_q_heads, max_context_len, partition_size);
+    const uint64_t ws_needed = stiles > 0 ? sp.total : plan.ws_total;
     kvp::DecodeArgs a;
     memset(&a, 0, sizeof a);
     if (ws_needed > 0) {
@@ -529,7 +536,7 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
             a.ws_ml = reinterpret_cast<float*>(ws);
         }
         a.ws_acc = reinterpret_cast<float*>(ws + plan.ws_first);
-        if (shared_blocks > 0) {
+        if (stiles > 0) {
             a.ws_pml = reinterpret_cast<float*>(ws + sp.pml_off);
             a.ws_pacc = reinterpret_cast<float*>(ws + sp.pacc_off);
         }
@@ -556,8 +563,9 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
         a.v_scale = pool->v_scale + (uint64_t)layer * pool->scale_layer;
     }
     hipError_t e;
-    if (shared_blocks > 0) {
-        a.shared_tiles = shared_blocks;   // block size 16: one tile per block
+    if (stiles > 0) {
+        a.shared_tiles = stiles;
+        a.shared_entries = (int32_t)((int64_t)stiles * kvp::kTileTokens / d.block_size);
         a.prefix_parts = sp.parts;
         a.prefix_part_tiles = sp.part_tiles;
         e = kvp::launch_decode_bf16_shared(a, num_q_heads / d.num_kv_heads, plan.workers,
@@ -649,8 +657,9 @@ kv_status paged_attention_shared_workspace_bytes(kv_pool_t pool, int32_t num_seq
                     pool->desc.num_kv_heads);
     const kv_status st = check_shared(pool->desc, num_seqs, max_context_len, max_blocks_per_seq, shared_blocks);
     if (st != KV_OK) return st;
-    *bytes = shared_blocks > 0 ? plan_shared(pool->desc, num_seqs, num_q_heads, max_context_len, shared_blocks).total
-                               : plan_decode(pool->desc, num_seqs, num_q_heads, max_context_len, 0).ws_total;
+    const int32_t stiles = shared_blocks > 0 ? shared_tiles_of(pool->desc, shared_blocks) : 0;
+    *bytes = stiles > 0 ? plan_shared(pool->desc, num_seqs, num_q_heads, max_context_len, stiles).total
+                        : plan_decode(pool->desc, num_seqs, num_q_heads, max_context_len, 0).ws_total;
     return ok();
 }
 

@@ -118,7 +118,7 @@ struct DecodeArgs {
     int32_t part_tokens;         // tokens per partition (multiple of 16)
     int32_t max_parts;           // ceil(max_context / part_tokens), >= 1
     float scale_log2;            // softmax scale * log2(e)
-    // Shared prefix (paged_attention_decode_shared, bf16, block size 16): the
+    // Shared prefix (paged_attention_decode_shared, bf16, block sizes 8..128): the
     // first shared_tiles table entries of every sequence name the same blocks.
     // The prefix waves leave (m, l, output) per (sequence, query head) and
     // part in slots 0 .. prefix_parts-1 of ws_pml / ws_pacc ([S][Hq][parts + 1]
@@ -126,6 +126,7 @@ struct DecodeArgs {
     // the prefix and leaves a (sequence, KV head) it covers whole in slot
     // prefix_parts; the fix-up merges them.  shared_tiles 0: none of this.
     int32_t shared_tiles;
+    int32_t shared_entries;      // table entries those tiles take: shared_tiles * 16 / block_size
     int32_t prefix_parts;
     int32_t prefix_part_tiles;   // tiles per part (the last part may have fewer)
     float* ws_pml;

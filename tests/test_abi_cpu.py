@@ -468,10 +468,20 @@ def test_shared_prefix_argument_checks_return_before_any_launch():
     assert _shared_ws(h, shared=-1)[0] == K.KV_ERR_INVALID_ARGUMENT
     K.lib.kv_pool_destroy(h)
     # other pools: unsupported
-    for kw in (dict(), dict(num_kv_heads=8, head_dim=64, dtype="bf16"),
-               dict(num_kv_heads=8, head_dim=128, dtype="bf16", block_size=32)):
+    for kw in (dict(), dict(num_kv_heads=8, head_dim=64, dtype="bf16")):
         st, h = _pool(**kw)
         assert st == K.KV_OK
         assert _shared(h, Hq=8 * (kw.get("num_kv_heads", 2) // 2)) == K.KV_ERR_UNSUPPORTED
         assert _shared_ws(h, Hq=8 * (kw.get("num_kv_heads", 2) // 2))[0] == K.KV_ERR_UNSUPPORTED
+        K.lib.kv_pool_destroy(h)
+    # bf16 / head_dim 128 at other block sizes: supported; the prefix states come on top of
+    # the plain workspace once the prefix holds a whole 16-token tile (one 8-token block does not)
+    for B, shared, extra in ((32, 4, True), (128, 2, True), (8, 2, True), (8, 1, False)):
+        st, h = _pool(num_kv_heads=8, head_dim=128, dtype="bf16", block_size=B)
+        assert st == K.KV_OK
+        st, need = _shared_ws(h, Hq=32, shared=shared)
+        assert st == K.KV_OK
+        plain = ctypes.c_uint64(0)
+        assert K.lib.paged_attention_workspace_bytes(h, 4, 32, 4096, 0, ctypes.byref(plain)) == K.KV_OK
+        assert (need > plain.value) == extra, (B, shared)
         K.lib.kv_pool_destroy(h)

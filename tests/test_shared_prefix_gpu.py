@@ -132,3 +132,29 @@ def test_shared_prefix_graph_replay():
         assert step.out_host().tobytes() == want
         step.attend()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("B,shared_blocks", [(8, 256), (8, 255), (32, 64), (64, 32), (128, 16)])
+def test_shared_prefix_other_block_sizes(B, shared_blocks):
+    """Block sizes 8..128: the prefix waves take the prefix's whole 16-token
+    tiles (with 8-token blocks an odd last block is read by the per-sequence
+    walks); oracle parity and agreement with the plain call."""
+    say(f"shared prefix: B={B} shared_blocks={shared_blocks}")
+    shape = kvgen.Shape("C4", kvgen.BF16, 32, 8, 128, B, 1.0)
+    wl = kvgen.make_workload("C4", seed=B, variant="sharp", poison=True, lengths=np.asarray(LENGTHS), shape=shape)
+    assert wl.info["shared_prefix_blocks"] == 2048 // B
+    ref = oracle.run_step(wl)
+    plain, shared = plain_and_shared(wl, shared_blocks)
+    check_step(shared, wl, ref, label=f"shared/B{B}/{shared_blocks}")
+    d = float(np.abs(to_f64(shared.out_host(), "bf16") - to_f64(plain.out_host(), "bf16")).max())
+    say(f"  max |shared - plain| = {d:.3e}")
+    assert d <= TOL["bf16"]
+
+
+def test_shared_prefix_full_c4_at_block_size_32():
+    say("shared prefix: full C4 batch at B = 32")
+    wl = kvgen.make_workload("C4", variant="sharp", poison=True, block_size=32)
+    assert wl.info["shared_prefix_blocks"] == 64
+    ref = oracle.run_step(wl)
+    shared = run_gpu(wl, partition_size=0, shared_blocks=64)
+    check_step(shared, wl, ref, label="C4 shared B32")
