@@ -59,6 +59,7 @@
 #include "fp8.hpp"
 #include "launch.hpp"
 #include "split.hpp"
+#include "table_index.hpp"
 
 namespace kvp {
 
@@ -403,7 +404,9 @@ struct WalkCtx {
     size_t head_stride;    // chunks between the tiles of consecutive KV heads in a block
     size_t block_stride;   // num_kv_heads * B * 16-byte chunks per row
     uint32_t num_blocks;
-    int max_blocks;        // table entries per sequence
+    int max_blocks;        // table entries per sequence (the row pitch)
+    int row_len;           // entries the walked row pointer can address: max_blocks, or what
+                           // follows a shared prefix when the walk starts after it
     bool pair8;            // B = 8: a 16-token tile is two blocks
     int sub_shift;         // B >= 16: log2(B / 16), tiles per block = 1 << sub_shift
     int k_off, v_off;      // this lane's K (16-byte units) / V (16-byte, FP8: 8-byte units) offset in a tile
@@ -478,6 +481,7 @@ __device__ __forceinline__ WalkCtx make_ctx(const DecodeArgs& a, int kv) {
     c.block_stride = (size_t)a.num_kv_heads * ((size_t)B * kRow);
     c.num_blocks = (uint32_t)a.num_blocks;
     c.max_blocks = a.max_blocks;
+    c.row_len = a.max_blocks;
     c.pair8 = kAnyB && B == 8;
     c.sub_shift = kAnyB ? 31 - __builtin_clz(B >= kTileTokens ? B / kTileTokens : 1) : 0;
     if constexpr (kFp8) {
@@ -581,19 +585,16 @@ __device__ __forceinline__ void append_into_fp8(TileF8& t, const AppendRow& app,
         if (4 * c.r + i == app.j) t.v[i] = vd;
 }
 
-// Table entries of tile e (16 tokens) of a sequence whose table row is `row`:
-// for B >= 16 the block holding it (entry e / (B/16)); for B = 8 the two
-// blocks holding its halves (entries 2e and 2e + 1; the second may lie past
-// the row when the tile is the last one, and is then never used).
+// Table entries of tile e (16 tokens) of a sequence whose table row is `row`
+// (c.row_len entries from there): for B >= 16 the block holding it (entry
+// e / (B/16)); for B = 8 the two blocks holding its halves (entries 2e and
+// 2e + 1; the second is not read when it lies past the row: the tile is then
+// the row's last one and its second half is never used).
 __device__ __forceinline__ int2 tile_entries(const int32_t* row, int e, bool valid, const WalkCtx& c) {
     int2 tv = make_int2(0, 0);
     if (valid) {
-        if (c.pair8) {
-            tv.x = row[2 * e];
-            if (2 * e + 1 < c.max_blocks) tv.y = row[2 * e + 1];
-        } else {
-            tv.x = row[e >> c.sub_shift];
-        }
+        tv.x = row[tile_first_entry(e, c.pair8, c.sub_shift)];
+        if (tile_has_second_entry(e, c.row_len, c.pair8)) tv.y = row[2 * e + 1];
     }
     return tv;
 }
@@ -1123,6 +1124,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         const bool whole = (b == 0) && (n_here == nblk);
 
         WalkCtx c = make_ctx<kAnyB, kFp8>(a, kv);
+        c.row_len = a.max_blocks - a.shared_entries;   // the walk's row starts after a shared prefix
         const bool use_pf = pf_valid && pf_seq == seq && b == 0;
         c.keep_v = use_pf ? keep_v_fetched<kFp8>(pf_tv0, pf_nb, seq, S) : keep_v_cached<kFp8>(a, seq, b, c);
         bf16x8_t qb[kKK];
@@ -1148,8 +1150,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
             if (nseq < S) {
                 // tiles 0..63 of the next sequence's row; a lane whose tile would
                 // need an entry past the row loads nothing (the walk never reads it)
-                const int row_len = a.max_blocks - a.shared_entries;
-                const bool ok = c.pair8 ? 2 * c.lane < row_len : (c.lane >> c.sub_shift) < row_len;
+                const bool ok = tile_in_row(c.lane, c.row_len, c.pair8, c.sub_shift);
                 const int2 pf = tile_entries(walk_row(a, nseq), c.lane, ok, c);
                 pf_tv0 = pf.x;
                 pf_tv1 = pf.y;
@@ -1355,7 +1356,7 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
             }
             if (nkv < Hkv && seq_first + (int64_t)nkv * nblk + nb < t_hi) {
                 const int e = nb + c.lane;
-                const bool ok = (c.pair8 ? 2 * e : e >> c.sub_shift) < a.max_blocks;
+                const bool ok = tile_in_row(e, c.row_len, c.pair8, c.sub_shift);
                 const int2 pf = tile_entries(a.tables + (size_t)seq * a.max_blocks, e, ok, c);
                 pf_tv0 = pf.x;
                 pf_tv1 = pf.y;

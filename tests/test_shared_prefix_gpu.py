@@ -158,3 +158,24 @@ def test_shared_prefix_full_c4_at_block_size_32():
     ref = oracle.run_step(wl)
     shared = run_gpu(wl, partition_size=0, shared_blocks=64)
     check_step(shared, wl, ref, label="C4 shared B32")
+
+
+def test_shared_prefix_block_size_8_odd_row_tail():
+    """B = 8 with a 256-block prefix and 293-entry rows: 37 entries follow the
+    prefix (an odd count), and the last two sequences fill their rows with
+    walks that end in the first half of a 16-token tile (L mod 16 = 7 and 8).
+    The walks and the next-walk prefetch read no table entry past the row (the
+    last row ends the table buffer); results against the oracle and the plain
+    call."""
+    lengths = [2100, 2049, 2300, 2343, 2344]
+    say(f"shared prefix: B=8, odd row tail, lengths={lengths}")
+    shape = kvgen.Shape("C4", kvgen.BF16, 32, 8, 128, 8, 1.0)
+    wl = kvgen.make_workload("C4", seed=21, variant="sharp", poison=True, lengths=np.asarray(lengths), shape=shape)
+    assert wl.info["shared_prefix_blocks"] == 256
+    assert wl.max_blocks_per_seq == 293 and (293 - 256) % 2 == 1
+    ref = oracle.run_step(wl)
+    plain, shared = plain_and_shared(wl, 256)
+    check_step(shared, wl, ref, label="shared/B8/odd tail")
+    d = float(np.abs(to_f64(shared.out_host(), "bf16") - to_f64(plain.out_host(), "bf16")).max())
+    say(f"  max |shared - plain| = {d:.3e}")
+    assert d <= TOL["bf16"]
