@@ -120,43 +120,67 @@ def nan_value(dtype: str):
 # ----------------------------------------------------------------------------
 
 class BlockAllocator:
-    """Free list plus per-block reference counts, as a block manager keeps them.
+    """Block manager fixture: which physical blocks are free and how many
+    tables name each of the others.
 
-    Behaviour follows the allocator described in section 4 ("Minimal
-    implementation") of the lattice-ai-eng "KV Cache & PagedAttention" page:
-    a block is taken from the end of the free list, an exhausted pool raises
-    ``MemoryError``, sharing raises the count, and releasing a block whose
-    count reaches zero puts it back on the end of the free list.
-    Utilization is the fraction of blocks not on the free list.
+    State is two arrays: ``_stack[:_top]`` holds the free block ids (the next
+    block handed out is ``_stack[_top - 1]``, and a released block goes back
+    on top, so the most recently freed block is reused first, as a LIFO free
+    list does), and ``_refs[b]`` counts the tables naming block ``b`` (0 for a
+    free block).  The behaviour is the block manager's contract as the pages
+    state it (lattice-ai-eng "KV Cache & PagedAttention", section 4; "GPU
+    paged KV cache", "Prefix sharing, reference counts, and copy-on-write"):
+    an empty pool is a ``MemoryError`` for the caller, sharing adds a
+    reference, a block returns to the pool when its last reference goes, and
+    utilization is the fraction of blocks in use.
     """
 
     def __init__(self, num_blocks: int, order: Optional[np.ndarray] = None):
-        self.num_blocks = int(num_blocks)
-        self.free: List[int] = list(range(self.num_blocks)) if order is None else [int(b) for b in order]
-        if sorted(self.free) != list(range(self.num_blocks)):
+        n = int(num_blocks)
+        ids = np.arange(n, dtype=np.int64) if order is None else np.asarray(order, dtype=np.int64).reshape(-1)
+        if ids.shape != (n,) or not np.array_equal(np.sort(ids), np.arange(n)):
             raise ValueError("free-list order must be a permutation of the pool")
-        self.refcount: Dict[int, int] = {}
+        self.num_blocks = n
+        self._stack = ids.astype(np.int32)
+        self._top = n
+        self._refs = np.zeros(n, dtype=np.int32)
+
+    def _held(self, b: int, what: str) -> int:
+        b = int(b)
+        if not 0 <= b < self.num_blocks or self._refs[b] <= 0:
+            raise ValueError(f"{what} of block {b} that holds no reference")
+        return b
 
     def alloc(self) -> int:
-        if not self.free:
+        if self._top == 0:
             raise MemoryError("KV block pool exhausted")
-        b = self.free.pop()
-        self.refcount[b] = 1
+        self._top -= 1
+        b = int(self._stack[self._top])
+        self._refs[b] = 1
         return b
 
     def release(self, b: int) -> None:
-        if self.refcount.get(b, 0) <= 0:
-            raise ValueError(f"release of block {b} that holds no reference")
-        self.refcount[b] -= 1
-        if self.refcount[b] == 0:
-            del self.refcount[b]
-            self.free.append(b)
+        b = self._held(b, "release")
+        self._refs[b] -= 1
+        if self._refs[b] == 0:
+            self._stack[self._top] = b
+            self._top += 1
 
     def share(self, b: int) -> int:
-        if self.refcount.get(b, 0) <= 0:
-            raise ValueError(f"share of unallocated block {b}")
-        self.refcount[b] += 1
+        b = self._held(b, "share")
+        self._refs[b] += 1
         return b
+
+    @property
+    def free(self) -> List[int]:
+        """Free blocks, the next to be handed out last."""
+        return [int(b) for b in self._stack[:self._top]]
+
+    @property
+    def refcount(self) -> Dict[int, int]:
+        """References of every block in use (a snapshot)."""
+        held = np.flatnonzero(self._refs)
+        return {int(b): int(self._refs[b]) for b in held}
 
     def fork(self, row) -> List[int]:
         """A child table naming the same blocks (every count goes up by one)."""
@@ -179,7 +203,7 @@ class BlockAllocator:
             row.append(self.alloc())
             return None
         old = int(row[b])
-        if self.refcount.get(old, 0) > 1:
+        if self._refs[old] > 1:
             new = self.alloc()
             self.release(old)
             row[b] = new
@@ -187,10 +211,10 @@ class BlockAllocator:
         return None
 
     def num_free(self) -> int:
-        return len(self.free)
+        return self._top
 
     def utilization(self) -> float:
-        return 1.0 - len(self.free) / self.num_blocks if self.num_blocks else 0.0
+        return 1.0 - self._top / self.num_blocks if self.num_blocks else 0.0
 
 
 # ----------------------------------------------------------------------------
@@ -292,6 +316,11 @@ CONFIGS = {
     "C4": dict(S=128, shape=Shape("C4", BF16, 32, 8, 128, 16, 1.0 / math.sqrt(128))),
     # long-context decode, split into 512-token partitions
     "C5": dict(S=8, shape=Shape("C5", BF16, 32, 8, 128, 16, 1.0 / math.sqrt(128), partition_size=512)),
+    # one GPU's share of the 70B-class layer under tensor parallelism over KV
+    # heads at TP = 8 (each GPU holds H_kv / 8 KV heads and their H_q / 8 query
+    # heads): the same batch as C3 (same seed: same lengths, tables and
+    # prefill chunk) with 8 query heads and 1 KV head
+    "C3TP8": dict(S=256, shape=Shape("C3", BF16, 8, 1, 128, 16, 1.0 / math.sqrt(128)), base="C3", seed=3),
 }
 
 VARIANTS = ("spec", "sharp", "hot", "needle")
@@ -323,8 +352,9 @@ def make_workload(name: str, seed: Optional[int] = None, variant: str = "spec", 
         shape = cfg["shape"]
     if block_size is not None:
         shape = dataclasses.replace(shape, block_size=int(block_size))
+    base = cfg.get("base", name) if cfg else name   # the configuration whose batch this one is
     if seed is None:
-        seed = int(name[1:]) if name[1:].isdigit() else 0
+        seed = cfg["seed"] if cfg and "seed" in cfg else (int(name[1:]) if name[1:].isdigit() else 0)
     S = num_seqs if num_seqs is not None else (cfg["S"] if cfg else len(lengths))
     B, Hkv, Hq, D, dt = shape.block_size, shape.num_kv_heads, shape.num_q_heads, shape.head_dim, shape.dtype
     ss = np.random.SeedSequence([seed, VARIANTS.index(variant), 1 if poison else 0])
@@ -333,7 +363,7 @@ def make_workload(name: str, seed: Optional[int] = None, variant: str = "spec", 
     rng_tab = np.random.default_rng(ss_tab)
 
     if lengths is None:
-        lengths = _lengths(shape.name if cfg is None else name, rng_len, S)
+        lengths = _lengths(shape.name if cfg is None else base, rng_len, S)
     lengths = np.asarray(lengths, dtype=np.int32)
     S = int(lengths.shape[0])
     nblk = np.array([_blocks_for(L, B) for L in lengths], dtype=np.int64)
@@ -391,7 +421,7 @@ def make_workload(name: str, seed: Optional[int] = None, variant: str = "spec", 
                     tables_rows[i].append(alloc.alloc())
         info["utilization"] = alloc.utilization()
     else:
-        prefill = 2048 if (name == "C3" and cfg is not None) else 0
+        prefill = 2048 if (base == "C3" and cfg is not None) else 0
         need = int(nblk.sum())
         N = num_blocks or max(1, int(math.ceil(1.25 * need))) + prefill // B
         alloc = BlockAllocator(N, rng_tab.permutation(N))
@@ -496,7 +526,7 @@ def make_workload(name: str, seed: Optional[int] = None, variant: str = "spec", 
         info["poison"] = True
 
     info["seed"] = seed
-    if name == "C3":
+    if base == "C3":
         info["lognormal_sigma"] = 1.0
     return Workload(name=name, variant=variant, dtype=dt, num_blocks=N, block_size=B,
                     num_kv_heads=Hkv, num_q_heads=Hq, head_dim=D,
