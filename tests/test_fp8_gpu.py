@@ -318,11 +318,18 @@ def test_copy_blocks_copies_codes_and_scales_of_every_layer():
 
 # ------------------------------------------------- the 8B-shaped decode batch --
 
-def test_8b_batch_pool_exact_and_sampled_sequences():
+@pytest.mark.parametrize("variant", ["spec", "sharp"])
+def test_8b_batch_pool_exact_and_every_sequence(variant):
+    """The full 8B-shaped batch on an FP8 pool, the fused append in the
+    balanced split (2048 workers): codes and scales bit-exact, and every one of
+    the 64 sequences within 2e-2 of the FP8 oracle (each sequence's blocks
+    gathered into a pool of their own, so the oracle runs one sequence at a time)."""
     import torch
     from paged_kv_cache_num_amd import DecodeStep
-    wl = kvgen.make_workload("C2", variant="spec", poison=True)
-    state = kvgen.fp8_pool_state(wl, seed=2, largest=3.0 / math.sqrt(128))
+    say(f"C2 fp8 full batch, {variant}")
+    wl = kvgen.make_workload("C2", variant=variant, poison=True)
+    largest = 3.0 / math.sqrt(128) if variant == "spec" else 3.0
+    state = kvgen.fp8_pool_state(wl, seed=2, largest=largest)
     step = DecodeStep.from_workload(wl, fp8_pool=state, partition_size=0)
     step.run_fused()
     torch.cuda.synchronize()
@@ -334,15 +341,39 @@ def test_8b_batch_pool_exact_and_sampled_sequences():
     assert np.isfinite(out).all()
     B = wl.block_size
     worst = 0.0
-    for i in (0, 5, 17, 33, 48, 63):
+    for i in range(wl.num_seqs):
         L = int(wl.context_lens[i])
         blocks = wl.block_tables[i, :-(-L // B)]
         sub = [a[blocks] for a in ref]
         want = ofp8.paged_attention(wl.q[i:i + 1], *sub, np.arange(blocks.size, dtype=np.int32)[None, :],
                                     np.array([L], dtype=np.int32), step.scale)
         worst = max(worst, float(np.abs(out[i] - want[0]).max()))
-    say(f"  C2 fp8 sampled: max |gpu - oracle| = {worst:.3e}")
+    say(f"  C2 fp8 {variant}, all {wl.num_seqs} sequences: max |gpu - oracle| = {worst:.3e}")
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("fused,partition", [(True, 0), (False, 512)])
+def test_tp8_shard_one_kv_head_every_sequence(fused, partition):
+    """One GPU's share of the 70B-class batch at TP = 8 (8 query heads, 1 KV
+    head, 256 sequences, the 2048-token prefill chunk) on an FP8 pool: codes
+    and scales bit-exact after the step, every sequence within 2e-2 of the
+    FP8 oracle."""
+    import torch
+    from paged_kv_cache_num_amd import DecodeStep
+    say(f"C3TP8 fp8 sharp, fused={fused}, partition={partition}")
+    wl = kvgen.make_workload("C3TP8", variant="sharp", poison=True)
+    state = kvgen.fp8_pool_state(wl, seed=3, largest=3.0)
+    step = DecodeStep.from_workload(wl, fp8_pool=state, partition_size=partition)
+    (step.run_fused if fused else step.run)()
+    torch.cuda.synchronize()
+    ref = ofp8.scatter(*state, wl.k_new, wl.v_new, step.slots_host, wl.block_size)
+    for name, g, w in zip(("K codes", "V codes", "K scales", "V scales"), step.pool_host() + step.scales_host(), ref):
+        assert g.tobytes() == w.tobytes(), f"C3TP8 fp8: {name} differ"
+    want = ofp8.paged_attention(wl.q, *ref, wl.block_tables, wl.context_lens, step.scale)
+    out = kvgen.bf16_bits_to_f32(step.out_host()).astype(np.float64)
+    err = float(np.abs(out - want).max())
+    say(f"  C3TP8 fp8: max |gpu - oracle| = {err:.3e}")
+    assert np.isfinite(out).all() and err <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("fused,partition", [(False, 0), (True, 0), (False, 512), (True, 512)])

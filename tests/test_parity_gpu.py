@@ -52,6 +52,21 @@ def test_c3_70b_gqa8_with_prefill_scatter(variant, partition):
     check_step(step, wl, ref, label=f"C3/{variant}/p{partition}")
 
 
+@pytest.mark.parametrize("variant", ["spec", "sharp", "hot", "needle"])
+@pytest.mark.parametrize("partition", [0, 512])
+def test_c3_tp8_shard_one_kv_head(variant, partition):
+    """One GPU's share of the 70B-class batch under tensor parallelism over KV
+    heads at TP = 8 ("KV Cache & PagedAttention", section 5: each GPU holds
+    H_kv / TP heads' cache): 8 query heads on 1 KV head, the same 256
+    sequences and prefill chunk; the balanced split walks 256 (sequence, KV
+    head) pairs over the whole GPU."""
+    say(f"C3TP8 variant={variant} partition={partition} S=256 Hq=8 Hkv=1 D=128 bf16, 2048-token prefill chunk")
+    wl = workload("C3TP8", variant)
+    ref = reference("C3TP8", variant)
+    step = run_gpu(wl, partition_size=partition)
+    check_step(step, wl, ref, label=f"C3TP8/{variant}/p{partition}")
+
+
 @pytest.mark.parametrize("partition", [0, 512])
 def test_c4_prefix_sharing_equals_private_copies(partition):
     say(f"C4 sharp S=128 shared 2048-token prefix, partition={partition}")
