@@ -11,6 +11,12 @@ Default workload: Llama-3-8B-shaped decode layer (64 sequences, 32 query /
 8 KV heads, head_dim 128, block 16, context lengths U[512, 4096], block tables
 from a shuffled free list over a pool of 1.25x the blocks needed, bf16).
 
+The pool holds ``--layers`` layers (default 4) and step i runs on layer
+i mod LAYERS, as a model's decode step runs its layers one after another: no
+call re-reads KV that the previous call left in L2 or the 256 MB MALL.  The
+same call repeated on one layer (``same_layer``) and with the caches flushed
+before it (``cold``) are reported beside it.
+
 The K timed steps are replays of one captured HIP graph holding the step's
 launches (how a serving loop submits its decode step), in two forms: scatter
 + attention, and, where every sequence writes one token at position L_i - 1,
@@ -42,7 +48,7 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_num_amd/csrc/decode.hip", "paged_kv_cache_num_amd/csrc/decode_mfma.hip",
                   "paged_kv_cache_num_amd/csrc/device_common.hpp", "paged_kv_cache_num_amd/csrc/split.hpp",
-                  "paged_kv_cache_num_amd/csrc/fp8.hpp"]
+                  "paged_kv_cache_num_amd/csrc/fp8.hpp", "paged_kv_cache_num_amd/csrc/table_index.hpp"]
 
 WORKLOADS = {
     "C1": "tiny fp32 paged decode: 4 sequences, lengths {17,33,100,200}, 8 query / 2 KV heads, head_dim 64, block 16, 64-block pool",
@@ -50,9 +56,10 @@ WORKLOADS = {
     "C3": "70B-class GQA decode layer: 256 sequences, 64 query / 8 KV heads, head_dim 128, block 16, lognormal lengths (median 1024, sigma 1, clip [16,8192]), permuted blocks, plus a 2048-token prefill-chunk scatter, bf16",
     "C4": "prefix-sharing decode: 128 sequences sharing 128 blocks (2048-token prefix) plus private suffixes U[64,512], 32 query / 8 KV heads, head_dim 128, bf16",
     "C5": "long-context split decode: 8 sequences, lengths U[32768,131072], 32 query / 8 KV heads, head_dim 128, partitions of 512 tokens, fragmented pool, bf16",
+    "C3TP8": "one GPU's share of the 70B-class GQA decode layer under tensor parallelism over KV heads at TP 8: the same 256 sequences, lengths and 2048-token prefill chunk, 8 query / 1 KV head, head_dim 128, block 16, bf16",
 }
 # 0 = balanced split across the GPU; C5 names 512-token partitions explicitly
-DEFAULT_PARTITION = {"C1": 0, "C2": 0, "C3": 0, "C4": 0, "C5": 512}
+DEFAULT_PARTITION = {"C1": 0, "C2": 0, "C3": 0, "C4": 0, "C5": 512, "C3TP8": 0}
 
 
 def kernel_sha() -> str:
@@ -274,6 +281,10 @@ def main(argv=None):
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="pool storage: the workload's bf16, or E4M3 codes with per-(block, KV head) scales "
                          "(q, new rows and outputs stay bf16)")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="layers in the pool; step i reads and writes layer i mod LAYERS, as a model's layers "
+                         "follow each other, so no call finds its own KV left in the caches by the previous one "
+                         "(1: every step on the same layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-flushed timing pass")
     ap.add_argument("--no-identity", action="store_true",
@@ -335,7 +346,8 @@ def main(argv=None):
 
     nbytes = algorithmic_bytes(wl, fp8=fp8)
     state = fp8_state(wl)
-    step = DecodeStep.from_workload(wl, partition_size=part, fp8_pool=state)
+    NL = max(1, args.layers)
+    step = DecodeStep.from_workload(wl, partition_size=part, fp8_pool=state, num_layers=NL)
     torch.cuda.synchronize()
 
     # achievable HBM read rate on this machine: a plain 16-byte-load read of 2 GiB (larger than the caches)
@@ -371,17 +383,19 @@ def main(argv=None):
         del src, dst
 
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
+        step.layer = i % NL
         step.run()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, events on the stream the kernels run on
+    # timed region: K whole steps, step i on layer i mod NL, events on the stream the kernels run on
     K = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        step.layer = i % NL
         a, b, c = ev[i]
         a.record()
         step.scatter()
@@ -400,6 +414,24 @@ def main(argv=None):
     step_bytes = nbytes["attn"] + nbytes["scatter"]
     eager_ms_per_step = ms_per_step
 
+    # the same attention call K times on one layer, back to back: what part of
+    # each call the caches (L2, 256 MB MALL) serve when it re-reads the KV the
+    # previous call read (reported beside the layer-rotating figure)
+    same_layer = None
+    if NL > 1:
+        step.layer = 0
+        sl_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            sl_ev[i][0].record()
+            step.attend()
+            sl_ev[i][1].record()
+        torch.cuda.synchronize()
+        sl_us = [a.elapsed_time(b) * 1e3 for a, b in sl_ev]
+        sl_mean = sum(sl_us) / K
+        same_layer = {"attn_us_mean": round(sl_mean, 2), "attn_us_p50": round(percentile(sl_us, 0.5), 2),
+                      "achieved_gbps": round(nbytes["attn"] / (sl_mean * 1e-6) / 1e9, 1),
+                      "frac": round(nbytes["attn"] / (sl_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
     # the same K steps replayed from one captured HIP graph (how a serving loop
     # submits its decode step): no launch gaps between the step's kernels
     # The same K steps replayed from one captured HIP graph (how a serving loop
@@ -414,27 +446,31 @@ def main(argv=None):
     if not args.eager:
         forms = [False] + ([True] if step.can_fuse and not args.no_fuse else [])
         for fused in forms:
-            graph = step.capture(fused=fused)
-            graph.replay()
+            graphs = []
+            for li in range(NL):        # one captured step per layer, replayed in layer order
+                step.layer = li
+                graphs.append(step.capture(fused=fused))
+            for g in graphs:
+                g.replay()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            for _ in range(K):
-                graph.replay()
+            for i in range(K):
+                graphs[i % NL].replay()
             torch.cuda.synchronize()
             t1 = time.perf_counter()
             graph_ms[fused] = (t1 - t0) * 1e3 / K
             # the same replays one at a time between events on the stream: the GPU's own time for one
             # replayed step, without the host's submission of the next one
             g_us = []
-            for _ in range(min(K, 50)):
+            for i in range(min(K, 50)):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-                graph.replay()
+                graphs[i % NL].replay()
                 b.record()
                 b.synchronize()
                 g_us.append(a.elapsed_time(b) * 1e3)
             graph_gpu_us[fused] = percentile(g_us, 0.5)
-            del graph
+            del graphs
             print(f"bench: timed {K} graph replays ({'fused append' if fused else 'scatter + attention'}), "
                   f"{graph_ms[fused] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         # both forms leave bitwise the same pool and output (checked below); the
@@ -443,6 +479,7 @@ def main(argv=None):
         ms_per_step = graph_ms[fused_on]
         launch = "hip_graph, fused append" if fused_on else "hip_graph, scatter + attention"
         # the fused form must leave the same pool and output as the two-call form
+        step.layer = 0
         step.run()
         torch.cuda.synchronize()
         ref_out = step.out.clone()
@@ -462,9 +499,11 @@ def main(argv=None):
     roofline_kernel = "paged_attention_decode"
     sb = int(wl.info.get("shared_prefix_blocks") or 0)
     if sb and not fp8 and part == 0 and wl.dtype == "bf16" and not args.no_shared:
-        sstep = DecodeStep.from_workload(wl, partition_size=0, shared_blocks=sb)
-        for _ in range(args.warmup):
+        sstep = DecodeStep.from_workload(wl, partition_size=0, shared_blocks=sb, num_layers=NL)
+        for i in range(args.warmup):
+            sstep.layer = i % NL
             sstep.run()
+        step.layer = sstep.layer = 0
         step.run()
         sstep.run()
         torch.cuda.synchronize()
@@ -472,6 +511,7 @@ def main(argv=None):
         assert diff <= 2e-2, f"shared-prefix call differs from the plain call by {diff}"
         sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
         for i in range(K):
+            sstep.layer = i % NL
             sstep.scatter()
             sev[i][0].record()
             sstep.attend()
@@ -481,15 +521,19 @@ def main(argv=None):
         sh_mean = sum(sh_us) / K
         sh_graph_ms = None
         if not args.eager:
-            graph = sstep.capture()
-            graph.replay()
+            graphs = []
+            for li in range(NL):
+                sstep.layer = li
+                graphs.append(sstep.capture())
+            for g in graphs:
+                g.replay()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            for _ in range(K):
-                graph.replay()
+            for i in range(K):
+                graphs[i % NL].replay()
             torch.cuda.synchronize()
             sh_graph_ms = (time.perf_counter() - t0) * 1e3 / K
-            del graph
+            del graphs
         shared = {"shared_blocks": sb, "attn_us_mean": round(sh_mean, 2),
                   "attn_us_p50": round(percentile(sh_us, 0.5), 2),
                   "achieved_gbps": round(nbytes["attn"] / (sh_mean * 1e-6) / 1e9, 1),
@@ -516,6 +560,7 @@ def main(argv=None):
         # evict L2 and the 256 MB MALL before every attention call by reading 2 GiB (outside its
         # events); a read leaves no dirty lines whose write-back would be charged to the kernel
         cold_us = []
+        head_step.layer = 0
         for _ in range(min(K, 30)):
             probe_read(big, sink)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -536,12 +581,14 @@ def main(argv=None):
     identity = None
     if not args.no_identity:
         dense_wl = kvgen.privatize_blocks(wl, contiguous=True)
-        dense = DecodeStep.from_workload(dense_wl, partition_size=part, fp8_pool=fp8_state(dense_wl))
-        for _ in range(args.warmup):
+        dense = DecodeStep.from_workload(dense_wl, partition_size=part, fp8_pool=fp8_state(dense_wl), num_layers=NL)
+        for i in range(args.warmup):
+            dense.layer = i % NL
             dense.attend()
         torch.cuda.synchronize()
         dense_us = []
-        for _ in range(K):
+        for i in range(K):
+            dense.layer = i % NL
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             dense.attend()
@@ -550,7 +597,8 @@ def main(argv=None):
             dense_us.append(a.elapsed_time(b) * 1e3)
         # the paged calls timed the same way (one call per synchronisation)
         paged_us = []
-        for _ in range(K):
+        for i in range(K):
+            step.layer = i % NL
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             step.attend()
@@ -672,7 +720,7 @@ def main(argv=None):
                    "head_dim": wl.head_dim, "block_size": wl.block_size, "partition_size": part,
                    "context_tokens": int(np.sum(wl.context_lens)), "scatter_tokens": wl.num_write_tokens,
                    "kv_dtype": "fp8_e4m3 codes + fp32 scale per (block, KV head)" if fp8 else wl.dtype,
-                   "seed": wl.info.get("seed")},
+                   "layers": NL, "seed": wl.info.get("seed")},
         "tokens_per_s_per_layer": round(wl.num_seqs / (ms_per_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "kernel": roofline_kernel, "achieved": round(achieved, 1),
@@ -686,6 +734,7 @@ def main(argv=None):
         "frac_of_read_probe": round(achieved / read_gbps, 4),
         "step_bytes": step_bytes,
         "cold": cold,
+        "same_layer": same_layer,
         "pool_utilization": round(float(wl.info.get("utilization") or 0.0), 4),
         "blocks_per_seq_mean": round(nbytes["blocks"] / max(1, wl.num_seqs), 2),
         "internal_waste_tokens": int(nbytes["blocks"] * wl.block_size - int(np.sum(wl.context_lens))),
