@@ -43,7 +43,9 @@
  * Conventions for every call:
  *   - Device pointers are borrowed: the caller allocates them and keeps them
  *     alive until the work queued on `stream` has finished.  The library never
- *     allocates device memory and never synchronises.
+ *     allocates device memory at run time and never synchronises (its one
+ *     static device array, the workspace of paged_attention_decode_noalloc,
+ *     is part of the loaded code object).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *     is queued and the call returns; results are ordered by the stream.
  *   - Host-checkable argument errors return a negative kv_status before any
@@ -369,6 +371,31 @@ kv_status paged_attention_decode_shared(kv_pool_t pool, int32_t layer, void* out
 kv_status paged_attention_shared_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int32_t num_q_heads,
                                                  int32_t max_context_len, int32_t max_blocks_per_seq,
                                                  int32_t shared_blocks, uint64_t* bytes);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * result as paged_attention_decode (bitwise: the same kernels), with the
+ * workspace taken from a static device array of KV_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on every GPU it runs on until the process ends.
+ * The call allocates and frees nothing.
+ *   Every argument as for paged_attention_decode, less the workspace.  The
+ *   device is the stream's (the current device for the NULL stream); the
+ *   first call on a device looks up that device's copy of the array.
+ *   Calls on one GPU share its array: calls that overlap in time on that GPU
+ *   (other streams, other host threads) race, and must be ordered by the
+ *   caller.  Nothing in the array needs to hold a given value on entry.
+ * Errors: as for paged_attention_decode; KV_ERR_WORKSPACE_TOO_SMALL when the
+ * call needs more than KV_NOALLOC_SCRATCH_BYTES of workspace
+ * (paged_attention_workspace_bytes tells); KV_ERR_HIP when the array cannot
+ * be looked up on the stream's device.
+ */
+#define KV_NOALLOC_SCRATCH_BYTES (64ull << 20)
+kv_status paged_attention_decode_noalloc(kv_pool_t pool, int32_t layer, void* out, const void* q,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                         float scale, int32_t max_context_len, int32_t partition_size,
+                                         void* stream);
 
 /* Static name of a status code ("KV_OK", ...); never NULL. */
 const char* kv_status_string(kv_status status);

@@ -2,6 +2,7 @@
 // The operations themselves are described in include/kvpool.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -477,13 +478,60 @@ kv_status paged_attention_workspace_bytes(kv_pool_t pool, int32_t num_seqs, int3
 
 namespace {
 
-// Shared body of paged_attention_decode and paged_attention_decode_append
-// (k_append / v_append null for the former).
+// Workspace of paged_attention_decode_noalloc: one static array per device.
+// In host code `scratch` only names the symbol; its device address on each
+// GPU comes from hipGetSymbolAddress, looked up once per device and kept.
+constexpr uint64_t kScratchBytes = KV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchMaxDevices];
+
+// Device address of `scratch` on device `dev`, looked up with that device
+// current (the caller's current device is restored).
+kv_status scratch_on_device(int dev, void** ptr) {
+    if (dev < 0 || dev >= kScratchMaxDevices)
+        return fail(KV_ERR_HIP, "device %d: the static workspace is kept for devices 0..%d", dev, kScratchMaxDevices - 1);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) {
+        *ptr = p;
+        return KV_OK;
+    }
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    const hipError_t look = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return hip_fail(e, "hipSetDevice (restore)");
+    if (look != hipSuccess || !p) return hip_fail(look != hipSuccess ? look : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    // several host threads may look it up at once: they find the same address
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    *ptr = p;
+    return KV_OK;
+}
+
+// Device of `stream` (the current device for the null stream).
+kv_status stream_device(void* stream, int* dev) {
+    hipError_t e;
+    if (stream) {
+        hipDevice_t d = 0;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &d);
+        *dev = (int)d;
+    } else {
+        e = hipGetDevice(dev);
+    }
+    return e == hipSuccess ? KV_OK : hip_fail(e, "device of the stream");
+}
+
+// Shared body of paged_attention_decode, paged_attention_decode_append,
+// paged_attention_decode_shared and paged_attention_decode_noalloc (k_append
+// / v_append null but for the append call; static_scratch: the workspace is
+// the stream's device's static array, once every argument has been checked).
 kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, const void* k_append,
                       const void* v_append, const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                       int32_t max_context_len, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-                      void* stream, int32_t shared_blocks = 0) {
+                      void* stream, int32_t shared_blocks = 0, bool static_scratch = false) {
     if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "pool is NULL");
     const kv_pool_desc& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers) return fail(KV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, d.num_layers);
@@ -524,6 +572,18 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
     const uint64_t ws_needed = stiles > 0 ? sp.total : plan.ws_total;
     kvp::DecodeArgs a;
     memset(&a, 0, sizeof a);
+    if (static_scratch && ws_needed > 0) {
+        if (ws_needed > kScratchBytes)
+            return fail(KV_ERR_WORKSPACE_TOO_SMALL,
+                        "paged_attention_decode_noalloc: this call needs %llu bytes of workspace, the static array "
+                        "holds %llu", (unsigned long long)ws_needed, (unsigned long long)kScratchBytes);
+        int dev = 0;
+        kv_status st = stream_device(stream, &dev);
+        if (st != KV_OK) return st;
+        st = scratch_on_device(dev, &workspace);
+        if (st != KV_OK) return st;
+        workspace_bytes = kScratchBytes;
+    }
     if (ws_needed > 0) {
         if (!workspace || workspace_bytes < ws_needed)
             return fail(KV_ERR_WORKSPACE_TOO_SMALL, "workspace of %llu bytes given, %llu needed",
@@ -632,6 +692,15 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
     return decode_impl(pool, layer, out, q, nullptr, nullptr, block_tables, max_blocks_per_seq, context_lens,
                        num_seqs, num_q_heads, scale, max_context_len, partition_size, workspace, workspace_bytes,
                        stream);
+}
+
+kv_status paged_attention_decode_noalloc(kv_pool_t pool, int32_t layer, void* out, const void* q,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                         float scale, int32_t max_context_len, int32_t partition_size,
+                                         void* stream) {
+    return decode_impl(pool, layer, out, q, nullptr, nullptr, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, scale, max_context_len, partition_size, nullptr, 0, stream, 0, true);
 }
 
 kv_status paged_attention_decode_shared(kv_pool_t pool, int32_t layer, void* out, const void* q,

@@ -23,6 +23,8 @@ KV_ERR_WORKSPACE_TOO_SMALL = -3
 KV_ERR_HIP = -4
 KV_ERR_OUT_OF_RANGE = -5
 
+KV_NOALLOC_SCRATCH_BYTES = 64 << 20   # the static workspace of paged_attention_decode_noalloc
+
 KV_F32 = 0
 KV_BF16 = 1
 KV_FP8_E4M3 = 2
@@ -33,6 +35,7 @@ EXPORTED = (
     "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
     "paged_attention_decode_append", "paged_attention_decode_shared", "paged_attention_shared_workspace_bytes",
+    "paged_attention_decode_noalloc",
     "kv_copy_blocks", "kv_swap_bytes", "kv_swap_out", "kv_swap_in",
     "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read", "kv_probe_table_walk",
     "kv_probe_e4m3_to_bf16", "kv_probe_f32_to_e4m3",
@@ -100,6 +103,8 @@ def _load():
     lib.paged_attention_decode_append.restype = ctypes.c_int
     lib.paged_attention_decode_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32,
                                                   vp, u64, vp]
+    lib.paged_attention_decode_noalloc.restype = ctypes.c_int
+    lib.paged_attention_decode_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32, vp]
     lib.kv_probe_copy.restype = ctypes.c_int
     lib.kv_probe_copy.argtypes = [vp, vp, u64, vp]
     lib.kv_probe_read.restype = ctypes.c_int
@@ -306,6 +311,27 @@ class KVPool:
                                           S, Hq, float(scale), int(max_context_len), int(partition_size),
                                           ws_ptr, int(ws_bytes), _stream_handle(stream)),
                "paged_attention_decode")
+
+    def paged_attention_decode_noalloc(self, layer: int, out, q, block_tables, context_lens, *,
+                                       scale: float, max_context_len: int, partition_size: int = 0,
+                                       stream=None) -> None:
+        """paged_attention_decode with the library's static per-device workspace
+        (allocates nothing; calls overlapping on one GPU race)."""
+        import torch
+        S, Hq, D = (int(x) for x in q.shape)
+        if tuple(out.shape) != (S, Hq, D) or D != self.head_dim:
+            raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim]")
+        if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+            raise ValueError("one table row and one length per sequence")
+        _check(lib.paged_attention_decode_noalloc(self.handle, int(layer),
+                                                  _dev_ptr(out, "out", self.torch_dtype),
+                                                  _dev_ptr(q, "q", self.torch_dtype),
+                                                  _dev_ptr(block_tables, "block_tables", torch.int32),
+                                                  int(block_tables.shape[1]),
+                                                  _dev_ptr(context_lens, "context_lens", torch.int32),
+                                                  S, Hq, float(scale), int(max_context_len), int(partition_size),
+                                                  _stream_handle(stream)),
+               "paged_attention_decode_noalloc")
 
     def shared_workspace_bytes(self, num_seqs: int, num_q_heads: int, max_context_len: int,
                                max_blocks_per_seq: int, shared_blocks: int) -> int:

@@ -485,3 +485,33 @@ def test_shared_prefix_argument_checks_return_before_any_launch():
         assert K.lib.paged_attention_workspace_bytes(h, 4, 32, 4096, 0, ctypes.byref(plain)) == K.KV_OK
         assert (need > plain.value) == extra, (B, shared)
         K.lib.kv_pool_destroy(h)
+
+
+def test_noalloc_decode_checks_return_before_any_launch():
+    """paged_attention_decode_noalloc: the same argument checks as the plain
+    call, and a call needing more than the static array's bytes is refused
+    with a clear error before any device work."""
+    st, h = _pool(head_dim=128, num_kv_heads=8, dtype="bf16", num_blocks=64)
+    L = K.lib
+
+    def call(**kw):
+        a = dict(layer=0, out=0x30000000, q=0x40000000, tables=0x50000000, mb=8192, lens=0x60000000, S=4, Hq=32,
+                 scale=0.125, max_ctx=200, part=0)
+        a.update(kw)
+        return L.paged_attention_decode_noalloc(h, a["layer"], a["out"], a["q"], a["tables"], a["mb"], a["lens"],
+                                                a["S"], a["Hq"], a["scale"], a["max_ctx"], a["part"], None)
+    assert L.paged_attention_decode_noalloc(None, 0, 0x30000000, 0x40000000, 0x50000000, 16, 0x60000000, 4, 32,
+                                            0.125, 200, 0, None) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(layer=1) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(Hq=24) == K.KV_ERR_UNSUPPORTED                     # group of 3
+    assert call(scale=0.0) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(part=40) == K.KV_ERR_INVALID_ARGUMENT
+    # 1024 sequences of 128K tokens in 16-token partitions: far more workspace than the array holds
+    need = ctypes.c_uint64(0)
+    assert L.paged_attention_workspace_bytes(h, 1024, 32, 131072, 16, ctypes.byref(need)) == K.KV_OK
+    assert need.value > K.KV_NOALLOC_SCRATCH_BYTES
+    assert call(S=1024, max_ctx=131072, part=16) == K.KV_ERR_WORKSPACE_TOO_SMALL
+    msg = L.kv_last_error_message().decode()
+    assert "static array" in msg and str(K.KV_NOALLOC_SCRATCH_BYTES) in msg, msg
+    assert call(S=0) == K.KV_OK                                    # nothing to do, nothing launched
+    L.kv_pool_destroy(h)
