@@ -1072,7 +1072,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
         if (ch < nchunks) {
-            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kTileTokens - 1) / kTileTokens);
+            const int64_t nt = (int64_t)Hkv * walk_span((len_c[ch] + kTileTokens - 1) / kTileTokens);
             int64_t incl = nt;
 #pragma unroll
             for (int off = 1; off < kWave; off <<= 1) {
@@ -1085,8 +1085,9 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         }
     }
     if (w == 0 && lane == 0) a.ws_prefix[S] = T;
-    int64_t t = slice_start(w, T, W);
-    const int64_t t_end = slice_start(w + 1, T, W);
+    const SliceWeights kw{a.slice_even, a.slice_odd};
+    int64_t t = slice_start(w, T, W, kw);
+    const int64_t t_end = slice_start(w + 1, T, W, kw);
     if (t >= t_end) return;
 
     // the sequence holding tile t: the lane whose [excl, excl + ntile) contains it
@@ -1095,7 +1096,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
         if (ch < nchunks && seq == S) {
-            const int64_t nt = (int64_t)Hkv * ((len_c[ch] + kTileTokens - 1) / kTileTokens);
+            const int64_t nt = (int64_t)Hkv * walk_span((len_c[ch] + kTileTokens - 1) / kTileTokens);
             const uint64_t bal = __builtin_amdgcn_ballot_w64(nt > 0 && ex_c[ch] <= t && t < ex_c[ch] + nt);
             if (bal) {
                 const int j = __builtin_ctzll(bal);
@@ -1108,9 +1109,15 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     seq = __builtin_amdgcn_readfirstlane(seq);
     L = __builtin_amdgcn_readfirstlane(L);
     int nblk = (L + kTileTokens - 1) / kTileTokens;   // 16-token tiles
-    int64_t off = t - seq_first;
-    int kv = (int)(off / nblk);
-    int b = (int)(off - (int64_t)kv * nblk);
+    // position t lies in the span of walk (seq, kv); t moves to the split
+    // position of the first tile this slice walks there (past the span's
+    // leading positions; at or past t_end when the slice ends among them)
+    const int64_t off = t - seq_first;
+    const int64_t span = walk_span(nblk);
+    int kv = (int)(off / span);
+    const int64_t at = off - (int64_t)kv * span;
+    int b = first_tile_at(at);
+    t += kPieceCost + b - at;
 
     bool first_piece = true;
     bool pf_valid = false;   // table entries of the next piece fetched ahead
@@ -1145,7 +1152,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         const int tv0_here = pf_tv0, tv1_here = pf_tv1;
         pf_valid = false;
         NextWalk nxt = no_next_walk();
-        if (b + n_here == nblk && t + n_here < t_end) {
+        if (b + n_here == nblk && t + n_here + kPieceCost < t_end) {
             const int nseq = kv + 1 < Hkv ? seq : seq + 1;
             if (nseq < S) {
                 // tiles 0..63 of the next sequence's row; a lane whose tile would
@@ -1219,7 +1226,8 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
             }
         }
 
-        // next piece
+        // next piece: the next walk's first tile is kPieceCost positions on
+        // (walks with no tiles take no positions)
         t += n_here;
         first_piece = false;
         b += n_here;
@@ -1233,6 +1241,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                     nblk = (L + kTileTokens - 1) / kTileTokens;
                 } while (nblk == 0 && seq < S && t < t_end);
             }
+            t += kPieceCost;
         }
     }
 }
@@ -1284,8 +1293,9 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
             T += __shfl(incl, kWave - 1, kWave);
         }
     }
-    const int64_t t_lo = slice_start(w, T, W);
-    const int64_t t_hi = slice_start(w + 1, T, W);
+    const SliceWeights kw{a.slice_even, a.slice_odd};
+    const int64_t t_lo = slice_start(w, T, W, kw);
+    const int64_t t_hi = slice_start(w + 1, T, W, kw);
     if (t_lo >= t_hi) return;
 
     int seq = S, L = 0;
@@ -1445,19 +1455,24 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     const int L = shared ? (L_all > a.shared_tiles * kTileTokens ? L_all - a.shared_tiles * kTileTokens : 0) : L_all;
     const int nblk = (L + kTileTokens - 1) / kTileTokens;   // 16-token tiles
     const int64_t W = num_workers;
-    const int64_t s0 = first_tile + (int64_t)kv * nblk;
-    const int64_t w0 = nblk > 0 ? worker_of(s0, T, W) : 0;
-    const int64_t w1 = nblk > 0 ? worker_of(s0 + nblk - 1, T, W) : 0;
+    const int64_t base = first_tile + (int64_t)kv * walk_span(nblk);   // the walk's split positions start here
+    const int64_t s0 = base + kPieceCost;                                // ... and its tile 0 sits here
+    const SliceWeights kw{a.slice_even, a.slice_odd};
+    const int64_t w0 = nblk > 0 ? worker_of(s0, T, W, kw) : 0;
+    const int64_t w1 = nblk > 0 ? worker_of(s0 + nblk - 1, T, W, kw) : 0;
     if (w0 == w1 && !shared) return;   // written by its worker
     // records of the slices that split the walk (none when one slice held it whole)
     const int nrec = (nblk > 0 && w0 != w1) ? (int)(w1 - w0 + 1) : 0;
 
-    // record slot of worker w0 + j, or -1 for an empty slice
+    // record slot of worker w0 + j, or -1 for an empty slice.  Worker w0 left
+    // its second record when its slice began before this walk's span (the
+    // positions just before the span are the last tiles of an earlier walk,
+    // which it walked first), else its first.
     auto slot_of = [&](int j) -> int64_t {
         const int64_t w = w0 + j;
-        const int64_t st = slice_start(w, T, W);
-        if (slice_start(w + 1, T, W) <= st) return -1;
-        return (w == w0 && st < s0) ? 2 * w + 1 : 2 * w;
+        const int64_t st = slice_start(w, T, W, kw);
+        if (slice_start(w + 1, T, W, kw) <= st) return -1;
+        return (w == w0 && st < base) ? 2 * w + 1 : 2 * w;
     };
 
     // Records are taken 64 at a time, lane j holding the (m, l) pairs of record
@@ -1631,10 +1646,10 @@ int streamk_workers(int group, bool fp8) {
 
 namespace {
 
+// The balanced walk (a.workers and the slice weights already set).
 template <bool kFp8>
-hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
+hipError_t launch_streamk_walk(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
     DecodeArgs a = a_in;
-    a.workers = workers;
     // decode append: a few extra single-wave workgroups store the new rows
     // (bf16: about 8 chunks per lane; FP8: about 4 rows per wave)
     int64_t extra = 0;
@@ -1648,7 +1663,6 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
     }
     dim3 grid((unsigned)(workers + extra));
     const bool any_b = a.block_size != kTileTokens;
-    dim3 fix((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     switch (group) {
         case 1:
             if (any_b) decode_bf16_streamk_kernel<1, true, kFp8><<<grid, kWave, 0, stream>>>(a);
@@ -1668,8 +1682,13 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
             break;
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+// The fix-up after the walk: merges the records of (sequence, KV head) pairs
+// split between workers (and, with a shared prefix, the prefix states).
+hipError_t launch_streamk_fixup(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+    dim3 fix((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     switch (group) {
         case 1: streamk_fixup_kernel<1><<<fix, kWave, 0, stream>>>(a, workers); break;
         case 2: streamk_fixup_kernel<2><<<fix, kWave, 0, stream>>>(a, workers); break;
@@ -1681,7 +1700,23 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
 }
 
 template <bool kFp8>
-hipError_t launch_partitions(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
+hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
+    DecodeArgs a = a_in;
+    a.workers = workers;
+    const SliceWeights kw = kFp8 ? kFp8SliceWeights : kBf16SliceWeights;
+    a.slice_even = (int32_t)kw.even;
+    a.slice_odd = (int32_t)kw.odd;
+    hipError_t e = launch_streamk_walk<kFp8>(a, group, workers, stream);
+    if (e != hipSuccess) return e;
+    return launch_streamk_fixup(a, group, workers, stream);
+}
+
+template <bool kFp8>
+hipError_t launch_partitions(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
+    DecodeArgs a = a_in;
+    const SliceWeights kw = kFp8 ? kFp8SliceWeights : kBf16SliceWeights;
+    a.slice_even = (int32_t)kw.even;
+    a.slice_odd = (int32_t)kw.odd;
     dim3 grid((unsigned)workers);
     const bool any_b = a.block_size != kTileTokens;
     switch (group) {

@@ -108,6 +108,8 @@ struct DecodeArgs {
     const float* k_scale;        // FP8 pools: the layer's block scales [num_blocks][Hkv]
     const float* v_scale;
     int32_t workers;             // balanced split: worker waves (the launch adds append waves past them)
+    int32_t slice_even;          // balanced split: tiles of a worker on an even XCD per slice_odd on an odd one
+    int32_t slice_odd;
     int32_t max_blocks;
     int32_t num_seqs;
     int32_t num_q_heads;

@@ -54,8 +54,8 @@ __global__ __launch_bounds__(64) void table_walk_kernel(const int32_t* __restric
     const int64_t w = blockIdx.x;
     const int64_t s = kGrouped ? (w % 8) * (W / 8) + w / 8 : w;
     auto clamp = [&](int L) { return L < 0 ? 0 : (L > max_context ? max_context : L); };
-    auto tiles = [&](int i) -> int64_t {
-        return i < S ? (int64_t)Hkv * ((clamp(lens[i]) + kvp::kBlockTokens - 1) / kvp::kBlockTokens) : 0;
+    auto tiles = [&](int i) -> int64_t {   // split positions of sequence i
+        return i < S ? (int64_t)Hkv * kvp::walk_span((clamp(lens[i]) + kvp::kBlockTokens - 1) / kvp::kBlockTokens) : 0;
     };
     int64_t T = 0;
     for (int b = 0; b < S; b += 64) {
@@ -63,8 +63,8 @@ __global__ __launch_bounds__(64) void table_walk_kernel(const int32_t* __restric
         for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
         T += x;
     }
-    int64_t t = kvp::slice_start(s, T, W);
-    const int64_t t_end = kvp::slice_start(s + 1, T, W);
+    int64_t t = kvp::slice_start(s, T, W, kvp::kBf16SliceWeights);
+    const int64_t t_end = kvp::slice_start(s + 1, T, W, kvp::kBf16SliceWeights);
     uint32_t acc = 0;
     // the sequence holding tile t, 64 sequences per step
     int seq = S;
@@ -90,16 +90,19 @@ __global__ __launch_bounds__(64) void table_walk_kernel(const int32_t* __restric
     for (; seq < S && t < t_end; ++seq) {
         const int L = __builtin_amdgcn_readfirstlane(clamp(lens[seq]));
         const int nblk = (L + kvp::kBlockTokens - 1) / kvp::kBlockTokens;
-        const int64_t seg_end = first + (int64_t)Hkv * nblk;
+        const int64_t span = kvp::walk_span(nblk);
+        const int64_t seg_end = first + (int64_t)Hkv * span;
         while (t < t_end && t < seg_end) {
+            // walk kv of this sequence: its tile b sits at position kPieceCost + b of its span
             const int64_t off = t - first;
-            const int kv = (int)(off / nblk);
-            const int b = (int)(off - (int64_t)kv * nblk);
-            const int n = (int)min((int64_t)(nblk - b), t_end - t);
+            const int kv = (int)(off / span);
+            const int b = kvp::first_tile_at(off - (int64_t)kv * span);
+            const int64_t tb = first + (int64_t)kv * span + kvp::kPieceCost + b;
+            const int n = (int)max((int64_t)0, min((int64_t)(nblk - b), t_end - tb));
             const int32_t* trow = tables + (size_t)seq * max_blocks + b;
             for (int k0 = 0; k0 < n; k0 += 64)
                 if (k0 + lane < n) acc ^= (uint32_t)trow[k0 + lane] + (uint32_t)kv;
-            t += n;
+            t = first + (int64_t)(kv + 1) * span;
         }
         first = seg_end;
     }

@@ -3,36 +3,64 @@
 // table-walk probe, so the probe walks exactly the decode's slices.
 #pragma once
 
-#include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define KVP_SPLIT_HD __host__ __device__
+#else
+#define KVP_SPLIT_HD
+#endif
+
 namespace kvp {
+
+// Split positions.  A (sequence, KV head) walk of nblk tiles takes nblk +
+// kPieceCost positions of the list that is cut into slices: kPieceCost
+// positions before its tiles stand for what starting a walk costs a worker
+// (query, table entries and the first tiles in flight before anything
+// streams; measured per worker on the 70B-shaped batch with the chip's
+// realtime counter: about one tile's time per walk, and the workers that
+// fell on runs of short sequences, ten to sixteen walks each, finished 15-30
+// us after the others).  Tile k of the walk sits at position kPieceCost + k of
+// its span; a slice that starts among the leading positions starts the walk
+// at tile 0, and one that ends there leaves the walk to the next worker.
+// A walk with no tiles takes no positions.
+constexpr int kPieceCost = 1;
+KVP_SPLIT_HD inline int64_t walk_span(int nblk) { return nblk > 0 ? (int64_t)nblk + kPieceCost : 0; }
+// The first tile a slice starting at position `off` of a walk's span walks.
+KVP_SPLIT_HD inline int first_tile_at(int64_t off) { return off > kPieceCost ? (int)(off - kPieceCost) : 0; }
 
 // Slice sizes.  Workgroups are dispatched round-robin over the eight XCDs,
 // so worker w runs on XCD w % 8.  Measured on MI355X (per-worker exit times
 // from the chip's realtime counter, and the XCC_ID register), the
-// odd-numbered XCDs stream the same tiles about 6 % slower than their even
-// neighbours, with the attention math or without it; a worker on an odd XCD
-// therefore gets 15 tiles for every 16 of a worker on an even one.  The
-// boundaries stay a function of T and W alone.
-//   cum(w) = 16 ceil(w / 2) + 15 floor(w / 2),  cum(2p) = 31p,  cum(2p + 1) = 31p + 16
-constexpr int64_t kEvenWeight = 16;
-constexpr int64_t kOddWeight = 15;
-__host__ __device__ inline int64_t cum_weight(int64_t w) {
-    return kEvenWeight * ((w + 1) / 2) + kOddWeight * (w / 2);
+// odd-numbered XCDs stream the same tiles a few percent slower than their even
+// neighbours, with the attention math or without it: over repeated calls of
+// the 8B- and 70B-shaped batches, layer after layer, 2.8-3.2% for bf16 tiles
+// and 4.9% for FP8 tiles.  A worker on an even XCD therefore gets `even`
+// tiles for every `odd` of a worker on an odd one; the boundaries stay a
+// function of T, W and the weights alone.
+//   cum(w) = even ceil(w / 2) + odd floor(w / 2),  cum(2p) = (even + odd) p,  cum(2p + 1) = (even + odd) p + even
+struct SliceWeights {
+    int64_t even, odd;
+};
+constexpr SliceWeights kBf16SliceWeights{33, 32};
+constexpr SliceWeights kFp8SliceWeights{21, 20};
+
+KVP_SPLIT_HD inline int64_t cum_weight(int64_t w, SliceWeights k) {
+    return k.even * ((w + 1) / 2) + k.odd * (w / 2);
 }
-__host__ __device__ inline int64_t slice_start(int64_t w, int64_t T, int64_t W) {
-    return T * cum_weight(w) / cum_weight(W);
+KVP_SPLIT_HD inline int64_t slice_start(int64_t w, int64_t T, int64_t W, SliceWeights k) {
+    return T * cum_weight(w, k) / cum_weight(W, k);
 }
 
 // Worker whose slice holds tile t (0 <= t < T): the largest w with
 // slice_start(w) <= t, i.e. cum(w) T <= (t + 1) cum(W) - 1, i.e.
-// cum(w) <= X = floor(((t + 1) cum(W) - 1) / T); with X = 31p + r that is
-// w = 2p + 1 when r >= 16, else 2p.
-__host__ __device__ inline int64_t worker_of(int64_t t, int64_t T, int64_t W) {
-    const int64_t X = ((t + 1) * cum_weight(W) - 1) / T;
-    const int64_t pair = kEvenWeight + kOddWeight;
-    const int64_t w = 2 * (X / pair) + (X % pair >= kEvenWeight ? 1 : 0);
+// cum(w) <= X = floor(((t + 1) cum(W) - 1) / T); with X = (even + odd) p + r
+// that is w = 2p + 1 when r >= even, else 2p.
+KVP_SPLIT_HD inline int64_t worker_of(int64_t t, int64_t T, int64_t W, SliceWeights k) {
+    const int64_t X = ((t + 1) * cum_weight(W, k) - 1) / T;
+    const int64_t pair = k.even + k.odd;
+    const int64_t w = 2 * (X / pair) + (X % pair >= k.even ? 1 : 0);
     return w < W - 1 ? w : W - 1;
 }
 

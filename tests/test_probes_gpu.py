@@ -16,15 +16,22 @@ def _need_gpu(gpu_available):
 
 
 def _cum(w):
-    return 16 * ((w + 1) // 2) + 15 * (w // 2)
+    # the bf16 decode's slice weights: 33 tiles on an even XCD for 32 on an odd one
+    return 33 * ((w + 1) // 2) + 32 * (w // 2)
+
+
+PIECE_COST = 1   # split positions before each (sequence, KV head) walk's tiles
 
 
 def _host_walk(tables, lens, hkv, max_context, W, grouped):
-    """Per-worker folded word: XOR over walked entries of (entry + kv), as uint32."""
+    """Per-worker folded word: XOR over walked entries of (entry + kv), as
+    uint32.  The split list gives each walk of n > 0 tiles n + PIECE_COST
+    positions, the first PIECE_COST of which stand for no tile."""
     lens = np.clip(lens, 0, max_context)
     nblk = (lens + 15) // 16
-    T = int(hkv * nblk.sum())
-    starts = np.concatenate([[0], np.cumsum(hkv * nblk)])
+    span = np.where(nblk > 0, nblk + PIECE_COST, 0)
+    T = int(hkv * span.sum())
+    starts = np.concatenate([[0], np.cumsum(hkv * span)])
     out = np.zeros(W, dtype=np.uint32)
     for w in range(W):
         s = (w % 8) * (W // 8) + w // 8 if grouped else w
@@ -33,8 +40,9 @@ def _host_walk(tables, lens, hkv, max_context, W, grouped):
         for t in range(t0, t1):
             seq = int(np.searchsorted(starts, t, side="right") - 1)
             off = t - starts[seq]
-            kv, b = divmod(off, int(nblk[seq]))
-            acc ^= np.uint32((int(tables[seq, b]) + kv) & 0xFFFFFFFF)
+            kv, at = divmod(off, int(span[seq]))
+            if at >= PIECE_COST:
+                acc ^= np.uint32((int(tables[seq, at - PIECE_COST]) + kv) & 0xFFFFFFFF)
         out[w] = acc
     return out
 
