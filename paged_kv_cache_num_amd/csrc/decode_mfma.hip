@@ -100,6 +100,18 @@ __device__ __forceinline__ float safe_ref(float m) { return m == -INFINITY ? 0.0
 __device__ __forceinline__ float readlane_f(float x, int src) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
 }
+// Inclusive prefix sum over the wave: within each row of 16 lanes by row
+// shifts of 1, 2, 4 and 8 (a lane without a source adds 0), then lane 15's
+// sum into rows 1 and 3 and lane 31's into rows 2 and 3 (row broadcasts).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
 __device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), src);
@@ -1067,36 +1079,35 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         const int i = ch * kWave + lane;
         len_c[ch] = (ch < nchunks && i < S) ? walk_len(a, i) : 0;
     }
+    // positions in 32 bits: the host takes this kernel only for batches of
+    // fewer than kMaxSplitPositions
     int64_t ex_c[kMaxChunks];
-    int64_t T = 0;
+    int T32 = 0;
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
         if (ch < nchunks) {
-            const int64_t nt = (int64_t)Hkv * walk_span((len_c[ch] + kTileTokens - 1) / kTileTokens);
-            int64_t incl = nt;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const int64_t y = __shfl_up(incl, off, kWave);
-                if (lane >= off) incl += y;
-            }
-            ex_c[ch] = T + incl - nt;
+            const int nt = Hkv * (int)walk_span((len_c[ch] + kTileTokens - 1) / kTileTokens, a.piece_cost);
+            const int incl = wave_inclusive_sum(nt);
+            ex_c[ch] = T32 + incl - nt;
             if (w == 0 && ch * kWave + lane < S) a.ws_prefix[ch * kWave + lane] = ex_c[ch];
-            T += __shfl(incl, kWave - 1, kWave);
+            T32 += __builtin_amdgcn_readlane(incl, kWave - 1);
         }
     }
+    asm volatile("" : "+v"(T32));   // kept in a vector register, as the walk's other split values
+    const int64_t T = T32;
     if (w == 0 && lane == 0) a.ws_prefix[S] = T;
     const SliceWeights kw{a.slice_even, a.slice_odd};
     int64_t t = slice_start(w, T, W, kw);
     const int64_t t_end = slice_start(w + 1, T, W, kw);
     if (t >= t_end) return;
 
-    // the sequence holding tile t: the lane whose [excl, excl + ntile) contains it
+    // the sequence holding position t: the lane whose [excl, excl + positions) contains it
     int seq = S, L = 0;
     int64_t seq_first = 0;
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
         if (ch < nchunks && seq == S) {
-            const int64_t nt = (int64_t)Hkv * walk_span((len_c[ch] + kTileTokens - 1) / kTileTokens);
+            const int nt = Hkv * (int)walk_span((len_c[ch] + kTileTokens - 1) / kTileTokens, a.piece_cost);
             const uint64_t bal = __builtin_amdgcn_ballot_w64(nt > 0 && ex_c[ch] <= t && t < ex_c[ch] + nt);
             if (bal) {
                 const int j = __builtin_ctzll(bal);
@@ -1113,11 +1124,13 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     // position of the first tile this slice walks there (past the span's
     // leading positions; at or past t_end when the slice ends among them)
     const int64_t off = t - seq_first;
-    const int64_t span = walk_span(nblk);
-    int kv = (int)(off / span);
+    const int64_t span = walk_span(nblk, a.piece_cost);
+    if (seq >= S || span <= 0) return;   // no sequence holds t: not reached with consistent lengths
+    int kv = (int)div_floor(off, span);
+    if (kv >= Hkv) return;
     const int64_t at = off - (int64_t)kv * span;
-    int b = first_tile_at(at);
-    t += kPieceCost + b - at;
+    int b = first_tile_at(at, a.piece_cost);
+    t += a.piece_cost + b - at;
 
     bool first_piece = true;
     bool pf_valid = false;   // table entries of the next piece fetched ahead
@@ -1152,7 +1165,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         const int tv0_here = pf_tv0, tv1_here = pf_tv1;
         pf_valid = false;
         NextWalk nxt = no_next_walk();
-        if (b + n_here == nblk && t + n_here + kPieceCost < t_end) {
+        if (b + n_here == nblk && t + n_here + a.piece_cost < t_end) {
             const int nseq = kv + 1 < Hkv ? seq : seq + 1;
             if (nseq < S) {
                 // tiles 0..63 of the next sequence's row; a lane whose tile would
@@ -1226,7 +1239,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
             }
         }
 
-        // next piece: the next walk's first tile is kPieceCost positions on
+        // next piece: the next walk's first tile is piece_cost positions on
         // (walks with no tiles take no positions)
         t += n_here;
         first_piece = false;
@@ -1241,7 +1254,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                     nblk = (L + kTileTokens - 1) / kTileTokens;
                 } while (nblk == 0 && seq < S && t < t_end);
             }
-            t += kPieceCost;
+            t += a.piece_cost;
         }
     }
 }
@@ -1455,8 +1468,8 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     const int L = shared ? (L_all > a.shared_tiles * kTileTokens ? L_all - a.shared_tiles * kTileTokens : 0) : L_all;
     const int nblk = (L + kTileTokens - 1) / kTileTokens;   // 16-token tiles
     const int64_t W = num_workers;
-    const int64_t base = first_tile + (int64_t)kv * walk_span(nblk);   // the walk's split positions start here
-    const int64_t s0 = base + kPieceCost;                                // ... and its tile 0 sits here
+    const int64_t base = first_tile + (int64_t)kv * walk_span(nblk, a.piece_cost);   // the walk's positions start here
+    const int64_t s0 = base + a.piece_cost;                                            // ... and its tile 0 sits here
     const SliceWeights kw{a.slice_even, a.slice_odd};
     const int64_t w0 = nblk > 0 ? worker_of(s0, T, W, kw) : 0;
     const int64_t w1 = nblk > 0 ? worker_of(s0 + nblk - 1, T, W, kw) : 0;
@@ -1706,6 +1719,7 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
     const SliceWeights kw = kFp8 ? kFp8SliceWeights : kBf16SliceWeights;
     a.slice_even = (int32_t)kw.even;
     a.slice_odd = (int32_t)kw.odd;
+    a.piece_cost = kFp8 ? kFp8PieceCost : kBf16PieceCost;
     hipError_t e = launch_streamk_walk<kFp8>(a, group, workers, stream);
     if (e != hipSuccess) return e;
     return launch_streamk_fixup(a, group, workers, stream);

@@ -11,6 +11,7 @@
 
 #include "kvpool.h"
 #include "launch.hpp"
+#include "split.hpp"
 
 struct kv_pool {
     kv_pool_desc desc;
@@ -86,8 +87,14 @@ Plan plan_decode(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, i
     Plan p;
     memset(&p, 0, sizeof p);
     const int group = num_q_heads / d.num_kv_heads;
+    // the balanced split counts its positions in 32 bits: at most
+    // ceil(max_context_len / 16) tiles plus the walk-start positions per
+    // (sequence, KV head)
+    const int64_t max_cost = kvp::kBf16PieceCost > kvp::kFp8PieceCost ? kvp::kBf16PieceCost : kvp::kFp8PieceCost;
+    const int64_t positions = (int64_t)num_seqs * d.num_kv_heads *
+                              (((int64_t)max_context_len + kvp::kTileTokens - 1) / kvp::kTileTokens + max_cost);
     if (partition_size == 0 && (d.dtype == KV_BF16 || d.dtype == KV_FP8_E4M3) && d.head_dim == 128 &&
-        num_seqs <= kvp::kStreamKMaxSeqs) {
+        num_seqs <= kvp::kStreamKMaxSeqs && positions < kvp::kMaxSplitPositions) {
         p.mode = Mode::kBalanced;
         p.workers = kvp::streamk_workers(group, d.dtype == KV_FP8_E4M3);
         p.part_tokens = 0;
@@ -166,6 +173,9 @@ kv_status check_shared(const kv_pool_desc& d, int32_t num_seqs, int32_t max_cont
         return fail(KV_ERR_UNSUPPORTED, "a shared prefix needs a bf16 pool with head_dim 128");
     if (num_seqs > kvp::kStreamKMaxSeqs)
         return fail(KV_ERR_UNSUPPORTED, "a shared prefix is handled for at most %d sequences", kvp::kStreamKMaxSeqs);
+    if (plan_decode(d, num_seqs, d.num_kv_heads, max_context_len, 0).mode != Mode::kBalanced)
+        return fail(KV_ERR_UNSUPPORTED, "a shared prefix needs the balanced split, which counts at most %lld positions",
+                    (long long)kvp::kMaxSplitPositions);
     if (shared_blocks > max_blocks_per_seq || (int64_t)shared_blocks * d.block_size > max_context_len)
         return fail(KV_ERR_INVALID_ARGUMENT, "shared_blocks %d exceeds max_blocks_per_seq %d or max_context_len %d / %d",
                     shared_blocks, max_blocks_per_seq, max_context_len, d.block_size);

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64) void table_walk_kernel(const int32_t* __restric
     const int64_t s = kGrouped ? (w % 8) * (W / 8) + w / 8 : w;
     auto clamp = [&](int L) { return L < 0 ? 0 : (L > max_context ? max_context : L); };
     auto tiles = [&](int i) -> int64_t {   // split positions of sequence i
-        return i < S ? (int64_t)Hkv * kvp::walk_span((clamp(lens[i]) + kvp::kBlockTokens - 1) / kvp::kBlockTokens) : 0;
+        return i < S ? (int64_t)Hkv * kvp::walk_span((clamp(lens[i]) + kvp::kBlockTokens - 1) / kvp::kBlockTokens, kvp::kBf16PieceCost) : 0;
     };
     int64_t T = 0;
     for (int b = 0; b < S; b += 64) {
@@ -90,14 +90,14 @@ __global__ __launch_bounds__(64) void table_walk_kernel(const int32_t* __restric
     for (; seq < S && t < t_end; ++seq) {
         const int L = __builtin_amdgcn_readfirstlane(clamp(lens[seq]));
         const int nblk = (L + kvp::kBlockTokens - 1) / kvp::kBlockTokens;
-        const int64_t span = kvp::walk_span(nblk);
+        const int64_t span = kvp::walk_span(nblk, kvp::kBf16PieceCost);
         const int64_t seg_end = first + (int64_t)Hkv * span;
         while (t < t_end && t < seg_end) {
-            // walk kv of this sequence: its tile b sits at position kPieceCost + b of its span
+            // walk kv of this sequence: its tile b sits at position kBf16PieceCost + b of its span
             const int64_t off = t - first;
             const int kv = (int)(off / span);
-            const int b = kvp::first_tile_at(off - (int64_t)kv * span);
-            const int64_t tb = first + (int64_t)kv * span + kvp::kPieceCost + b;
+            const int b = kvp::first_tile_at(off - (int64_t)kv * span, kvp::kBf16PieceCost);
+            const int64_t tb = first + (int64_t)kv * span + kvp::kBf16PieceCost + b;
             const int n = (int)max((int64_t)0, min((int64_t)(nblk - b), t_end - tb));
             const int32_t* trow = tables + (size_t)seq * max_blocks + b;
             for (int k0 = 0; k0 < n; k0 += 64)

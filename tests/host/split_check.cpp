@@ -40,10 +40,10 @@ struct Batch {
     int hkv;
 };
 
-void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw) {
+void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw, int cost) {
     const int S = (int)bt.nblk.size(), Hkv = bt.hkv;
     std::vector<int64_t> first(S + 1, 0);
-    for (int i = 0; i < S; ++i) first[i + 1] = first[i] + (int64_t)Hkv * kvp::walk_span(bt.nblk[i]);
+    for (int i = 0; i < S; ++i) first[i + 1] = first[i] + (int64_t)Hkv * kvp::walk_span(bt.nblk[i], cost);
     const int64_t T = first[S];
     // walked[seq][kv][b] = worker
     std::vector<std::vector<std::vector<int64_t>>> walked(S);
@@ -58,12 +58,12 @@ void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw) {
         int seq = 0;
         while (!(first[seq] <= t && t < first[seq + 1])) ++seq;   // a sequence with positions
         int nblk = bt.nblk[seq];
-        const int64_t span = kvp::walk_span(nblk);
+        const int64_t span = kvp::walk_span(nblk, cost);
         const int64_t off = t - first[seq];
         int kv = (int)(off / span);
         const int64_t at = off - (int64_t)kv * span;
-        int b = kvp::first_tile_at(at);
-        t += kvp::kPieceCost + b - at;
+        int b = kvp::first_tile_at(at, cost);
+        t += cost + b - at;
         bool first_piece = true;
         while (t < t_end && seq < S) {
             const int n_here = (int)std::min<int64_t>(nblk - b, t_end - t);
@@ -91,7 +91,7 @@ void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw) {
                         nblk = seq < S ? bt.nblk[seq] : 0;
                     } while (nblk == 0 && seq < S && t < t_end);
                 }
-                t += kvp::kPieceCost;
+                t += cost;
             }
         }
     }
@@ -103,8 +103,8 @@ void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw) {
         for (int kv = 0; kv < Hkv; ++kv) {
             for (int k = 0; k < nblk; ++k) CHECK(walked[seq][kv][k] >= 0, "tile not walked seq=%d kv=%d b=%d", seq, kv, k);
             if (nblk == 0) continue;
-            const int64_t base = first[seq] + (int64_t)kv * kvp::walk_span(nblk);
-            const int64_t s0 = base + kvp::kPieceCost;
+            const int64_t base = first[seq] + (int64_t)kv * kvp::walk_span(nblk, cost);
+            const int64_t s0 = base + cost;
             const int64_t w0 = kvp::worker_of(s0, T, W, kw), w1 = kvp::worker_of(s0 + nblk - 1, T, W, kw);
             CHECK(walked[seq][kv][0] == w0 && walked[seq][kv][nblk - 1] == w1, "owners seq=%d kv=%d", seq, kv);
             if (w0 == w1) {
@@ -158,8 +158,20 @@ void check_table_index() {
 
 }  // namespace
 
+void check_div_floor() {
+    std::mt19937_64 rng(7);
+    for (int i = 0; i < 2000000; ++i) {
+        const int64_t den = 1 + (int64_t)(rng() % ((i & 1) ? 70000 : ((int64_t)1 << 31) - 1));
+        int64_t num = (int64_t)(rng() % ((int64_t)1 << (i % 3 == 0 ? 50 : 47)));
+        if (i % 4 == 1) num = (num / den) * den;       // exact multiples
+        if (i % 4 == 2 && num >= den) num = (num / den) * den - 1;   // just below one
+        CHECK(kvp::div_floor(num, den) == num / den, "div_floor(%lld, %lld)", (long long)num, (long long)den);
+    }
+}
+
 int main() {
     check_table_index();
+    check_div_floor();
     std::mt19937_64 rng(12345);
     const kvp::SliceWeights weights[] = {kvp::kBf16SliceWeights, kvp::kFp8SliceWeights, {1, 1}};
     const int64_t workers[] = {1, 7, 64, 1024, 2048};
@@ -179,15 +191,16 @@ int main() {
             bt.nblk.push_back(n);
         }
         for (auto kw : weights)
-            for (int64_t W : workers) {
-                check_split(bt, W, kw);
-                ++cases;
-            }
+            for (int64_t W : workers)
+                for (int cost : {0, 1, kvp::kBf16PieceCost, kvp::kFp8PieceCost, 7}) {
+                    check_split(bt, W, kw, cost);
+                    ++cases;
+                }
     }
     // all-empty and single-walk batches
-    check_split(Batch{{0, 0, 0}, 8}, 1024, kvp::kBf16SliceWeights);
-    check_split(Batch{{1}, 1}, 1024, kvp::kBf16SliceWeights);
-    check_split(Batch{{5000}, 1}, 1024, kvp::kBf16SliceWeights);
+    check_split(Batch{{0, 0, 0}, 8}, 1024, kvp::kBf16SliceWeights, kvp::kBf16PieceCost);
+    check_split(Batch{{1}, 1}, 1024, kvp::kBf16SliceWeights, kvp::kBf16PieceCost);
+    check_split(Batch{{5000}, 1}, 1024, kvp::kFp8SliceWeights, kvp::kFp8PieceCost);
     std::printf("%d split cases, %s\n", cases + 3, failures ? "FAILED" : "ok");
     return failures ? 1 : 0;
 }

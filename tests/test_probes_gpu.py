@@ -20,7 +20,7 @@ def _cum(w):
     return 33 * ((w + 1) // 2) + 32 * (w // 2)
 
 
-PIECE_COST = 1   # split positions before each (sequence, KV head) walk's tiles
+PIECE_COST = 2   # split positions before each (sequence, KV head) walk's tiles (bf16 tiles)
 
 
 def _host_walk(tables, lens, hkv, max_context, W, grouped):
