@@ -477,7 +477,9 @@ def main(argv=None):
         # headline is the faster one on this batch
         fused_on = True in graph_ms and graph_ms[True] < graph_ms[False]
         ms_per_step = graph_ms[fused_on]
-        launch = "hip_graph, fused append" if fused_on else "hip_graph, scatter + attention"
+        fused_name = ("fused append + other rows (paged_attention_decode_step)" if step.num_other_tokens
+                      else "fused append (paged_attention_decode_append)")
+        launch = f"hip_graph, {fused_name}" if fused_on else "hip_graph, scatter + attention"
         # the fused form must leave the same pool and output as the two-call form
         step.layer = 0
         step.run()

@@ -332,6 +332,32 @@ kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out
                                         void* stream);
 
 /*
+ * GPU step with other rows: reshape_and_cache(pool, layer, k_rows, v_rows,
+ * row_slots, num_rows) followed by paged_attention_decode_append with the
+ * remaining arguments, in one call; the result, pool included, is bitwise
+ * that of the two calls.  The other rows are those of tokens that this step's
+ * attention does not read, such as a prefill chunk of a sequence outside the
+ * decode batch ([KVC] "The write path: slot mapping and scatter").
+ *   k_rows, v_rows: device, [num_rows][H_kv][D] in the pool dtype (bf16 for FP8), 16-byte aligned.
+ *   row_slots:      device, int64 [num_rows], 8-byte aligned; a slot < 0 or >= N * B is skipped.
+ *   num_rows:       host, >= 0; 0 makes this paged_attention_decode_append.
+ *   Every other argument, and every error, as for paged_attention_decode_append;
+ *   with num_seqs = 0 only the rows are stored.
+ * Precondition: no slot of row_slots lies in a block that the attention reads
+ * (named by sequence i's table within its first L_i positions) or that a
+ * decode row is appended to.  In the balanced mode with a bf16 pool the rows
+ * are stored by extra waves of the attention's launch, each lane moving
+ * several 16-byte chunks (one kernel, then the fix-up); otherwise the scatter
+ * kernel runs first.
+ */
+kv_status paged_attention_decode_step(kv_pool_t pool, int32_t layer, void* out, const void* q, const void* k_new,
+                                      const void* v_new, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                                      int32_t max_context_len, int32_t partition_size, const void* k_rows,
+                                      const void* v_rows, const int64_t* row_slots, int64_t num_rows, void* workspace,
+                                      uint64_t workspace_bytes, void* stream);
+
+/*
  * GPU step, a batch with a common prefix ([KVC] "Prefix sharing, reference
  * counts, and copy-on-write"; [PIF] "03 Sharing via copy-on-write"): the same
  * result as paged_attention_decode with partition_size 0, up to rounding

@@ -949,6 +949,60 @@ __device__ __forceinline__ void append_scatter_waves(const DecodeArgs& a, int64_
     }
 }
 
+// Other rows of the step (reshape_and_cache of rows_k / rows_v to
+// rows_slots, e.g. a prefill chunk of a sequence outside the batch), stored by
+// nx more waves of the balanced launch: wave x takes rows x, x + nx, ...; a
+// row's K and V chunks, numbered ({K,V} * Hkv + head) * 16 + chunk, go out
+// kRowChunks per lane per round, the round's loads all in flight before its
+// stores, and the next row's slot is read while this one moves.  Block sizes
+// are powers of two, so the slot splits with shifts (a 64-bit division per
+// chunk on these waves slowed the walk beside them by 8 %).  A slot outside
+// the pool is skipped.  The caller guarantees that no slot lies in a block
+// this launch's attention reads.
+constexpr int kRowChunks = 4;
+
+__device__ __forceinline__ void rows_scatter_waves(const DecodeArgs& a, int64_t x, int64_t nx) {
+    const int lane = threadIdx.x;
+    const int per_head = a.num_kv_heads * kRC;
+    const int per_token = 2 * per_head;
+    const int bshift = __builtin_ctz((unsigned)a.block_size);
+    const int64_t num_slots = (int64_t)a.num_blocks << bshift;
+    const uint4* ksrc = reinterpret_cast<const uint4*>(a.rows_k);
+    const uint4* vsrc = reinterpret_cast<const uint4*>(a.rows_v);
+    uint4* kdst = const_cast<uint4*>(reinterpret_cast<const uint4*>(a.k_layer));
+    uint4* vdst = const_cast<uint4*>(reinterpret_cast<const uint4*>(a.v_layer));
+    int64_t next = x < a.num_rows ? a.rows_slots[x] : -1;
+    for (int64_t t = x; t < a.num_rows; t += nx) {
+        const int64_t slot = next;   // wave-uniform
+        next = t + nx < a.num_rows ? a.rows_slots[t + nx] : -1;
+        if (slot < 0 || slot >= num_slots) continue;
+        const int64_t block = slot >> bshift;
+        // chunk (h, c) of the row goes to ((block * Hkv + h) * B + offset) * 16 + c
+        const int64_t row0 = (((block * a.num_kv_heads) << bshift) + (slot - (block << bshift))) * kRC;
+        const int64_t src0 = t * per_head;
+        for (int i0 = 0; i0 < per_token; i0 += kWave * kRowChunks) {
+            uint4 v[kRowChunks];
+            int64_t dst[kRowChunks];
+            bool is_v[kRowChunks];
+            // loads unconditional (a lane past the row reads its last chunk
+            // again and stores nothing), so a round's loads are all in flight
+#pragma unroll
+            for (int u = 0; u < kRowChunks; ++u) {
+                const int item = i0 + u * kWave + lane;
+                const int it = item < per_token ? item : per_token - 1;
+                is_v[u] = it >= per_head;
+                const int rem = it - (is_v[u] ? per_head : 0);
+                dst[u] = item < per_token ? row0 + ((int64_t)(rem >> 4) << (bshift + 4)) + (rem & (kRC - 1)) : -1;
+                v[u] = (is_v[u] ? vsrc : ksrc)[src0 + rem];
+            }
+            asm volatile("" ::: "memory");   // the round's loads all issued before its first store
+#pragma unroll
+            for (int u = 0; u < kRowChunks; ++u)
+                if (dst[u] >= 0) (is_v[u] ? vdst : kdst)[dst[u]] = v[u];
+        }
+    }
+}
+
 // The same for FP8 pools: one (sequence, {K,V}, KV head) row per wave and
 // step, quantized with its block's scale; a row at position 0 of its block
 // sets that scale first (fp8_store_row).
@@ -1059,9 +1113,13 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                 return;
             }
         }
-        // decode append: the pool side
-        if constexpr (kFp8) append_fp8_waves(a, w - W, (int64_t)gridDim.x - W);
-        else append_scatter_waves(a, w - W, (int64_t)gridDim.x - W);
+        const int64_t x = w - W;
+        if (x < a.append_waves) {   // decode append: the pool side
+            if constexpr (kFp8) append_fp8_waves(a, x, a.append_waves);
+            else append_scatter_waves(a, x, a.append_waves);
+        } else {
+            if constexpr (!kFp8) rows_scatter_waves(a, x - a.append_waves, (int64_t)gridDim.x - W - a.append_waves);
+        }
         return;
     }
     const int S = a.num_seqs;
@@ -1666,13 +1724,22 @@ hipError_t launch_streamk_walk(const DecodeArgs& a_in, int group, int workers, h
     // decode append: a few extra single-wave workgroups store the new rows
     // (bf16: about 8 chunks per lane; FP8: about 4 rows per wave)
     int64_t extra = 0;
+    a.append_waves = 0;
     if (a.shared_tiles > 0) {   // the prefix walks: (column block, KV head, part)
         extra = ((int64_t)a.num_seqs * group + 15) / 16 * a.num_kv_heads * a.prefix_parts;
-    } else if (a.k_append) {
-        const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * (kFp8 ? 1 : kRC);
-        const int64_t per_wave = kFp8 ? 4 : 8 * kWave;
-        extra = (items + per_wave - 1) / per_wave;
-        extra = extra < 1 ? 1 : (extra > 256 ? 256 : extra);
+    } else {
+        if (a.k_append) {
+            const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * (kFp8 ? 1 : kRC);
+            const int64_t per_wave = kFp8 ? 4 : 8 * kWave;
+            extra = (items + per_wave - 1) / per_wave;
+            extra = extra < 1 ? 1 : (extra > 256 ? 256 : extra);
+            a.append_waves = (int32_t)extra;
+        }
+        // other rows: up to 768 waves (a row or a few each), so that they are
+        // done while the workers still scan lengths and fetch their first
+        // tiles; with 256 waves (nine rows each on the 70B-shaped step) the
+        // step took 2 us longer, and the walk is HBM-bound either way
+        if (!kFp8 && a.num_rows > 0) extra += a.num_rows < 768 ? a.num_rows : 768;
     }
     dim3 grid((unsigned)(workers + extra));
     const bool any_b = a.block_size != kTileTokens;

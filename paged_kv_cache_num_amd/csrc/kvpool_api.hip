@@ -182,6 +182,43 @@ kv_status check_shared(const kv_pool_desc& d, int32_t num_seqs, int32_t max_cont
     return KV_OK;
 }
 
+// Arguments of a batch of rows to store (reshape_and_cache and the rows of
+// paged_attention_decode_step).
+kv_status check_rows(kv_pool_t pool, const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                     int64_t num_tokens) {
+    if (num_tokens < 0) return fail(KV_ERR_INVALID_ARGUMENT, "num_tokens %lld < 0", (long long)num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!k_new || !v_new || !slot_mapping) return fail(KV_ERR_INVALID_ARGUMENT, "NULL device pointer");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) return fail(KV_ERR_INVALID_ARGUMENT, "slot_mapping must be 8-byte aligned");
+    if (pool->desc.num_kv_heads > (1 << 20))   // the kernels number a token's chunks in 32 bits
+        return fail(KV_ERR_UNSUPPORTED, "num_kv_heads %d above 2^20", pool->desc.num_kv_heads);
+    return ok();
+}
+
+// The scatter kernel for num_tokens > 0 checked rows (FP8 pools: quantized, with block scales).
+hipError_t launch_rows(kv_pool_t pool, int32_t layer, const void* k_new, const void* v_new,
+                       const int64_t* slot_mapping, int64_t num_tokens, void* stream) {
+    kvp::ScatterArgs a;
+    memset(&a, 0, sizeof a);
+    a.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
+    a.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_slots = (int64_t)pool->desc.num_blocks * pool->desc.block_size;
+    a.block_size = pool->desc.block_size;
+    a.num_kv_heads = pool->desc.num_kv_heads;
+    a.row_chunks = pool->desc.head_dim * pool->elem_bytes / 16;
+    if (pool->desc.dtype == KV_FP8_E4M3) {
+        a.k_scale = pool->k_scale + (uint64_t)layer * pool->scale_layer;
+        a.v_scale = pool->v_scale + (uint64_t)layer * pool->scale_layer;
+        return kvp::launch_scatter_fp8(a, static_cast<hipStream_t>(stream));
+    }
+    return kvp::launch_scatter(a, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -328,33 +365,9 @@ kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, co
     if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "pool is NULL");
     if (layer < 0 || layer >= pool->desc.num_layers)
         return fail(KV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, pool->desc.num_layers);
-    if (num_tokens < 0) return fail(KV_ERR_INVALID_ARGUMENT, "num_tokens %lld < 0", (long long)num_tokens);
-    if (num_tokens == 0) return ok();
-    if (!k_new || !v_new || !slot_mapping) return fail(KV_ERR_INVALID_ARGUMENT, "NULL device pointer");
-    if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new must be 16-byte aligned");
-    if (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) return fail(KV_ERR_INVALID_ARGUMENT, "slot_mapping must be 8-byte aligned");
-    if (pool->desc.num_kv_heads > (1 << 20))   // the kernels number a token's chunks in 32 bits
-        return fail(KV_ERR_UNSUPPORTED, "num_kv_heads %d above 2^20", pool->desc.num_kv_heads);
-    kvp::ScatterArgs a;
-    memset(&a, 0, sizeof a);
-    a.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
-    a.v_layer = pool->v_base + (uint64_t)layer * pool->layer_bytes;
-    a.k_new = k_new;
-    a.v_new = v_new;
-    a.slot_mapping = slot_mapping;
-    a.num_tokens = num_tokens;
-    a.num_slots = (int64_t)pool->desc.num_blocks * pool->desc.block_size;
-    a.block_size = pool->desc.block_size;
-    a.num_kv_heads = pool->desc.num_kv_heads;
-    a.row_chunks = pool->desc.head_dim * pool->elem_bytes / 16;
-    hipError_t e;
-    if (pool->desc.dtype == KV_FP8_E4M3) {
-        a.k_scale = pool->k_scale + (uint64_t)layer * pool->scale_layer;
-        a.v_scale = pool->v_scale + (uint64_t)layer * pool->scale_layer;
-        e = kvp::launch_scatter_fp8(a, static_cast<hipStream_t>(stream));
-    } else {
-        e = kvp::launch_scatter(a, static_cast<hipStream_t>(stream));
-    }
+    const kv_status st = check_rows(pool, k_new, v_new, slot_mapping, num_tokens);
+    if (st != KV_OK || num_tokens == 0) return st;
+    const hipError_t e = launch_rows(pool, layer, k_new, v_new, slot_mapping, num_tokens, stream);
     if (e != hipSuccess) return hip_fail(e, "scatter launch");
     return ok();
 }
@@ -541,10 +554,16 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
                       const void* v_append, const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                       int32_t max_context_len, int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-                      void* stream, int32_t shared_blocks = 0, bool static_scratch = false) {
+                      void* stream, int32_t shared_blocks = 0, bool static_scratch = false,
+                      const void* rows_k = nullptr, const void* rows_v = nullptr, const int64_t* rows_slots = nullptr,
+                      int64_t num_rows = 0) {
     if (!pool) return fail(KV_ERR_INVALID_ARGUMENT, "pool is NULL");
     const kv_pool_desc& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers) return fail(KV_ERR_INVALID_ARGUMENT, "layer %d outside [0, %d)", layer, d.num_layers);
+    {
+        const kv_status st = check_rows(pool, rows_k, rows_v, rows_slots, num_rows);
+        if (st != KV_OK) return st;
+    }
     if (num_seqs < 0 || max_context_len < 0 || partition_size < 0 || max_blocks_per_seq <= 0)
         return fail(KV_ERR_INVALID_ARGUMENT, "negative size argument");
     if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads != 0)
@@ -563,7 +582,11 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
     if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(KV_ERR_INVALID_ARGUMENT, "scale must be finite and positive");
     if (num_seqs > 65535 || num_q_heads > 65535)
         return fail(KV_ERR_UNSUPPORTED, "num_seqs %d / num_q_heads %d above the 65535 grid limit", num_seqs, num_q_heads);
-    if (num_seqs == 0) return ok();
+    if (num_seqs == 0) {   // nothing to attend; other rows are still stored
+        if (num_rows == 0) return ok();
+        const hipError_t e = launch_rows(pool, layer, rows_k, rows_v, rows_slots, num_rows, stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "scatter launch");
+    }
     if (!out || !q || !block_tables || !context_lens) return fail(KV_ERR_INVALID_ARGUMENT, "NULL device pointer");
     if (!aligned16(out) || !aligned16(q)) return fail(KV_ERR_INVALID_ARGUMENT, "q/out must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(block_tables) | reinterpret_cast<uintptr_t>(context_lens)) & 3u)
@@ -638,20 +661,37 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
         a.shared_entries = (int32_t)((int64_t)stiles * kvp::kTileTokens / d.block_size);
         a.prefix_parts = sp.parts;
         a.prefix_part_tiles = sp.part_tiles;
-        e = kvp::launch_decode_bf16_shared(a, num_q_heads / d.num_kv_heads, plan.workers,
-                                           static_cast<hipStream_t>(stream));
+        e = num_rows > 0 ? launch_rows(pool, layer, rows_k, rows_v, rows_slots, num_rows, stream) : hipSuccess;
+        if (e == hipSuccess)
+            e = kvp::launch_decode_bf16_shared(a, num_q_heads / d.num_kv_heads, plan.workers,
+                                               static_cast<hipStream_t>(stream));
     } else if (plan.mode == Mode::kBalanced) {
         // the worker that owns each (sequence, KV head)'s last block uses the new row
-        // (FP8: quantized in registers); extra waves of the same launch store it
+        // (FP8: quantized in registers); extra waves of the same launch store it.
+        // Other rows: bf16 pools store them from more waves of the launch, FP8
+        // pools (block scales to set) with the scatter kernel first.
         a.k_append = k_append;
         a.v_append = v_append;
-        const int group = num_q_heads / d.num_kv_heads;
-        e = fp8 ? kvp::launch_decode_fp8_streamk(a, group, plan.workers, static_cast<hipStream_t>(stream))
-                : kvp::launch_decode_bf16_streamk(a, group, plan.workers, static_cast<hipStream_t>(stream));
-    } else {
-        // the new rows first (FP8: quantized, with the scale of a block they open), then the decode
         e = hipSuccess;
-        if (append) {
+        if (num_rows > 0) {
+            if (fp8) {
+                e = launch_rows(pool, layer, rows_k, rows_v, rows_slots, num_rows, stream);
+            } else {
+                a.rows_k = rows_k;
+                a.rows_v = rows_v;
+                a.rows_slots = rows_slots;
+                a.num_rows = num_rows;
+            }
+        }
+        const int group = num_q_heads / d.num_kv_heads;
+        if (e == hipSuccess) {
+            e = fp8 ? kvp::launch_decode_fp8_streamk(a, group, plan.workers, static_cast<hipStream_t>(stream))
+                    : kvp::launch_decode_bf16_streamk(a, group, plan.workers, static_cast<hipStream_t>(stream));
+        }
+    } else {
+        // other rows, then the new rows (FP8: quantized, with the scale of a block they open), then the decode
+        e = num_rows > 0 ? launch_rows(pool, layer, rows_k, rows_v, rows_slots, num_rows, stream) : hipSuccess;
+        if (append && e == hipSuccess) {
             kvp::AppendArgs w;
             memset(&w, 0, sizeof w);
             w.k_layer = pool->k_base + (uint64_t)layer * pool->layer_bytes;
@@ -740,6 +780,18 @@ kv_status paged_attention_shared_workspace_bytes(kv_pool_t pool, int32_t num_seq
     *bytes = stiles > 0 ? plan_shared(pool->desc, num_seqs, num_q_heads, max_context_len, stiles).total
                         : plan_decode(pool->desc, num_seqs, num_q_heads, max_context_len, 0).ws_total;
     return ok();
+}
+
+kv_status paged_attention_decode_step(kv_pool_t pool, int32_t layer, void* out, const void* q, const void* k_new,
+                                      const void* v_new, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                                      int32_t max_context_len, int32_t partition_size, const void* k_rows,
+                                      const void* v_rows, const int64_t* row_slots, int64_t num_rows, void* workspace,
+                                      uint64_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && (!k_new || !v_new)) return fail(KV_ERR_INVALID_ARGUMENT, "k_new/v_new is NULL");
+    return decode_impl(pool, layer, out, q, k_new, v_new, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_q_heads, scale, max_context_len, partition_size, workspace, workspace_bytes, stream, 0, false,
+                       k_rows, v_rows, row_slots, num_rows);
 }
 
 kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out, const void* q, const void* k_new,

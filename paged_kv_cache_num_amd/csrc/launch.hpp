@@ -19,7 +19,8 @@ struct ScatterArgs {
     const int64_t* slot_mapping; // [T]
     int64_t num_tokens;
     int64_t num_slots;           // num_blocks * block_size
-    int32_t block_size;          // tokens per block
+    int32_t block_size;          // tokens per block (a power of two)
+    int32_t block_shift;         // log2(block_size), set by the launcher
     int32_t num_kv_heads;
     int32_t row_chunks;          // 16-byte chunks per (token, head) row = D * elem / 16
     float* k_scale;              // FP8 pools: the layer's scales [num_blocks][Hkv], else null
@@ -107,7 +108,14 @@ struct DecodeArgs {
     const void* v_append;
     const float* k_scale;        // FP8 pools: the layer's block scales [num_blocks][Hkv]
     const float* v_scale;
-    int32_t workers;             // balanced split: worker waves (the launch adds append waves past them)
+    // balanced split, bf16 pools: other rows stored by extra waves of the same
+    // launch (reshape_and_cache semantics; slots the attention does not read)
+    const void* rows_k;          // [num_rows][Hkv][D]
+    const void* rows_v;
+    const int64_t* rows_slots;   // [num_rows]
+    int64_t num_rows;
+    int32_t append_waves;        // balanced split: extra waves storing the decode rows (set by the launcher)
+    int32_t workers;             // balanced split: worker waves (the launch adds append / row waves past them)
     int32_t slice_even;          // balanced split: tiles of a worker on an even XCD per slice_odd on an odd one
     int32_t slice_odd;
     int32_t piece_cost;          // balanced split: positions before each (sequence, KV head) walk's tiles

@@ -35,7 +35,7 @@ EXPORTED = (
     "kv_build_slot_mapping",
     "reshape_and_cache", "paged_attention_workspace_bytes", "paged_attention_decode",
     "paged_attention_decode_append", "paged_attention_decode_shared", "paged_attention_shared_workspace_bytes",
-    "paged_attention_decode_noalloc",
+    "paged_attention_decode_noalloc", "paged_attention_decode_step",
     "kv_copy_blocks", "kv_swap_bytes", "kv_swap_out", "kv_swap_in",
     "kv_status_string", "kv_last_error_message", "kv_probe_copy", "kv_probe_read", "kv_probe_table_walk",
     "kv_probe_e4m3_to_bf16", "kv_probe_f32_to_e4m3",
@@ -103,6 +103,9 @@ def _load():
     lib.paged_attention_decode_append.restype = ctypes.c_int
     lib.paged_attention_decode_append.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32,
                                                   vp, u64, vp]
+    lib.paged_attention_decode_step.restype = ctypes.c_int
+    lib.paged_attention_decode_step.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32,
+                                                vp, vp, vp, i64, vp, u64, vp]
     lib.paged_attention_decode_noalloc.restype = ctypes.c_int
     lib.paged_attention_decode_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, vp, i32, i32, f32, i32, i32, vp]
     lib.kv_probe_copy.restype = ctypes.c_int
@@ -430,6 +433,43 @@ class KVPool:
                                                  S, Hq, float(scale), int(max_context_len), int(partition_size),
                                                  ws_ptr, int(ws_bytes), _stream_handle(stream)),
                "paged_attention_decode_append")
+
+    def paged_attention_decode_step(self, layer: int, out, q, k_new, v_new, block_tables, context_lens,
+                                    k_rows, v_rows, row_slots, *, scale: float, max_context_len: int,
+                                    partition_size: int = 0, workspace=None, stream=None) -> None:
+        """Store other rows (reshape_and_cache of k_rows / v_rows to row_slots),
+        append each sequence's new row at position L_i - 1 and attend, in one
+        call.  The other rows' slots must lie in blocks the attention does not
+        read (a prefill chunk of a sequence outside the batch)."""
+        import torch
+        S, Hq, D = (int(x) for x in q.shape)
+        R = int(row_slots.shape[0])
+        if tuple(out.shape) != (S, Hq, D) or D != self.head_dim:
+            raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim]")
+        if tuple(k_new.shape) != (S, self.num_kv_heads, D) or tuple(v_new.shape) != (S, self.num_kv_heads, D):
+            raise ValueError("k_new/v_new must be [num_seqs][num_kv_heads][head_dim]")
+        if tuple(k_rows.shape) != (R, self.num_kv_heads, D) or tuple(v_rows.shape) != (R, self.num_kv_heads, D):
+            raise ValueError("k_rows/v_rows must be [num_rows][num_kv_heads][head_dim]")
+        if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+            raise ValueError("one table row and one length per sequence")
+        ws_ptr, ws_bytes = None, 0
+        if workspace is not None:
+            ws_ptr = _dev_ptr(workspace, "workspace")
+            ws_bytes = workspace.numel() * workspace.element_size()
+        _check(lib.paged_attention_decode_step(self.handle, int(layer),
+                                               _dev_ptr(out, "out", self.torch_dtype),
+                                               _dev_ptr(q, "q", self.torch_dtype),
+                                               _dev_ptr(k_new, "k_new", self.torch_dtype),
+                                               _dev_ptr(v_new, "v_new", self.torch_dtype),
+                                               _dev_ptr(block_tables, "block_tables", torch.int32),
+                                               int(block_tables.shape[1]),
+                                               _dev_ptr(context_lens, "context_lens", torch.int32),
+                                               S, Hq, float(scale), int(max_context_len), int(partition_size),
+                                               _dev_ptr(k_rows, "k_rows", self.torch_dtype),
+                                               _dev_ptr(v_rows, "v_rows", self.torch_dtype),
+                                               _dev_ptr(row_slots, "row_slots", torch.int64), R,
+                                               ws_ptr, int(ws_bytes), _stream_handle(stream)),
+               "paged_attention_decode_step")
 
 
 def probe_copy(dst, src, stream=None) -> None:

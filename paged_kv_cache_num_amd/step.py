@@ -168,14 +168,22 @@ class DecodeStep:
 
     def run_fused(self, stream=None):
         """The same step with the decode appends folded into the attention call
-        (paged_attention_decode_append); other writes still go through
-        reshape_and_cache first."""
+        (paged_attention_decode_append), and the other writes (rows of
+        sequences outside the batch, such as a prefill chunk) with them
+        (paged_attention_decode_step)."""
         if not self.can_fuse:
             raise ValueError("some sequence has no single-row write at position L_i - 1")
         if self.shared_blocks:
             raise ValueError("the shared-prefix call has no decode-append form")
         if self.num_other_tokens:
-            self.pool.reshape_and_cache(self.layer, self.other_k, self.other_v, self.other_slots, stream=stream)
+            # the other rows (a prefill chunk of a sequence outside the batch) in the same call
+            self.pool.paged_attention_decode_step(self.layer, self.out, self.q, self.append_k, self.append_v,
+                                                  self.block_tables, self.context_lens, self.other_k, self.other_v,
+                                                  self.other_slots, scale=self.scale,
+                                                  max_context_len=self.max_context_len,
+                                                  partition_size=self.partition_size, workspace=self.workspace,
+                                                  stream=stream)
+            return
         self.pool.paged_attention_decode_append(self.layer, self.out, self.q, self.append_k, self.append_v,
                                                 self.block_tables, self.context_lens, scale=self.scale,
                                                 max_context_len=self.max_context_len,

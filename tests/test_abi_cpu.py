@@ -515,3 +515,31 @@ def test_noalloc_decode_checks_return_before_any_launch():
     assert "static array" in msg and str(K.KV_NOALLOC_SCRATCH_BYTES) in msg, msg
     assert call(S=0) == K.KV_OK                                    # nothing to do, nothing launched
     L.kv_pool_destroy(h)
+
+
+def test_decode_step_row_checks_return_before_any_launch():
+    """paged_attention_decode_step: the other rows' arguments are checked
+    (count, NULL pointers, alignment) before any device work, as are the
+    decode arguments; no rows and no sequences is a no-op."""
+    st, h = _pool(head_dim=128, num_kv_heads=8, dtype="bf16", num_blocks=64)
+    L = K.lib
+
+    def call(**kw):
+        a = dict(layer=0, out=0x30000000, q=0x40000000, kn=0x70000000, vn=0x71000000, tables=0x50000000, mb=16,
+                 lens=0x60000000, S=4, Hq=32, scale=0.125, max_ctx=200, part=0, kr=0x72000000, vr=0x73000000,
+                 slots=0x74000000, R=2048, ws=None, wsb=0)
+        a.update(kw)
+        return L.paged_attention_decode_step(h, a["layer"], a["out"], a["q"], a["kn"], a["vn"], a["tables"], a["mb"],
+                                             a["lens"], a["S"], a["Hq"], a["scale"], a["max_ctx"], a["part"],
+                                             a["kr"], a["vr"], a["slots"], a["R"], a["ws"], a["wsb"], None)
+    assert call(R=-1) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(kr=None) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(slots=None) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(vr=0x73000008) == K.KV_ERR_INVALID_ARGUMENT         # not 16-byte aligned
+    assert call(slots=0x74000004) == K.KV_ERR_INVALID_ARGUMENT      # not 8-byte aligned
+    assert call(kn=None) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(layer=1) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(Hq=24) == K.KV_ERR_UNSUPPORTED
+    assert call(part=40) == K.KV_ERR_INVALID_ARGUMENT
+    assert call(S=0, R=0) == K.KV_OK                                 # nothing to do, nothing launched
+    L.kv_pool_destroy(h)

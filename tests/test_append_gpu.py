@@ -5,7 +5,8 @@ step (reshape_and_cache of each sequence's new row at position L_i - 1, then
 paged_attention_decode), and match the oracle within the dtype's tolerance.
 Covered: the balanced mode (where the wave reading each last block writes the
 row), the fixed-partition and fp32 / D = 64 modes (a scatter kernel first),
-prefix-shared blocks, a step with an extra prefill write, and edge lengths.
+prefix-shared blocks, steps with a prefill chunk of another sequence stored in
+the same call (paged_attention_decode_step), and edge lengths.
 """
 import numpy as np
 import pytest
@@ -41,8 +42,12 @@ def _same(two, fused, label):
     assert kf.tobytes() == k2.tobytes() and vf.tobytes() == v2.tobytes(), f"{label}: pool differs"
 
 
+# C3 and its TP-8 shard carry a 2048-token prefill chunk of a sequence outside
+# the batch: the fused step stores it in the same call (paged_attention_decode_step;
+# balanced mode: extra waves of the attention's launch, partitions: the scatter kernel first)
 CASES = [("C1", "sharp", 0), ("C1", "hot", 32), ("C2", "spec", 0), ("C2", "needle", 0), ("C2", "sharp", 512),
-         ("C3", "needle", 0), ("C4", "sharp", 0), ("C5", "needle", 0), ("C5", "sharp", 512)]
+         ("C3", "needle", 0), ("C3", "sharp", 512), ("C3TP8", "spec", 0), ("C4", "sharp", 0), ("C5", "needle", 0),
+         ("C5", "sharp", 512)]
 
 
 @pytest.mark.parametrize("name,variant,partition", CASES)
@@ -96,10 +101,11 @@ def test_fused_many_layers_writes_only_its_layer():
         assert k.tobytes() == wl.k_pool.tobytes() and v.tobytes() == wl.v_pool.tobytes(), "wrote outside its layer"
 
 
-def test_fused_graph_replays_match_eager():
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_fused_graph_replays_match_eager(name):
     import torch
-    say("C2 sharp: HIP graph of the fused step")
-    wl = workload("C2", "sharp")
+    say(f"{name} sharp: HIP graph of the fused step")
+    wl = workload(name, "sharp")
     two, fused = _both(wl, partition_size=0)
     eager = fused.out_host()
     graph = fused.capture(fused=True)
@@ -111,3 +117,6 @@ def test_fused_graph_replays_match_eager():
         torch.cuda.synchronize()
         del junk
         assert fused.out_host().tobytes() == eager.tobytes(), f"replay {i} differs"
+    k2, v2 = two.pool_host()
+    kf, vf = fused.pool_host()
+    assert kf.tobytes() == k2.tobytes() and vf.tobytes() == v2.tobytes(), "pool after the replays differs"

@@ -240,3 +240,33 @@ def test_balanced_merge_reads_fresh_partial_states(name, variant, num_seqs):
         err = max_err(step.out_host(), ref["out"], wl.dtype)
         say(f"  after poisoning: max err {err:.3e}")
         assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("T", [2051, 4099])
+def test_large_ragged_scatter_bit_exact(T):
+    """reshape_and_cache with thousands of rows (the kernel then moves four
+    tokens per workgroup) and a count that is not a multiple of four, with
+    padding slots (-1) and slots past the pool mixed in: the pool equals the
+    oracle's scatter of the in-range rows, byte for byte."""
+    import torch
+    from paged_kv_cache_num_amd.kvpool import KVPool
+    from paged_kv_cache_num_amd.step import to_device, to_host
+    N, H, B, D = 700, 8, 16, 128
+    say(f"scatter of {T} rows into an [{N}][{H}][{B}][{D}] bf16 pool, padding and out-of-range slots")
+    rng = np.random.default_rng(T)
+    kp = rng.integers(0, 1 << 16, size=(N, H, B, D), dtype=np.uint16)
+    vp = rng.integers(0, 1 << 16, size=(N, H, B, D), dtype=np.uint16)
+    kn = rng.integers(0, 1 << 16, size=(T, H, D), dtype=np.uint16)
+    vn = rng.integers(0, 1 << 16, size=(T, H, D), dtype=np.uint16)
+    slots = rng.permutation(N * B)[:T].astype(np.int64)
+    slots[::7] = -1
+    slots[5::97] = N * B + 3
+    keep = (slots >= 0) & (slots < N * B)
+    want_k, want_v = oracle.scatter(kp, vp, kn[keep], vn[keep], slots[keep])
+    pool = KVPool(to_device(kp, "bf16"), to_device(vp, "bf16"), num_layers=1, num_blocks=N, block_size=B,
+                  num_kv_heads=H, head_dim=D)
+    pool.reshape_and_cache(0, to_device(kn, "bf16"), to_device(vn, "bf16"),
+                           torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert to_host(pool.k, "bf16").tobytes() == want_k.tobytes()
+    assert to_host(pool.v, "bf16").tobytes() == want_v.tobytes()
