@@ -132,7 +132,7 @@ def traffic_for(config: str, partition: int, block_size: int = 16, kv_dtype: str
 
 
 ATTN_KERNEL_MARKERS = ("decode_bf16_streamk_kernel", "streamk_fixup_kernel", "decode_bf16_mfma_kernel",
-                       "decode_kernel", "reduce_kernel")
+                       "decode_partitions_kernel", "decode_kernel", "reduce_kernel")
 
 
 def record_traffic(fetch_csv: str, write_csv: str, copy_mib: int, config: str, partition: int,
@@ -200,21 +200,42 @@ def percentile(xs, q):
 CPU_SAMPLE_SECONDS = 10.0   # the oracle's sample: repeated until about this much CPU work is timed
 
 
-def cpu_baseline(wl, bytes_total):
+def cpu_baseline(wl, bytes_total, nbytes=None):
+    """The oracle's whole step (oracle.run_step's three calls: slot mapping,
+    scatter, fp64 attention), repeated for about CPU_SAMPLE_SECONDS; the
+    write path (slot mapping + scatter) and the attention are also timed
+    apart.  The oracle's scatter returns new copies of the pools, so its
+    time includes copying them."""
     import oracle
     threads = oracle.default_threads()
-    reps, total = 0, 0.0
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    reps, total, t_write, t_attn = 0, 0.0, 0.0, 0.0
     while total < CPU_SAMPLE_SECONDS and reps < 1000:
         t0 = time.perf_counter()
-        oracle.run_step(wl, threads=threads)
-        total += time.perf_counter() - t0
+        slots = oracle.slot_mapping(wl.all_tables(), wl.block_size, wl.num_blocks, wl.write_seq, wl.write_start,
+                                    wl.write_count)
+        kp, vp = oracle.scatter(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, slots)
+        t1 = time.perf_counter()
+        oracle.paged_attention(wl.q, kp, vp, wl.dtype, wl.block_tables, wl.context_lens, scale, threads)
+        t2 = time.perf_counter()
+        t_write += t1 - t0
+        t_attn += t2 - t1
+        total += t2 - t0
         reps += 1
+        del kp, vp
     dt = total / reps
-    return {"value": round(bytes_total / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 4), "repeats": reps, "seconds_total": round(total, 2),
-            "sample": f"the whole {wl.name} step (all {wl.num_seqs} sequences): slot mapping, scatter and fp64 "
-                      f"attention, run {reps} times (mean per step)",
-            "tokens_per_s_per_layer": round(wl.num_seqs / dt, 3)}
+    res = {"value": round(bytes_total / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "seconds": round(dt, 4), "repeats": reps, "seconds_total": round(total, 2),
+           "sample": f"the whole {wl.name} step (all {wl.num_seqs} sequences): slot mapping, scatter and fp64 "
+                     f"attention, run {reps} times (mean per step)",
+           "tokens_per_s_per_layer": round(wl.num_seqs / dt, 3),
+           "write_path_seconds": round(t_write / reps, 5), "attention_seconds": round(t_attn / reps, 5)}
+    if nbytes is not None:
+        res["write_path_gbps"] = round(nbytes["scatter"] / (t_write / reps) / 1e9, 4)
+        res["attention_gbps"] = round(nbytes["attn"] / (t_attn / reps) / 1e9, 4)
+        res["write_path_note"] = ("slot mapping and scatter; the oracle's scatter copies both pools first "
+                                  "(it returns new arrays), which dominates its time")
+    return res
 
 
 def cpu_baseline_fp8(wl, state, nseq: int = 16):
@@ -305,6 +326,10 @@ def main(argv=None):
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run made with "
                          "--probe-copy-mib into the traffic record used by the roofline line, and exit")
     ap.add_argument("--record-command", default="", help="command line stored with --record-traffic")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="run only the headline attention call (warmup + steps, layer after layer; the "
+                         "shared-prefix call for a batch with a shared prompt) and exit: the run that "
+                         "hardware counters are collected over for --record-traffic")
     args = ap.parse_args(argv)
 
     if args.record_traffic:
@@ -382,6 +407,18 @@ def main(argv=None):
               f"{2 * n / copy_us / 1e3:.1f} GB/s (read+write)", file=sys.stderr, flush=True)
         del src, dst
 
+    sb = int(wl.info.get("shared_prefix_blocks") or 0)
+    shared_ok = bool(sb) and not fp8 and part == 0 and wl.dtype == "bf16" and not args.no_shared
+    if args.attn_only:
+        call = DecodeStep.from_workload(wl, partition_size=0, shared_blocks=sb, num_layers=NL) if shared_ok else step
+        n = args.warmup + args.steps
+        for i in range(n):
+            call.layer = i % NL
+            call.attend()
+        torch.cuda.synchronize()
+        print(f"bench: {n} {'shared-prefix' if shared_ok else 'plain'} attention calls", file=sys.stderr, flush=True)
+        return 0
+
     print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step.layer = i % NL
@@ -414,26 +451,6 @@ def main(argv=None):
     step_bytes = nbytes["attn"] + nbytes["scatter"]
     eager_ms_per_step = ms_per_step
 
-    # the same attention call K times on one layer, back to back: what part of
-    # each call the caches (L2, 256 MB MALL) serve when it re-reads the KV the
-    # previous call read (reported beside the layer-rotating figure)
-    same_layer = None
-    if NL > 1:
-        step.layer = 0
-        sl_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-        for i in range(K):
-            sl_ev[i][0].record()
-            step.attend()
-            sl_ev[i][1].record()
-        torch.cuda.synchronize()
-        sl_us = [a.elapsed_time(b) * 1e3 for a, b in sl_ev]
-        sl_mean = sum(sl_us) / K
-        same_layer = {"attn_us_mean": round(sl_mean, 2), "attn_us_p50": round(percentile(sl_us, 0.5), 2),
-                      "achieved_gbps": round(nbytes["attn"] / (sl_mean * 1e-6) / 1e9, 1),
-                      "frac": round(nbytes["attn"] / (sl_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
-
-    # the same K steps replayed from one captured HIP graph (how a serving loop
-    # submits its decode step): no launch gaps between the step's kernels
     # The same K steps replayed from one captured HIP graph (how a serving loop
     # submits its decode step), in two forms: scatter + attention, and the
     # decode appends folded into the attention call (paged_attention_decode_append;
@@ -499,8 +516,7 @@ def main(argv=None):
     shared = None
     head_step = step
     roofline_kernel = "paged_attention_decode"
-    sb = int(wl.info.get("shared_prefix_blocks") or 0)
-    if sb and not fp8 and part == 0 and wl.dtype == "bf16" and not args.no_shared:
+    if shared_ok:
         sstep = DecodeStep.from_workload(wl, partition_size=0, shared_blocks=sb, num_layers=NL)
         for i in range(args.warmup):
             sstep.layer = i % NL
@@ -556,6 +572,24 @@ def main(argv=None):
         else:
             del sstep
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # the same attention call K times on one layer, back to back: what part of
+    # each call the caches (L2, 256 MB MALL) serve when it re-reads the KV the
+    # previous call read (reported beside the layer-rotating figure)
+    same_layer = None
+    if NL > 1:
+        head_step.layer = 0
+        sl_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            sl_ev[i][0].record()
+            head_step.attend()
+            sl_ev[i][1].record()
+        torch.cuda.synchronize()
+        sl_us = [a.elapsed_time(b) * 1e3 for a, b in sl_ev]
+        sl_mean = sum(sl_us) / K
+        same_layer = {"attn_us_mean": round(sl_mean, 2), "attn_us_p50": round(percentile(sl_us, 0.5), 2),
+                      "achieved_gbps": round(nbytes["attn"] / (sl_mean * 1e-6) / 1e9, 1),
+                      "frac": round(nbytes["attn"] / (sl_mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
     cold = None
     if not args.no_cold:
@@ -748,7 +782,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline_fp8(wl, state) if fp8 else cpu_baseline(wl, step_bytes)
+        result["cpu_baseline"] = cpu_baseline_fp8(wl, state) if fp8 else cpu_baseline(wl, step_bytes, nbytes)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
