@@ -160,6 +160,9 @@ kv_status kv_pool_destroy(kv_pool_t pool);
  * (null pointer, negative count or start, row outside [0, num_rows), capacity
  * too small), KV_ERR_OUT_OF_RANGE (p / B >= max_blocks_per_seq, or a table
  * entry outside [0, num_blocks)).  Nothing is written past the first error.
+ * A library built with KV_DEBUG (python -m paged_kv_cache_num_amd.build --debug)
+ * also refuses, with KV_ERR_INVALID_ARGUMENT, two writes to one slot in the same
+ * call (the scatter would apply them in no defined order); *num_tokens is then 0.
  */
 kv_status kv_build_slot_mapping(const int32_t* block_tables, int32_t num_rows,
                                 int32_t max_blocks_per_seq, int32_t block_size, int32_t num_blocks,

@@ -10,6 +10,7 @@
 #include <new>
 
 #include "kvpool.h"
+#include "host_logic.hpp"
 #include "launch.hpp"
 #include "split.hpp"
 
@@ -43,26 +44,16 @@ kv_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int elem_bytes_of(int32_t dtype) {
-    return dtype == KV_F32 ? 4 : (dtype == KV_BF16 ? 2 : (dtype == KV_FP8_E4M3 ? 1 : 0));
-}
+int elem_bytes_of(int32_t dtype) { return kvp::host::elem_bytes_of(dtype); }
 
-bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
-    if (a != 0 && b > UINT64_MAX / a) return false;
-    *out = a * b;
-    return true;
-}
+// a host_logic.hpp status, its message recorded as the last error
+kv_status from_host(kv_status s, const kvp::host::Message& m) { return s == KV_OK ? ok() : fail(s, "%s", m.text); }
 
-kv_status check_desc(const kv_pool_desc* d) {
-    if (!d) return fail(KV_ERR_INVALID_ARGUMENT, "descriptor is NULL");
-    if (d->num_layers <= 0 || d->num_blocks <= 0 || d->block_size <= 0 || d->num_kv_heads <= 0 ||
-        d->head_dim <= 0)
-        return fail(KV_ERR_INVALID_ARGUMENT,
-                    "descriptor sizes must be positive (layers %d, blocks %d, block_size %d, kv_heads %d, head_dim %d)",
-                    d->num_layers, d->num_blocks, d->block_size, d->num_kv_heads, d->head_dim);
-    if (elem_bytes_of(d->dtype) == 0) return fail(KV_ERR_INVALID_ARGUMENT, "unknown dtype %d", d->dtype);
-    return KV_OK;
-}
+#if defined(KV_DEBUG) && KV_DEBUG
+constexpr bool kDebugChecks = true;    // host-side precondition checks of the debug build
+#else
+constexpr bool kDebugChecks = false;
+#endif
 
 kv_status hip_fail(hipError_t e, const char* what) {
     return fail(KV_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
@@ -239,29 +230,14 @@ const char* kv_last_error_message(void) { return g_last_error; }
 
 kv_status kv_pool_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tensor) {
     if (!bytes_per_tensor) return fail(KV_ERR_INVALID_ARGUMENT, "bytes_per_tensor is NULL");
-    kv_status s = check_desc(desc);
-    if (s != KV_OK) return s;
-    uint64_t v = (uint64_t)elem_bytes_of(desc->dtype);
-    if (!mul_ok(v, (uint64_t)desc->head_dim, &v) || !mul_ok(v, (uint64_t)desc->num_kv_heads, &v) ||
-        !mul_ok(v, (uint64_t)desc->block_size, &v) || !mul_ok(v, (uint64_t)desc->num_blocks, &v) ||
-        !mul_ok(v, (uint64_t)desc->num_layers, &v))
-        return fail(KV_ERR_INVALID_ARGUMENT, "pool size overflows 64 bits");
-    *bytes_per_tensor = v;
-    return ok();
+    kvp::host::Message m;
+    return from_host(kvp::host::pool_bytes(desc, bytes_per_tensor, m), m);
 }
 
 kv_status kv_pool_scale_bytes(const kv_pool_desc* desc, uint64_t* bytes_per_tensor) {
     if (!bytes_per_tensor) return fail(KV_ERR_INVALID_ARGUMENT, "bytes_per_tensor is NULL");
-    *bytes_per_tensor = 0;
-    kv_status s = check_desc(desc);
-    if (s != KV_OK) return s;
-    if (desc->dtype != KV_FP8_E4M3) return ok();
-    uint64_t v = 4;
-    if (!mul_ok(v, (uint64_t)desc->num_kv_heads, &v) || !mul_ok(v, (uint64_t)desc->num_blocks, &v) ||
-        !mul_ok(v, (uint64_t)desc->num_layers, &v))
-        return fail(KV_ERR_INVALID_ARGUMENT, "scale size overflows 64 bits");
-    *bytes_per_tensor = v;
-    return ok();
+    kvp::host::Message m;
+    return from_host(kvp::host::scale_bytes(desc, bytes_per_tensor, m), m);
 }
 
 namespace {
@@ -330,34 +306,11 @@ kv_status kv_build_slot_mapping(const int32_t* block_tables, int32_t num_rows, i
                                 int32_t block_size, int32_t num_blocks, const int32_t* write_seq,
                                 const int32_t* write_start, const int32_t* write_count, int32_t num_requests,
                                 int64_t* slot_mapping, int64_t capacity, int64_t* num_tokens) {
-    if (!num_tokens) return fail(KV_ERR_INVALID_ARGUMENT, "num_tokens is NULL");
-    *num_tokens = 0;
-    if (num_requests < 0 || num_rows < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0 || capacity < 0)
-        return fail(KV_ERR_INVALID_ARGUMENT, "negative or zero size argument");
-    if (num_requests > 0 && (!block_tables || !write_seq || !write_start || !write_count || (!slot_mapping && capacity > 0)))
-        return fail(KV_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-    int64_t n = 0;
-    for (int32_t r = 0; r < num_requests; ++r) {
-        const int32_t row = write_seq[r];
-        if (row < 0 || row >= num_rows) return fail(KV_ERR_INVALID_ARGUMENT, "request %d names row %d of %d", r, row, num_rows);
-        if (write_start[r] < 0 || write_count[r] < 0)
-            return fail(KV_ERR_INVALID_ARGUMENT, "request %d has negative start or count", r);
-        const int32_t* trow = block_tables + (int64_t)row * max_blocks_per_seq;
-        for (int64_t p = write_start[r], e = (int64_t)write_start[r] + write_count[r]; p < e; ++p) {
-            const int64_t lb = p / block_size;
-            if (lb >= max_blocks_per_seq)
-                return fail(KV_ERR_OUT_OF_RANGE, "request %d position %lld is past its %d-entry table row", r,
-                            (long long)p, max_blocks_per_seq);
-            const int32_t phys = trow[lb];
-            if (phys < 0 || phys >= num_blocks)
-                return fail(KV_ERR_OUT_OF_RANGE, "row %d entry %lld = %d is outside the %d-block pool", row,
-                            (long long)lb, phys, num_blocks);
-            if (n >= capacity) return fail(KV_ERR_INVALID_ARGUMENT, "slot_mapping capacity %lld too small", (long long)capacity);
-            slot_mapping[n++] = (int64_t)phys * block_size + (p - lb * block_size);
-        }
-    }
-    *num_tokens = n;
-    return ok();
+    kvp::host::Message m;
+    return from_host(kvp::host::build_slot_mapping(block_tables, num_rows, max_blocks_per_seq, block_size, num_blocks,
+                                                   write_seq, write_start, write_count, num_requests, slot_mapping,
+                                                   capacity, num_tokens, kDebugChecks, m),
+                     m);
 }
 
 kv_status reshape_and_cache(kv_pool_t pool, int32_t layer, const void* k_new, const void* v_new,
