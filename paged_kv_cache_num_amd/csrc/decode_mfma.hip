@@ -981,24 +981,35 @@ __device__ __forceinline__ void rows_scatter_waves(const DecodeArgs& a, int64_t 
         const int64_t row0 = (((block * a.num_kv_heads) << bshift) + (slot - (block << bshift))) * kRC;
         const int64_t src0 = t * per_head;
         for (int i0 = 0; i0 < per_token; i0 += kWave * kRowChunks) {
-            uint4 v[kRowChunks];
-            int64_t dst[kRowChunks];
-            bool is_v[kRowChunks];
             // loads unconditional (a lane past the row reads its last chunk
-            // again and stores nothing), so a round's loads are all in flight
-#pragma unroll
-            for (int u = 0; u < kRowChunks; ++u) {
+            // again and stores nothing), so a round's loads are all in flight;
+            // four named chunks, not an array: an array here was placed in LDS
+            // by the compiler, each load waited for and copied there
+            struct Chunk {
+                uint4 v;
+                int64_t dst;   // -1: nothing to store
+                bool is_v;
+            };
+            auto load = [&](int u) __attribute__((always_inline)) {
                 const int item = i0 + u * kWave + lane;
                 const int it = item < per_token ? item : per_token - 1;
-                is_v[u] = it >= per_head;
-                const int rem = it - (is_v[u] ? per_head : 0);
-                dst[u] = item < per_token ? row0 + ((int64_t)(rem >> 4) << (bshift + 4)) + (rem & (kRC - 1)) : -1;
-                v[u] = (is_v[u] ? vsrc : ksrc)[src0 + rem];
-            }
+                Chunk ch;
+                ch.is_v = it >= per_head;
+                const int rem = it - (ch.is_v ? per_head : 0);
+                ch.dst = item < per_token ? row0 + ((int64_t)(rem >> 4) << (bshift + 4)) + (rem & (kRC - 1)) : -1;
+                ch.v = (ch.is_v ? vsrc : ksrc)[src0 + rem];
+                return ch;
+            };
+            auto store = [&](const Chunk& ch) __attribute__((always_inline)) {
+                if (ch.dst >= 0) (ch.is_v ? vdst : kdst)[ch.dst] = ch.v;
+            };
+            static_assert(kRowChunks == 4, "four named chunks");
+            const Chunk c0 = load(0), c1 = load(1), c2 = load(2), c3 = load(3);
             asm volatile("" ::: "memory");   // the round's loads all issued before its first store
-#pragma unroll
-            for (int u = 0; u < kRowChunks; ++u)
-                if (dst[u] >= 0) (is_v[u] ? vdst : kdst)[dst[u]] = v[u];
+            store(c0);
+            store(c1);
+            store(c2);
+            store(c3);
         }
     }
 }
@@ -1738,7 +1749,7 @@ hipError_t launch_streamk_walk(const DecodeArgs& a_in, int group, int workers, h
         // other rows: up to 768 waves (a row or a few each), so that they are
         // done while the workers still scan lengths and fetch their first
         // tiles; with 256 waves (nine rows each on the 70B-shaped step) the
-        // step took 2 us longer, and the walk is HBM-bound either way
+        // step took 2 us longer
         if (!kFp8 && a.num_rows > 0) extra += a.num_rows < 768 ? a.num_rows : 768;
     }
     dim3 grid((unsigned)(workers + extra));
