@@ -120,3 +120,17 @@ def test_fused_graph_replays_match_eager(name):
     k2, v2 = two.pool_host()
     kf, vf = fused.pool_host()
     assert kf.tobytes() == k2.tobytes() and vf.tobytes() == v2.tobytes(), "pool after the replays differs"
+
+
+@pytest.mark.parametrize("B", [8, 64])
+def test_step_with_prefill_rows_other_block_sizes(B):
+    """paged_attention_decode_step at block sizes other than 16: the extra
+    waves that store the 2048-token prefill chunk split each slot with the
+    block size's shift.  Bitwise the two-call step, and the oracle."""
+    say(f"C3 (48 sequences) at B={B}: step with the prefill chunk vs two calls")
+    wl = kvgen.make_workload("C3", variant="sharp", poison=True, num_seqs=48, block_size=B)
+    assert wl.extra_tables.shape[0] == 1
+    ref = oracle.run_step(wl)
+    two, fused = _both(wl, partition_size=0)
+    _same(two, fused, f"C3/48/B{B}")
+    check_step(fused, wl, ref, label=f"C3/48/B{B} step")
