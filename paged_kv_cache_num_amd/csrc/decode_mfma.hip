@@ -1060,56 +1060,142 @@ __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x,
 // ---------------------------------------------------------------------------
 constexpr int kPrefixDepth = 2;   // prefix tiles are mostly cache hits: two in flight per wave
 
+// The walk of a prefix wave: nk tiles from tile b0 of the row, every one for
+// kPrefixSets sets of sixteen query columns (st[j] / qb[j]), so that one load
+// of a tile serves 16 * kPrefixSets columns.  Per tile the score MFMAs of all
+// sets run first, then the K half is refilled, the V operands repacked and the
+// V half refilled, then each set's softmax and P V.  Tiles come through the
+// plain walk's table mapping; past the end a refill repeats the last tile (an
+// L2 hit) and the repeated steps are fully masked (first token at L).
+__device__ __forceinline__ void prefix_walk(State (&st)[kPrefixSets], const bf16x8_t (&qb)[kPrefixSets][kKK],
+                                            const int32_t* row, int nk, int b0, int L, const WalkCtx& c) {
+    Tile tt[kPrefixDepth];
+    auto tile_ptrs = [&](int tv0, int tv1, int e, int k, const uint4*& kt, const uint4*& vt) {
+        uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane(tv0, k);
+        p0 = p0 < c.num_blocks ? p0 : c.num_blocks - 1;   // stay inside the pool whatever the table says
+        if (c.pair8) {
+            uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane(tv1, k);
+            p1 = p1 < c.num_blocks ? p1 : c.num_blocks - 1;
+            kt = c.kpool + (size_t)(c.n < 8 ? p0 : p1) * c.block_stride + c.head_off;
+            vt = c.vpool + (size_t)(c.r < 2 ? p0 : p1) * c.block_stride + c.head_off;
+        } else {
+            const size_t base = (size_t)p0 * c.block_stride + c.head_off +
+                                (size_t)(e & ((1 << c.sub_shift) - 1)) * (kTileTokens * kRC);
+            kt = c.kpool + base;
+            vt = c.vpool + base;
+        }
+    };
+    for (int k0 = 0; k0 < nk; k0 += 64) {
+        const int nc = min(64, nk - k0);
+        const int2 tv = tile_entries(row, b0 + k0 + c.lane, c.lane < nc, c);
+        const uint4 *kt, *vt;
+#pragma unroll
+        for (int s = 0; s < kPrefixDepth; ++s) {
+            const int k = min(s, nc - 1);
+            tile_ptrs(tv.x, tv.y, b0 + k0 + k, k, kt, vt);
+            load_k(tt[s], kt, c.k_off);
+            asm volatile("" : : : "memory");
+            load_v(tt[s], vt, c.v_off, true);
+            asm volatile("" : : : "memory");
+        }
+        for (int k = 0; k < nc; k += kPrefixDepth) {
+#pragma unroll
+            for (int s = 0; s < kPrefixDepth; ++s) {
+                const int kn = min(k + s + kPrefixDepth, nc - 1);
+                tile_ptrs(tv.x, tv.y, b0 + k0 + kn, kn, kt, vt);
+                __builtin_amdgcn_sched_barrier(0);
+                const int tok = k + s < nc ? (b0 + k0 + k + s) * kTileTokens : L;
+                f32x4_t sc[kPrefixSets];
+#pragma unroll
+                for (int j = 0; j < kPrefixSets; ++j) {
+                    sc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < kKK; ++kk)
+                        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tt[s].k[kk]),
+                                                                        qb[j][kk], sc[j], 0, 0, 0);
+                    asm volatile("" : "+v"(sc[j]) : : "memory");
+                }
+                load_k(tt[s], kt, c.k_off);
+                uint32_t ev[4][2], od[4][2];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t x0 = (&tt[s].v[0].x)[w], x1 = (&tt[s].v[1].x)[w];
+                    const uint32_t x2 = (&tt[s].v[2].x)[w], x3 = (&tt[s].v[3].x)[w];
+                    ev[w][0] = (x0 & 0xFFFFu) | (x1 << 16);
+                    ev[w][1] = (x2 & 0xFFFFu) | (x3 << 16);
+                    od[w][0] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+                    od[w][1] = (x2 >> 16) | (x3 & 0xFFFF0000u);
+                }
+                asm volatile("" : "+v"(ev[0][0]), "+v"(ev[0][1]), "+v"(ev[1][0]), "+v"(ev[1][1]), "+v"(ev[2][0]),
+                             "+v"(ev[2][1]), "+v"(ev[3][0]), "+v"(ev[3][1]), "+v"(od[0][0]), "+v"(od[0][1]),
+                             "+v"(od[1][0]), "+v"(od[1][1]), "+v"(od[2][0]), "+v"(od[2][1]), "+v"(od[3][0]),
+                             "+v"(od[3][1]) : : "memory");
+                load_v(tt[s], vt, c.v_off, true);
+#pragma unroll
+                for (int j = 0; j < kPrefixSets; ++j)
+                    softmax_pv<16>(st[j], sc[j], ev, od, tok, L, c.r, c.n, c.sl2, 1.0f);
+            }
+        }
+    }
+}
+
+// One prefix wave: (column group, KV head, part).  A column group is
+// 16 * kPrefixSets query columns; column n of set j is query head n % G of
+// sequence (group * kPrefixSets + j) * 16 / G + n / G (zero past the batch).
 template <int G, bool kAnyB>
 __device__ void prefix_wave(const DecodeArgs& a, int64_t idx) {
-    constexpr int kSeqs = 16 / G;   // sequences per column block
+    constexpr int kSeqs = 16 / G;   // sequences per set of sixteen columns
     const int Hkv = a.num_kv_heads;
-    const int blocks = (a.num_seqs * G + 15) / 16;
+    const int groups = ((a.num_seqs * G + 15) / 16 + kPrefixSets - 1) / kPrefixSets;
     const int kv = (int)(idx % Hkv);
-    const int qb = (int)((idx / Hkv) % blocks);
-    const int p = (int)(idx / ((int64_t)Hkv * blocks));
+    const int qg = (int)((idx / Hkv) % groups);
+    const int p = (int)(idx / ((int64_t)Hkv * groups));
     const int b0 = p * a.prefix_part_tiles;
     const int nk = min(a.prefix_part_tiles, a.shared_tiles - b0);   // >= 1: the host sizes the parts
 
     WalkCtx c = make_ctx<kAnyB, false>(a, kv);
-    c.keep_v = true;   // every column block reads these tiles
-    // column n: query head n % G of sequence qb * kSeqs + n / G (zero past the batch)
-    const int col_seq = qb * kSeqs + c.n / G;
-    const bool col_ok = col_seq < a.num_seqs;
-    const size_t col_row = (size_t)(col_ok ? col_seq : 0) * a.num_q_heads + (size_t)kv * G + c.n % G;
-    bf16x8_t qb_op[kKK];
-    const uint4* qrow = reinterpret_cast<const uint4*>(a.q) + col_row * kRC;
+    bf16x8_t qb_op[kPrefixSets][kKK];
+    State st[kPrefixSets];
 #pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) {
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (col_ok) x = qrow[kk * 4 + c.r];
-        qb_op[kk] = __builtin_bit_cast(bf16x8_t, x);
+    for (int j = 0; j < kPrefixSets; ++j) {
+        const int col_seq = (qg * kPrefixSets + j) * kSeqs + c.n / G;
+        const bool col_ok = col_seq < a.num_seqs;
+        const size_t col_row = (size_t)(col_ok ? col_seq : 0) * a.num_q_heads + (size_t)kv * G + c.n % G;
+        const uint4* qrow = reinterpret_cast<const uint4*>(a.q) + col_row * kRC;
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) {
+            uint4 x = make_uint4(0u, 0u, 0u, 0u);
+            if (col_ok) x = qrow[kk * 4 + c.r];
+            qb_op[j][kk] = __builtin_bit_cast(bf16x8_t, x);
+        }
+        init_state(st[j]);
     }
-    State st;
-    init_state(st);
-    AppendRow none;
-    none.active = false;
-    none.opens = false;
-    none.krow = none.vrow = nullptr;
-    typename TileOf<false>::type tt[kPrefixDepth];
     // every sequence covers the whole prefix: no position is masked
-    walk<16, kPrefixDepth, false>(st, tt, false, qb_op, a.tables, 1, nk, b0, a.shared_tiles * kTileTokens, c, none);
-    const float l_tot = total_l(st);
+    prefix_walk(st, qb_op, a.tables, nk, b0, a.shared_tiles * kTileTokens, c);
 
     // lane (r, n): outputs of columns 4r .. 4r+3, dims 8n .. 8n+7; (m, l) of column n
     const int slots = a.prefix_parts + 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = 4 * c.r + j;
-        const int sq = qb * kSeqs + col / G;
-        if (sq < a.num_seqs) {
-            const size_t row = (size_t)sq * a.num_q_heads + (size_t)kv * G + col % G;
-            float4* dst = reinterpret_cast<float4*>(a.ws_pacc + (row * slots + p) * kD + c.n * 8);
-            dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
-            dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
+    for (int j = 0; j < kPrefixSets; ++j) {
+        const float l_tot = total_l(st[j]);
+        const int seq0 = (qg * kPrefixSets + j) * kSeqs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int col = 4 * c.r + i;
+            const int sq = seq0 + col / G;
+            if (sq < a.num_seqs) {
+                const size_t row = (size_t)sq * a.num_q_heads + (size_t)kv * G + col % G;
+                float4* dst = reinterpret_cast<float4*>(a.ws_pacc + (row * slots + p) * kD + c.n * 8);
+                dst[0] = make_float4(st[j].o[0][i], st[j].o[1][i], st[j].o[2][i], st[j].o[3][i]);
+                dst[1] = make_float4(st[j].o[4][i], st[j].o[5][i], st[j].o[6][i], st[j].o[7][i]);
+            }
+        }
+        const int sq = seq0 + c.n / G;
+        if (c.r == 0 && sq < a.num_seqs) {
+            const size_t row = (size_t)sq * a.num_q_heads + (size_t)kv * G + c.n % G;
+            reinterpret_cast<float2*>(a.ws_pml)[row * slots + p] = make_float2(st[j].m, l_tot);
         }
     }
-    if (c.r == 0 && col_ok) reinterpret_cast<float2*>(a.ws_pml)[col_row * slots + p] = make_float2(st.m, l_tot);
 }
 
 template <int G, bool kAnyB, bool kFp8>
@@ -1736,8 +1822,8 @@ hipError_t launch_streamk_walk(const DecodeArgs& a_in, int group, int workers, h
     // (bf16: about 8 chunks per lane; FP8: about 4 rows per wave)
     int64_t extra = 0;
     a.append_waves = 0;
-    if (a.shared_tiles > 0) {   // the prefix walks: (column block, KV head, part)
-        extra = ((int64_t)a.num_seqs * group + 15) / 16 * a.num_kv_heads * a.prefix_parts;
+    if (a.shared_tiles > 0) {   // the prefix walks: (column group, KV head, part)
+        extra = prefix_column_groups(a.num_seqs, group) * a.num_kv_heads * a.prefix_parts;
     } else {
         if (a.k_append) {
             const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * (kFp8 ? 1 : kRC);

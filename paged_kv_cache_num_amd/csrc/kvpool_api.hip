@@ -143,8 +143,8 @@ SharedPlan plan_shared(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_he
     memset(&sp, 0, sizeof sp);
     sp.base = plan_decode(d, num_seqs, num_q_heads, max_context_len, 0);
     const int64_t group = num_q_heads / d.num_kv_heads;
-    const int64_t column_blocks = ((int64_t)num_seqs * group + 15) / 16 * d.num_kv_heads;
-    const int64_t want = ((int64_t)sp.base.workers / 2 + column_blocks - 1) / (column_blocks > 0 ? column_blocks : 1);
+    const int64_t column_groups = kvp::prefix_column_groups(num_seqs, group) * d.num_kv_heads;
+    const int64_t want = ((int64_t)sp.base.workers / 2 + column_groups - 1) / (column_groups > 0 ? column_groups : 1);
     int64_t parts = want < 1 ? 1 : (want > shared_tiles ? shared_tiles : want);
     sp.part_tiles = (int32_t)((shared_tiles + parts - 1) / parts);
     sp.parts = (int32_t)((shared_tiles + sp.part_tiles - 1) / sp.part_tiles);

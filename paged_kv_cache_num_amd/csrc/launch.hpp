@@ -10,6 +10,13 @@ constexpr int kBlockTokens = 16;   // block size of the fp32 / head_dim-64 decod
 constexpr int kTileTokens = 16;    // tokens per K/V tile of the bf16 decode kernels (the MFMA height)
 constexpr int kStreamKMaxSeqs = 1024;        // batch size up to which the balanced split is used
 constexpr int kStreamKDefaultWorkers = 1024; // worker count when no device can be queried
+// Shared-prefix decode: sets of sixteen query columns that one prefix wave
+// walks the prefix for (one load of a tile serves all of them).
+constexpr int kPrefixSets = 2;
+// Column groups of a batch: 16 * kPrefixSets query columns each.
+inline int64_t prefix_column_groups(int64_t num_seqs, int64_t group) {
+    return ((num_seqs * group + 15) / 16 + kPrefixSets - 1) / kPrefixSets;
+}
 
 struct ScatterArgs {
     void* k_layer;               // layer base of the K pool
