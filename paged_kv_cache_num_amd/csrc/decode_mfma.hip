@@ -1060,6 +1060,46 @@ __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x,
 // ---------------------------------------------------------------------------
 constexpr int kPrefixDepth = 2;   // prefix tiles are mostly cache hits: two in flight per wave
 
+// Finished states a worker keeps in LDS instead of storing them at once.  A
+// worker's stores and its loads share one in-order counter, so a store issued
+// between two walks holds up the next walk's tile waits until it has
+// completed; states of walks that another walk of the same worker follows
+// are therefore parked here and stored when the worker's work is done.  Only
+// lanes 16 * ceil(G / 4) and up hold no head's accumulators; (m, l) of head n
+// sit in lane n.  `tag` says where the state goes (kernel-specific).
+template <int G, int kSlots>
+struct Parked {
+    static constexpr int kLanes = 16 * ((G + 3) / 4);
+    f32x4_t o[kSlots][8][kLanes];
+    float2 ml[kSlots][16];
+    int4 tag[kSlots];
+
+    __device__ __forceinline__ void put(int i, const State& st, float l_tot, int4 t, int lane) {
+        if (lane < kLanes) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[i][e][lane] = st.o[e];
+        }
+        if (lane < 16) ml[i][lane] = make_float2(st.m, l_tot);
+        if (lane == 0) tag[i] = t;
+    }
+    // the state (with its whole softmax sum in l) and the tag, wave-uniform
+    __device__ __forceinline__ int4 get(int i, State& st, int lane) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st.o[e] = lane < kLanes ? o[i][e][lane] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const float2 v = lane < 16 ? ml[i][lane] : make_float2(0.0f, 0.0f);
+        st.m = v.x;
+        st.l = v.y;
+        const int4 t = tag[i];
+        return make_int4(__builtin_amdgcn_readfirstlane(t.x), __builtin_amdgcn_readfirstlane(t.y),
+                         __builtin_amdgcn_readfirstlane(t.z), __builtin_amdgcn_readfirstlane(t.w));
+    }
+};
+// parked states per worker: the balanced split (a few walks per worker), and
+// the fixed partitions (a few more, 16 KiB of LDS per worker)
+constexpr int kParkedPieces = 3;
+template <int G>
+constexpr int parked_partitions() { return 16384 / (16 * ((G + 3) / 4) * 128); }
+
 // The walk of a prefix wave: nk tiles from tile b0 of the row, every one for
 // kPrefixSets sets of sixteen query columns (st[j] / qb[j]), so that one load
 // of a tile serves 16 * kPrefixSets columns.  Per tile the score MFMAs of all
@@ -1287,6 +1327,64 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     int b = first_tile_at(at, a.piece_cost);
     t += a.piece_cost + b - at;
 
+    // The stores that end a piece: its output rows (a walk it covered whole),
+    // its state after a shared prefix, or its split record.  A piece that
+    // another piece of this slice follows is parked in LDS instead (Parked)
+    // and stored when the slice ends.
+    auto emit = [&](const State& so, float l_tot, int seq_, int kv_, bool whole_, bool first_)
+        __attribute__((always_inline)) {
+        const int r = lane >> 4, n = lane & 15;
+        if (whole_ && a.shared_tiles > 0) {   // after a shared prefix: a state for the fix-up to merge
+            const int slots = a.prefix_parts + 1;
+            const size_t row0 = (size_t)seq_ * a.num_q_heads + (size_t)kv_ * G;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * r + j;
+                if (h < G) {
+                    float4* dst = reinterpret_cast<float4*>(a.ws_pacc + ((row0 + h) * slots + a.prefix_parts) * kD +
+                                                            n * 8);
+                    dst[0] = make_float4(so.o[0][j], so.o[1][j], so.o[2][j], so.o[3][j]);
+                    dst[1] = make_float4(so.o[4][j], so.o[5][j], so.o[6][j], so.o[7][j]);
+                }
+            }
+            if (r == 0 && n < G)
+                reinterpret_cast<float2*>(a.ws_pml)[(row0 + n) * slots + a.prefix_parts] = make_float2(so.m, l_tot);
+        } else if (whole_) {
+            uint4* orow = reinterpret_cast<uint4*>(a.out) + ((size_t)seq_ * a.num_q_heads + (size_t)kv_ * G) * kRC;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * r + j;
+                const float lh = __shfl(l_tot, h & 15, kWave);
+                if (h < G) {
+                    const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+                    uint4 o;
+                    o.x = pack_bf16x2(so.o[0][j] * inv, so.o[1][j] * inv);
+                    o.y = pack_bf16x2(so.o[2][j] * inv, so.o[3][j] * inv);
+                    o.z = pack_bf16x2(so.o[4][j] * inv, so.o[5][j] * inv);
+                    o.w = pack_bf16x2(so.o[6][j] * inv, so.o[7][j] * inv);
+                    orow[h * kRC + n] = o;
+                }
+            }
+        } else {
+            float* rec = record_ptr<G>(a, 2 * w + (first_ ? 0 : 1));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * r + j;
+                if (h < G) {
+                    float4* dst = reinterpret_cast<float4*>(rec + h * kD + n * 8);
+                    dst[0] = make_float4(so.o[0][j], so.o[1][j], so.o[2][j], so.o[3][j]);
+                    dst[1] = make_float4(so.o[4][j], so.o[5][j], so.o[6][j], so.o[7][j]);
+                }
+            }
+            if (r == 0 && n < G) {
+                rec[G * kD + 2 * n] = so.m;
+                rec[G * kD + 2 * n + 1] = l_tot;
+            }
+        }
+    };
+    __shared__ Parked<G, kParkedPieces> parked;   // tag: (sequence, KV head, whole, first piece)
+    int nparked = 0;
+
     bool first_piece = true;
     bool pf_valid = false;   // table entries of the next piece fetched ahead
     int pf_seq = -1, pf_tv0 = 0, pf_tv1 = 0, pf_nb = 0;
@@ -1346,52 +1444,11 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
                                                app, use_pf, tv0_here, tv1_here, nxt);
         const float l_tot = total_l(st);
 
-        if (whole && a.shared_tiles > 0) {   // after a shared prefix: a state for the fix-up to merge
-            const int slots = a.prefix_parts + 1;
-            const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int h = 4 * c.r + j;
-                if (h < G) {
-                    float4* dst = reinterpret_cast<float4*>(a.ws_pacc + ((row0 + h) * slots + a.prefix_parts) * kD +
-                                                            c.n * 8);
-                    dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
-                    dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
-                }
-            }
-            if (c.r == 0 && c.n < G)
-                reinterpret_cast<float2*>(a.ws_pml)[(row0 + c.n) * slots + a.prefix_parts] = make_float2(st.m, l_tot);
-        } else if (whole) {
-            uint4* orow = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * kRC;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int h = 4 * c.r + j;
-                const float lh = __shfl(l_tot, h & 15, kWave);
-                if (h < G) {
-                    const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-                    uint4 o;
-                    o.x = pack_bf16x2(st.o[0][j] * inv, st.o[1][j] * inv);
-                    o.y = pack_bf16x2(st.o[2][j] * inv, st.o[3][j] * inv);
-                    o.z = pack_bf16x2(st.o[4][j] * inv, st.o[5][j] * inv);
-                    o.w = pack_bf16x2(st.o[6][j] * inv, st.o[7][j] * inv);
-                    orow[h * kRC + c.n] = o;
-                }
-            }
+        const bool more = t + n_here < t_end;   // another piece follows in this slice
+        if (more && nparked < kParkedPieces) {
+            parked.put(nparked++, st, l_tot, make_int4(seq, kv, whole ? 1 : 0, first_piece ? 1 : 0), lane);
         } else {
-            float* rec = record_ptr<G>(a, 2 * w + (first_piece ? 0 : 1));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int h = 4 * c.r + j;
-                if (h < G) {
-                    float4* dst = reinterpret_cast<float4*>(rec + h * kD + c.n * 8);
-                    dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
-                    dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
-                }
-            }
-            if (c.r == 0 && c.n < G) {
-                rec[G * kD + 2 * c.n] = st.m;
-                rec[G * kD + 2 * c.n + 1] = l_tot;
-            }
+            emit(st, l_tot, seq, kv, whole, first_piece);
         }
 
         // next piece: the next walk's first tile is piece_cost positions on
@@ -1411,6 +1468,11 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
             }
             t += a.piece_cost;
         }
+    }
+    for (int i = 0; i < nparked; ++i) {
+        State so;
+        const int4 tag = parked.get(i, so, lane);
+        emit(so, so.l, tag.x, tag.y, tag.z != 0, tag.w != 0);
     }
 }
 
@@ -1489,6 +1551,48 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
     int b = (int)(off - (int64_t)kv * nblk);
     b = (b + pt - 1) / pt * pt;   // the first partition that starts in this slice
 
+    // The stores that end a partition: the output rows (a context of one
+    // partition) or its state for the merge; parked in LDS while another
+    // partition of this slice follows (Parked).
+    auto emit = [&](const State& so, float l_tot, int seq_, int kv_, int part_, bool whole_)
+        __attribute__((always_inline)) {
+        const int r = lane >> 4, n = lane & 15;
+        if (whole_) {   // the whole context: the output itself
+            uint4* orow = reinterpret_cast<uint4*>(a.out) + ((size_t)seq_ * a.num_q_heads + (size_t)kv_ * G) * kRC;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * r + j;
+                const float lh = __shfl(l_tot, h & 15, kWave);
+                if (h < G) {
+                    const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+                    uint4 o;
+                    o.x = pack_bf16x2(so.o[0][j] * inv, so.o[1][j] * inv);
+                    o.y = pack_bf16x2(so.o[2][j] * inv, so.o[3][j] * inv);
+                    o.z = pack_bf16x2(so.o[4][j] * inv, so.o[5][j] * inv);
+                    o.w = pack_bf16x2(so.o[6][j] * inv, so.o[7][j] * inv);
+                    orow[h * kRC + n] = o;
+                }
+            }
+        } else {   // this partition's (m, l, unnormalised output) for the merge kernel
+            const size_t row0 = (size_t)seq_ * a.num_q_heads + (size_t)kv_ * G;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int h = 4 * r + j;
+                if (h < G) {
+                    const size_t slot = (row0 + h) * a.max_parts + part_;
+                    float4* dst = reinterpret_cast<float4*>(a.ws_acc + slot * kD + n * 8);
+                    dst[0] = make_float4(so.o[0][j], so.o[1][j], so.o[2][j], so.o[3][j]);
+                    dst[1] = make_float4(so.o[4][j], so.o[5][j], so.o[6][j], so.o[7][j]);
+                }
+            }
+            if (r == 0 && n < G)
+                reinterpret_cast<float2*>(a.ws_ml)[(row0 + n) * a.max_parts + part_] = make_float2(so.m, l_tot);
+        }
+    };
+    constexpr int kParked = parked_partitions<G>();
+    __shared__ Parked<G, kParked> parked;   // tag: (sequence, KV head, partition, whole context)
+    int nparked = 0;
+
     AppendRow none;
     none.active = false;
     none.opens = false;
@@ -1558,39 +1662,18 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
         primed = walk<G, kPartitionDepth, kFp8>(st, tt, primed && use_pf, qb, a.tables + (size_t)seq * a.max_blocks,
                                                 1, n_here, b, L, c, none, use_pf, tv0_here, tv1_here, nxt);
         const float l_tot = total_l(st);
-
-        if (nparts == 1) {   // the whole context: the output itself
-            uint4* orow = reinterpret_cast<uint4*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * kRC;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int h = 4 * c.r + j;
-                const float lh = __shfl(l_tot, h & 15, kWave);
-                if (h < G) {
-                    const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-                    uint4 o;
-                    o.x = pack_bf16x2(st.o[0][j] * inv, st.o[1][j] * inv);
-                    o.y = pack_bf16x2(st.o[2][j] * inv, st.o[3][j] * inv);
-                    o.z = pack_bf16x2(st.o[4][j] * inv, st.o[5][j] * inv);
-                    o.w = pack_bf16x2(st.o[6][j] * inv, st.o[7][j] * inv);
-                    orow[h * kRC + c.n] = o;
-                }
-            }
-        } else {   // this partition's (m, l, unnormalised output) for the merge kernel
-            const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int h = 4 * c.r + j;
-                if (h < G) {
-                    const size_t slot = (row0 + h) * a.max_parts + part;
-                    float4* dst = reinterpret_cast<float4*>(a.ws_acc + slot * kD + c.n * 8);
-                    dst[0] = make_float4(st.o[0][j], st.o[1][j], st.o[2][j], st.o[3][j]);
-                    dst[1] = make_float4(st.o[4][j], st.o[5][j], st.o[6][j], st.o[7][j]);
-                }
-            }
-            if (c.r == 0 && c.n < G)
-                reinterpret_cast<float2*>(a.ws_ml)[(row0 + c.n) * a.max_parts + part] = make_float2(st.m, l_tot);
-        }
+        // another partition of this slice follows (the next one starts here)
+        const bool more = seq_first + (int64_t)kv * nblk + min(b + pt, nblk) < t_hi;
+        if (more && nparked < kParked)
+            parked.put(nparked++, st, l_tot, make_int4(seq, kv, part, nparts == 1 ? 1 : 0), lane);
+        else
+            emit(st, l_tot, seq, kv, part, nparts == 1);
         b += pt;
+    }
+    for (int i = 0; i < nparked; ++i) {
+        State so;
+        const int4 tag = parked.get(i, so, lane);
+        emit(so, so.l, tag.x, tag.y, tag.z, tag.w != 0);
     }
 }
 
