@@ -206,26 +206,13 @@ __device__ __forceinline__ bf16x8_t as_operand(uint32_t a, uint32_t b, uint32_t 
 // to pair the same token in A and B, so lane (r, n) puts P_hi and P_lo of
 // head n, tokens 4r..4r+3 (already where the score MFMA left them) in its
 // eight A positions and dim 8n + e of the same four tokens, twice, in its
-// eight B positions.
-template <int G>
-__device__ __forceinline__ void softmax_pv(State& st, f32x4_t s, uint32_t (&ev)[4][2], uint32_t (&od)[4][2],
-                                           int tok0, int L, int r, int n, float sl2, float vscale) {
-    if (tok0 + kTileTokens > L) {   // last, partially filled tile (wave-uniform branch)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (tok0 + 4 * r + i >= L) {
-                s[i] = -INFINITY;
-                // stale slots may hold NaN; P is 0 there
-                const uint32_t keep = (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    ev[w][i >> 1] &= keep;
-                    od[w][i >> 1] &= keep;
-                }
-            }
-        }
-    }
-
+// eight B positions.  softmax_pv_core takes the tile once it is masked, with
+// vop(e) giving the B operand of the product for dims 8n + e (built from ev /
+// od by softmax_pv; built once per tile and shared by several query column
+// sets in the prefix walk).
+template <int G, class VOp>
+__device__ __forceinline__ void softmax_pv_core(State& st, const f32x4_t& s, VOp vop, int r, int n, float sl2,
+                                                float vscale) {
     // This row's max of head n.  The reference m is shared by the four rows
     // (their P meet in one MFMA), so it only moves, to the block max over all
     // rows, when some row would exceed it by more than 2^kLazy.
@@ -260,12 +247,36 @@ __device__ __forceinline__ void softmax_pv(State& st, f32x4_t s, uint32_t (&ev)[
     const uint32_t l23 = bf16_pair(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
     const bf16x8_t pa = as_operand(h01, h23, l01, l23);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        st.o[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            pa, as_operand(ev[w][0], ev[w][1], ev[w][0], ev[w][1]), st.o[2 * w], 0, 0, 0);
-        st.o[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            pa, as_operand(od[w][0], od[w][1], od[w][0], od[w][1]), st.o[2 * w + 1], 0, 0, 0);
+    for (int e = 0; e < 8; ++e) st.o[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vop(e), st.o[e], 0, 0, 0);
+}
+
+template <int G>
+__device__ __forceinline__ void softmax_pv(State& st, f32x4_t s, uint32_t (&ev)[4][2], uint32_t (&od)[4][2],
+                                           int tok0, int L, int r, int n, float sl2, float vscale) {
+    if (tok0 + kTileTokens > L) {   // last, partially filled tile (wave-uniform branch)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (tok0 + 4 * r + i >= L) {
+                s[i] = -INFINITY;
+                // stale slots may hold NaN; P is 0 there
+                const uint32_t keep = (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    ev[w][i >> 1] &= keep;
+                    od[w][i >> 1] &= keep;
+                }
+            }
+        }
     }
+
+    softmax_pv_core<G>(
+        st, s,
+        [&](int e) __attribute__((always_inline)) {
+            const int w = e >> 1;
+            return (e & 1) ? as_operand(od[w][0], od[w][1], od[w][0], od[w][1])
+                           : as_operand(ev[w][0], ev[w][1], ev[w][0], ev[w][1]);
+        },
+        r, n, sl2, vscale);
 }
 
 // One bf16 tile: scores on MFMA, then the steps of softmax_pv written out in
@@ -1058,7 +1069,6 @@ __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x,
 // takes KV head idx mod H_kv, so with eight KV heads the waves of one XCD
 // share one head's prefix tiles in its L2.
 // ---------------------------------------------------------------------------
-constexpr int kPrefixDepth = 2;   // prefix tiles are mostly cache hits: two in flight per wave
 
 // Finished states a worker keeps in LDS instead of storing them at once.  A
 // worker's stores and its loads share one in-order counter, so a store issued
@@ -1102,14 +1112,20 @@ constexpr int parked_partitions() { return 16384 / (16 * ((G + 3) / 4) * 128); }
 
 // The walk of a prefix wave: nk tiles from tile b0 of the row, every one for
 // kPrefixSets sets of sixteen query columns (st[j] / qb[j]), so that one load
-// of a tile serves 16 * kPrefixSets columns.  Per tile the score MFMAs of all
-// sets run first, then the K half is refilled, the V operands repacked and the
-// V half refilled, then each set's softmax and P V.  Tiles come through the
-// plain walk's table mapping; past the end a refill repeats the last tile (an
-// L2 hit) and the repeated steps are fully masked (first token at L).
+// of a tile serves 16 * kPrefixSets columns.  One tile is in registers: per
+// tile the score MFMAs of all sets run first, then the K half is refilled
+// with the next tile, the V half is repacked into the eight P V operands
+// (once for all sets) and refilled, then each set's softmax and P V.  Every
+// position of the prefix is below every length, so nothing is masked.  The
+// walk is bound by its own instructions, not by the loads (one tile ahead
+// measured as fast as two to four), so the registers a second tile would
+// take hold the operands instead; the last refill repeats the last tile.
+// The walk of each chunk of up to 64 tiles starts `rot` tiles into it and
+// wraps around: the waves that read the same tiles for other columns start at
+// other tiles.
 __device__ __forceinline__ void prefix_walk(State (&st)[kPrefixSets], const bf16x8_t (&qb)[kPrefixSets][kKK],
-                                            const int32_t* row, int nk, int b0, int L, const WalkCtx& c) {
-    Tile tt[kPrefixDepth];
+                                            const int32_t* row, int nk, int b0, int rot, const WalkCtx& c) {
+    Tile tt;
     auto tile_ptrs = [&](int tv0, int tv1, int e, int k, const uint4*& kt, const uint4*& vt) {
         uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane(tv0, k);
         p0 = p0 < c.num_blocks ? p0 : c.num_blocks - 1;   // stay inside the pool whatever the table says
@@ -1127,54 +1143,48 @@ __device__ __forceinline__ void prefix_walk(State (&st)[kPrefixSets], const bf16
     };
     for (int k0 = 0; k0 < nk; k0 += 64) {
         const int nc = min(64, nk - k0);
+        const int r0 = rot % nc;
+        auto rk = [&](int k) { return k + r0 < nc ? k + r0 : k + r0 - nc; };   // step k (< nc) -> its tile
         const int2 tv = tile_entries(row, b0 + k0 + c.lane, c.lane < nc, c);
         const uint4 *kt, *vt;
+        tile_ptrs(tv.x, tv.y, b0 + k0 + rk(0), rk(0), kt, vt);
+        load_k(tt, kt, c.k_off);
+        asm volatile("" : : : "memory");
+        load_v(tt, vt, c.v_off, true);
+        asm volatile("" : : : "memory");
+        for (int k = 0; k < nc; ++k) {
+            const int kn = rk(min(k + 1, nc - 1));
+            tile_ptrs(tv.x, tv.y, b0 + k0 + kn, kn, kt, vt);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4_t sc[kPrefixSets];
 #pragma unroll
-        for (int s = 0; s < kPrefixDepth; ++s) {
-            const int k = min(s, nc - 1);
-            tile_ptrs(tv.x, tv.y, b0 + k0 + k, k, kt, vt);
-            load_k(tt[s], kt, c.k_off);
-            asm volatile("" : : : "memory");
-            load_v(tt[s], vt, c.v_off, true);
-            asm volatile("" : : : "memory");
-        }
-        for (int k = 0; k < nc; k += kPrefixDepth) {
+            for (int j = 0; j < kPrefixSets; ++j) {
+                sc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < kPrefixDepth; ++s) {
-                const int kn = min(k + s + kPrefixDepth, nc - 1);
-                tile_ptrs(tv.x, tv.y, b0 + k0 + kn, kn, kt, vt);
-                __builtin_amdgcn_sched_barrier(0);
-                const int tok = k + s < nc ? (b0 + k0 + k + s) * kTileTokens : L;
-                f32x4_t sc[kPrefixSets];
-#pragma unroll
-                for (int j = 0; j < kPrefixSets; ++j) {
-                    sc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int kk = 0; kk < kKK; ++kk)
-                        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tt[s].k[kk]),
-                                                                        qb[j][kk], sc[j], 0, 0, 0);
-                    asm volatile("" : "+v"(sc[j]) : : "memory");
-                }
-                load_k(tt[s], kt, c.k_off);
-                uint32_t ev[4][2], od[4][2];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t x0 = (&tt[s].v[0].x)[w], x1 = (&tt[s].v[1].x)[w];
-                    const uint32_t x2 = (&tt[s].v[2].x)[w], x3 = (&tt[s].v[3].x)[w];
-                    ev[w][0] = (x0 & 0xFFFFu) | (x1 << 16);
-                    ev[w][1] = (x2 & 0xFFFFu) | (x3 << 16);
-                    od[w][0] = (x0 >> 16) | (x1 & 0xFFFF0000u);
-                    od[w][1] = (x2 >> 16) | (x3 & 0xFFFF0000u);
-                }
-                asm volatile("" : "+v"(ev[0][0]), "+v"(ev[0][1]), "+v"(ev[1][0]), "+v"(ev[1][1]), "+v"(ev[2][0]),
-                             "+v"(ev[2][1]), "+v"(ev[3][0]), "+v"(ev[3][1]), "+v"(od[0][0]), "+v"(od[0][1]),
-                             "+v"(od[1][0]), "+v"(od[1][1]), "+v"(od[2][0]), "+v"(od[2][1]), "+v"(od[3][0]),
-                             "+v"(od[3][1]) : : "memory");
-                load_v(tt[s], vt, c.v_off, true);
-#pragma unroll
-                for (int j = 0; j < kPrefixSets; ++j)
-                    softmax_pv<16>(st[j], sc[j], ev, od, tok, L, c.r, c.n, c.sl2, 1.0f);
+                for (int kk = 0; kk < kKK; ++kk)
+                    sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tt.k[kk]), qb[j][kk],
+                                                                    sc[j], 0, 0, 0);
+                asm volatile("" : "+v"(sc[j]) : : "memory");
             }
+            load_k(tt, kt, c.k_off);
+            // operand e: dim 8n + e of tokens 4r..4r+3, twice (P_hi and P_lo positions)
+            bf16x8_t vop[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x0 = (&tt.v[0].x)[w], x1 = (&tt.v[1].x)[w];
+                const uint32_t x2 = (&tt.v[2].x)[w], x3 = (&tt.v[3].x)[w];
+                const uint32_t e0 = (x0 & 0xFFFFu) | (x1 << 16), e1 = (x2 & 0xFFFFu) | (x3 << 16);
+                const uint32_t o0 = (x0 >> 16) | (x1 & 0xFFFF0000u), o1 = (x2 >> 16) | (x3 & 0xFFFF0000u);
+                vop[2 * w] = as_operand(e0, e1, e0, e1);
+                vop[2 * w + 1] = as_operand(o0, o1, o0, o1);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(vop[e]) : : "memory");
+            load_v(tt, vt, c.v_off, true);
+#pragma unroll
+            for (int j = 0; j < kPrefixSets; ++j)
+                softmax_pv_core<16>(st[j], sc[j], [&](int e) __attribute__((always_inline)) { return vop[e]; }, c.r,
+                                    c.n, c.sl2, 1.0f);
         }
     }
 }
@@ -1211,7 +1221,7 @@ __device__ void prefix_wave(const DecodeArgs& a, int64_t idx) {
         init_state(st[j]);
     }
     // every sequence covers the whole prefix: no position is masked
-    prefix_walk(st, qb_op, a.tables, nk, b0, a.shared_tiles * kTileTokens, c);
+    prefix_walk(st, qb_op, a.tables, nk, b0, qg, c);
 
     // lane (r, n): outputs of columns 4r .. 4r+3, dims 8n .. 8n+7; (m, l) of column n
     const int slots = a.prefix_parts + 1;
