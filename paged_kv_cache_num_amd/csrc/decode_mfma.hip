@@ -77,6 +77,7 @@ constexpr float kLazy = 8.0f;      // log2 headroom before the running max is mo
 // slices does: more requests in flight per wave than the memory system turns
 // into bandwidth.  Fixed partitions, whose walks are short: two (one measured
 // 2% slower on the long-context batch).
+constexpr int kFixupMinWaves = 1024;   // fix-up grids are split over query heads up to this many waves
 constexpr int kBalancedDepth = 1;
 constexpr int kPartitionDepth = 2;
 
@@ -1693,22 +1694,28 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
 // states its slices left.  With fewer tiles than workers some slices are
 // empty; they left nothing and are skipped.
 //
-// One wave: lanes first read the (m, l) pairs of up to 64 records at once and
-// reduce them across the wave; then each lane sums two dims of every head
-// over the records, several records' loads in flight at a time.
-template <int G>
+// One wave per GH of the G query heads: lanes first read the (m, l) pairs of
+// up to 64 records at once and reduce them across the wave; then each lane
+// sums two dims of each of its heads over the records, several records'
+// loads in flight at a time.  Splitting a pair's heads over G / GH waves
+// shortens each wave's chain of dependent steps when there are few pairs
+// (see launch_streamk_fixup).
+template <int G, int GH>
 __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int num_workers) {
-    const int kv = blockIdx.x;
+    static_assert(G % GH == 0, "a wave takes GH of the group's G heads");
+    const int kv = blockIdx.x / (G / GH);
+    const int h0 = (blockIdx.x % (G / GH)) * GH;   // the wave's first head within the group
     const int seq = blockIdx.y;
     const int lane = threadIdx.x;
     // the length and the two prefix sums are independent: one memory round trip for all three
     const int L_all = clamp_len(a.lens[seq], a.max_context);
     const int64_t T = a.ws_prefix[a.num_seqs];
     const int64_t first_tile = a.ws_prefix[seq];
-    uint32_t* out = reinterpret_cast<uint32_t*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G) * (kD / 2);
+    uint32_t* out =
+        reinterpret_cast<uint32_t*>(a.out) + ((size_t)seq * a.num_q_heads + (size_t)kv * G + h0) * (kD / 2);
     if (L_all == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) out[h * (kD / 2) + lane] = 0u;
+        for (int h = 0; h < GH; ++h) out[h * (kD / 2) + lane] = 0u;
         return;
     }
     // with a shared prefix the balanced walk covered only the tokens after it
@@ -1743,27 +1750,27 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     // order, kU records' loads in flight at a time, and stops after the last
     // record (a wave-uniform test: most pairs have two or three records).
     constexpr int kU = 8;
-    float M[G], den[G], n0[G], n1[G];
+    float M[GH], den[GH], n0[GH], n1[GH];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < GH; ++h) {
         M[h] = -INFINITY;
         den[h] = n0[h] = n1[h] = 0.0f;
     }
     const int d = lane * 2;
     if (shared) {
         // the prefix parts, then (when one slice held the rest whole) its state,
-        // in slot order; each lane two dims of every head
+        // in slot order; each lane two dims of each of its heads
         const int slots = a.prefix_parts + 1;
         const int nslot = a.prefix_parts + (nblk > 0 && w0 == w1 ? 1 : 0);
-        const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G;
-        constexpr int kUP = 32 / G;   // slots in flight per batch (128 registers of loads)
+        const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G + h0;
+        constexpr int kUP = 32 / GH;   // slots in flight per batch (128 registers of loads)
         for (int p0 = 0; p0 < nslot; p0 += kUP) {
-            float2 ml[kUP][G], x[kUP][G];
+            float2 ml[kUP][GH], x[kUP][GH];
 #pragma unroll
             for (int u = 0; u < kUP; ++u) {
                 const bool live = p0 + u < nslot;   // wave-uniform
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
+                for (int h = 0; h < GH; ++h) {
                     const size_t slot = (row0 + h) * slots + (live ? p0 + u : 0);
                     ml[u][h] = live ? reinterpret_cast<const float2*>(a.ws_pml)[slot] : make_float2(-INFINITY, 0.0f);
                     x[u][h] = live ? *reinterpret_cast<const float2*>(a.ws_pacc + slot * kD + d)
@@ -1771,7 +1778,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
                 }
             }
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
+            for (int h = 0; h < GH; ++h) {
                 float mb = M[h];
 #pragma unroll
                 for (int u = 0; u < kUP; ++u) mb = fmaxf(mb, ml[u][h].x);
@@ -1793,34 +1800,34 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     for (int j0 = 0; j0 < nrec; j0 += kWave) {
         const int cnt = min(kWave, nrec - j0);
         const int64_t slot = lane < cnt ? slot_of(j0 + lane) : -1;
-        float m_j[G], l_j[G], f_j[G];
+        float m_j[GH], l_j[GH], f_j[GH];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
+        for (int h = 0; h < GH; ++h) {
             m_j[h] = -INFINITY;
             l_j[h] = 0.0f;
         }
         if (slot >= 0) {
-            const float* ml = record_ptr<G>(a, slot) + G * kD;
+            const float* ml = record_ptr<G>(a, slot) + G * kD + 2 * h0;
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
+            for (int h = 0; h < GH; ++h) {
                 m_j[h] = ml[2 * h];
                 l_j[h] = ml[2 * h + 1];
             }
         }
         for (int jj = 0; jj < cnt; jj += kU) {
-            float2 x[kU][G];
+            float2 x[kU][GH];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int64_t sl = readlane64(slot, min(jj + u, cnt - 1));
                 const bool live = jj + u < cnt && sl >= 0;   // wave-uniform
-                const float* rec = record_ptr<G>(a, live ? sl : 0);
+                const float* rec = record_ptr<G>(a, live ? sl : 0) + h0 * kD;
 #pragma unroll
-                for (int h = 0; h < G; ++h)
+                for (int h = 0; h < GH; ++h)
                     x[u][h] = live ? *reinterpret_cast<const float2*>(rec + h * kD + d) : make_float2(0.0f, 0.0f);
             }
             if (jj == 0) {   // the block's weights, while the first loads are in flight
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
+                for (int h = 0; h < GH; ++h) {
                     const float m_new = fmaxf(M[h], wave_max(m_j[h]));
                     const float corr = fast_exp2(M[h] - safe_ref(m_new));   // 0 for the first block
                     n0[h] *= corr;
@@ -1838,7 +1845,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
             for (int u = 0; u < kU; ++u) {
                 if (jj + u < cnt) {   // wave-uniform
 #pragma unroll
-                    for (int h = 0; h < G; ++h) {
+                    for (int h = 0; h < GH; ++h) {
                         const float f = readlane_f(f_j[h], jj + u);
                         n0[h] = fmaf(x[u][h].x, f, n0[h]);
                         n1[h] = fmaf(x[u][h].y, f, n1[h]);
@@ -1848,7 +1855,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
         }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < GH; ++h) {
         const float inv = den[h] > 0.0f ? 1.0f / den[h] : 0.0f;
         out[h * (kD / 2) + lane] = pack_bf16x2(n0[h] * inv, n1[h] * inv);
     }
@@ -1958,12 +1965,27 @@ hipError_t launch_streamk_walk(const DecodeArgs& a_in, int group, int workers, h
 // The fix-up after the walk: merges the records of (sequence, KV head) pairs
 // split between workers (and, with a shared prefix, the prefix states).
 hipError_t launch_streamk_fixup(const DecodeArgs& a, int group, int workers, hipStream_t stream) {
-    dim3 fix((unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    switch (group) {
-        case 1: streamk_fixup_kernel<1><<<fix, kWave, 0, stream>>>(a, workers); break;
-        case 2: streamk_fixup_kernel<2><<<fix, kWave, 0, stream>>>(a, workers); break;
-        case 4: streamk_fixup_kernel<4><<<fix, kWave, 0, stream>>>(a, workers); break;
-        case 8: streamk_fixup_kernel<8><<<fix, kWave, 0, stream>>>(a, workers); break;
+    // GH query heads per wave: the pair's heads go to several waves while
+    // the grid would hold fewer than kFixupMinWaves (measured, same box:
+    // 70B TP-8 shard, 256 pairs of 8 heads, 54.0 -> 49.5 us per call with two
+    // heads per wave; 8B shape 103.2 -> 102.5 us; batches of 1024 pairs or
+    // more run slower split: 70B shape 274 -> 275 us, prefix sharing 45.4 ->
+    // 46.3 us)
+    const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+    int gh = group;
+    while (gh > 1 && pairs * (group / gh) < kFixupMinWaves) gh /= 2;
+    const dim3 grid((unsigned)(a.num_kv_heads * (group / gh)), (unsigned)a.num_seqs);
+    switch (group * 16 + gh) {
+        case 1 * 16 + 1: streamk_fixup_kernel<1, 1><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 2 * 16 + 1: streamk_fixup_kernel<2, 1><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 2 * 16 + 2: streamk_fixup_kernel<2, 2><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 4 * 16 + 1: streamk_fixup_kernel<4, 1><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 4 * 16 + 2: streamk_fixup_kernel<4, 2><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 4 * 16 + 4: streamk_fixup_kernel<4, 4><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 8 * 16 + 1: streamk_fixup_kernel<8, 1><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 8 * 16 + 2: streamk_fixup_kernel<8, 2><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 8 * 16 + 4: streamk_fixup_kernel<8, 4><<<grid, kWave, 0, stream>>>(a, workers); break;
+        case 8 * 16 + 8: streamk_fixup_kernel<8, 8><<<grid, kWave, 0, stream>>>(a, workers); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
