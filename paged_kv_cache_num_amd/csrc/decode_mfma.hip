@@ -1757,50 +1757,14 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
         den[h] = n0[h] = n1[h] = 0.0f;
     }
     const int d = lane * 2;
-    if (shared) {
-        // the prefix parts, then (when one slice held the rest whole) its state,
-        // in slot order; each lane two dims of each of its heads
-        const int slots = a.prefix_parts + 1;
-        const int nslot = a.prefix_parts + (nblk > 0 && w0 == w1 ? 1 : 0);
-        const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G + h0;
-        constexpr int kUP = 32 / GH;   // slots in flight per batch (128 registers of loads)
-        for (int p0 = 0; p0 < nslot; p0 += kUP) {
-            float2 ml[kUP][GH], x[kUP][GH];
-#pragma unroll
-            for (int u = 0; u < kUP; ++u) {
-                const bool live = p0 + u < nslot;   // wave-uniform
-#pragma unroll
-                for (int h = 0; h < GH; ++h) {
-                    const size_t slot = (row0 + h) * slots + (live ? p0 + u : 0);
-                    ml[u][h] = live ? reinterpret_cast<const float2*>(a.ws_pml)[slot] : make_float2(-INFINITY, 0.0f);
-                    x[u][h] = live ? *reinterpret_cast<const float2*>(a.ws_pacc + slot * kD + d)
-                                   : make_float2(0.0f, 0.0f);
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                float mb = M[h];
-#pragma unroll
-                for (int u = 0; u < kUP; ++u) mb = fmaxf(mb, ml[u][h].x);
-                const float corr = fast_exp2(M[h] - safe_ref(mb));   // 0 for the first batch
-                n0[h] *= corr;
-                n1[h] *= corr;
-                den[h] *= corr;
-                M[h] = mb;
-#pragma unroll
-                for (int u = 0; u < kUP; ++u) {
-                    const float f = fast_exp2(ml[u][h].x - safe_ref(mb));   // 0 for an absent slot
-                    den[h] = fmaf(ml[u][h].y, f, den[h]);
-                    n0[h] = fmaf(x[u][h].x, f, n0[h]);
-                    n1[h] = fmaf(x[u][h].y, f, n1[h]);
-                }
-            }
-        }
-    }
-    for (int j0 = 0; j0 < nrec; j0 += kWave) {
-        const int cnt = min(kWave, nrec - j0);
-        const int64_t slot = lane < cnt ? slot_of(j0 + lane) : -1;
-        float m_j[GH], l_j[GH], f_j[GH];
+    // The first 64 records' (m, l) pairs and the first kU records' partial
+    // outputs are loaded before anything is merged: with a shared prefix their
+    // round trip overlaps the prefix states' one.
+    int cnt = min(kWave, nrec);
+    int64_t slot = lane < cnt ? slot_of(lane) : -1;
+    float m_j[GH], l_j[GH], f_j[GH];
+    float2 x[kU][GH];
+    auto load_ml = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
             m_j[h] = -INFINITY;
@@ -1814,17 +1778,70 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
                 l_j[h] = ml[2 * h + 1];
             }
         }
-        for (int jj = 0; jj < cnt; jj += kU) {
-            float2 x[kU][GH];
+    };
+    auto load_x = [&](int jj) __attribute__((always_inline)) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int64_t sl = readlane64(slot, min(jj + u, cnt - 1));
-                const bool live = jj + u < cnt && sl >= 0;   // wave-uniform
-                const float* rec = record_ptr<G>(a, live ? sl : 0) + h0 * kD;
+        for (int u = 0; u < kU; ++u) {
+            const int64_t sl = readlane64(slot, min(jj + u, cnt - 1));
+            const bool live = jj + u < cnt && sl >= 0;   // wave-uniform
+            const float* rec = record_ptr<G>(a, live ? sl : 0) + h0 * kD;
 #pragma unroll
-                for (int h = 0; h < GH; ++h)
-                    x[u][h] = live ? *reinterpret_cast<const float2*>(rec + h * kD + d) : make_float2(0.0f, 0.0f);
+            for (int h = 0; h < GH; ++h)
+                x[u][h] = live ? *reinterpret_cast<const float2*>(rec + h * kD + d) : make_float2(0.0f, 0.0f);
+        }
+    };
+    if (nrec > 0) {
+        load_ml();
+        load_x(0);
+    }
+    if (shared) {
+        // the prefix parts, then (when one slice held the rest whole) its state,
+        // in slot order; each lane two dims of each of its heads
+        const int slots = a.prefix_parts + 1;
+        const int nslot = a.prefix_parts + (nblk > 0 && w0 == w1 ? 1 : 0);
+        const size_t row0 = (size_t)seq * a.num_q_heads + (size_t)kv * G + h0;
+        constexpr int kUP = 32 / GH;   // slots in flight per batch (128 registers of loads)
+        for (int p0 = 0; p0 < nslot; p0 += kUP) {
+            float2 pml[kUP][GH], px[kUP][GH];
+#pragma unroll
+            for (int u = 0; u < kUP; ++u) {
+                const bool live = p0 + u < nslot;   // wave-uniform
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    const size_t ps = (row0 + h) * slots + (live ? p0 + u : 0);
+                    pml[u][h] = live ? reinterpret_cast<const float2*>(a.ws_pml)[ps] : make_float2(-INFINITY, 0.0f);
+                    px[u][h] = live ? *reinterpret_cast<const float2*>(a.ws_pacc + ps * kD + d)
+                                    : make_float2(0.0f, 0.0f);
+                }
             }
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                float mb = M[h];
+#pragma unroll
+                for (int u = 0; u < kUP; ++u) mb = fmaxf(mb, pml[u][h].x);
+                const float corr = fast_exp2(M[h] - safe_ref(mb));   // 0 for the first batch
+                n0[h] *= corr;
+                n1[h] *= corr;
+                den[h] *= corr;
+                M[h] = mb;
+#pragma unroll
+                for (int u = 0; u < kUP; ++u) {
+                    const float f = fast_exp2(pml[u][h].x - safe_ref(mb));   // 0 for an absent slot
+                    den[h] = fmaf(pml[u][h].y, f, den[h]);
+                    n0[h] = fmaf(px[u][h].x, f, n0[h]);
+                    n1[h] = fmaf(px[u][h].y, f, n1[h]);
+                }
+            }
+        }
+    }
+    for (int j0 = 0; j0 < nrec; j0 += kWave) {
+        if (j0 > 0) {   // the next 64 records (the first block's loads were issued above)
+            cnt = min(kWave, nrec - j0);
+            slot = lane < cnt ? slot_of(j0 + lane) : -1;
+            load_ml();
+        }
+        for (int jj = 0; jj < cnt; jj += kU) {
+            if (j0 > 0 || jj > 0) load_x(jj);
             if (jj == 0) {   // the block's weights, while the first loads are in flight
 #pragma unroll
                 for (int h = 0; h < GH; ++h) {
