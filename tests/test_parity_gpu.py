@@ -270,3 +270,41 @@ def test_large_ragged_scatter_bit_exact(T):
     torch.cuda.synchronize()
     assert to_host(pool.k, "bf16").tobytes() == want_k.tobytes()
     assert to_host(pool.v, "bf16").tobytes() == want_v.tobytes()
+
+
+# The fix-up gives each wave GH of a (sequence, KV head) pair's G query heads,
+# GH halved from G while the grid would hold fewer than 1024 waves.  One case
+# per (G, GH) the host can pick, with lengths that split every walk over
+# several workers' records: (Hq, Hkv, sequences, GH expected).
+FIXUP_SPLITS = [
+    (8, 8, 16, 1),      # G = 1
+    (16, 8, 32, 1),     # G = 2: 256 pairs
+    (16, 8, 128, 2),    #        1024 pairs
+    (32, 8, 16, 1),     # G = 4: 128 pairs
+    (32, 8, 64, 2),     #        512 pairs
+    (32, 8, 128, 4),    #        1024 pairs
+    (64, 8, 8, 1),      # G = 8: 64 pairs
+    (64, 8, 32, 2),     #        256 pairs
+    (64, 8, 64, 4),     #        512 pairs
+    (64, 8, 128, 8),    #        1024 pairs
+]
+
+
+@pytest.mark.parametrize("hq,hkv,num_seqs,gh", FIXUP_SPLITS)
+def test_fixup_heads_per_wave(hq, hkv, num_seqs, gh):
+    g = hq // hkv
+    pairs = num_seqs * hkv
+    expect = g
+    while expect > 1 and pairs * (g // expect) < 1024:
+        expect //= 2
+    assert expect == gh, "the case no longer hits the heads-per-wave it is meant for"
+    rng = np.random.default_rng(1000 + 10 * g + num_seqs)
+    lengths = rng.integers(16, 1200, size=num_seqs).astype(np.int32)
+    lengths[0] = 1   # a single-token walk among the split ones
+    say(f"fix-up G={g} GH={gh}: Hq={hq} Hkv={hkv} S={num_seqs} lengths {int(lengths.min())}..{int(lengths.max())}")
+    for variant in ("sharp", "hot"):
+        wl = kvgen.custom_workload(lengths=lengths, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
+                                   dtype="bf16", seed=31 + g, variant=variant, poison=True)
+        ref = oracle.run_step(wl)
+        step = run_gpu(wl, partition_size=0)
+        check_step(step, wl, ref, check_pool=False, label=f"fix-up G={g} GH={gh}/{variant}")
