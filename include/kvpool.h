@@ -348,10 +348,13 @@ kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out
  *   with num_seqs = 0 only the rows are stored.
  * Precondition: no slot of row_slots lies in a block that the attention reads
  * (named by sequence i's table within its first L_i positions) or that a
- * decode row is appended to.  In the balanced mode with a bf16 pool the rows
- * are stored by extra waves of the attention's launch, each lane moving
- * several 16-byte chunks (one kernel, then the fix-up); otherwise the scatter
- * kernel runs first.
+ * decode row is appended to.  In the balanced mode the rows are stored by
+ * extra waves of the attention's launch (one kernel, then the fix-up): for a
+ * bf16 pool each lane moves several 16-byte chunks; for an FP8 pool a wave
+ * takes sixteen rows of one KV head, sets the scales of the blocks whose row 0
+ * they hold from every row this call puts into those blocks and stores those
+ * blocks' codes, and quantizes any other row with its block's stored scale.
+ * In the other modes the scatter kernels run first.
  */
 kv_status paged_attention_decode_step(kv_pool_t pool, int32_t layer, void* out, const void* q, const void* k_new,
                                       const void* v_new, const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -57,6 +57,7 @@
 
 #include "device_common.hpp"
 #include "fp8.hpp"
+#include "fp8_rows.hpp"
 #include "launch.hpp"
 #include "split.hpp"
 #include "table_index.hpp"
@@ -1026,30 +1027,89 @@ __device__ __forceinline__ void rows_scatter_waves(const DecodeArgs& a, int64_t 
     }
 }
 
-// The same for FP8 pools: one (sequence, {K,V}, KV head) row per wave and
-// step, quantized with its block's scale; a row at position 0 of its block
-// sets that scale first (fp8_store_row).
+// The same for FP8 pools: (sequence, {K,V}, KV head) rows, quantized with
+// their block's scale; a row at position 0 of its block sets that scale from
+// itself alone first (as fp8_store_row).  Wave x takes four consecutive rows
+// at a time, x * 4 .. x * 4 + 3, then x * 4 + 4 nx, ...; the lengths, table
+// entries and rows of the four are loaded together.  With two FP8 workers on
+// every SIMD these waves only find a slot as workers finish, so their time
+// is the tail of the launch: one row at a time (three dependent loads each)
+// they took up to 29 us on the 70B-shaped step.
+constexpr int kAppendFp8Rows = 4;
+
 __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x, int64_t nx) {
     const int lane = threadIdx.x;
     const int H = a.num_kv_heads;
     const int64_t items = (int64_t)a.num_seqs * 2 * H;
-    for (int64_t item = x; item < items; item += nx) {
-        const int64_t i = item / (2 * H);
-        const int which = (int)((item / H) & 1);
-        const int h = (int)(item - (i * 2 + which) * H);
-        const int L = clamp_len(a.lens[i], a.max_context);
-        if (L == 0) continue;
-        const int pos = L - 1;
-        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / a.block_size];
-        if (block < 0 || block >= a.num_blocks) continue;
-        const int j = pos % a.block_size;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(which == 0 ? a.k_append : a.v_append) +
-                              (i * H + h) * (kD / 2);
-        uint16_t* dst = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(which == 0 ? a.k_layer : a.v_layer)) +
-                        ((block * H + h) * a.block_size + j) * (kD / 2);
-        float* scale = const_cast<float*>(which == 0 ? a.k_scale : a.v_scale) + block * H + h;
-        fp8_store_row(src, dst, scale, j == 0, lane);
+    for (int64_t i0 = x * kAppendFp8Rows; i0 < items; i0 += nx * kAppendFp8Rows) {
+        int L[kAppendFp8Rows];
+        int64_t seq[kAppendFp8Rows];
+        int which[kAppendFp8Rows], h[kAppendFp8Rows];
+#pragma unroll
+        for (int u = 0; u < kAppendFp8Rows; ++u) {
+            const int64_t item = i0 + u < items ? i0 + u : items - 1;
+            seq[u] = item / (2 * H);
+            which[u] = (int)((item / H) & 1);
+            h[u] = (int)(item - (seq[u] * 2 + which[u]) * H);
+            L[u] = i0 + u < items ? clamp_len(a.lens[seq[u]], a.max_context) : 0;
+        }
+        int64_t block[kAppendFp8Rows];
+#pragma unroll
+        for (int u = 0; u < kAppendFp8Rows; ++u)
+            block[u] = L[u] > 0 ? a.tables[seq[u] * (int64_t)a.max_blocks + (L[u] - 1) / a.block_size] : -1;
+        uint32_t w[kAppendFp8Rows];
+        float stored[kAppendFp8Rows];
+#pragma unroll
+        for (int u = 0; u < kAppendFp8Rows; ++u) {
+            const bool ok = block[u] >= 0 && block[u] < a.num_blocks;   // wave-uniform
+            const bool opens = (L[u] - 1) % a.block_size == 0;
+            const float* sp = which[u] == 0 ? a.k_scale : a.v_scale;
+            w[u] = ok ? reinterpret_cast<const uint32_t*>(which[u] == 0 ? a.k_append : a.v_append)
+                            [(seq[u] * H + h[u]) * (kD / 2) + lane]
+                      : 0u;
+            stored[u] = (ok && !opens) ? sp[block[u] * H + h[u]] : 1.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kAppendFp8Rows; ++u) {
+            if (!(block[u] >= 0 && block[u] < a.num_blocks)) continue;   // wave-uniform
+            const int j = (L[u] - 1) % a.block_size;
+            float sc = stored[u];
+            if (j == 0) {
+                sc = e4m3_block_scale(wave_max(abs_max2(w[u], 0.0f)));
+                if (lane == 0) const_cast<float*>(which[u] == 0 ? a.k_scale : a.v_scale)[block[u] * H + h[u]] = sc;
+            }
+            uint16_t* dst = const_cast<uint16_t*>(
+                                reinterpret_cast<const uint16_t*>(which[u] == 0 ? a.k_layer : a.v_layer)) +
+                            ((block[u] * H + h[u]) * a.block_size + j) * (kD / 2);
+            dst[lane] = (uint16_t)bf16x2_to_e4m3x2(w[u], sc);
+        }
     }
+}
+
+// Other rows of the step on an FP8 pool (reshape_and_cache of rows_k /
+// rows_v to rows_slots with the block scale rule), stored by nx more waves of
+// the balanced launch: wave x takes the (16-token chunk, KV head) items x,
+// x + nx, ... of the rows (fp8_store_chunk: a block opened by these rows gets
+// its scales and all its rows' codes from the wave holding its row 0, any
+// other row is quantized with the stored scale).  Bitwise the scatter
+// kernels' result; the caller guarantees that no slot lies in a block this
+// launch's attention reads or appends to.
+__device__ __forceinline__ void fp8_rows_waves(const DecodeArgs& a, int64_t x, int64_t nx) {
+    Fp8Rows r;
+    r.slots = a.rows_slots;
+    r.T = a.num_rows;
+    r.k_new = reinterpret_cast<const uint32_t*>(a.rows_k);
+    r.v_new = reinterpret_cast<const uint32_t*>(a.rows_v);
+    r.k_codes = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.k_layer));
+    r.v_codes = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.v_layer));
+    r.k_scale = const_cast<float*>(a.k_scale);
+    r.v_scale = const_cast<float*>(a.v_scale);
+    r.B = a.block_size;
+    r.H = a.num_kv_heads;
+    r.num_slots = (int64_t)a.num_blocks * a.block_size;
+    const int64_t items = (a.num_rows + 15) / 16 * a.num_kv_heads;
+    for (int64_t item = x; item < items; item += nx)
+        fp8_store_chunk(r, item / r.H * 16, (int)(item % r.H), threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1266,7 +1326,9 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
             if constexpr (kFp8) append_fp8_waves(a, x, a.append_waves);
             else append_scatter_waves(a, x, a.append_waves);
         } else {
-            if constexpr (!kFp8) rows_scatter_waves(a, x - a.append_waves, (int64_t)gridDim.x - W - a.append_waves);
+            const int64_t nrow_waves = (int64_t)gridDim.x - W - a.append_waves;
+            if constexpr (kFp8) fp8_rows_waves(a, x - a.append_waves, nrow_waves);
+            else rows_scatter_waves(a, x - a.append_waves, nrow_waves);
         }
         return;
     }
@@ -1943,17 +2005,23 @@ hipError_t launch_streamk_walk(const DecodeArgs& a_in, int group, int workers, h
         extra = prefix_column_groups(a.num_seqs, group) * a.num_kv_heads * a.prefix_parts;
     } else {
         if (a.k_append) {
+            // bf16: beside the workers from the start; FP8: at the launch's tail (see append_fp8_waves)
             const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * (kFp8 ? 1 : kRC);
-            const int64_t per_wave = kFp8 ? 4 : 8 * kWave;
+            const int64_t per_wave = kFp8 ? kAppendFp8Rows : 8 * kWave;
+            const int64_t cap = kFp8 ? 1024 : 256;
             extra = (items + per_wave - 1) / per_wave;
-            extra = extra < 1 ? 1 : (extra > 256 ? 256 : extra);
+            extra = extra < 1 ? 1 : (extra > cap ? cap : extra);
             a.append_waves = (int32_t)extra;
         }
         // other rows: up to 768 waves (a row or a few each), so that they are
         // done while the workers still scan lengths and fetch their first
         // tiles; with 256 waves (nine rows each on the 70B-shaped step) the
-        // step took 2 us longer
-        if (!kFp8 && a.num_rows > 0) extra += a.num_rows < 768 ? a.num_rows : 768;
+        // step took 2 us longer.  FP8 pools: one (16-token chunk, KV head) item a wave.
+        if (a.num_rows > 0) {
+            const int64_t items = kFp8 ? (a.num_rows + 15) / 16 * a.num_kv_heads : a.num_rows;
+            const int64_t cap = kFp8 ? 1024 : 768;
+            extra += items < cap ? items : cap;
+        }
     }
     dim3 grid((unsigned)(workers + extra));
     const bool any_b = a.block_size != kTileTokens;

@@ -21,6 +21,7 @@
 
 #include "device_common.hpp"
 #include "fp8.hpp"
+#include "fp8_rows.hpp"
 #include "launch.hpp"
 
 namespace kvp {
@@ -32,23 +33,16 @@ constexpr int kRowWords = kD8 / 2;       // 32-bit words (bf16 pairs) per k_new 
 constexpr int kRowChunks8 = kD8 / 16;    // 16-byte chunks per code row
 constexpr int kQuantThreads = 256;
 
-__device__ __forceinline__ int64_t readlane64_i(int64_t x, int src) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), src);
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
 // One wave per (16-token chunk, KV head): grid (chunks, H), grid-stride over
 // the chunks, so a wave usually has at most one block to open.  The wave finds
 // the tokens of its chunk that write row 0 of a block and takes the amax of
 // head h's K and V rows (lane l: dims 2l and 2l + 1) over every row this call
 // writes into that block, sixteen rows at a time: lanes 0..15 list the writers
 // of rows g .. g+15 (from the run that follows the token, else by searching
-// the whole mapping, 512 slots per step), and their 32 row loads go out
-// together.
-constexpr int kRowGroup = 16;  // block rows gathered per round (all of them for 8-token blocks)
+// the whole mapping, 512 slots per step: fp8_row_writers), and their 32 row
+// loads go out together.
+constexpr int kRowGroup = kFp8RowGroup;
 constexpr int kScaleChunk = 16;
-constexpr int kSearchUnroll = 8;
 
 __global__ __launch_bounds__(kWave) void fp8_scale_kernel(ScatterArgs a) {
     const int lane = threadIdx.x;
@@ -56,7 +50,6 @@ __global__ __launch_bounds__(kWave) void fp8_scale_kernel(ScatterArgs a) {
     const int h = blockIdx.y;
     const int B = a.block_size;
     const int R = B < kRowGroup ? B : kRowGroup;   // rows per round
-    const uint64_t run_mask = (1ull << R) - 1;
     const int64_t T = a.num_tokens;
     const uint32_t* kn = reinterpret_cast<const uint32_t*>(a.k_new);
     const uint32_t* vn = reinterpret_cast<const uint32_t*>(a.v_new);
@@ -67,48 +60,23 @@ __global__ __launch_bounds__(kWave) void fp8_scale_kernel(ScatterArgs a) {
         while (starts) {
             const int j = __builtin_ctzll(starts);
             starts &= starts - 1;
-            const int64_t first = readlane64_i(slot, j);   // slot of row 0
+            const int64_t first = fp8_readlane64(slot, j);   // slot of row 0
             const int64_t blk = first / B;
             float ak = 0.0f, av = 0.0f;
             for (int g = 0; g < B; g += R) {
                 // lane i < R: the token writing row g + i of the block, or -1
-                int64_t tok = -1;
-                const int64_t tl = c0 + j + g + lane;
-                const bool in_run = lane < R && tl < T && a.slot_mapping[tl] == first + g + lane;
-                if (__builtin_amdgcn_ballot_w64(in_run) == run_mask) {
-                    tok = in_run ? tl : -1;
-                } else {
-                    const int64_t lo = first + g;
-                    for (int64_t s0 = 0; s0 < T; s0 += kSearchUnroll * kWave) {
-                        int64_t sl[kSearchUnroll];
-#pragma unroll
-                        for (int u = 0; u < kSearchUnroll; ++u) {
-                            const int64_t ts = s0 + u * kWave + lane;
-                            sl[u] = ts < T ? a.slot_mapping[ts] : -1;
-                        }
-#pragma unroll
-                        for (int u = 0; u < kSearchUnroll; ++u) {
-                            uint64_t hit = __builtin_amdgcn_ballot_w64(sl[u] >= lo && sl[u] < lo + R);
-                            while (hit) {
-                                const int jj = __builtin_ctzll(hit);
-                                hit &= hit - 1;
-                                const int row = (int)(readlane64_i(sl[u], jj) - lo);
-                                if (lane == row) tok = s0 + u * kWave + jj;
-                            }
-                        }
-                    }
-                }
+                const int64_t tok = fp8_row_writers(a.slot_mapping, T, c0 + j + g, first + g, R, lane);
                 uint32_t wk[kRowGroup], wv[kRowGroup];
 #pragma unroll
                 for (int i = 0; i < kRowGroup; ++i) {
-                    const int64_t ti = readlane64_i(tok, i);
+                    const int64_t ti = fp8_readlane64(tok, i);
                     const size_t w = ((size_t)(ti < 0 ? 0 : ti) * H + h) * kRowWords + lane;
                     wk[i] = kn[w];
                     wv[i] = vn[w];
                 }
 #pragma unroll
                 for (int i = 0; i < kRowGroup; ++i) {
-                    if (readlane64_i(tok, i) >= 0) {
+                    if (fp8_readlane64(tok, i) >= 0) {
                         ak = abs_max2(wk[i], ak);
                         av = abs_max2(wv[i], av);
                     }

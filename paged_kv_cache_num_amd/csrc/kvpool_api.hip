@@ -621,20 +621,16 @@ kv_status decode_impl(kv_pool_t pool, int32_t layer, void* out, const void* q, c
     } else if (plan.mode == Mode::kBalanced) {
         // the worker that owns each (sequence, KV head)'s last block uses the new row
         // (FP8: quantized in registers); extra waves of the same launch store it.
-        // Other rows: bf16 pools store them from more waves of the launch, FP8
-        // pools (block scales to set) with the scatter kernel first.
+        // Other rows are stored by more waves of the launch (FP8: each wave
+        // sets the scales of the blocks its rows open).
         a.k_append = k_append;
         a.v_append = v_append;
         e = hipSuccess;
         if (num_rows > 0) {
-            if (fp8) {
-                e = launch_rows(pool, layer, rows_k, rows_v, rows_slots, num_rows, stream);
-            } else {
-                a.rows_k = rows_k;
-                a.rows_v = rows_v;
-                a.rows_slots = rows_slots;
-                a.num_rows = num_rows;
-            }
+            a.rows_k = rows_k;
+            a.rows_v = rows_v;
+            a.rows_slots = rows_slots;
+            a.num_rows = num_rows;
         }
         const int group = num_q_heads / d.num_kv_heads;
         if (e == hipSuccess) {

@@ -115,8 +115,9 @@ struct DecodeArgs {
     const void* v_append;
     const float* k_scale;        // FP8 pools: the layer's block scales [num_blocks][Hkv]
     const float* v_scale;
-    // balanced split, bf16 pools: other rows stored by extra waves of the same
-    // launch (reshape_and_cache semantics; slots the attention does not read)
+    // balanced split: other rows stored by extra waves of the same launch
+    // (reshape_and_cache semantics, FP8 pools with the block scale rule; slots
+    // the attention does not read)
     const void* rows_k;          // [num_rows][Hkv][D]
     const void* rows_v;
     const int64_t* rows_slots;   // [num_rows]

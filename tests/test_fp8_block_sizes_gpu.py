@@ -192,3 +192,76 @@ def test_decode_is_independent_of_block_placement(B):
         torch.cuda.synchronize()
         outs.append(step.out_host())
     assert outs[0].tobytes() == outs[1].tobytes()
+
+
+# --------------------------------------------- the step with other rows --
+
+@pytest.mark.parametrize("shuffled", [False, True])
+@pytest.mark.parametrize("B", [8, 16, 32, 64, 128])
+def test_step_rows_bitwise_the_scatter_then_the_append(B, shuffled):
+    """paged_attention_decode_step on an FP8 pool stores the other rows from
+    extra waves of the attention's launch, with the block scale rule: the rows
+    of the scatter test above (a prefill chunk over two whole blocks and part
+    of a third, with a loud row; a row opening a block alone; rows continuing a
+    block with its stored scale and opening the next; a padding row and an
+    out-of-pool slot; in token order or shuffled, which sends the writers'
+    search through the whole mapping) beside a decode batch on other blocks.
+    Codes, scales and output are bitwise those of reshape_and_cache followed
+    by paged_attention_decode_append; the pool is the oracle's scatter of the
+    rows and the appended rows; the output is within 2e-2 of the oracle."""
+    import torch
+    say(f"fp8 step with other rows B={B} shuffled={shuffled}")
+    N, H, Hq = 80, 4, 16
+    pool_a, state = _fp8_pool(2, N, H, B, seed=7)
+    pool_b, _ = _fp8_pool(2, N, H, B, seed=7)
+    perm = np.random.default_rng([23, B]).permutation(N).astype(np.int32)
+    row_tables, dec_tables = perm[:32].reshape(4, 8), perm[32:64].reshape(4, 8)
+    ws, wst, wc = [0, 1, 2, 3], [0, B, 3, 0], [2 * B + 5, 1, B, 1]
+    slots = oracle.slot_mapping(row_tables, B, N, ws, wst, wc)
+    T = slots.size
+    ss = np.random.SeedSequence([31, B])
+    kn = kvgen.normal_fill((T, H, 128), ss.spawn(1)[0], 1.0, "bf16")
+    vn = kvgen.normal_fill((T, H, 128), ss.spawn(1)[0], 1.0, "bf16")
+    kn[B - 1] = kvgen.f32_to_bf16_bits(kvgen.bf16_bits_to_f32(kn[B - 1]) * 40.0)
+    slots = np.concatenate([slots[:7], [-1], slots[7:], [N * B + 3]]).astype(np.int64)
+    pad = np.zeros((1, H, 128), dtype=np.uint16)
+    kn = np.concatenate([kn[:7], pad, kn[7:], pad])
+    vn = np.concatenate([vn[:7], pad, vn[7:], pad])
+    if shuffled:
+        p = np.random.default_rng(6).permutation(slots.size)
+        slots, kn, vn = slots[p], kn[p], vn[p]
+    # the decode batch: last positions at row 0 of a block, inside one, at a block's end
+    lens = np.array([1, B + 1, 3 * B, 5 * B + 3], dtype=np.int32)
+    S = lens.size
+    q = kvgen.normal_fill((S, Hq, 128), ss.spawn(1)[0], 1.0, "bf16")
+    ka = kvgen.normal_fill((S, H, 128), ss.spawn(1)[0], 1.0, "bf16")
+    va = kvgen.normal_fill((S, H, 128), ss.spawn(1)[0], 1.0, "bf16")
+    bf = lambda a: _cuda(a.view(np.int16)).view(torch.bfloat16)
+    scale = 1.0 / math.sqrt(128)
+    outs = []
+    for pool, fused in ((pool_a, True), (pool_b, False)):
+        ws_bytes = pool.workspace_bytes(S, Hq, int(lens.max()), 0)
+        work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        out = torch.zeros((S, Hq, 128), dtype=torch.bfloat16, device="cuda")
+        args = dict(scale=scale, max_context_len=int(lens.max()), partition_size=0, workspace=work)
+        if fused:
+            pool.paged_attention_decode_step(1, out, bf(q), bf(ka), bf(va), _cuda(dec_tables), _cuda(lens),
+                                             bf(kn), bf(vn), _cuda(slots), **args)
+        else:
+            pool.reshape_and_cache(1, bf(kn), bf(vn), _cuda(slots))
+            pool.paged_attention_decode_append(1, out, bf(q), bf(ka), bf(va), _cuda(dec_tables), _cuda(lens), **args)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16).cpu().numpy())
+    assert outs[0].tobytes() == outs[1].tobytes(), "output differs from the two-call step"
+    for li in (0, 1):
+        for name, g, w in zip(("K codes", "V codes", "K scales", "V scales"), _host(pool_a, li), _host(pool_b, li)):
+            assert g.tobytes() == w.tobytes(), f"B={B} layer {li}: {name} differ from the two-call step"
+    app_slots = oracle.slot_mapping(dec_tables, B, N, list(range(S)), list(lens - 1), [1] * S)
+    want = ofp8.scatter(*ofp8.scatter(*state, kn, vn, slots, B), ka, va, app_slots, B)
+    for name, g, w in zip(("K codes", "V codes", "K scales", "V scales"), _host(pool_a, 1), want):
+        assert g.tobytes() == w.tobytes(), f"B={B}: {name} differ from the oracle's scatter"
+    ref = ofp8.paged_attention(q, *want, dec_tables, lens, scale)
+    got = kvgen.bf16_bits_to_f32(outs[0].view(np.uint16)).astype(np.float64)
+    err = float(np.abs(got - ref).max())
+    say(f"  B={B} shuffled={shuffled}: max |gpu - oracle| = {err:.3e}")
+    assert np.isfinite(got).all() and err <= TOL["bf16"]
