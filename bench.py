@@ -48,7 +48,8 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_num_amd/csrc/decode.hip", "paged_kv_cache_num_amd/csrc/decode_mfma.hip",
                   "paged_kv_cache_num_amd/csrc/device_common.hpp", "paged_kv_cache_num_amd/csrc/split.hpp",
-                  "paged_kv_cache_num_amd/csrc/fp8.hpp", "paged_kv_cache_num_amd/csrc/table_index.hpp"]
+                  "paged_kv_cache_num_amd/csrc/fp8.hpp", "paged_kv_cache_num_amd/csrc/table_index.hpp",
+                  "paged_kv_cache_num_amd/csrc/fp8_rows.hpp"]
 
 WORKLOADS = {
     "C1": "tiny fp32 paged decode: 4 sequences, lengths {17,33,100,200}, 8 query / 2 KV heads, head_dim 64, block 16, 64-block pool",

@@ -104,7 +104,8 @@ __device__ __forceinline__ void fp8_put_row(const Fp8Rows& r, int64_t blk, int h
 // memory round trips: its slots, the run check of its opener (the other
 // tokens find their block's row-0 token among the chunk's slots), its rows.
 __device__ __forceinline__ void fp8_store_chunk(const Fp8Rows& r, int64_t c0, int h, int lane) {
-    const int B = r.B;
+    const int B = r.B;   // a power of two (8 .. 128): slots split with shifts, not 64-bit divisions
+    const int bshift = __builtin_ctz((unsigned)B);
     const int R = B < kFp8RowGroup ? B : kFp8RowGroup;
     const int64_t t = c0 + lane;
     const int64_t slot = (lane < 16 && t < r.T) ? r.slots[t] : -1;
@@ -113,12 +114,12 @@ __device__ __forceinline__ void fp8_store_chunk(const Fp8Rows& r, int64_t c0, in
     const size_t row_words = (size_t)r.H * kFp8RowWords;
 
     // blocks opened by a token of this chunk
-    uint64_t starts = __builtin_amdgcn_ballot_w64(valid && slot % B == 0);
+    uint64_t starts = __builtin_amdgcn_ballot_w64(valid && (slot & (B - 1)) == 0);
     while (starts) {
         const int j = __builtin_ctzll(starts);
         starts &= starts - 1;
         const int64_t first = fp8_readlane64(slot, j);
-        const int64_t blk = first / B;
+        const int64_t blk = first >> bshift;
         float ak = 0.0f, av = 0.0f;
         uint32_t wk[kFp8RowGroup], wv[kFp8RowGroup];
         int64_t tok = -1;
@@ -167,10 +168,10 @@ __device__ __forceinline__ void fp8_store_chunk(const Fp8Rows& r, int64_t c0, in
     // block's row 0.  The token that would (c0 + lane - offset, if the rows
     // came as a run) is checked first, from a lane of this chunk or by one
     // load; the tokens still in doubt search the mapping together.
-    const bool other = valid && slot % B != 0;
-    const int64_t blk = other ? slot / B : 0;
-    const int off = other ? (int)(slot - blk * B) : 0;
-    const int64_t want = blk * B;
+    const bool other = valid && (slot & (B - 1)) != 0;
+    const int64_t blk = other ? slot >> bshift : 0;
+    const int off = other ? (int)(slot & (B - 1)) : 0;
+    const int64_t want = blk << bshift;
     const int64_t tg = c0 + lane - off;
     const int src = (int)(tg - c0);   // < 16 for the tokens of this chunk
     const int64_t s_in = fp8_shfl64(slot, src >= 0 ? src : 0);
