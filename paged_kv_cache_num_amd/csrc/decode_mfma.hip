@@ -1364,7 +1364,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     asm volatile("" : "+v"(T32));   // kept in a vector register, as the walk's other split values
     const int64_t T = T32;
     if (w == 0 && lane == 0) a.ws_prefix[S] = T;
-    const SliceWeights kw{a.slice_even, a.slice_odd};
+    const SliceWeights kw{a.slice_even, a.slice_odd, a.slice_lead, a.slice_trail};
     int64_t t = slice_start(w, T, W, kw);
     const int64_t t_end = slice_start(w + 1, T, W, kw);
     if (t >= t_end) return;
@@ -1596,7 +1596,7 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
             T += __shfl(incl, kWave - 1, kWave);
         }
     }
-    const SliceWeights kw{a.slice_even, a.slice_odd};
+    const SliceWeights kw{a.slice_even, a.slice_odd, a.slice_lead, a.slice_trail};
     const int64_t t_lo = slice_start(w, T, W, kw);
     const int64_t t_hi = slice_start(w + 1, T, W, kw);
     if (t_lo >= t_hi) return;
@@ -1787,7 +1787,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     const int64_t W = num_workers;
     const int64_t base = first_tile + (int64_t)kv * walk_span(nblk, a.piece_cost);   // the walk's positions start here
     const int64_t s0 = base + a.piece_cost;                                            // ... and its tile 0 sits here
-    const SliceWeights kw{a.slice_even, a.slice_odd};
+    const SliceWeights kw{a.slice_even, a.slice_odd, a.slice_lead, a.slice_trail};
     const int64_t w0 = nblk > 0 ? worker_of(s0, T, W, kw) : 0;
     const int64_t w1 = nblk > 0 ? worker_of(s0 + nblk - 1, T, W, kw) : 0;
     if (w0 == w1 && !shared) return;   // written by its worker
@@ -2083,6 +2083,8 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
     const SliceWeights kw = kFp8 ? kFp8SliceWeights : kBf16SliceWeights;
     a.slice_even = (int32_t)kw.even;
     a.slice_odd = (int32_t)kw.odd;
+    a.slice_lead = (int32_t)kw.lead;
+    a.slice_trail = (int32_t)kw.trail;
     a.piece_cost = kFp8 ? kFp8PieceCost : kBf16PieceCost;
     hipError_t e = launch_streamk_walk<kFp8>(a, group, workers, stream);
     if (e != hipSuccess) return e;
@@ -2095,6 +2097,8 @@ hipError_t launch_partitions(const DecodeArgs& a_in, int group, int workers, hip
     const SliceWeights kw = kFp8 ? kFp8SliceWeights : kBf16SliceWeights;
     a.slice_even = (int32_t)kw.even;
     a.slice_odd = (int32_t)kw.odd;
+    a.slice_lead = (int32_t)kw.lead;
+    a.slice_trail = (int32_t)kw.trail;
     dim3 grid((unsigned)workers);
     const bool any_b = a.block_size != kTileTokens;
     switch (group) {

@@ -126,6 +126,8 @@ struct DecodeArgs {
     int32_t workers;             // balanced split: worker waves (the launch adds append / row waves past them)
     int32_t slice_even;          // balanced split: tiles of a worker on an even XCD per slice_odd on an odd one
     int32_t slice_odd;
+    int32_t slice_lead;          // balanced split: weight factor of workers [0, W/2)
+    int32_t slice_trail;         // ... and of workers [W/2, W)
     int32_t piece_cost;          // balanced split: positions before each (sequence, KV head) walk's tiles
     int32_t max_blocks;
     int32_t num_seqs;

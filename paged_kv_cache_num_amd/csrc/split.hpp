@@ -43,12 +43,21 @@ KVP_SPLIT_HD inline int first_tile_at(int64_t off, int cost) { return off > cost
 // and 4.9% for FP8 tiles.  A worker on an even XCD therefore gets `even`
 // tiles for every `odd` of a worker on an odd one; the boundaries stay a
 // function of T, W and the weights alone.
-//   cum(w) = even ceil(w / 2) + odd floor(w / 2),  cum(2p) = (even + odd) p,  cum(2p + 1) = (even + odd) p + even
+//   C(w) = even ceil(w / 2) + odd floor(w / 2),  C(2p) = (even + odd) p,  C(2p + 1) = (even + odd) p + even
+// With two worker waves on every SIMD (FP8 tiles), the second half of the
+// workers is dispatched after the first has taken a wave slot on every SIMD,
+// and the older wave on a SIMD wins its issue arbitration: on the 8B-shaped
+// batch the workers past W/2 ended 2.2% later than the others, in one clean
+// step at W/2.  The first half's weights are multiplied by `lead`, the second
+// half's by `trail`:
+//   cum(w) = lead C(min(w, W/2)) + trail (C(w) - C(min(w, W/2)))
+constexpr int64_t kFp8Lead = 45, kFp8Trail = 44;
 struct SliceWeights {
     int64_t even, odd;
+    int64_t lead, trail;
 };
-constexpr SliceWeights kBf16SliceWeights{33, 32};
-constexpr SliceWeights kFp8SliceWeights{21, 20};
+constexpr SliceWeights kBf16SliceWeights{33, 32, 1, 1};
+constexpr SliceWeights kFp8SliceWeights{21, 20, kFp8Lead, kFp8Trail};
 
 // floor(num / den) for 0 <= num < 2^53 and 0 < den < 2^31.  The quotient in
 // double precision is within one of the answer (both operands are exact and
@@ -66,26 +75,38 @@ KVP_SPLIT_HD inline int64_t div_floor(int64_t num, int64_t den) {
 }
 
 // The balanced split's positions are counted in 32 bits in the kernel's scan
-// (and T cum(W) must stay below 2^53 for div_floor): batches with more
-// positions take another kernel.
+// (and T cum(W) must stay below 2^53 for div_floor: with the FP8 weights and
+// 2048 workers cum(W) is below 2^21): batches with more positions take
+// another kernel.
 constexpr int64_t kMaxSplitPositions = (int64_t)1 << 31;
 
-KVP_SPLIT_HD inline int64_t cum_weight(int64_t w, SliceWeights k) {
+KVP_SPLIT_HD inline int64_t parity_weight(int64_t w, SliceWeights k) {
     return k.even * ((w + 1) / 2) + k.odd * (w / 2);
 }
+// the largest w with C(w) <= Y: with Y = (even + odd) p + r, w = 2p + 1 when r >= even, else 2p
+KVP_SPLIT_HD inline int64_t parity_inverse(int64_t Y, SliceWeights k) {
+    const int64_t pair = k.even + k.odd;
+    const int64_t p = div_floor(Y, pair);
+    return 2 * p + (Y - p * pair >= k.even ? 1 : 0);
+}
+KVP_SPLIT_HD inline int64_t cum_weight(int64_t w, int64_t W, SliceWeights k) {
+    const int64_t ch = parity_weight(w < W / 2 ? w : W / 2, k);
+    return k.lead * ch + k.trail * (parity_weight(w, k) - ch);
+}
 KVP_SPLIT_HD inline int64_t slice_start(int64_t w, int64_t T, int64_t W, SliceWeights k) {
-    return div_floor(T * cum_weight(w, k), cum_weight(W, k));
+    return div_floor(T * cum_weight(w, W, k), cum_weight(W, W, k));
 }
 
 // Worker whose slice holds tile t (0 <= t < T): the largest w with
 // slice_start(w) <= t, i.e. cum(w) T <= (t + 1) cum(W) - 1, i.e.
-// cum(w) <= X = floor(((t + 1) cum(W) - 1) / T); with X = (even + odd) p + r
-// that is w = 2p + 1 when r >= even, else 2p.
+// cum(w) <= X = floor(((t + 1) cum(W) - 1) / T).  Below the first half's
+// total lead C(W/2) that is C(w) <= floor(X / lead); above it
+// C(w) <= C(W/2) + floor((X - lead C(W/2)) / trail).
 KVP_SPLIT_HD inline int64_t worker_of(int64_t t, int64_t T, int64_t W, SliceWeights k) {
-    const int64_t X = div_floor((t + 1) * cum_weight(W, k) - 1, T);
-    const int64_t pair = k.even + k.odd;
-    const int64_t p = div_floor(X, pair);
-    const int64_t w = 2 * p + (X - p * pair >= k.even ? 1 : 0);
+    const int64_t X = div_floor((t + 1) * cum_weight(W, W, k) - 1, T);
+    const int64_t ch = parity_weight(W / 2, k);
+    const int64_t w = X < k.lead * ch ? parity_inverse(div_floor(X, k.lead), k)
+                                      : parity_inverse(ch + div_floor(X - k.lead * ch, k.trail), k);
     return w < W - 1 ? w : W - 1;
 }
 

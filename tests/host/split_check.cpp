@@ -173,8 +173,12 @@ int main() {
     check_table_index();
     check_div_floor();
     std::mt19937_64 rng(12345);
-    const kvp::SliceWeights weights[] = {kvp::kBf16SliceWeights, kvp::kFp8SliceWeights, {1, 1}};
-    const int64_t workers[] = {1, 7, 64, 1024, 2048};
+    // the decode's weights, plain equal slices, and lopsided parity and half
+    // weights (the first or the second half heavier), so that every branch of
+    // worker_of's inversion is taken with odd and even worker counts
+    const kvp::SliceWeights weights[] = {kvp::kBf16SliceWeights, kvp::kFp8SliceWeights, {1, 1, 1, 1},
+                                         {3, 1, 5, 2}, {1, 4, 2, 7}};
+    const int64_t workers[] = {1, 7, 64, 1024, 2048, 2049};
     int cases = 0;
     for (int rep = 0; rep < 60; ++rep) {
         Batch bt;
