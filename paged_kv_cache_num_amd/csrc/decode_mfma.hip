@@ -1986,7 +1986,7 @@ int streamk_workers(int group, bool fp8) {
         (void)hipGetLastError();
         return kStreamKDefaultWorkers;
     }
-    const int workers = cus * min(per_cu, waves_per_cu);
+    const int workers = min(cus * min(per_cu, waves_per_cu), kMaxSplitWorkers);
     cached[dev][fp8][group].store(workers, std::memory_order_relaxed);
     return workers;
 }

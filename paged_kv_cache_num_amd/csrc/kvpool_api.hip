@@ -121,8 +121,9 @@ Plan plan_decode(const kv_pool_desc& d, int32_t num_seqs, int32_t num_q_heads, i
 // [S][Hq][parts + 1] x (m, l) and x head_dim.  The prefix is cut into parts
 // so that about one prefix wave runs for every two workers of the balanced
 // split (they share the launch), every part non-empty.  On the 128-sequence
-// prefix-sharing batch (2 parts) the call took 51 us; with one prefix wave
-// per worker 55 us, two 60 us, a single part 66 us.
+// prefix-sharing batch (4 parts of 32 tiles, 512 prefix waves) the call took
+// 44.8 us on one layer back to back, against 57.5 / 49.8 / 47.0 / 49.6 us
+// with 2 / 3 / 6 / 8 parts.
 struct SharedPlan {
     Plan base;
     int32_t parts;

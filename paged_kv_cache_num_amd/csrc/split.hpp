@@ -75,10 +75,16 @@ KVP_SPLIT_HD inline int64_t div_floor(int64_t num, int64_t den) {
 }
 
 // The balanced split's positions are counted in 32 bits in the kernel's scan
-// (and T cum(W) must stay below 2^53 for div_floor: with the FP8 weights and
-// 2048 workers cum(W) is below 2^21): batches with more positions take
-// another kernel.
+// (and T cum(W) must stay below 2^53 for div_floor): batches with more
+// positions take another kernel, and the worker count is capped so that
+// cum(W) <= max(lead, trail) max(even, odd) W stays below 2^21.
 constexpr int64_t kMaxSplitPositions = (int64_t)1 << 31;
+constexpr int kMaxSplitWorkers = 2048;
+static_assert(kMaxSplitPositions * (kFp8SliceWeights.lead * kFp8SliceWeights.even * kMaxSplitWorkers) <
+                      ((int64_t)1 << 53) &&
+                  kMaxSplitPositions * (kBf16SliceWeights.lead * kBf16SliceWeights.even * kMaxSplitWorkers) <
+                      ((int64_t)1 << 53),
+              "split positions times cum(W) must stay exact in double precision");
 
 KVP_SPLIT_HD inline int64_t parity_weight(int64_t w, SliceWeights k) {
     return k.even * ((w + 1) / 2) + k.odd * (w / 2);
