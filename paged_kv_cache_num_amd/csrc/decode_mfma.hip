@@ -1364,9 +1364,8 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     asm volatile("" : "+v"(T32));   // kept in a vector register, as the walk's other split values
     const int64_t T = T32;
     if (w == 0 && lane == 0) a.ws_prefix[S] = T;
-    const SliceWeights kw{a.slice_even, a.slice_odd, a.slice_lead, a.slice_trail};
-    int64_t t = slice_start(w, T, W, kw);
-    const int64_t t_end = slice_start(w + 1, T, W, kw);
+    int64_t t = slice_start(w, T, a.split);
+    const int64_t t_end = slice_start(w + 1, T, a.split);
     if (t >= t_end) return;
 
     // the sequence holding position t: the lane whose [excl, excl + positions) contains it
@@ -1596,9 +1595,8 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
             T += __shfl(incl, kWave - 1, kWave);
         }
     }
-    const SliceWeights kw{a.slice_even, a.slice_odd, a.slice_lead, a.slice_trail};
-    const int64_t t_lo = slice_start(w, T, W, kw);
-    const int64_t t_hi = slice_start(w + 1, T, W, kw);
+    const int64_t t_lo = slice_start(w, T, a.split);
+    const int64_t t_hi = slice_start(w + 1, T, a.split);
     if (t_lo >= t_hi) return;
 
     int seq = S, L = 0;
@@ -1787,9 +1785,9 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     const int64_t W = num_workers;
     const int64_t base = first_tile + (int64_t)kv * walk_span(nblk, a.piece_cost);   // the walk's positions start here
     const int64_t s0 = base + a.piece_cost;                                            // ... and its tile 0 sits here
-    const SliceWeights kw{a.slice_even, a.slice_odd, a.slice_lead, a.slice_trail};
-    const int64_t w0 = nblk > 0 ? worker_of(s0, T, W, kw) : 0;
-    const int64_t w1 = nblk > 0 ? worker_of(s0 + nblk - 1, T, W, kw) : 0;
+    const double rcp_T = nblk > 0 ? 1.0 / (double)T : 0.0;
+    const int64_t w0 = nblk > 0 ? worker_of(s0, T, rcp_T, a.split) : 0;
+    const int64_t w1 = nblk > 0 ? worker_of(s0 + nblk - 1, T, rcp_T, a.split) : 0;
     if (w0 == w1 && !shared) return;   // written by its worker
     // records of the slices that split the walk (none when one slice held it whole)
     const int nrec = (nblk > 0 && w0 != w1) ? (int)(w1 - w0 + 1) : 0;
@@ -1800,8 +1798,8 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     // which it walked first), else its first.
     auto slot_of = [&](int j) -> int64_t {
         const int64_t w = w0 + j;
-        const int64_t st = slice_start(w, T, W, kw);
-        if (slice_start(w + 1, T, W, kw) <= st) return -1;
+        const int64_t st = slice_start(w, T, a.split);
+        if (slice_start(w + 1, T, a.split) <= st) return -1;
         return (w == w0 && st < base) ? 2 * w + 1 : 2 * w;
     };
 
@@ -2080,11 +2078,7 @@ template <bool kFp8>
 hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
     DecodeArgs a = a_in;
     a.workers = workers;
-    const SliceWeights kw = kFp8 ? kFp8SliceWeights : kBf16SliceWeights;
-    a.slice_even = (int32_t)kw.even;
-    a.slice_odd = (int32_t)kw.odd;
-    a.slice_lead = (int32_t)kw.lead;
-    a.slice_trail = (int32_t)kw.trail;
+    a.split = split_consts(workers, kFp8 ? kFp8SliceWeights : kBf16SliceWeights);
     a.piece_cost = kFp8 ? kFp8PieceCost : kBf16PieceCost;
     hipError_t e = launch_streamk_walk<kFp8>(a, group, workers, stream);
     if (e != hipSuccess) return e;
@@ -2094,11 +2088,7 @@ hipError_t launch_streamk(const DecodeArgs& a_in, int group, int workers, hipStr
 template <bool kFp8>
 hipError_t launch_partitions(const DecodeArgs& a_in, int group, int workers, hipStream_t stream) {
     DecodeArgs a = a_in;
-    const SliceWeights kw = kFp8 ? kFp8SliceWeights : kBf16SliceWeights;
-    a.slice_even = (int32_t)kw.even;
-    a.slice_odd = (int32_t)kw.odd;
-    a.slice_lead = (int32_t)kw.lead;
-    a.slice_trail = (int32_t)kw.trail;
+    a.split = split_consts(workers, kFp8 ? kFp8SliceWeights : kBf16SliceWeights);
     dim3 grid((unsigned)workers);
     const bool any_b = a.block_size != kTileTokens;
     switch (group) {

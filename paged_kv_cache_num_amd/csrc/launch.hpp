@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "split.hpp"
+
 namespace kvp {
 
 constexpr int kBlockTokens = 16;   // block size of the fp32 / head_dim-64 decode kernel
@@ -102,6 +104,7 @@ struct SwapArgs {
 hipError_t launch_swap(const SwapArgs& a, bool out, hipStream_t stream);
 
 struct DecodeArgs {
+    SplitConsts split;           // balanced split and partitions on its workers: W, weights, reciprocals
     const void* k_layer;
     const void* v_layer;
     const void* q;               // [S][Hq][D]
@@ -124,10 +127,6 @@ struct DecodeArgs {
     int64_t num_rows;
     int32_t append_waves;        // balanced split: extra waves storing the decode rows (set by the launcher)
     int32_t workers;             // balanced split: worker waves (the launch adds append / row waves past them)
-    int32_t slice_even;          // balanced split: tiles of a worker on an even XCD per slice_odd on an odd one
-    int32_t slice_odd;
-    int32_t slice_lead;          // balanced split: weight factor of workers [0, W/2)
-    int32_t slice_trail;         // ... and of workers [W/2, W)
     int32_t piece_cost;          // balanced split: positions before each (sequence, KV head) walk's tiles
     int32_t max_blocks;
     int32_t num_seqs;

@@ -63,8 +63,9 @@ __global__ __launch_bounds__(64) void table_walk_kernel(const int32_t* __restric
         for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
         T += x;
     }
-    int64_t t = kvp::slice_start(s, T, W, kvp::kBf16SliceWeights);
-    const int64_t t_end = kvp::slice_start(s + 1, T, W, kvp::kBf16SliceWeights);
+    const kvp::SplitConsts sc = kvp::split_consts(W, kvp::kBf16SliceWeights);
+    int64_t t = kvp::slice_start(s, T, sc);
+    const int64_t t_end = kvp::slice_start(s + 1, T, sc);
     uint32_t acc = 0;
     // the sequence holding tile t, 64 sequences per step
     int seq = S;

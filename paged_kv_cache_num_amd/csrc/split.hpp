@@ -75,7 +75,7 @@ KVP_SPLIT_HD inline int64_t div_floor(int64_t num, int64_t den) {
 }
 
 // The balanced split's positions are counted in 32 bits in the kernel's scan
-// (and T cum(W) must stay below 2^53 for div_floor): batches with more
+// (and T cum(W) must stay below 2^53 for the divisions): batches with more
 // positions take another kernel, and the worker count is capped so that
 // cum(W) <= max(lead, trail) max(even, odd) W stays below 2^21.
 constexpr int64_t kMaxSplitPositions = (int64_t)1 << 31;
@@ -86,34 +86,73 @@ static_assert(kMaxSplitPositions * (kFp8SliceWeights.lead * kFp8SliceWeights.eve
                       ((int64_t)1 << 53),
               "split positions times cum(W) must stay exact in double precision");
 
+// floor(num / den) given rcp, the double nearest 1 / den, for 0 <= num < 2^53,
+// 0 < den < 2^31 and num / den <= 2^31 - 1: num * rcp is within (num / den)
+// 2^-52 (< 2^-21) of num / den, so it stays below 2^31 and its truncation is
+// off by at most one, which one step corrects.  A multiply where div_floor divides: a double division is a
+// chain of a dozen dependent instructions on the GPU, and this arithmetic
+// sits on the path of every worker's start and of the fix-up (its two
+// worker_of calls took about 1 us of a call with divisions).
+KVP_SPLIT_HD inline int64_t div_floor_rcp(int64_t num, int64_t den, double rcp) {
+    int64_t q = (int64_t)(int32_t)((double)num * rcp);
+    if (q * den > num) {
+        --q;
+    } else if ((q + 1) * den <= num) {
+        ++q;
+    }
+    return q;
+}
+
 KVP_SPLIT_HD inline int64_t parity_weight(int64_t w, SliceWeights k) {
     return k.even * ((w + 1) / 2) + k.odd * (w / 2);
-}
-// the largest w with C(w) <= Y: with Y = (even + odd) p + r, w = 2p + 1 when r >= even, else 2p
-KVP_SPLIT_HD inline int64_t parity_inverse(int64_t Y, SliceWeights k) {
-    const int64_t pair = k.even + k.odd;
-    const int64_t p = div_floor(Y, pair);
-    return 2 * p + (Y - p * pair >= k.even ? 1 : 0);
 }
 KVP_SPLIT_HD inline int64_t cum_weight(int64_t w, int64_t W, SliceWeights k) {
     const int64_t ch = parity_weight(w < W / 2 ? w : W / 2, k);
     return k.lead * ch + k.trail * (parity_weight(w, k) - ch);
 }
-KVP_SPLIT_HD inline int64_t slice_start(int64_t w, int64_t T, int64_t W, SliceWeights k) {
-    return div_floor(T * cum_weight(w, W, k), cum_weight(W, W, k));
+
+// One launch's split: W workers, the weights, cum(W), and the reciprocals of
+// the divisors that do not depend on the batch (set on the host, so a kernel
+// divides only by T, once).
+struct SplitConsts {
+    SliceWeights k;
+    int64_t W, cum_W;
+    double rcp_cum_W, rcp_pair, rcp_lead, rcp_trail;
+};
+KVP_SPLIT_HD inline SplitConsts split_consts(int64_t W, SliceWeights k) {
+    SplitConsts s;
+    s.k = k;
+    s.W = W;
+    s.cum_W = cum_weight(W, W, k);
+    s.rcp_cum_W = 1.0 / (double)s.cum_W;
+    s.rcp_pair = 1.0 / (double)(k.even + k.odd);
+    s.rcp_lead = 1.0 / (double)k.lead;
+    s.rcp_trail = 1.0 / (double)k.trail;
+    return s;
 }
 
-// Worker whose slice holds tile t (0 <= t < T): the largest w with
-// slice_start(w) <= t, i.e. cum(w) T <= (t + 1) cum(W) - 1, i.e.
-// cum(w) <= X = floor(((t + 1) cum(W) - 1) / T).  Below the first half's
-// total lead C(W/2) that is C(w) <= floor(X / lead); above it
-// C(w) <= C(W/2) + floor((X - lead C(W/2)) / trail).
-KVP_SPLIT_HD inline int64_t worker_of(int64_t t, int64_t T, int64_t W, SliceWeights k) {
-    const int64_t X = div_floor((t + 1) * cum_weight(W, W, k) - 1, T);
-    const int64_t ch = parity_weight(W / 2, k);
-    const int64_t w = X < k.lead * ch ? parity_inverse(div_floor(X, k.lead), k)
-                                      : parity_inverse(ch + div_floor(X - k.lead * ch, k.trail), k);
-    return w < W - 1 ? w : W - 1;
+// the largest w with C(w) <= Y: with Y = (even + odd) p + r, w = 2p + 1 when r >= even, else 2p
+KVP_SPLIT_HD inline int64_t parity_inverse(int64_t Y, const SplitConsts& s) {
+    const int64_t pair = s.k.even + s.k.odd;
+    const int64_t p = div_floor_rcp(Y, pair, s.rcp_pair);
+    return 2 * p + (Y - p * pair >= s.k.even ? 1 : 0);
+}
+// T cum(w) < 2^52 (T < kMaxSplitPositions, cum(W) < 2^21), quotient <= T < 2^31
+KVP_SPLIT_HD inline int64_t slice_start(int64_t w, int64_t T, const SplitConsts& s) {
+    return div_floor_rcp(T * cum_weight(w, s.W, s.k), s.cum_W, s.rcp_cum_W);
+}
+
+// Worker whose slice holds tile t (0 <= t < T; rcp_T the double nearest
+// 1 / T): the largest w with slice_start(w) <= t, i.e. cum(w) T <= (t + 1)
+// cum(W) - 1, i.e. cum(w) <= X = floor(((t + 1) cum(W) - 1) / T) (X < cum(W)).
+// Below the first half's total lead C(W/2) that is C(w) <= floor(X / lead);
+// above it C(w) <= C(W/2) + floor((X - lead C(W/2)) / trail).
+KVP_SPLIT_HD inline int64_t worker_of(int64_t t, int64_t T, double rcp_T, const SplitConsts& s) {
+    const int64_t X = div_floor_rcp((t + 1) * s.cum_W - 1, T, rcp_T);
+    const int64_t ch = parity_weight(s.W / 2, s.k);
+    const int64_t w = X < s.k.lead * ch ? parity_inverse(div_floor_rcp(X, s.k.lead, s.rcp_lead), s)
+                                        : parity_inverse(ch + div_floor_rcp(X - s.k.lead * ch, s.k.trail, s.rcp_trail), s);
+    return w < s.W - 1 ? w : s.W - 1;
 }
 
 }  // namespace kvp

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cmath>
+#include <algorithm>
 #include <cstdlib>
 #include <map>
 #include <random>
@@ -50,9 +51,11 @@ void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw, int cost) {
     for (int i = 0; i < S; ++i) walked[i].assign(Hkv, std::vector<int64_t>(bt.nblk[i], -1));
     std::map<int64_t, std::pair<int, int>> records;   // record slot -> walk
     if (T == 0) return;
+    const kvp::SplitConsts sc = kvp::split_consts(W, kw);
+    const double rcp_T = 1.0 / (double)T;
     for (int64_t w = 0; w < W; ++w) {
-        int64_t t = kvp::slice_start(w, T, W, kw);
-        const int64_t t_end = kvp::slice_start(w + 1, T, W, kw);
+        int64_t t = kvp::slice_start(w, T, sc);
+        const int64_t t_end = kvp::slice_start(w + 1, T, sc);
         CHECK(t <= t_end && t_end <= T, "slice bounds w=%lld", (long long)w);
         if (t >= t_end) continue;
         int seq = 0;
@@ -105,7 +108,7 @@ void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw, int cost) {
             if (nblk == 0) continue;
             const int64_t base = first[seq] + (int64_t)kv * kvp::walk_span(nblk, cost);
             const int64_t s0 = base + cost;
-            const int64_t w0 = kvp::worker_of(s0, T, W, kw), w1 = kvp::worker_of(s0 + nblk - 1, T, W, kw);
+            const int64_t w0 = kvp::worker_of(s0, T, rcp_T, sc), w1 = kvp::worker_of(s0 + nblk - 1, T, rcp_T, sc);
             CHECK(walked[seq][kv][0] == w0 && walked[seq][kv][nblk - 1] == w1, "owners seq=%d kv=%d", seq, kv);
             if (w0 == w1) {
                 CHECK(recs_per_walk.count(std::make_pair(seq, kv)) == 0, "whole walk left a record seq=%d kv=%d", seq, kv);
@@ -113,8 +116,8 @@ void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw, int cost) {
             }
             int found = 0;
             for (int64_t w = w0; w <= w1; ++w) {
-                const int64_t st = kvp::slice_start(w, T, W, kw);
-                if (kvp::slice_start(w + 1, T, W, kw) <= st) continue;   // empty slice
+                const int64_t st = kvp::slice_start(w, T, sc);
+                if (kvp::slice_start(w + 1, T, sc) <= st) continue;   // empty slice
                 const int64_t slot = (w == w0 && st < base) ? 2 * w + 1 : 2 * w;
                 auto it = records.find(slot);
                 CHECK(it != records.end() && it->second == std::make_pair(seq, kv),
@@ -127,8 +130,8 @@ void check_split(const Batch& bt, int64_t W, kvp::SliceWeights kw, int cost) {
     }
     // worker_of inverts slice_start
     for (int64_t t = 0; t < T; t += 1 + T / 5000) {
-        const int64_t w = kvp::worker_of(t, T, W, kw);
-        CHECK(kvp::slice_start(w, T, W, kw) <= t && t < kvp::slice_start(w + 1, T, W, kw), "worker_of t=%lld",
+        const int64_t w = kvp::worker_of(t, T, rcp_T, sc);
+        CHECK(kvp::slice_start(w, T, sc) <= t && t < kvp::slice_start(w + 1, T, sc), "worker_of t=%lld",
               (long long)t);
     }
 }
@@ -169,9 +172,64 @@ void check_div_floor() {
     }
 }
 
+// floor division by a multiply with the reciprocal: exact over its whole
+// domain (num < 2^53, den < 2^31, quotient <= 2^31 - 1), exact multiples and
+// remainders of den - 1 included, against integer division
+void check_div_floor_rcp() {
+    std::mt19937_64 rng(11);
+    const int64_t kQMax = ((int64_t)1 << 31) - 1, kNumMax = ((int64_t)1 << 53) - 1;
+    for (int i = 0; i < 4000000; ++i) {
+        int64_t den;
+        switch (i % 4) {
+            case 0: den = 1 + (int64_t)(rng() % 64); break;
+            case 1: den = 1 + (int64_t)(rng() % ((int64_t)1 << 21)); break;
+            case 2: den = ((int64_t)1 << 31) - 1 - (int64_t)(rng() % 1024); break;
+            default: den = 1 + (int64_t)(rng() % (((int64_t)1 << 31) - 1)); break;
+        }
+        const int64_t qmax = std::min(kQMax, (kNumMax - (den - 1)) / den);
+        int64_t q = (int64_t)(rng() % (uint64_t)(qmax + 1));
+        if (i % 7 == 0) q = qmax;
+        if (i % 11 == 0) q = qmax - (int64_t)(rng() % 8) < 0 ? 0 : qmax - (int64_t)(rng() % 8);
+        // num / den itself at most 2^31 - 1: the largest quotient only with no remainder
+        const int64_t r = (i % 3 == 0 || q == kQMax) ? 0 : (i % 3 == 1 ? den - 1 : (int64_t)(rng() % (uint64_t)den));
+        const int64_t num = q * den + r;
+        CHECK(num >= 0 && num <= kNumMax, "domain");
+        const double rcp = 1.0 / (double)den;
+        CHECK(kvp::div_floor_rcp(num, den, rcp) == q, "div_floor_rcp(%lld, %lld) = %lld, want %lld", (long long)num,
+              (long long)den, (long long)kvp::div_floor_rcp(num, den, rcp), (long long)q);
+    }
+}
+
+// The split at its limits: the most positions one launch takes and the most
+// workers, with either pool's weights
+void check_split_limits() {
+    for (auto kw : {kvp::kBf16SliceWeights, kvp::kFp8SliceWeights}) {
+        const int64_t W = kvp::kMaxSplitWorkers;
+        const kvp::SplitConsts sc = kvp::split_consts(W, kw);
+        for (int64_t T : {kvp::kMaxSplitPositions - 1, kvp::kMaxSplitPositions - 2, (int64_t)1 << 30, (int64_t)12345}) {
+            const double rcp_T = 1.0 / (double)T;
+            CHECK(kvp::slice_start(0, T, sc) == 0 && kvp::slice_start(W, T, sc) == T, "ends T=%lld", (long long)T);
+            int64_t prev = 0;
+            for (int64_t w = 1; w <= W; ++w) {
+                const int64_t st = kvp::slice_start(w, T, sc);
+                // exact: floor(T cum(w) / cum(W)) in 128-bit integers
+                const __int128 want = (__int128)T * kvp::cum_weight(w, W, kw) / sc.cum_W;
+                CHECK(st == (int64_t)want && st >= prev, "slice_start w=%lld T=%lld", (long long)w, (long long)T);
+                prev = st;
+            }
+            for (int64_t t : {(int64_t)0, T / 3, T / 2, T - 2, T - 1}) {
+                const int64_t w = kvp::worker_of(t, T, rcp_T, sc);
+                CHECK(kvp::slice_start(w, T, sc) <= t && t < kvp::slice_start(w + 1, T, sc), "worker_of limits");
+            }
+        }
+    }
+}
+
 int main() {
     check_table_index();
     check_div_floor();
+    check_div_floor_rcp();
+    check_split_limits();
     std::mt19937_64 rng(12345);
     // the decode's weights, plain equal slices, and lopsided parity and half
     // weights (the first or the second half heavier), so that every branch of
