@@ -909,6 +909,21 @@ __device__ __forceinline__ int clamp_len(int L, int max_context) {
     return L < 0 ? 0 : (L > max_context ? max_context : L);
 }
 
+// floor(num / den) for 0 <= num < 2^31, 0 < den < 2^31 and a quotient below
+// 2^20: the float product with v_rcp_f32's reciprocal (within one ulp) is
+// within 2^-21.4 relative, so less than one, of the quotient, and one step
+// corrects its truncation.  A float multiply and a check where a double
+// division is a dozen dependent instructions, on every worker's start.
+__device__ __forceinline__ int div_small(int64_t num, int64_t den) {
+    int q = (int)((float)num * __builtin_amdgcn_rcpf((float)den));
+    if ((int64_t)q * den > num) {
+        --q;
+    } else if ((int64_t)(q + 1) * den <= num) {
+        ++q;
+    }
+    return q;
+}
+
 // Tokens of sequence i that the balanced walk covers: its context past a
 // shared prefix (all of it when there is none).
 __device__ __forceinline__ int walk_len(const DecodeArgs& a, int i) {
@@ -1393,7 +1408,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     const int64_t off = t - seq_first;
     const int64_t span = walk_span(nblk, a.piece_cost);
     if (seq >= S || span <= 0) return;   // no sequence holds t: not reached with consistent lengths
-    int kv = (int)div_floor(off, span);
+    int kv = div_small(off, span);   // < Hkv: off < Hkv span <= T < 2^31
     if (kv >= Hkv) return;
     const int64_t at = off - (int64_t)kv * span;
     int b = first_tile_at(at, a.piece_cost);
