@@ -931,6 +931,16 @@ __device__ __forceinline__ int walk_len(const DecodeArgs& a, int i) {
     return L > 0 ? L : 0;
 }
 
+// The raw lengths of every chunk of 64 sequences (lane l of chunk c holds
+// sequence 64 c + l; lanes past the batch read its last sequence), all loaded
+// before any is used, so that the chunks share one memory round trip: a
+// guarded load whose value is used at once is waited for chunk by chunk.
+template <int N>
+__device__ __forceinline__ void load_chunk_lens(const DecodeArgs& a, int S, int nchunks, int lane, int (&raw)[N]) {
+#pragma unroll
+    for (int ch = 0; ch < N; ++ch) raw[ch] = ch < nchunks ? a.lens[min(ch * kWave + lane, S - 1)] : 0;
+}
+
 // Table row of sequence i from the first tile the balanced walk covers.
 __device__ __forceinline__ const int32_t* walk_row(const DecodeArgs& a, int i) {
     return a.tables + (size_t)i * a.max_blocks + a.shared_entries;
@@ -1357,10 +1367,11 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
     constexpr int kMaxChunks = kStreamKMaxSeqs / kWave;
     const int nchunks = (S + kWave - 1) / kWave;
     int len_c[kMaxChunks];
+    load_chunk_lens(a, S, nchunks, lane, len_c);
 #pragma unroll
     for (int ch = 0; ch < kMaxChunks; ++ch) {
-        const int i = ch * kWave + lane;
-        len_c[ch] = (ch < nchunks && i < S) ? walk_len(a, i) : 0;
+        const int L = clamp_len(len_c[ch], a.max_context) - a.shared_tiles * kTileTokens;   // walk_len
+        len_c[ch] = (ch < nchunks && ch * kWave + lane < S && L > 0) ? L : 0;
     }
     // positions in 32 bits: the host takes this kernel only for batches of
     // fewer than kMaxSplitPositions
@@ -1589,11 +1600,10 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
     constexpr int kMaxChunks = kStreamKMaxSeqs / kWave;
     const int nchunks = (S + kWave - 1) / kWave;
     int len_c[kMaxChunks];
+    load_chunk_lens(a, S, nchunks, lane, len_c);
 #pragma unroll
-    for (int ch = 0; ch < kMaxChunks; ++ch) {
-        const int i = ch * kWave + lane;
-        len_c[ch] = (ch < nchunks && i < S) ? clamp_len(a.lens[i], a.max_context) : 0;
-    }
+    for (int ch = 0; ch < kMaxChunks; ++ch)
+        len_c[ch] = (ch < nchunks && ch * kWave + lane < S) ? clamp_len(len_c[ch], a.max_context) : 0;
     int64_t ex_c[kMaxChunks];
     int64_t T = 0;
 #pragma unroll
