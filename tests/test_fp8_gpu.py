@@ -402,3 +402,23 @@ def test_graph_replays_match_eager_steps(fused, partition):
         assert np.array_equal(step.out_host(), eager), f"replay {i}: output differs from the eager step"
         for g, w in zip(step.pool_host() + step.scales_host(), pool):
             assert g.tobytes() == w.tobytes(), f"replay {i}: pool differs"
+
+
+@pytest.mark.parametrize("S,partition", [(1024, 0), (1000, 64)])
+def test_decode_at_the_balanced_split_batch_limit(S, partition):
+    """1024 sequences (every chunk of the worker prologue's length scan) and a
+    ragged 1000, on an FP8 pool: pool and outputs against the oracle."""
+    import torch
+    from paged_kv_cache_num_amd import DecodeStep
+    say(f"fp8 S={S} partition={partition}")
+    lengths = np.random.default_rng(S + 7).integers(0, 200, S)
+    lengths[-1] = 199
+    wl = kvgen.custom_workload(lengths=lengths, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16",
+                               seed=49, variant="sharp", poison=True)
+    state = kvgen.fp8_pool_state(wl, seed=11)
+    step = DecodeStep.from_workload(wl, fp8_pool=state, partition_size=partition)
+    assert step.workspace is not None
+    step.run()
+    torch.cuda.synchronize()
+    ref_pool, ref_out = _reference(wl, state, step.slots_host, step.scale)
+    _check(step, wl, ref_pool, ref_out, f"fp8 S={S} p{partition}")

@@ -308,3 +308,20 @@ def test_fixup_heads_per_wave(hq, hkv, num_seqs, gh):
         ref = oracle.run_step(wl)
         step = run_gpu(wl, partition_size=0)
         check_step(step, wl, ref, check_pool=False, label=f"fix-up G={g} GH={gh}/{variant}")
+
+
+# The balanced split's batch limit: the worker prologue loads the lengths of
+# up to 16 chunks of 64 sequences at once and scans them chunk by chunk; the
+# partitions kernel does the same.  1024 sequences fill every chunk, 1000
+# leave the last one ragged, 65 put one sequence in a second chunk.
+@pytest.mark.parametrize("S,partition", [(1024, 0), (1000, 0), (65, 0), (1024, 64), (1000, 128)])
+def test_batch_size_up_to_the_balanced_split_limit(S, partition):
+    say(f"bf16 S={S} partition={partition}: every chunk of the length scan")
+    lengths = np.random.default_rng(S + partition).integers(0, 300, S)
+    lengths[-1] = 299   # the last sequence of the last chunk holds tiles
+    wl = kvgen.custom_workload(lengths=lengths, num_q_heads=16, num_kv_heads=4, head_dim=128, dtype="bf16",
+                               seed=47, variant="sharp", poison=True)
+    ref = oracle.run_step(wl)
+    step = run_gpu(wl, partition_size=partition)
+    assert step.workspace is not None   # the balanced split or the partitions on its workers
+    check_step(step, wl, ref, label=f"S={S} p{partition}")
