@@ -254,8 +254,9 @@ kv_status kv_swap_in(kv_pool_t pool, const int32_t* blocks, int32_t num_blocks, 
  * holds one fp32 running max, sum and unnormalised output per (sequence,
  * query head, partition); in the balanced mode, the tiles before each
  * sequence (int64, num_seqs + 1) and at most two fp32 partial states per
- * worker.  The balanced-mode size depends on the current device's compute
- * unit count: query it on the device that will run the call.
+ * worker (one worker wave per SIMD for bf16 pools, two for FP8 pools, at
+ * most 2048).  The balanced-mode size depends on the current device's
+ * compute unit count: query it on the device that will run the call.
  * Errors: KV_ERR_INVALID_ARGUMENT (null, negative sizes, partition_size not a
  * multiple of the block size, num_q_heads not a multiple of num_kv_heads).
  */
