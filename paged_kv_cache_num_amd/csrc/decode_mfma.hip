@@ -1834,7 +1834,7 @@ __global__ __launch_bounds__(kWave) void streamk_fixup_kernel(DecodeArgs a, int 
     // sum); every lane then sums two dims of every head over the records in
     // order, kU records' loads in flight at a time, and stops after the last
     // record (a wave-uniform test: most pairs have two or three records).
-    constexpr int kU = 8;
+    constexpr int kU = GH >= 8 ? 4 : 8;   // eight heads a wave: 4 records' outputs, so the wave stays within 256 VGPRs
     float M[GH], den[GH], n0[GH], n1[GH];
 #pragma unroll
     for (int h = 0; h < GH; ++h) {

@@ -86,29 +86,38 @@ static_assert(kMaxSplitPositions * (kFp8SliceWeights.lead * kFp8SliceWeights.eve
                       ((int64_t)1 << 53),
               "split positions times cum(W) must stay exact in double precision");
 
-// floor(num / den) given rcp, the double nearest 1 / den, for 0 <= num < 2^53,
-// 0 < den < 2^31 and num / den <= 2^31 - 1: num * rcp is within (num / den)
-// 2^-52 (< 2^-21) of num / den, so it stays below 2^31 and its truncation is
-// off by at most one, which one step corrects.  A multiply where div_floor divides: a double division is a
-// chain of a dozen dependent instructions on the GPU, and this arithmetic
-// sits on the path of every worker's start and of the fix-up (its two
-// worker_of calls took about 1 us of a call with divisions).
-KVP_SPLIT_HD inline int64_t div_floor_rcp(int64_t num, int64_t den, double rcp) {
-    int64_t q = (int64_t)(int32_t)((double)num * rcp);
-    if (q * den > num) {
+// floor(num / den) given rcp, the double nearest 1 / den, for integers held
+// exactly in doubles with 0 <= num < 2^52, 0 < den < 2^31 and num / den <=
+// 2^31 - 1: num * rcp is within (num / den) 2^-52 (< 2^-21) of num / den, so
+// it stays below 2^31 and its truncation is off by at most one, which one step
+// corrects; the step's products stay below 2^53, so they and its comparisons
+// are exact.  Multiplies where a division and 64-bit integer products would
+// be: a double division is a chain of a dozen dependent instructions on the
+// GPU and a 64-bit product several quarter-rate ones, and this arithmetic sits
+// on the path of every worker's start and of the fix-up (its two worker_of
+// calls took about 1 us of a call with divisions).
+KVP_SPLIT_HD inline int64_t div_floor_rcp_d(double num, double den, double rcp) {
+    int64_t q = (int64_t)(int32_t)(num * rcp);
+    if ((double)q * den > num) {
         --q;
-    } else if ((q + 1) * den <= num) {
+    } else if ((double)(q + 1) * den <= num) {
         ++q;
     }
     return q;
 }
+KVP_SPLIT_HD inline int64_t div_floor_rcp(int64_t num, int64_t den, double rcp) {
+    return div_floor_rcp_d((double)num, (double)den, rcp);
+}
 
+// C(w) and cum(w) for 0 <= w <= W <= kMaxSplitWorkers (and the host check's
+// odd weights and counts): every product and sum stays far below 2^31.
 KVP_SPLIT_HD inline int64_t parity_weight(int64_t w, SliceWeights k) {
-    return k.even * ((w + 1) / 2) + k.odd * (w / 2);
+    const int32_t v = (int32_t)w;
+    return (int64_t)((int32_t)k.even * ((v + 1) >> 1) + (int32_t)k.odd * (v >> 1));
 }
 KVP_SPLIT_HD inline int64_t cum_weight(int64_t w, int64_t W, SliceWeights k) {
-    const int64_t ch = parity_weight(w < W / 2 ? w : W / 2, k);
-    return k.lead * ch + k.trail * (parity_weight(w, k) - ch);
+    const int32_t ch = (int32_t)parity_weight(w < W / 2 ? w : W / 2, k);
+    return (int64_t)((int32_t)k.lead * ch + (int32_t)k.trail * ((int32_t)parity_weight(w, k) - ch));
 }
 
 // One launch's split: W workers, the weights, cum(W), and the reciprocals of
@@ -137,9 +146,10 @@ KVP_SPLIT_HD inline int64_t parity_inverse(int64_t Y, const SplitConsts& s) {
     const int64_t p = div_floor_rcp(Y, pair, s.rcp_pair);
     return 2 * p + (Y - p * pair >= s.k.even ? 1 : 0);
 }
-// T cum(w) < 2^52 (T < kMaxSplitPositions, cum(W) < 2^21), quotient <= T < 2^31
+// T cum(w) < 2^52 (T < kMaxSplitPositions, cum(W) < 2^21) is exact as a
+// double product; the quotient is at most T < 2^31
 KVP_SPLIT_HD inline int64_t slice_start(int64_t w, int64_t T, const SplitConsts& s) {
-    return div_floor_rcp(T * cum_weight(w, s.W, s.k), s.cum_W, s.rcp_cum_W);
+    return div_floor_rcp_d((double)T * (double)cum_weight(w, s.W, s.k), (double)s.cum_W, s.rcp_cum_W);
 }
 
 // Worker whose slice holds tile t (0 <= t < T; rcp_T the double nearest
@@ -148,7 +158,7 @@ KVP_SPLIT_HD inline int64_t slice_start(int64_t w, int64_t T, const SplitConsts&
 // Below the first half's total lead C(W/2) that is C(w) <= floor(X / lead);
 // above it C(w) <= C(W/2) + floor((X - lead C(W/2)) / trail).
 KVP_SPLIT_HD inline int64_t worker_of(int64_t t, int64_t T, double rcp_T, const SplitConsts& s) {
-    const int64_t X = div_floor_rcp((t + 1) * s.cum_W - 1, T, rcp_T);
+    const int64_t X = div_floor_rcp_d((double)(t + 1) * (double)s.cum_W - 1.0, (double)T, rcp_T);
     const int64_t ch = parity_weight(s.W / 2, s.k);
     const int64_t w = X < s.k.lead * ch ? parity_inverse(div_floor_rcp(X, s.k.lead, s.rcp_lead), s)
                                         : parity_inverse(ch + div_floor_rcp(X - s.k.lead * ch, s.k.trail, s.rcp_trail), s);

@@ -173,11 +173,11 @@ void check_div_floor() {
 }
 
 // floor division by a multiply with the reciprocal: exact over its whole
-// domain (num < 2^53, den < 2^31, quotient <= 2^31 - 1), exact multiples and
+// domain (num < 2^52, den < 2^31, quotient <= 2^31 - 1), exact multiples and
 // remainders of den - 1 included, against integer division
 void check_div_floor_rcp() {
     std::mt19937_64 rng(11);
-    const int64_t kQMax = ((int64_t)1 << 31) - 1, kNumMax = ((int64_t)1 << 53) - 1;
+    const int64_t kQMax = ((int64_t)1 << 31) - 1, kNumMax = ((int64_t)1 << 52) - 1;
     for (int i = 0; i < 4000000; ++i) {
         int64_t den;
         switch (i % 4) {
