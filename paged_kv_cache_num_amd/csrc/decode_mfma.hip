@@ -965,21 +965,24 @@ __device__ __forceinline__ float* record_ptr(const DecodeArgs& a, int64_t slot) 
 // outside the pool is skipped, as by the scatter.  Items are numbered
 // ((seq * 2 + {K,V}) * Hkv + head) * kRC + chunk, one 16-byte chunk each.
 __device__ __forceinline__ void append_scatter_waves(const DecodeArgs& a, int64_t x, int64_t nx) {
-    const int64_t per_seq = 2LL * a.num_kv_heads * kRC;
-    const int64_t items = (int64_t)a.num_seqs * per_seq;
-    for (int64_t item = x * kWave + threadIdx.x; item < items; item += nx * kWave) {
-        const int64_t i = item / per_seq;
-        const int64_t rem = item - i * per_seq;
-        const int which = (int)(rem / ((int64_t)a.num_kv_heads * kRC));
-        const int64_t rem2 = rem - (int64_t)which * a.num_kv_heads * kRC;
-        const int h = (int)(rem2 / kRC);
-        const int ch = (int)(rem2 - (int64_t)h * kRC);
+    // item ((seq * 2 + which) * Hkv + h) * kRC + chunk, in 32 bits (at most 1024 sequences);
+    // block sizes are powers of two
+    static_assert(kRC == 16, "a row is 16 chunks of 16 bytes");
+    const int H = a.num_kv_heads;
+    const int bshift = __builtin_ctz((unsigned)a.block_size);
+    const int items = a.num_seqs * 2 * H * kRC;
+    for (int item = (int)x * kWave + (int)threadIdx.x; item < items; item += (int)nx * kWave) {
+        const int ch = item & (kRC - 1);
+        const int q = (item >> 4) / H;   // seq * 2 + which (kRC = 16 chunks a row)
+        const int h = (item >> 4) - q * H;
+        const int which = q & 1;
+        const int64_t i = q >> 1;
         const int L = clamp_len(a.lens[i], a.max_context);
         if (L == 0) continue;
         const int pos = L - 1;
-        const int64_t block = a.tables[i * (int64_t)a.max_blocks + pos / a.block_size];
+        const int64_t block = a.tables[i * (int64_t)a.max_blocks + (pos >> bshift)];
         if (block < 0 || block >= a.num_blocks) continue;
-        const int64_t dst = ((block * a.num_kv_heads + h) * a.block_size + pos % a.block_size) * kRC + ch;
+        const int64_t dst = ((block * H + h) * a.block_size + (pos & (a.block_size - 1))) * kRC + ch;
         const int64_t src = (i * a.num_kv_heads + h) * kRC + ch;
         const uint4* from = reinterpret_cast<const uint4*>(which == 0 ? a.k_append : a.v_append);
         uint4* to = const_cast<uint4*>(reinterpret_cast<const uint4*>(which == 0 ? a.k_layer : a.v_layer));
@@ -1065,29 +1068,32 @@ constexpr int kAppendFp8Rows = 4;
 __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x, int64_t nx) {
     const int lane = threadIdx.x;
     const int H = a.num_kv_heads;
-    const int64_t items = (int64_t)a.num_seqs * 2 * H;
-    for (int64_t i0 = x * kAppendFp8Rows; i0 < items; i0 += nx * kAppendFp8Rows) {
+    const int bshift = __builtin_ctz((unsigned)a.block_size);   // block sizes are powers of two
+    // items (sequence, K or V, KV head) in 32 bits: at most 1024 sequences
+    const int items = a.num_seqs * 2 * H;
+    for (int i0 = (int)x * kAppendFp8Rows; i0 < items; i0 += (int)nx * kAppendFp8Rows) {
         int L[kAppendFp8Rows];
         int64_t seq[kAppendFp8Rows];
         int which[kAppendFp8Rows], h[kAppendFp8Rows];
 #pragma unroll
         for (int u = 0; u < kAppendFp8Rows; ++u) {
-            const int64_t item = i0 + u < items ? i0 + u : items - 1;
-            seq[u] = item / (2 * H);
-            which[u] = (int)((item / H) & 1);
-            h[u] = (int)(item - (seq[u] * 2 + which[u]) * H);
+            const int item = i0 + u < items ? i0 + u : items - 1;
+            const int r = item / H;   // 2 seq + which
+            seq[u] = r >> 1;
+            which[u] = r & 1;
+            h[u] = item - r * H;
             L[u] = i0 + u < items ? clamp_len(a.lens[seq[u]], a.max_context) : 0;
         }
         int64_t block[kAppendFp8Rows];
 #pragma unroll
         for (int u = 0; u < kAppendFp8Rows; ++u)
-            block[u] = L[u] > 0 ? a.tables[seq[u] * (int64_t)a.max_blocks + (L[u] - 1) / a.block_size] : -1;
+            block[u] = L[u] > 0 ? a.tables[seq[u] * (int64_t)a.max_blocks + ((L[u] - 1) >> bshift)] : -1;
         uint32_t w[kAppendFp8Rows];
         float stored[kAppendFp8Rows];
 #pragma unroll
         for (int u = 0; u < kAppendFp8Rows; ++u) {
             const bool ok = block[u] >= 0 && block[u] < a.num_blocks;   // wave-uniform
-            const bool opens = (L[u] - 1) % a.block_size == 0;
+            const bool opens = ((L[u] - 1) & (a.block_size - 1)) == 0;
             const float* sp = which[u] == 0 ? a.k_scale : a.v_scale;
             w[u] = ok ? reinterpret_cast<const uint32_t*>(which[u] == 0 ? a.k_append : a.v_append)
                             [(seq[u] * H + h[u]) * (kD / 2) + lane]
@@ -1097,7 +1103,7 @@ __device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x,
 #pragma unroll
         for (int u = 0; u < kAppendFp8Rows; ++u) {
             if (!(block[u] >= 0 && block[u] < a.num_blocks)) continue;   // wave-uniform
-            const int j = (L[u] - 1) % a.block_size;
+            const int j = (L[u] - 1) & (a.block_size - 1);
             float sc = stored[u];
             if (j == 0) {
                 sc = e4m3_block_scale(wave_max(abs_max2(w[u], 0.0f)));
