@@ -1139,8 +1139,11 @@ __device__ __forceinline__ void fp8_rows_waves(const DecodeArgs& a, int64_t x, i
     r.H = a.num_kv_heads;
     r.num_slots = (int64_t)a.num_blocks * a.block_size;
     const int64_t items = (a.num_rows + 15) / 16 * a.num_kv_heads;
-    for (int64_t item = x; item < items; item += nx)
-        fp8_store_chunk(r, item / r.H * 16, (int)(item % r.H), threadIdx.x);
+    const bool narrow = items < ((int64_t)1 << 31);   // the usual case: a 32-bit division
+    for (int64_t item = x; item < items; item += nx) {
+        const int64_t c = narrow ? (int64_t)((uint32_t)item / (uint32_t)r.H) : item / r.H;   // 16-token chunk
+        fp8_store_chunk(r, c * 16, (int)(item - c * r.H), threadIdx.x);
+    }
 }
 
 // ---------------------------------------------------------------------------
