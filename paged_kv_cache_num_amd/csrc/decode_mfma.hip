@@ -559,8 +559,10 @@ __device__ __forceinline__ void init_state(State& st) {
 // whether it sees the old or the new row.
 struct AppendRow {
     bool active;
+    bool store;           // FP8 pools: the walk also stores the row (codes and, opening a block, its scales)
     int tok0;             // first token of the block holding position L - 1
     int j;                // (L - 1) % 16: the row within its 16-token tile
+    int brow;             // (L - 1) % B: the row within its block
     bool opens;           // (L - 1) % B == 0: the row is row 0 of its block
     const uint4* krow;    // the new K row (16 chunks)
     const uint4* vrow;
@@ -585,16 +587,28 @@ __device__ __forceinline__ void append_into(Tile& t, const AppendRow& app, const
 // dims 32r + 4m .. +3 (m = 0..7) from lane 16r + 2m, V dims 8n .. 8n+7 from
 // lanes 4n and 4n + 2.  When the row is row 0 of its block (app.opens) it
 // alone sets the block's scales, which then replace the scales read for the
-// block (the pool side writes them concurrently).  kscale / vscale are the
-// scales of the block holding the row (with 8-token blocks, the tile's half).
+// block.  kscale / vscale are the scales of the block holding the row (with
+// 8-token blocks, the tile's half).  With app.store the wave also stores the
+// row's codes at kdst / vdst (lane l: dims 2l, 2l + 1, as fp8_store_row) and,
+// opening the block, its scales at ksd / vsd: the one wave that walks a (sequence,
+// KV head)'s last tile is the pool side of its append.
 __device__ __forceinline__ void append_into_fp8(TileF8& t, const AppendRow& app, uint32_t kw, uint32_t vw,
-                                                const WalkCtx& c, float& kscale, float& vscale) {
+                                                const WalkCtx& c, float& kscale, float& vscale, uint16_t* kdst,
+                                                uint16_t* vdst, float* ksd, float* vsd) {
     if (app.opens) {   // wave-uniform
         kscale = e4m3_block_scale(wave_max(abs_max2(kw, 0.0f)));
         vscale = e4m3_block_scale(wave_max(abs_max2(vw, 0.0f)));
     }
     const uint32_t k2 = bf16x2_to_e4m3x2(kw, kscale);   // codes of dims 2l, 2l + 1
     const uint32_t v2 = bf16x2_to_e4m3x2(vw, vscale);
+    if (app.store) {   // wave-uniform
+        kdst[c.lane] = (uint16_t)k2;
+        vdst[c.lane] = (uint16_t)v2;
+        if (app.opens && c.lane == 0) {
+            *ksd = kscale;
+            *vsd = vscale;
+        }
+    }
     const uint32_t k4 = k2 | ((uint32_t)__shfl_down((int)k2, 1, kWave) << 16);   // even lanes: dims 2l .. 2l+3
     const uint32_t v4 = v2 | ((uint32_t)__shfl_down((int)v2, 1, kWave) << 16);
     uint32_t kd[8];
@@ -770,10 +784,22 @@ __device__ __forceinline__ void walk_policy(State& st, typename TileOf<kFp8>::ty
                         vsc1 = readlane_f(vs_l1, ks);
                     }
                     if (app.active && tok == app.tok0 && row_in_pool(tv0, tv1, k + s, app.j)) {
-                        if (c.pair8 && app.j >= 8)
-                            append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc1, vsc1);
+                        const bool hi = c.pair8 && app.j >= 8;   // B = 8: the tile's second block
+                        uint16_t *kd = nullptr, *vd = nullptr;
+                        float *ksd = nullptr, *vsd = nullptr;
+                        if (app.store) {
+                            const size_t blk = (uint32_t)__builtin_amdgcn_readlane(hi ? tv1 : tv0, k + s);
+                            // 16-byte chunks to the block's rows of this head, then 64 code pairs a row
+                            const size_t at = (blk * c.block_stride + c.head_off) * 8 + (size_t)app.brow * (kD / 2);
+                            kd = reinterpret_cast<uint16_t*>(const_cast<uint4*>(c.kpool)) + at;
+                            vd = reinterpret_cast<uint16_t*>(const_cast<uint4*>(c.vpool)) + at;
+                            ksd = const_cast<float*>(c.ksc) + blk * c.nkvh;
+                            vsd = const_cast<float*>(c.vsc) + blk * c.nkvh;
+                        }
+                        if (hi)
+                            append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc1, vsc1, kd, vd, ksd, vsd);
                         else
-                            append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc, vsc);
+                            append_into_fp8(tt[s], app, new_kw, new_vw, c, ksc, vsc, kd, vd, ksd, vsd);
                     }
                     // lane (r, n) holds the scores and probabilities of tokens 4r .. 4r+3
                     const bool second = c.pair8 && c.r >= 2;
@@ -841,7 +867,9 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_bf16_mfma_kernel(Decode
     const int nk = first < b_end ? (b_end - first + kWaves - 1) / kWaves : 0;
     AppendRow none;
     none.active = false;
+    none.store = false;
     none.opens = false;
+    none.brow = 0;
     none.krow = none.vrow = nullptr;
     typename TileOf<kFp8>::type tt[2];
     walk<G, 2, kFp8>(st, tt, false, qb, a.tables + (size_t)seq * a.max_blocks, kWaves, nk, first, L, c, none);
@@ -1051,68 +1079,6 @@ __device__ __forceinline__ void rows_scatter_waves(const DecodeArgs& a, int64_t 
             store(c1);
             store(c2);
             store(c3);
-        }
-    }
-}
-
-// The same for FP8 pools: (sequence, {K,V}, KV head) rows, quantized with
-// their block's scale; a row at position 0 of its block sets that scale from
-// itself alone first (as fp8_store_row).  Wave x takes four consecutive rows
-// at a time, x * 4 .. x * 4 + 3, then x * 4 + 4 nx, ...; the lengths, table
-// entries and rows of the four are loaded together.  With two FP8 workers on
-// every SIMD these waves only find a slot as workers finish, so their time
-// is the tail of the launch: one row at a time (three dependent loads each)
-// they took up to 29 us on the 70B-shaped step.
-constexpr int kAppendFp8Rows = 4;
-
-__device__ __forceinline__ void append_fp8_waves(const DecodeArgs& a, int64_t x, int64_t nx) {
-    const int lane = threadIdx.x;
-    const int H = a.num_kv_heads;
-    const int bshift = __builtin_ctz((unsigned)a.block_size);   // block sizes are powers of two
-    // items (sequence, K or V, KV head) in 32 bits: at most 1024 sequences
-    const int items = a.num_seqs * 2 * H;
-    for (int i0 = (int)x * kAppendFp8Rows; i0 < items; i0 += (int)nx * kAppendFp8Rows) {
-        int L[kAppendFp8Rows];
-        int64_t seq[kAppendFp8Rows];
-        int which[kAppendFp8Rows], h[kAppendFp8Rows];
-#pragma unroll
-        for (int u = 0; u < kAppendFp8Rows; ++u) {
-            const int item = i0 + u < items ? i0 + u : items - 1;
-            const int r = item / H;   // 2 seq + which
-            seq[u] = r >> 1;
-            which[u] = r & 1;
-            h[u] = item - r * H;
-            L[u] = i0 + u < items ? clamp_len(a.lens[seq[u]], a.max_context) : 0;
-        }
-        int64_t block[kAppendFp8Rows];
-#pragma unroll
-        for (int u = 0; u < kAppendFp8Rows; ++u)
-            block[u] = L[u] > 0 ? a.tables[seq[u] * (int64_t)a.max_blocks + ((L[u] - 1) >> bshift)] : -1;
-        uint32_t w[kAppendFp8Rows];
-        float stored[kAppendFp8Rows];
-#pragma unroll
-        for (int u = 0; u < kAppendFp8Rows; ++u) {
-            const bool ok = block[u] >= 0 && block[u] < a.num_blocks;   // wave-uniform
-            const bool opens = ((L[u] - 1) & (a.block_size - 1)) == 0;
-            const float* sp = which[u] == 0 ? a.k_scale : a.v_scale;
-            w[u] = ok ? reinterpret_cast<const uint32_t*>(which[u] == 0 ? a.k_append : a.v_append)
-                            [(seq[u] * H + h[u]) * (kD / 2) + lane]
-                      : 0u;
-            stored[u] = (ok && !opens) ? sp[block[u] * H + h[u]] : 1.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < kAppendFp8Rows; ++u) {
-            if (!(block[u] >= 0 && block[u] < a.num_blocks)) continue;   // wave-uniform
-            const int j = (L[u] - 1) & (a.block_size - 1);
-            float sc = stored[u];
-            if (j == 0) {
-                sc = e4m3_block_scale(wave_max(abs_max2(w[u], 0.0f)));
-                if (lane == 0) const_cast<float*>(which[u] == 0 ? a.k_scale : a.v_scale)[block[u] * H + h[u]] = sc;
-            }
-            uint16_t* dst = const_cast<uint16_t*>(
-                                reinterpret_cast<const uint16_t*>(which[u] == 0 ? a.k_layer : a.v_layer)) +
-                            ((block[u] * H + h[u]) * a.block_size + j) * (kD / 2);
-            dst[lane] = (uint16_t)bf16x2_to_e4m3x2(w[u], sc);
         }
     }
 }
@@ -1357,8 +1323,7 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         }
         const int64_t x = w - W;
         if (x < a.append_waves) {   // decode append: the pool side
-            if constexpr (kFp8) append_fp8_waves(a, x, a.append_waves);
-            else append_scatter_waves(a, x, a.append_waves);
+            if constexpr (!kFp8) append_scatter_waves(a, x, a.append_waves);   // FP8: the walk stores the rows
         } else {
             const int64_t nrow_waves = (int64_t)gridDim.x - W - a.append_waves;
             if constexpr (kFp8) fp8_rows_waves(a, x - a.append_waves, nrow_waves);
@@ -1514,9 +1479,11 @@ __global__ __launch_bounds__(kWave) void decode_bf16_streamk_kernel(DecodeArgs a
         // the piece that ends with the sequence's last block takes the appended row
         AppendRow app;
         app.active = a.k_append != nullptr && b + n_here == nblk;
+        app.store = kFp8;   // FP8: the pool side of the append is this walk (no append waves)
         app.tok0 = (nblk - 1) * kTileTokens;
         app.j = (L - 1) % kTileTokens;
-        app.opens = (L - 1) % (kAnyB ? a.block_size : kTileTokens) == 0;
+        app.brow = (L - 1) & ((kAnyB ? a.block_size : kTileTokens) - 1);   // block sizes are powers of two
+        app.opens = app.brow == 0;
         app.krow = reinterpret_cast<const uint4*>(a.k_append) + ((size_t)seq * Hkv + kv) * kRC;
         app.vrow = reinterpret_cast<const uint4*>(a.v_append) + ((size_t)seq * Hkv + kv) * kRC;
         // The next piece of this slice, if it starts a new (sequence, KV head),
@@ -1700,7 +1667,9 @@ __global__ __launch_bounds__(kWave) void decode_partitions_kernel(DecodeArgs a) 
 
     AppendRow none;
     none.active = false;
+    none.store = false;
     none.opens = false;
+    none.brow = 0;
     none.krow = none.vrow = nullptr;
     bool pf_valid = false;   // table entries of the next partition fetched ahead
     int pf_kv = -1, pf_b = -1, pf_tv0 = 0, pf_tv1 = 0, pf_nb = 0;
@@ -2036,11 +2005,14 @@ hipError_t launch_streamk_walk(const DecodeArgs& a_in, int group, int workers, h
     if (a.shared_tiles > 0) {   // the prefix walks: (column group, KV head, part)
         extra = prefix_column_groups(a.num_seqs, group) * a.num_kv_heads * a.prefix_parts;
     } else {
-        if (a.k_append) {
-            // bf16: beside the workers from the start; FP8: at the launch's tail (see append_fp8_waves)
-            const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * (kFp8 ? 1 : kRC);
-            const int64_t per_wave = kFp8 ? kAppendFp8Rows : 8 * kWave;
-            const int64_t cap = kFp8 ? 1024 : 256;
+        if (a.k_append && !kFp8) {
+            // bf16: beside the workers from the start.  FP8 pools: the walk that
+            // takes a (sequence, KV head)'s last tile stores the row (AppendRow::store);
+            // waves past the workers would only run at the launch's tail, once FP8
+            // workers free their wave slots (8B-shaped step 71.0 us with them)
+            const int64_t items = (int64_t)a.num_seqs * 2 * a.num_kv_heads * kRC;
+            const int64_t per_wave = 8 * kWave;
+            const int64_t cap = 256;
             extra = (items + per_wave - 1) / per_wave;
             extra = extra < 1 ? 1 : (extra > cap ? cap : extra);
             a.append_waves = (int32_t)extra;
