@@ -325,8 +325,8 @@ kv_status paged_attention_decode(kv_pool_t pool, int32_t layer, void* out, const
  * other modes run a small scatter kernel first.  A block index outside the pool
  * is skipped, as by reshape_and_cache.  FP8 pools: the row is quantized (a row
  * at position 0 of its block sets that block's scales from itself alone); in
- * the balanced mode the attention kernel does it, other modes run a small
- * append kernel first.
+ * the balanced mode the wave that walks the sequence's last tile of a KV head
+ * stores that head's row, other modes run a small append kernel first.
  */
 kv_status paged_attention_decode_append(kv_pool_t pool, int32_t layer, void* out, const void* q,
                                         const void* k_new, const void* v_new, const int32_t* block_tables,
